@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""E2-TTT chunk-update throughput on one MI355X.
+
+One step = one e2ttt_chunk_forward call over the whole workload (scalar
+kernels, fast-weight forward/backward at the chunk-start weights, both
+gradient aggregations, state transition and chunk outputs for every chunk of
+every (batch, head)), inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "E2-TTT chunk-update tokens/sec at 1 GPU + % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / packed VALU)
+PEAK_HBM_GBS = 8000.0
+LOOP_SRC = os.path.join(ROOT, "chunk_weight_rnn_amd", "csrc", "swiglu_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_loop_1p3b.json")
+
+
+def flops_per_token_head(cfg: synth.Config) -> dict:
+    """Algorithmic MFMA-able flops per token per head, split by stage."""
+    D, Hd = cfg.D, cfg.Hd
+    if cfg.kind == "swiglu":
+        return {"grad": 6 * D * Hd, "aggregate": 12 * D * Hd, "apply": 6 * D * Hd}
+    if cfg.kind == "mlp":
+        fwd = 4 * D * Hd if cfg.loss == "mse" else 2 * D * Hd
+        return {"grad": fwd + 2 * D * Hd, "aggregate": 8 * D * Hd, "apply": 4 * D * Hd}
+    return {"grad": 2 * D * D, "aggregate": 4 * D * D, "apply": 2 * D * D}
+
+
+def alg_bytes(cfg: synth.Config) -> int:
+    es = 2 if cfg.io_dtype == "bf16" else 4
+    BH = cfg.B * cfg.H
+    return BH * cfg.T * cfg.D * es * 4 + BH * cfg.T * 4 * 3 + BH * cfg.P * 4 * 4
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing on the library's stream)."""
+
+    def __init__(self, n: int):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.rt.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h)
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.rt.hipEventSynchronize(b) == 0
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def measured_traffic(loop_launch_bytes_alg: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        sha = hashlib.sha256(open(LOOP_SRC, "rb").read()).hexdigest()
+        if t.get("source_sha256") != sha:
+            return None
+        return float(t["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload (whole batch
+    rows: every head of one sequence), timed on the host cores."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    x = synth.make_inputs(cfg, seed=0)
+    f = lambda t: t.double().numpy()
+    rows, wall = 0, 0.0
+    for b in range(cfg.B):
+        sl = {n: f(t[b:b + 1]) for n, t in x.items()}
+        t0 = time.perf_counter()
+        oracle.chunk_forward(cfg.kind, cfg.loss, sl["q"], sl["k"], sl["v"], sl["eta"], sl["alpha"], sl["beta"],
+                             sl["W0"], sl["M0"], cfg.chunk, cfg.Hd)
+        wall += time.perf_counter() - t0
+        rows += 1
+        if wall >= budget_s:
+            break
+    tokens = rows * cfg.T
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} of {cfg.B} batch rows (all {cfg.H} heads x {cfg.T} tokens each), "
+                      f"fp64 numpy closed form, {wall:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="swiglu_1p3b", choices=list(synth.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the (batch, head) recurrences would shard across GPUs without communication).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import chunk_weight_rnn_amd as e2
+    lib = e2.library()
+
+    cfg = synth.CONFIGS[args.config]
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
+    out = torch.empty_like(x["q"])
+    W = torch.empty_like(x["W0"])
+    M = torch.empty_like(x["M0"])
+    desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
+    ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    hev = HipEvents(4 * max(args.steps, 1))
+
+    def step(i=None):
+        evs = None
+        if i is not None:
+            evs = (ctypes.c_void_p * 4)(*hev.ev[4 * i:4 * i + 4])
+        st = lib.e2ttt_chunk_forward_events(ctypes.byref(desc), p(x["q"]), p(x["k"]), p(x["v"]), p(x["eta"]),
+                                            p(x["alpha"]), p(x["beta"]), p(x["W0"]), p(x["M0"]), p(out), p(W),
+                                            p(M), p(ws), ctypes.c_size_t(ws_bytes), hs, evs)
+        if st != 0:
+            raise e2.E2TTTError("e2ttt_chunk_forward_events", st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = 1e3 * wall / args.steps
+    stages = {"logscan": [], "loop": [], "apply": []}
+    for i in range(args.steps):
+        e = hev.ev[4 * i:4 * i + 4]
+        stages["logscan"].append(hev.elapsed_ms(e[0], e[1]))
+        stages["loop"].append(hev.elapsed_ms(e[1], e[2]))
+        stages["apply"].append(hev.elapsed_ms(e[2], e[3]))
+    st_ms = {k: sum(v) / len(v) for k, v in stages.items()}
+
+    tokens = cfg.B * cfg.T
+    fpt = flops_per_token_head(cfg)
+    heads_tokens = cfg.B * cfg.H * cfg.T
+    peak = PEAK_BF16_TFLOPS if cfg.io_dtype == "bf16" and cfg.kind == "swiglu" else PEAK_F32_TFLOPS
+    loop_flops = (fpt["grad"] + fpt["aggregate"]) * heads_tokens
+    loop_tflops = loop_flops / (st_ms["loop"] * 1e-3) / 1e12
+    call_flops = sum(fpt.values()) * heads_tokens
+    call_tflops = call_flops / (ms_step * 1e-3) / 1e12
+    traffic = measured_traffic(0.0) if args.config == "swiglu_1p3b" else None
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.io_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.notes}", "kind": cfg.kind, "loss": cfg.loss, "B": cfg.B,
+                   "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk, "io": cfg.io_dtype,
+                   "state": "f32"},
+        "roofline": {"bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
+                     "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,
+                     "traffic": traffic,
+                     "per_launch": f"{(fpt['grad'] + fpt['aggregate'])} flop/token/head x {heads_tokens} "
+                                   f"token-heads = {loop_flops:.4g} flop"},
+        "whole_call": {"tflops": call_tflops, "frac_of_peak": call_tflops / peak,
+                       "hbm_alg_GBs": alg_bytes(cfg) / (ms_step * 1e-3) / 1e9},
+        "stages_ms": st_ms,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,137 @@
+"""MI355X (gfx950) E2-TTT chunk update: Python binding of libe2ttt.so.
+
+Argument marshalling only: every step of the chunk update runs in the HIP
+kernels behind the C ABI (include/e2ttt.h).  PyTorch supplies device memory
+and the current HIP stream.  There is no CPU fallback: without the built
+library, or with tensors that are not on a GPU, every entry point raises.
+
+Method: "Rethinking Expressivity and Efficiency in Test-Time Training"
+(E2-TTT).  For each chunk, gradients of the fast-weight loss at the
+chunk-start weights feed a closed-form transition that reproduces the
+chunk-end weights W and momentum M of the per-token recurrence
+M_t = beta_t M_{t-1} + eta_t g_t, W_t = alpha_t W_{t-1} - M_t, and the chunk
+output comes from the chunk-start weights.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import E2TTTError, FLAG_FORCE_GENERIC, make_desc
+
+__all__ = ["chunk_forward", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
+           "library"]
+
+
+def library():
+    return _lib.load()
+
+
+def _io_name(t: torch.Tensor) -> str:
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def param_count(kind: str, D: int, Hd: int = 0) -> int:
+    return int(library().e2ttt_param_count(ctypes.byref(make_desc(kind, "mse", "f32", 1, 1, 0, D, Hd, 1))))
+
+
+def workspace_size(kind, loss, io_dtype, B, H, T, D, Hd, chunk, flags=0) -> int:
+    d = make_desc(kind, loss, io_dtype, B, H, T, D, Hd, chunk, flags)
+    n = library().e2ttt_workspace_size(ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise E2TTTError("e2ttt_workspace_size", 1)
+    return int(n)
+
+
+def path(kind, loss, io_dtype, B, H, T, D, Hd, chunk, flags=0) -> int:
+    return int(library().e2ttt_path(ctypes.byref(make_desc(kind, loss, io_dtype, B, H, T, D, Hd, chunk, flags))))
+
+
+def validate(desc, ptrs) -> int:
+    arr = (ctypes.c_void_p * 11)(*[ctypes.c_void_p(p) for p in ptrs])
+    return int(library().e2ttt_validate(ctypes.byref(desc), arr))
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
+                  out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False, stream=None):
+    """Run the chunk update; returns (out, W_end, M_end).
+
+    q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
+    eta, alpha, beta: [B, H, T] float32; W0, M0: [B, H, P] float32.
+    ``W_end=W0`` / ``M_end=M0`` update the state in place.
+    """
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("eta", eta), ("alpha", alpha), ("beta", beta),
+                    ("W0", W0), ("M0", M0)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    io = _io_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("eta", eta), ("alpha", alpha), ("beta", beta), ("W0", W0), ("M0", M0)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    B, H, T, D = q.shape
+    flags = FLAG_FORCE_GENERIC if force_generic else 0
+    desc = make_desc(kind, loss, io, B, H, T, D, Hd, chunk, flags)
+    P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
+    if tuple(W0.shape) != (B, H, P) or tuple(M0.shape) != (B, H, P):
+        raise ValueError(f"W0/M0 must have shape {(B, H, P)}")
+    if tuple(eta.shape) != (B, H, T) or alpha.shape != eta.shape or beta.shape != eta.shape:
+        raise ValueError(f"eta/alpha/beta must have shape {(B, H, T)}")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    if out is None:
+        out = torch.empty_like(q)
+    if W_end is None:
+        W_end = torch.empty_like(W0)
+    if M_end is None:
+        M_end = torch.empty_like(M0)
+    ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
+    if ws_bytes == ctypes.c_size_t(-1).value:
+        raise E2TTTError("e2ttt_workspace_size", 1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.e2ttt_chunk_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha),
+                                 _ptr(beta), _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end),
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(stream))
+    if st != 0:
+        raise E2TTTError("e2ttt_chunk_forward", st)
+    return out, W_end, M_end
+
+
+def logscan(eta, alpha, beta, *, chunk: int, stream=None):
+    """The scalar-kernel step alone: returns (cM, cW, scal[B, H, T/chunk, 4])."""
+    lib = library()
+    for name, t in (("eta", eta), ("alpha", alpha), ("beta", beta)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    B, H, T = eta.shape
+    if chunk < 1 or T % chunk:
+        raise ValueError("T must be a multiple of chunk")
+    cM = torch.empty_like(eta)
+    cW = torch.empty_like(eta)
+    scal = torch.empty(B, H, T // chunk, 4, dtype=torch.float32, device=eta.device)
+    desc = make_desc("linear", "mse", "f32", B, H, T, 1, 0, chunk)
+    st = lib.e2ttt_logscan(ctypes.byref(desc), _ptr(eta), _ptr(alpha), _ptr(beta), _ptr(cM), _ptr(cW),
+                           _ptr(scal), _stream_handle(stream))
+    if st != 0:
+        raise E2TTTError("e2ttt_logscan", st)
+    return cM, cW, scal

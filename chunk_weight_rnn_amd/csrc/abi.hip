@@ -1,0 +1,205 @@
+// Host side of the C ABI declared in include/e2ttt.h: descriptor and pointer
+// validation (pure host code, callable without a GPU), workspace layout and
+// dispatch of the device kernels on the caller's stream.
+#include <stdint.h>
+
+#include "e2ttt_internal.h"
+
+namespace e2ttt {
+
+static bool desc_ok(const e2ttt_desc* d) {
+    if (!d) return false;
+    if (d->kind < E2TTT_LINEAR || d->kind > E2TTT_SWIGLU) return false;
+    if (d->loss < E2TTT_LOSS_MSE || d->loss > E2TTT_LOSS_NEGDOT) return false;
+    if (d->io_dtype < E2TTT_F32 || d->io_dtype > E2TTT_BF16) return false;
+    if (d->B < 0 || d->H < 0 || d->T < 0 || d->D < 1 || d->chunk < 1) return false;
+    if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
+    if (d->T % d->chunk != 0) return false;
+    // keep every product used for indexing far from int64 overflow
+    const int64_t lim = (int64_t)1 << 40;
+    if (d->B > lim || d->H > lim || d->T > lim || d->D > 65536 || d->Hd > 65536) return false;
+    if (d->B * d->H > lim || d->B * d->H * d->T > lim) return false;
+    return true;
+}
+
+static int path_of(const e2ttt_desc& d) {
+    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d)) return 1;
+    return 0;
+}
+
+static bool generic_supported(const e2ttt_desc& d) {
+    if (d.D > 256) return false;
+    if (d.kind != E2TTT_LINEAR && d.Hd > 1024) return false;
+    return true;
+}
+
+Workspace workspace_layout(const e2ttt_desc& d, int path) {
+    Workspace w{};
+    const size_t BH = (size_t)(d.B * d.H);
+    const size_t T = (size_t)d.T;
+    const size_t nc = (size_t)(d.T / d.chunk);
+    const size_t P = (size_t)e2ttt_param_count(&d);
+    size_t off = 0;
+    w.cM = off;
+    off += align_up(BH * T * sizeof(float));
+    w.cW = off;
+    off += align_up(BH * T * sizeof(float));
+    w.scal = off;
+    off += align_up(BH * nc * 4 * sizeof(float));
+    w.gacc = w.snap = off;
+    if (path == 0)
+        off += align_up(BH * 2 * P * sizeof(float));
+    else
+        off += align_up(BH * nc * P * 2);
+    w.total = (BH * T == 0) ? 0 : off;
+    return w;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+static bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace e2ttt
+
+using namespace e2ttt;
+
+extern "C" {
+
+int64_t e2ttt_param_count(const e2ttt_desc* d) {
+    if (!d) return -1;
+    switch (d->kind) {
+        case E2TTT_LINEAR: return d->D * d->D;
+        case E2TTT_MLP: return 2 * d->D * d->Hd;
+        case E2TTT_SWIGLU: return 3 * d->D * d->Hd;
+        default: return -1;
+    }
+}
+
+size_t e2ttt_workspace_size(const e2ttt_desc* d) {
+    if (!desc_ok(d)) return (size_t)-1;
+    return workspace_layout(*d, path_of(*d)).total;
+}
+
+int e2ttt_path(const e2ttt_desc* d) {
+    if (!desc_ok(d)) return -E2TTT_ERR_INVALID_ARG;
+    return path_of(*d);
+}
+
+int e2ttt_validate(const e2ttt_desc* d, const void* const ptrs[11]) {
+    if (!desc_ok(d) || !ptrs) return E2TTT_ERR_INVALID_ARG;
+    if (path_of(*d) == 0 && !generic_supported(*d)) return E2TTT_ERR_UNSUPPORTED;
+    const size_t BH = (size_t)(d->B * d->H);
+    const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
+    const size_t P = (size_t)e2ttt_param_count(d);
+    const size_t bytes[11] = {BH * d->T * d->D * es, BH * d->T * d->D * es, BH * d->T * d->D * es,
+                              BH * d->T * 4,         BH * d->T * 4,         BH * d->T * 4,
+                              BH * P * 4,            BH * P * 4,            BH * d->T * d->D * es,
+                              BH * P * 4,            BH * P * 4};
+    const size_t align[11] = {16, 16, 16, 4, 4, 4, 16, 16, 16, 16, 16};
+    for (int i = 0; i < 11; ++i) {
+        if (bytes[i] == 0) continue;
+        if (!ptrs[i]) return E2TTT_ERR_INVALID_ARG;
+        if ((uintptr_t)ptrs[i] % align[i]) return E2TTT_ERR_INVALID_ARG;
+    }
+    Range r[11];
+    for (int i = 0; i < 11; ++i) r[i] = {(uintptr_t)ptrs[i], (uintptr_t)ptrs[i] + bytes[i]};
+    // outputs: 8 = out, 9 = W_end, 10 = M_end
+    for (int o = 8; o < 11; ++o) {
+        if (bytes[o] == 0) continue;
+        for (int i = 0; i < 11; ++i) {
+            if (i == o || bytes[i] == 0) continue;
+            if (o == 9 && i == 6 && ptrs[9] == ptrs[6]) continue;   // W_end == W0: in place
+            if (o == 10 && i == 7 && ptrs[10] == ptrs[7]) continue;  // M_end == M0: in place
+            if (overlap(r[o], r[i])) return E2TTT_ERR_ALIAS;
+        }
+    }
+    return E2TTT_OK;
+}
+
+int e2ttt_chunk_forward(const e2ttt_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                        const float* alpha, const float* beta, const float* W0, const float* M0, void* out,
+                        float* W_end, float* M_end, void* workspace, size_t workspace_bytes, void* stream) {
+    return e2ttt_chunk_forward_events(d, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, workspace,
+                                      workspace_bytes, stream, nullptr);
+}
+
+int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                               const float* alpha, const float* beta, const float* W0, const float* M0, void* out,
+                               float* W_end, float* M_end, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const events[4]) {
+    const void* ptrs[11] = {q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end};
+    const int st = e2ttt_validate(d, ptrs);
+    if (st != E2TTT_OK) return st;
+    const int path = path_of(*d);
+    const Workspace ws = workspace_layout(*d, path);
+    if (ws.total > 0) {
+        if (!workspace || workspace_bytes < ws.total || (uintptr_t)workspace % kAlign) return E2TTT_ERR_WORKSPACE;
+        const Range wr{(uintptr_t)workspace, (uintptr_t)workspace + ws.total};
+        const size_t BH = (size_t)(d->B * d->H);
+        const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
+        const size_t P = (size_t)e2ttt_param_count(d);
+        const size_t bytes[11] = {BH * d->T * d->D * es, BH * d->T * d->D * es, BH * d->T * d->D * es,
+                                  BH * d->T * 4, BH * d->T * 4, BH * d->T * 4, BH * P * 4, BH * P * 4,
+                                  BH * d->T * d->D * es, BH * P * 4, BH * P * 4};
+        for (int i = 0; i < 11; ++i)
+            if (bytes[i] && overlap(wr, Range{(uintptr_t)ptrs[i], (uintptr_t)ptrs[i] + bytes[i]}))
+                return E2TTT_ERR_ALIAS;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t BH = d->B * d->H;
+    if (BH == 0) return E2TTT_OK;
+    const size_t P = (size_t)e2ttt_param_count(d);
+    if (d->T == 0) {
+        if (W_end != W0 && hipMemcpyAsync(W_end, W0, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        if (M_end != M0 && hipMemcpyAsync(M_end, M0, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        return E2TTT_OK;
+    }
+    char* wsb = (char*)workspace;
+    float* cM = (float*)(wsb + ws.cM);
+    float* cW = (float*)(wsb + ws.cW);
+    float* scal = (float*)(wsb + ws.scal);
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+        for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
+    if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
+    if (launch_logscan(BH, d->T, d->chunk, eta, alpha, beta, cM, cW, scal, s) != hipSuccess) return E2TTT_ERR_HIP;
+    if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
+    hipError_t e;
+    if (path == 1) {
+        e = launch_swiglu_mfma(*d, q, k, v, cM, cW, scal, W0, M0, out, W_end, M_end, wsb + ws.snap, s, ev[2]);
+    } else {
+        e = launch_generic(*d, q, k, v, cM, cW, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc), s);
+        if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
+    }
+    if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
+    return e == hipSuccess ? E2TTT_OK : E2TTT_ERR_HIP;
+}
+
+int e2ttt_logscan(const e2ttt_desc* d, const float* eta, const float* alpha, const float* beta, float* cM,
+                  float* cW, float* scal, void* stream) {
+    if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1 || d->T % d->chunk) return E2TTT_ERR_INVALID_ARG;
+    const int64_t BH = d->B * d->H;
+    if (BH * d->T == 0) return E2TTT_OK;
+    if (!eta || !alpha || !beta || !cM || !cW || !scal) return E2TTT_ERR_INVALID_ARG;
+    return launch_logscan(BH, d->T, d->chunk, eta, alpha, beta, cM, cW, scal, (hipStream_t)stream) == hipSuccess
+               ? E2TTT_OK
+               : E2TTT_ERR_HIP;
+}
+
+const char* e2ttt_status_string(int s) {
+    switch (s) {
+        case E2TTT_OK: return "ok";
+        case E2TTT_ERR_INVALID_ARG: return "invalid argument";
+        case E2TTT_ERR_UNSUPPORTED: return "unsupported shape";
+        case E2TTT_ERR_ALIAS: return "output aliases another buffer";
+        case E2TTT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case E2TTT_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/e2ttt.h"
+
+namespace e2ttt {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of the workspace sections for one call.
+struct Workspace {
+    size_t cM, cW, scal;  // logscan outputs (fp32)
+    size_t gacc;          // portable path: per-head gradient accumulators (fp32, 2*P)
+    size_t snap;          // MFMA path: bf16 chunk-start weight snapshots (B*H*nc*P)
+    size_t total;
+};
+
+Workspace workspace_layout(const e2ttt_desc& d, int path);
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, const float* eta, const float* alpha,
+                          const float* beta, float* cM, float* cW, float* scal, hipStream_t s);
+
+hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v,
+                          const float* cM, const float* cW, const float* scal, const float* W0,
+                          const float* M0, void* out, float* W_end, float* M_end, float* gacc,
+                          hipStream_t s);
+
+// SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
+bool swiglu_mfma_supported(const e2ttt_desc& d);
+// ev_mid (may be null) is recorded between the chunk-loop and output launches.
+hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
+                              const float* cM, const float* cW, const float* scal, const float* W0,
+                              const float* M0, void* out, float* W_end, float* M_end, void* snap,
+                              hipStream_t s, hipEvent_t ev_mid);
+
+}  // namespace e2ttt

@@ -1,0 +1,162 @@
+/*
+ * e2ttt.h -- C ABI of the MI355X (gfx950) E2-TTT chunk-update library.
+ *
+ * Operation ("Rethinking Expressivity and Efficiency in Test-Time Training",
+ * E2-TTT; abstract, and the atlas summary's "Approach"): the fast weight W of
+ * every (batch, head) is updated token by token with per-token learning rate
+ * eta_t, momentum beta_t and decay alpha_t,
+ *
+ *     M_t = beta_t * M_{t-1} + eta_t * g_t,     W_t = alpha_t * W_{t-1} - M_t,
+ *
+ * where g_t is the gradient of token t's fast-weight loss taken at the weights
+ * the token's chunk started with.  The library evaluates the closed-form
+ * chunk transition that gives the exact chunk-end (W, M) of that recurrence
+ * (a momentum kernel and a weight kernel from log-space suffix sums of
+ * log alpha and log beta, then two coefficient-weighted gradient
+ * aggregations) and the chunk output y_t = f_{W_chunk_start}(q_t) (arxivlens
+ * "Limitations": the output stays fixed within a chunk).
+ *
+ * Fast weights (per head; k, q, v are D-vectors):
+ *   E2TTT_LINEAR  y = W k                         W [D][D]
+ *   E2TTT_MLP     y = W2 silu(W1 k)               W1 [Hd][D], W2 [D][Hd]
+ *   E2TTT_SWIGLU  y = (silu(k W1) * (k W3)) W2    W1, W3 [D][Hd], W2 [Hd][D]
+ * Losses: E2TTT_LOSS_MSE 0.5*||y - v||^2, E2TTT_LOSS_NEGDOT -<y, v>.
+ * The per-(b,h) parameter vector packs the matrices in the order listed,
+ * each row-major fp32: P = D*D, 2*D*Hd or 3*D*Hd floats.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or synchronises.  Work is queued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and runs
+ *     asynchronously.
+ *   - Return values report argument validation synchronously; a failed
+ *     kernel launch returns E2TTT_ERR_HIP.  No exception crosses the ABI.
+ *   - NaN/Inf in the inputs propagate; the hot path performs no checks.
+ *   - The library keeps no mutable global state; calls on different streams
+ *     may run concurrently as long as they do not share output or workspace
+ *     buffers.
+ */
+#ifndef E2TTT_H
+#define E2TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define E2TTT_API __attribute__((visibility("default")))
+#else
+#define E2TTT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { E2TTT_LINEAR = 0, E2TTT_MLP = 1, E2TTT_SWIGLU = 2 } e2ttt_kind;
+typedef enum { E2TTT_LOSS_MSE = 0, E2TTT_LOSS_NEGDOT = 1 } e2ttt_loss;
+typedef enum { E2TTT_F32 = 0, E2TTT_BF16 = 1 } e2ttt_dtype; /* dtype of q, k, v, out */
+
+typedef enum {
+    E2TTT_OK = 0,
+    E2TTT_ERR_INVALID_ARG = 1, /* bad enum, negative size, T % chunk != 0, null or misaligned pointer */
+    E2TTT_ERR_UNSUPPORTED = 2, /* shape outside what any kernel handles (e.g. D > 256, Hd > 1024) */
+    E2TTT_ERR_ALIAS = 3,       /* an output overlaps an input or another output */
+    E2TTT_ERR_WORKSPACE = 4,   /* workspace null or smaller than e2ttt_workspace_size() */
+    E2TTT_ERR_HIP = 5          /* a kernel launch failed */
+} e2ttt_status;
+
+/* flags */
+#define E2TTT_FLAG_FORCE_GENERIC 1 /* run the portable fp32 kernel even where the MFMA path applies */
+
+typedef struct {
+    int32_t kind;     /* e2ttt_kind */
+    int32_t loss;     /* e2ttt_loss */
+    int32_t io_dtype; /* e2ttt_dtype of q, k, v, out */
+    int32_t flags;    /* E2TTT_FLAG_* */
+    int64_t B, H, T;  /* batch, heads, tokens per sequence */
+    int64_t D;        /* head dim (k, q, v, out width) */
+    int64_t Hd;       /* hidden width of MLP / SwiGLU fast weights; ignored for LINEAR */
+    int64_t chunk;    /* tokens per chunk; T must be a multiple */
+} e2ttt_desc;
+
+/* Floats per (b, h) in the packed fast-weight vector; -1 for a bad desc. */
+E2TTT_API int64_t e2ttt_param_count(const e2ttt_desc* desc);
+
+/* Bytes of scratch e2ttt_chunk_forward needs for `desc` (0 when B*H*T == 0,
+ * (size_t)-1 for a bad desc).  Contents need not be initialised. */
+E2TTT_API size_t e2ttt_workspace_size(const e2ttt_desc* desc);
+
+/* Which device path e2ttt_chunk_forward takes: 0 = portable fp32 kernel,
+ * 1 = SwiGLU bf16 MFMA path; negative e2ttt_status for a bad desc. */
+E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
+
+/*
+ * Host-only validation of a call, touching no device memory (usable without
+ * a GPU).  ptrs[] holds, in order: q, k, v, eta, alpha, beta, W0, M0, out,
+ * W_end, M_end.  Returns E2TTT_OK or the first problem found:
+ *   - sizes: B, H, T >= 0; D >= 1; chunk >= 1; T % chunk == 0; Hd >= 1 for
+ *     MLP / SWIGLU; enums in range (E2TTT_ERR_INVALID_ARG);
+ *   - pointers: non-null when the tensor is non-empty, 16-byte aligned
+ *     (eta, alpha, beta: 4-byte aligned) (E2TTT_ERR_INVALID_ARG);
+ *   - shape support: E2TTT_ERR_UNSUPPORTED when neither device path handles
+ *     the shape (portable path: D <= 256 and Hd <= 1024);
+ *   - aliasing: W_end may equal W0 and M_end may equal M0 exactly (in-place
+ *     update); any other byte overlap between an output and an input or two
+ *     outputs is E2TTT_ERR_ALIAS.
+ */
+E2TTT_API int e2ttt_validate(const e2ttt_desc* desc, const void* const ptrs[11]);
+
+/*
+ * The chunk update over whole sequences (the hot path).
+ *   q, k, v   [B][H][T][D]  io_dtype, contiguous
+ *   eta, alpha, beta [B][H][T] fp32 (domain: eta >= 0, alpha, beta in [0, 1])
+ *   W0, M0    [B][H][P] fp32 chunk-0 fast weight and momentum
+ *   out       [B][H][T][D]  io_dtype: out_t = f_{W at t's chunk start}(q_t)
+ *   W_end, M_end [B][H][P] fp32 state after the last chunk (may be W0 / M0)
+ *   workspace device scratch of >= e2ttt_workspace_size(desc) bytes, 256-byte
+ *             aligned; clobbered.
+ * T == 0 copies W0 -> W_end and M0 -> M_end; B*H == 0 does nothing.
+ * Ragged tails (T % chunk != 0) are rejected with E2TTT_ERR_INVALID_ARG.
+ */
+E2TTT_API int e2ttt_chunk_forward(const e2ttt_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        const float* eta, const float* alpha, const float* beta,
+                        const float* W0, const float* M0,
+                        void* out, float* W_end, float* M_end,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * e2ttt_chunk_forward plus per-stage timing for profilers and benchmarks.
+ * `events` holds 4 hipEvent_t created by the caller (hipEventCreate); they
+ * are recorded on `stream` before the scalar-kernel launch, after it, after
+ * the chunk-loop launch and after the output launch, so
+ * hipEventElapsedTime(events[1], events[2]) is the chunk-loop kernel's
+ * duration.  events == NULL behaves exactly like e2ttt_chunk_forward.
+ */
+E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        const float* eta, const float* alpha, const float* beta,
+                        const float* W0, const float* M0,
+                        void* out, float* W_end, float* M_end,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const events[4]);
+
+/*
+ * The scalar-kernel step alone (per-subsystem parity).  For every chunk of
+ * every (b, h), from log-space suffix sums of log alpha and log beta:
+ *   cM[b][h][t] = eta_t * m_t,  m_t = prod_{s after t in its chunk} beta_s
+ *   cW[b][h][t] = eta_t * w_t,  w_t = sum_{tau >= t} alpha(tau:end] * beta(t:tau]
+ *   scal[b][h][c][0..3] = { prod alpha, prod beta, gamma = beta_first * w_first, 0 }
+ * eta, alpha, beta, cM, cW: [B][H][T] fp32; scal: [B][H][T/chunk][4] fp32.
+ * Only desc->B, H, T and chunk are read.
+ */
+E2TTT_API int e2ttt_logscan(const e2ttt_desc* desc, const float* eta, const float* alpha, const float* beta,
+                  float* cM, float* cW, float* scal, void* stream);
+
+/* Static, human-readable name of a status code. */
+E2TTT_API const char* e2ttt_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* E2TTT_H */

@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and validates descriptors and pointers (no GPU needed: only
+entry points that return before touching a device are called)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "e2ttt.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from chunk_weight_rnn_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from chunk_weight_rnn_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _desc(kind="swiglu", loss="negdot", io="bf16", B=2, H=3, T=256, D=128, Hd=256, chunk=64, flags=0):
+    from chunk_weight_rnn_amd._lib import make_desc
+    return make_desc(kind, loss, io, B, H, T, D, Hd, chunk, flags)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = set(re.findall(r"E2TTT_API[^;(]*?\b(e2ttt_\w+)\s*\(", open(HEADER).read()))
+    assert len(names) == 8
+    from chunk_weight_rnn_amd import _lib
+    assert names == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_param_count_and_paths(lib):
+    for cfg in synth.CONFIGS.values():
+        d = _desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
+        assert lib.e2ttt_param_count(ctypes.byref(d)) == cfg.P
+        path = lib.e2ttt_path(ctypes.byref(d))
+        assert path == (1 if cfg.kind == "swiglu" else 0)
+        assert lib.e2ttt_workspace_size(ctypes.byref(d)) > 0
+    d = _desc(flags=1)
+    assert lib.e2ttt_path(ctypes.byref(d)) == 0
+
+
+def test_workspace_size_rules(lib):
+    d = _desc(B=0)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 0
+    d = _desc(T=0)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 0
+    d = _desc(T=100, chunk=64)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    # MFMA path needs the snapshots: grows with the number of chunks
+    a = lib.e2ttt_workspace_size(ctypes.byref(_desc(chunk=64)))
+    b = lib.e2ttt_workspace_size(ctypes.byref(_desc(chunk=256)))
+    assert a > b
+
+
+def _ptrs(desc, base=1 << 40, gap=1 << 32):
+    # 11 disjoint, 256-aligned fake device addresses (never dereferenced)
+    return [base + i * gap for i in range(11)]
+
+
+def _validate(lib, d, ptrs):
+    arr = (ctypes.c_void_p * 11)(*[ctypes.c_void_p(p) for p in ptrs])
+    return lib.e2ttt_validate(ctypes.byref(d), arr)
+
+
+def test_validate_ok_and_in_place(lib):
+    d = _desc()
+    p = _ptrs(d)
+    assert _validate(lib, d, p) == 0
+    p2 = list(p)
+    p2[9] = p2[6]   # W_end == W0
+    p2[10] = p2[7]  # M_end == M0
+    assert _validate(lib, d, p2) == 0
+
+
+@pytest.mark.parametrize("field,value", [("kind", 7), ("loss", -1), ("io_dtype", 2), ("B", -1), ("D", 0),
+                                         ("chunk", 0), ("Hd", 0)])
+def test_validate_bad_desc(lib, field, value):
+    d = _desc()
+    setattr(d, field, value)
+    assert _validate(lib, d, _ptrs(d)) == 1
+
+
+def test_validate_ragged_tail_rejected(lib):
+    d = _desc(T=100, chunk=64)
+    assert _validate(lib, d, _ptrs(d)) == 1
+
+
+def test_validate_null_and_misaligned(lib):
+    d = _desc()
+    for i in range(11):
+        p = _ptrs(d)
+        p[i] = 0
+        assert _validate(lib, d, p) == 1, i
+    p = _ptrs(d)
+    p[0] += 2  # q not 16-byte aligned
+    assert _validate(lib, d, p) == 1
+    p = _ptrs(d)
+    p[3] += 4  # eta only needs 4-byte alignment
+    assert _validate(lib, d, p) == 0
+    # empty tensors may be null
+    d0 = _desc(B=0)
+    assert _validate(lib, d0, [0] * 11) == 0
+
+
+def test_validate_aliasing(lib):
+    d = _desc()
+    p = _ptrs(d)
+    p[8] = p[0] + 64  # out overlaps q
+    assert _validate(lib, d, p) == 3
+    p = _ptrs(d)
+    p[9] = p[7]  # W_end == M0
+    assert _validate(lib, d, p) == 3
+    p = _ptrs(d)
+    p[10] = p[9]  # M_end == W_end
+    assert _validate(lib, d, p) == 3
+    p = _ptrs(d)
+    p[9] = p[6] + 16  # W_end partially overlapping W0
+    assert _validate(lib, d, p) == 3
+
+
+def test_validate_unsupported_shape(lib):
+    d = _desc(kind="linear", loss="mse", io="f32", D=512, Hd=0)
+    assert _validate(lib, d, _ptrs(d)) == 2
+    d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=2048)
+    assert _validate(lib, d, _ptrs(d)) == 2
+    # the MFMA path covers wide SwiGLU hidden layers
+    d = _desc(Hd=2048)
+    assert _validate(lib, d, _ptrs(d)) == 0
+
+
+def test_chunk_forward_rejects_before_launch(lib):
+    d = _desc(T=100, chunk=64)
+    v = ctypes.c_void_p
+    args = [v(1 << 40)] * 11
+    assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 1
+    d = _desc()
+    args = [v((1 << 40) + i * (1 << 32)) for i in range(11)]
+    # workspace missing
+    assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 4
+    # workspace too small
+    assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(1 << 50), ctypes.c_size_t(16), v(0)) == 4
+    assert lib.e2ttt_chunk_forward(None, *args, v(0), ctypes.c_size_t(0), v(0)) == 1
+    assert lib.e2ttt_logscan(None, v(0), v(0), v(0), v(0), v(0), v(0), v(0)) == 1
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.e2ttt_status_string(s)
+    assert lib.e2ttt_status_string(99) == b"unknown status"
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import chunk_weight_rnn_amd as e2
+    x = synth.make_inputs(synth.CONFIGS["tiny_linear"])
+    with pytest.raises(ValueError):
+        e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"],
+                         chunk=16, kind="linear", loss="mse")
+    with pytest.raises(ValueError):
+        e2.logscan(x["eta"], x["alpha"], x["beta"], chunk=16)
+    assert isinstance(torch.__version__, str)

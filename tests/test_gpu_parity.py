@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element.
+
+Tolerances, err = max|gpu - oracle| / max|oracle| per tensor: 1e-4 for fp32
+I/O, 2e-2 for bf16 I/O with fp32 accumulation.  Every W and M matrix, the
+update W_end - W0 and the output are checked separately, so an error in the
+(small) gradient aggregation cannot hide under the large W0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import chunk_weight_rnn_amd as e2
+    e2.library()
+    return e2
+
+
+# ---------------------------------------------------------------------------
+# scalar kernels (e2ttt_logscan)
+# ---------------------------------------------------------------------------
+LOGSCAN_CASES = [(1, 2, 256, 16, "random"), (2, 3, 2048, 64, "random"), (1, 4, 2048, 256, "random"),
+                 (2, 2, 2048, 1024, "random"), (1, 1, 9, 3, "random"), (1, 2, 7, 1, "random"),
+                 (1, 2, 512, 128, "edges"), (1, 1, 1024, 1024, "ones"), (1, 1, 256, 64, "zero_beta")]
+
+
+@pytest.mark.parametrize("B,H,T,C,gates", LOGSCAN_CASES)
+def test_logscan_parity(B, H, T, C, gates):
+    e2 = _lib()
+    gu.note(f"logscan B={B} H={H} T={T} C={C} gates={gates}")
+    g = torch.Generator().manual_seed(T + C)
+    eta = 0.1 * torch.nn.functional.softplus(torch.randn(B, H, T, generator=g))
+    alpha = torch.sigmoid(4 + torch.randn(B, H, T, generator=g))
+    beta = torch.sigmoid(2 + torch.randn(B, H, T, generator=g))
+    if gates == "edges":
+        alpha[..., ::37] = 0.0
+        beta[..., 5::41] = 0.0
+        alpha[..., 7::53] = 1.0
+        beta[..., 11::29] = 1.0
+        eta[..., 3::31] = 0.0
+    elif gates == "ones":
+        alpha[:] = 1.0
+        beta[:] = 1.0
+    elif gates == "zero_beta":
+        beta[:] = 0.0
+    cM, cW, scal = e2.logscan(eta.cuda(), alpha.cuda(), beta.cuda(), chunk=C)
+    torch.cuda.synchronize()
+    nc = T // C
+    a = alpha.double().numpy().reshape(B, H, nc, C)
+    b = beta.double().numpy().reshape(B, H, nc, C)
+    e = eta.double().numpy().reshape(B, H, nc, C)
+    m, w, A, Bb, gamma = oracle.chunk_coefficients(a, b)
+    got_cM = cM.cpu().double().numpy().reshape(B, H, nc, C)
+    got_cW = cW.cpu().double().numpy().reshape(B, H, nc, C)
+    s = scal.cpu().double().numpy()
+    assert np.all(np.isfinite(got_cM)) and np.all(np.isfinite(got_cW)) and np.all(np.isfinite(s))
+    # fp32 coefficients; products below 1e-12 (e.g. prod beta over 1024
+    # tokens ~ 1e-80) underflow and are compared absolutely (gu.err floor)
+    assert gu.err(got_cM, m * e) < 1e-5
+    assert gu.err(got_cW, w * e) < 1e-5
+    assert gu.err(s[..., 0], A) < 1e-5
+    assert gu.err(s[..., 1], Bb) < 1e-5
+    assert gu.err(s[..., 2], gamma) < 1e-5
+    if gates == "ones":  # integer weights C-i+1 survive the log-space round trip
+        assert gu.err(got_cW / e, w) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_config_parity(name):
+    """Stated input distributions, whole sequence.  The SwiGLU states decay
+    towards the W = 0 fixed point and the MLP/MSE state diverges after a few
+    chunks; see gpu_util for how underflowed / diverged values are handled."""
+    _lib()
+    cfg = synth.CONFIGS[name]
+    gu.note(f"config {name}: kind={cfg.kind} B={cfg.B} H={cfg.H} T={cfg.T} C={cfg.chunk} io={cfg.io_dtype}")
+    x = synth.make_inputs(cfg, seed=0)
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy(), allow_diverged=(cfg.kind == "mlp"))
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_config_prefix_state(name):
+    """Full B, H, D, Hd and chunk; the first chunks only, where the carried
+    state is still O(1e-3 .. 1) in every workload (sampled outputs)."""
+    _lib()
+    base = synth.CONFIGS[name]
+    n = 3 if base.kind == "mlp" else 2
+    cfg = base.with_(T=min(base.T, n * base.chunk))
+    gu.note(f"prefix {name}: T={cfg.T}")
+    x = synth.make_inputs(cfg, seed=0)
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+@pytest.mark.parametrize("name", [n for n in synth.CONFIGS if n != "tiny_linear"])
+def test_config_persistent_state(name):
+    """Full shapes with slower decay, so every chunk's state and output stay
+    well inside fp32 range for the whole sequence."""
+    _lib()
+    cfg = synth.CONFIGS[name]
+    gu.note(f"persistent {name}")
+    x = gu.persistent_gates(cfg, synth.make_inputs(cfg, seed=0))
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+# ---------------------------------------------------------------------------
+# MFMA path: several tiles, slices, chunk sizes, carried momentum, edge gates
+# ---------------------------------------------------------------------------
+MFMA_CASES = [
+    dict(B=1, H=1, T=64, Hd=64, chunk=64),      # one slice, one block, one chunk
+    dict(B=1, H=3, T=256, Hd=192, chunk=128),   # 3 slices, 4-wave apply, 2 chunks
+    dict(B=2, H=3, T=384, Hd=128, chunk=64),    # 12 workgroups (no XCD remap), 6 chunks
+    dict(B=2, H=4, T=512, Hd=256, chunk=512),   # one long chunk of 8 blocks
+    dict(B=1, H=2, T=1024, Hd=320, chunk=256),  # 5 slices
+]
+
+
+@pytest.mark.parametrize("i", range(len(MFMA_CASES)))
+@pytest.mark.parametrize("gates", ["random", "edges"])
+def test_swiglu_mfma_cases(i, gates):
+    _lib()
+    c = MFMA_CASES[i]
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"mfma{i}_{gates}", **c)
+    gu.note(f"mfma case {i} gates={gates}: {c}")
+    x = synth.make_inputs(cfg, seed=10 + i, m0_scale=0.5)
+    if gates == "edges":
+        x["alpha"][..., ::37] = 0.0
+        x["beta"][..., 5::41] = 0.0
+        x["eta"][..., 3::31] = 0.0
+        x["alpha"][..., 1::19] = 1.0
+        x["beta"][..., 2::23] = 1.0
+    import chunk_weight_rnn_amd as e2
+    assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+# ---------------------------------------------------------------------------
+# portable fp32 path: every kind and loss, ragged-looking chunk sizes
+# ---------------------------------------------------------------------------
+GENERIC = [(k, l) for k in ("linear", "mlp", "swiglu") for l in ("mse", "negdot")]
+
+
+@pytest.mark.parametrize("kind,loss", GENERIC)
+@pytest.mark.parametrize("chunk", [1, 3, 16])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_generic_parity(kind, loss, chunk, io):
+    _lib()
+    D, Hd = (48, 40) if kind != "linear" else (40, 0)
+    cfg = synth.Config(f"gen_{kind}_{loss}_{chunk}_{io}", kind, loss, 2, 2, 4 * chunk + (0 if chunk > 1 else 5),
+                       D, Hd, chunk, io)
+    gu.note(f"generic {cfg}")
+    x = synth.make_inputs(cfg, seed=chunk, m0_scale=0.5)
+    if kind == "mlp" and loss == "mse":
+        x["eta"] = x["eta"] / D  # the stated eta makes MLP/MSE diverge within 3 chunks
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    # arithmetic is fp32 either way; only a bf16 output is rounded
+    gu.assert_close(cfg, got, ref, x["W0"].numpy(), tol=1e-4, out_tol=(1e-4 if io == "f32" else 1e-2))
+
+
+def test_force_generic_on_mfma_shape():
+    _lib()
+    cfg = synth.CONFIGS["swiglu_340m"].with_(name="forced_generic", B=1, H=2, T=512, chunk=128)
+    gu.note("force generic on a SwiGLU bf16 shape")
+    x = synth.make_inputs(cfg, seed=5, m0_scale=0.5)
+    got = gu.run_gpu(cfg, x, force_generic=True)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy(), tol=1e-4, out_tol=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# state handling: in place, resume, empty, determinism, aliasing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["swiglu_340m", "mlp_fp32"])
+def test_in_place_update(name):
+    _lib()
+    cfg = synth.CONFIGS[name].with_(B=1, H=2, T=4 * synth.CONFIGS[name].chunk)
+    gu.note(f"in place {cfg}")
+    x = synth.make_inputs(cfg, seed=3, m0_scale=0.5)
+    ref = gu.run_gpu(cfg, x)
+    got = gu.run_gpu(cfg, x, in_place=True)
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["swiglu_1p3b", "mlp_fp32", "tiny_linear"])
+def test_resume_bitwise(name):
+    e2 = _lib()
+    base = synth.CONFIGS[name]
+    cfg = base.with_(B=1, H=2, T=6 * base.chunk)
+    gu.note(f"resume {cfg}")
+    x = gu.to_dev(synth.make_inputs(cfg, seed=4, m0_scale=0.5))
+    kw = dict(chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd)
+    full = e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], **kw)
+    T1 = 2 * cfg.chunk
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o1, W1, M1 = e2.chunk_forward(*(sl(x[n], 0, T1) for n in ("q", "k", "v", "eta", "alpha", "beta")),
+                                  x["W0"], x["M0"], **kw)
+    o2, W2, M2 = e2.chunk_forward(*(sl(x[n], T1, cfg.T) for n in ("q", "k", "v", "eta", "alpha", "beta")),
+                                  W1, M1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=2), full[0])
+    assert torch.equal(W2, full[1]) and torch.equal(M2, full[2])
+
+
+def test_empty_inputs():
+    e2 = _lib()
+    gu.note("empty inputs")
+    cfg = synth.CONFIGS["swiglu_340m"]
+    P = cfg.P
+    for B, T in ((0, 256), (1, 0)):
+        q = torch.zeros(B, 2, T, 128, dtype=torch.bfloat16, device="cuda")
+        g = torch.rand(B, 2, T, device="cuda")
+        W0 = torch.randn(B, 2, P, device="cuda")
+        M0 = torch.randn(B, 2, P, device="cuda")
+        out, W, M = e2.chunk_forward(q, q, q, g, g, g, W0, M0, chunk=256, kind="swiglu", loss="negdot", Hd=256)
+        torch.cuda.synchronize()
+        assert out.shape == q.shape
+        assert torch.equal(W, W0) and torch.equal(M, M0)
+
+
+def test_deterministic():
+    _lib()
+    cfg = synth.CONFIGS["swiglu_340m"].with_(B=2, H=4, T=1024)
+    gu.note("determinism")
+    x = synth.make_inputs(cfg, seed=8, m0_scale=0.5)
+    a = gu.run_gpu(cfg, x)
+    b = gu.run_gpu(cfg, x)
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)
+
+
+def test_alias_rejected():
+    e2 = _lib()
+    cfg = synth.CONFIGS["swiglu_340m"].with_(B=1, H=1, T=256)
+    x = gu.to_dev(synth.make_inputs(cfg))
+    with pytest.raises(e2.E2TTTError) as ei:
+        e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"],
+                         chunk=256, kind="swiglu", loss="negdot", Hd=256, out=x["q"])
+    assert ei.value.status == 3
