@@ -21,9 +21,19 @@
 // independent slices of 64.  One workgroup (4 wavefronts, one per SIMD) owns
 // one (b, h, slice) for the whole sequence and keeps that slice's fp32 W and M
 // (6 x 128 x 64 values) resident as MFMA accumulators of the aggregation GEMM
-// across all chunks.  The epilogue therefore never touches HBM: W and M are
-// rescaled in registers at each chunk start and the aggregation MFMAs
-// accumulate straight into them.
+// across all chunks: the epilogue never touches HBM.
+//
+// gfx950 specifics used here:
+//   * K and V token blocks are copied HBM -> LDS by global_load_lds_dwordx4
+//     (no registers), one block ahead of use, into a row-major layout;
+//   * the grad GEMMs read K/V rows from it with ds_read_b128 and the
+//     aggregation reads K^T / V^T fragments from the same buffer with the
+//     LDS transpose read ds_read_b64_tr_b16 (within a 16-lane group, lane p
+//     loads row p/4, columns 4(p%4)..+3, and lane i receives 4 consecutive
+//     rows of column i), so nothing is ever written transposed;
+//   * every LDS layout uses an XOR swizzle of 16-byte chunks instead of
+//     padding, chosen so both the row reads and the transpose reads are
+//     bank-conflict free.
 //
 // The output needs every hidden unit of the head, so the loop kernel writes a
 // bf16 snapshot of each chunk-start weight slice and a second, fully
@@ -37,18 +47,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 constexpr int D = 128;   // head dim
 constexpr int S = 64;    // hidden units per workgroup slice
 constexpr int CB = 64;   // tokens per block inside a chunk
 constexpr int NT = 256;  // 4 wavefronts
-
-// LDS pitches (bf16 elements); +8 keeps 16-byte row accesses bank-conflict free
-constexpr int PW = D + 8;   // weight slices [S][PW]
-constexpr int PK = CB + 8;  // K^T, V^T [D][PK]
-constexpr int PDT = CB + 8; // scaled backward factors [S][PDT]
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -63,7 +68,40 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
     return r;
 }
 
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// 16-byte chunk swizzle of a 256-byte row t (row-major [t][128] bf16): the 8
+// rows read at one chunk by 8 lanes of ds_read_b128 land in 8 different bank
+// groups, and so do the 4 rows x 2 chunks of one 16-lane transpose read.
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// 32x16 MFMA operand fragment transposed out of a swizzled row-major
+// [rows][128] bf16 LDS buffer: operand row = source column col0 + lane%32,
+// operand k 0..3 = source rows rbase0..+3, k 4..7 = source rows rbase1..+3.
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* buf, int rbase0, int rbase1, int col0, int lane) {
+    const int p = lane & 15, G = lane >> 4;
+    const int col = col0 + 16 * (G & 1) + 4 * (p & 3);
+    const int chunk = col >> 3;
+    const int half = p & 1;
+    const int r0 = rbase0 + (p >> 2);
+    const int r1 = rbase1 + (p >> 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swz(r0)) + 8 * half));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swz(r1)) + 8 * half));
+    bf16x8 r;
+    r[0] = lo[0];
+    r[1] = lo[1];
+    r[2] = lo[2];
+    r[3] = lo[3];
+    r[4] = hi[0];
+    r[5] = hi[1];
+    r[6] = hi[2];
+    r[7] = hi[3];
+    return r;
+}
 
 struct LoopArgs {
     const __bf16* k;
@@ -80,56 +118,41 @@ struct LoopArgs {
     int Hd, C, nc, nsl, nwg, xcd_map;
 };
 
-struct alignas(16) Lds {
-    __bf16 wsl[3][S][PW];  // chunk-start weights: W1^T, W3^T, W2 rows of the slice
-    __bf16 kt[D][PK];      // K^T of the current token block
-    __bf16 vt[D][PK];      // V^T
-    __bf16 dt[6][S][PDT];  // c-scaled factors, hidden-major: 1M 1W 3M 3W 2M 2W
-};
+// LDS of the loop kernel (bytes): exactly the 160 KB of a gfx950 CU
+constexpr int KV_BYTES = 64 * 256;             // one [64 tokens][128] bf16 matrix
+constexpr int OFF_KV = 0;                      // [2 buffers][K, V]
+constexpr int OFF_DT = OFF_KV + 4 * KV_BYTES;  // [6][64 hidden][64 tokens] bf16 scaled factors
+constexpr int DT_BYTES = 6 * 64 * 128;
+constexpr int OFF_WS = OFF_DT + DT_BYTES;      // [3][64 hidden][128 d] bf16 chunk-start weights
+constexpr int LOOP_LDS = OFF_WS + 3 * 64 * 256;
+static_assert(LOOP_LDS == 160 * 1024, "loop kernel LDS budget");
+
+__device__ __forceinline__ int kv_off(int buf, int mat, int t, int chunk) {
+    return OFF_KV + (2 * buf + mat) * KV_BYTES + t * 256 + 16 * (chunk ^ swz(t));
+}
+// scaled factors: row j holds 64 tokens = 8 chunks, swizzled by j
+__device__ __forceinline__ int dt_off(int ty, int j, int chunk) {
+    return OFF_DT + ty * 8192 + j * 128 + 16 * (chunk ^ (j & 7));
+}
+// chunk-start weight slices W1^T, W3^T, W2 rows: [3][64 hidden][128 d], swizzled by j
+__device__ __forceinline__ int ws_off(int m, int j, int chunk) {
+    return OFF_WS + m * 16384 + j * 256 + 16 * (chunk ^ (j & 7));
+}
 
 // tile element (lane l, register r) of a 32x32 MFMA accumulator:
 //   col = l % 32, row = 8*(r/4) + 4*(l/32) + r%4
-
-// Aggregation over one token block.  The wave owns row tiles {rt0, rt0+1} of
-// D and hidden half h of the slice for all three matrices: acc[rr][2m] and
-// acc[rr][2m+1] are the M and W parts of matrix m (0: W1, 1: W3, 2: W2^T).
-__device__ __forceinline__ void aggregate_block(f32x16 (&acc)[2][6], const Lds& L, int lane, int rt0, int h) {
-    const int li = lane & 31, lg = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < CB / 16; ++ks) {
-        const int kc = 16 * ks + 8 * lg;
-        bf16x8 ak[2], av[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            ak[rr] = *(const bf16x8*)&L.kt[32 * (rt0 + rr) + li][kc];
-            av[rr] = *(const bf16x8*)&L.vt[32 * (rt0 + rr) + li][kc];
-        }
-#pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            const bf16x8 bm = *(const bf16x8*)&L.dt[2 * m][32 * h + li][kc];
-            const bf16x8 bw = *(const bf16x8*)&L.dt[2 * m + 1][32 * h + li][kc];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const bf16x8 a = (m < 2) ? ak[rr] : av[rr];
-                acc[rr][2 * m] = mfma32(a, bm, acc[rr][2 * m]);
-                acc[rr][2 * m + 1] = mfma32(a, bw, acc[rr][2 * m + 1]);
-            }
-        }
-    }
-}
+//
+// State ownership: wave w owns row tiles {rt0, rt0+1} (rt0 = 2(w&1)) of D
+// and hidden half hh = w>>1 of the slice, for all three matrices:
+// acc[rr][2m] / acc[rr][2m+1] are the M / W parts of matrix m
+// (0: W1, 1: W3, 2: W2 held transposed as [d][j]).
 
 // State tiles <-> packed fp32 parameters (W1 [D][Hd] | W3 [D][Hd] | W2 [Hd][D]).
-// Element (lane, r) of the tile for pair p and row tile rt sits at
-//   mat < 2: mat*D*Hd + d*Hd + j      mat == 2: 2*D*Hd + j*D + d
-// with d = 32 rt + 8 (r/4) + 4 lg + r%4 and j = j0 + 32 h + li.  Addresses
-// are split into a wave-uniform base plus one 32-bit lane offset
-// (laneA = 4 lg Hd + li for [d][j], laneB = li D + 4 lg for [j][d]).
 template <bool STORE>
 __device__ __forceinline__ void state_io(f32x16 (&acc)[2][6], float* W, float* M, int rt0, int h, int j0, int Hd,
                                          unsigned laneA, unsigned laneB) {
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-        const int mat = p;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
 #pragma unroll
@@ -138,8 +161,8 @@ __device__ __forceinline__ void state_io(f32x16 (&acc)[2][6], float* W, float* M
                 float* wb;
                 float* mb;
                 unsigned lo;
-                if (mat < 2) {
-                    const int64_t ub = (int64_t)mat * D * Hd + (int64_t)dr * Hd + j0 + 32 * h;
+                if (p < 2) {
+                    const int64_t ub = (int64_t)p * D * Hd + (int64_t)dr * Hd + j0 + 32 * h;
                     wb = W + ub;
                     mb = M + ub;
                     lo = laneA;
@@ -161,36 +184,9 @@ __device__ __forceinline__ void state_io(f32x16 (&acc)[2][6], float* W, float* M
     }
 }
 
-// Chunk start: write the bf16 weights (LDS operand slices and the global
-// snapshot W1^T [Hd][D] | W3^T [Hd][D] | W2 [Hd][D], all hidden-major), then
-// rescale the state: W <- A W - gamma M, M <- Bb M.
-__device__ __forceinline__ void chunk_start(f32x16 (&acc)[2][6], Lds& L, __bf16* snap, int lane, int rt0, int h,
-                                            int j0, int Hd, float A, float Bb, float gamma) {
-    const int li = lane & 31, lg = lane >> 5;
-    const int jl = 32 * h + li;
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-        __bf16* base = snap + (int64_t)m * Hd * D + (int64_t)(j0 + 32 * h) * D + 32 * rt0 + li * D + 4 * lg;
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const f32x16 w = acc[rr][2 * m + 1];
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const bf16x4 v4 = pack4(w[4 * qd], w[4 * qd + 1], w[4 * qd + 2], w[4 * qd + 3]);
-                *(bf16x4*)&L.wsl[m][jl][32 * (rt0 + rr) + 8 * qd + 4 * lg] = v4;
-                *(bf16x4*)&base[32 * rr + 8 * qd] = v4;
-            }
-            const f32x16 mm = acc[rr][2 * m];
-            acc[rr][2 * m + 1] = A * w - gamma * mm;
-            acc[rr][2 * m] = Bb * mm;
-        }
-    }
-}
-
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 swiglu_loop_kernel(LoopArgs a) {
-    __shared__ Lds L;
-    __shared__ alignas(16) float cbuf[2][2][CB];  // per-token cM, cW of a block, double-buffered
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LOOP_LDS];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int lane = tid & 63;
@@ -211,127 +207,158 @@ swiglu_loop_kernel(LoopArgs a) {
     const float* cMb = a.cM + bh * T;
     const float* cWb = a.cW + bh * T;
 
-    // state ownership: wave -> row tiles (of D) {rt0, rt0+1} x hidden half hh of the slice
-    const int rt0 = 2 * (wave & 1);
-    const int hh = wave >> 1;
-    // grad ownership: wave -> token rows [32*gr, +32) x hidden cols [32*gc, +32) of the slice
-    const int gr = wave >> 1, gc = wave & 1;
+    const int rt0 = 2 * (wave & 1), hh = wave >> 1;  // state / aggregation ownership
+    const int gr = wave >> 1, gc = wave & 1;         // grad: token rows 32gr.., hidden cols 32gc..
 
-    const unsigned laneA = (unsigned)(4 * lg * Hd + li);
-    const unsigned laneB = (unsigned)(li * D + 4 * lg);
-    const unsigned laneK = (unsigned)(li * D + 8 * lg);  // A-operand rows of K / V
+    // HBM -> LDS copy of one token block's K and V rows: wave w moves rows
+    // [16w, 16w+16) of both, 4 rows (1 KB) per instruction; lane L writes row
+    // r0 + L/16 at physical chunk L%16, which holds logical chunk (L%16)^swz(row).
+    auto issue_kv = [&](int blk, int buf) {
+        const int64_t tb = (int64_t)blk * CB;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const __bf16* src = m == 0 ? kb : vb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r0 = 16 * wave + 4 * i;
+                const int row = r0 + (lane >> 4);
+                const int c = (lane & 15) ^ swz(row);
+                __builtin_amdgcn_global_load_lds((const void*)(src + (tb + row) * D + 8 * c),
+                                                 (lds_void_t*)(smem + OFF_KV + (2 * buf + m) * KV_BYTES + r0 * 256),
+                                                 16, 0, 0);
+            }
+        }
+    };
 
     f32x16 acc[2][6];
+    const unsigned laneA = (unsigned)(4 * lg * Hd + li);
+    const unsigned laneB = (unsigned)(li * D + 4 * lg);
     state_io<false>(acc, (float*)a.W0 + bh * P, (float*)a.M0 + bh * P, rt0, hh, j0, Hd, laneA, laneB);
 
     const int nblk = (int)(T / CB);
     const int bpc = a.C / CB;
 
-    // A operands of the next block's grad GEMMs (K and V rows), prefetched
-    bf16x8 ka[8], va[8];
-    auto prefetch = [&](int blk) {
-        const __bf16* kr = kb + ((int64_t)blk * CB + 32 * gr) * D;
-        const __bf16* vr = vb + ((int64_t)blk * CB + 32 * gr) * D;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            ka[ks] = *(const bf16x8*)&kr[laneK + 16 * ks];
-            va[ks] = *(const bf16x8*)&vr[laneK + 16 * ks];
-        }
-    };
-    prefetch(0);
-    if (wave == 0) {
-        cbuf[0][0][lane] = cMb[lane];
-        cbuf[0][1][lane] = cWb[lane];
-    }
+    issue_kv(0, 0);
+    wait_vmem();
+    __syncthreads();
 
     for (int blk = 0; blk < nblk; ++blk) {
-        const int c = blk / bpc;
+        const int buf = blk & 1;
+        const bool more = blk + 1 < nblk;
         if (blk % bpc == 0) {
+            // ---- chunk start: bf16 weights -> LDS operand slices + global snapshot; rescale state
+            const int c = blk / bpc;
             const float* sc = a.scal + (bh * a.nc + c) * 4;
             const float A = sc[0], Bb = sc[1], gamma = sc[2];
             __bf16* snap = a.snap + (bh * a.nc + c) * P;
-            chunk_start(acc, L, snap, lane, rt0, hh, j0, Hd, A, Bb, gamma);
+            const int jl = 32 * hh + li;
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                __bf16* base = snap + (int64_t)m * Hd * D + (int64_t)(j0 + 32 * hh) * D + 32 * rt0 + li * D + 4 * lg;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const f32x16 w = acc[rr][2 * m + 1];
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const bf16x4 v4 = pack4(w[4 * qd], w[4 * qd + 1], w[4 * qd + 2], w[4 * qd + 3]);
+                        *(bf16x4*)(smem + ws_off(m, jl, 4 * (rt0 + rr) + qd) + 8 * lg) = v4;
+                        *(bf16x4*)&base[32 * rr + 8 * qd] = v4;
+                    }
+                    const f32x16 mm = acc[rr][2 * m];
+                    acc[rr][2 * m + 1] = A * w - gamma * mm;
+                    acc[rr][2 * m] = Bb * mm;
+                }
+            }
             __syncthreads();
         }
 
-        // ---- K^T (waves with gc == 0) or V^T (gc == 1) of token rows gr into LDS,
-        // transposed out of the A-operand registers: lane holds row t = 32 gr + li,
-        // d = 16 ks + 8 lg + e
-        if (gc == 0) {
+        // ---- next block's K/V copy runs behind this block's work
+        if (more) issue_kv(blk + 1, buf ^ 1);
+        // ---- this block's coefficients (cM, cW of the lane's 16 tokens)
+        f32x4 cm4[4], cw4[4];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) L.kt[16 * ks + 8 * lg + e][32 * gr + li] = ka[ks][e];
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) L.vt[16 * ks + 8 * lg + e][32 * gr + li] = va[ks][e];
+        for (int qd = 0; qd < 4; ++qd) {
+            const int64_t t = (int64_t)blk * CB + 32 * gr + 8 * qd + 4 * lg;
+            cm4[qd] = *(const f32x4*)&cMb[t];
+            cw4[qd] = *(const f32x4*)&cWb[t];
         }
 
         // ---- grad: H1, H3, V W2^T for token rows gr, hidden cols gc
         f32x16 h1 = {}, h3 = {}, hv = {};
+        {
+            const int t = 32 * gr + li;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int kc = 16 * ks + 8 * lg;
-            const bf16x8 b1 = *(const bf16x8*)&L.wsl[0][32 * gc + li][kc];
-            const bf16x8 b3 = *(const bf16x8*)&L.wsl[1][32 * gc + li][kc];
-            const bf16x8 b2 = *(const bf16x8*)&L.wsl[2][32 * gc + li][kc];
-            h1 = mfma32(ka[ks], b1, h1);
-            h3 = mfma32(ka[ks], b3, h3);
-            hv = mfma32(va[ks], b2, hv);
+            for (int ks = 0; ks < 8; ++ks) {
+                const int jw = 32 * gc + li;
+                const bf16x8 ak = *(const bf16x8*)(smem + kv_off(buf, 0, t, 2 * ks + lg));
+                const bf16x8 av = *(const bf16x8*)(smem + kv_off(buf, 1, t, 2 * ks + lg));
+                h1 = mfma32(ak, *(const bf16x8*)(smem + ws_off(0, jw, 2 * ks + lg)), h1);
+                h3 = mfma32(ak, *(const bf16x8*)(smem + ws_off(1, jw, 2 * ks + lg)), h3);
+                hv = mfma32(av, *(const bf16x8*)(smem + ws_off(2, jw, 2 * ks + lg)), hv);
+            }
         }
         // ---- elementwise backward and coefficient scaling -> LDS (hidden-major)
+        // du = -hv: 1M = -cm*a, 1W = cw*a, 3M = -cm*b, 3W = cw*b, 2M = -cm*u,
+        // 2W = cw*u, where a = hv*h3*silu'(h1), b = hv*silu(h1)
         {
             const int jl = 32 * gc + li;
-            const float(*cb)[CB] = cbuf[blk & 1];
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const int tcol = 32 * gr + 8 * qd + 4 * lg;
-                const f32x4 cm4 = *(const f32x4*)&cb[0][tcol];
-                const f32x4 cw4 = *(const f32x4*)&cb[1][tcol];
                 float o[6][4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * qd + e;
-                    const float x1 = h1[r], x3 = h3[r], du = -hv[r];
-                    const float sg = sigm(x1);
+                    const float x1 = h1[r], x3 = h3[r], y = hv[r];
+                    const float sg = fast_sigmoid(x1);
                     const float s1 = x1 * sg;
                     const float u = s1 * x3;
-                    const float dh3 = du * s1;
-                    const float dh1 = du * x3 * sg * (1.f + x1 * (1.f - sg));
-                    const float cm = cm4[e], cw = cw4[e];
-                    o[0][e] = cm * dh1;
-                    o[1][e] = -cw * dh1;
-                    o[2][e] = cm * dh3;
-                    o[3][e] = -cw * dh3;
-                    o[4][e] = -cm * u;
+                    const float ds = sg + s1 * (1.f - sg);
+                    const float av = y * x3 * ds;
+                    const float bv = y * s1;
+                    const float ncm = -cm4[qd][e], cw = cw4[qd][e];
+                    o[0][e] = ncm * av;
+                    o[1][e] = cw * av;
+                    o[2][e] = ncm * bv;
+                    o[3][e] = cw * bv;
+                    o[4][e] = ncm * u;
                     o[5][e] = cw * u;
                 }
 #pragma unroll
                 for (int ty = 0; ty < 6; ++ty)
-                    *(bf16x4*)&L.dt[ty][jl][tcol] = pack4(o[ty][0], o[ty][1], o[ty][2], o[ty][3]);
+                    *(bf16x4*)(smem + dt_off(ty, jl, 4 * gr + qd) + 8 * lg) =
+                        pack4(o[ty][0], o[ty][1], o[ty][2], o[ty][3]);
             }
         }
         __syncthreads();
 
-        // ---- prefetch the next block (K/V rows to registers, coefficients to LDS)
-        const bool more = blk + 1 < nblk;
-        float cm_n = 0.f, cw_n = 0.f;
-        if (more) {
-            prefetch(blk + 1);
-            if (wave == 0) {
-                cm_n = cMb[(int64_t)(blk + 1) * CB + lane];
-                cw_n = cWb[(int64_t)(blk + 1) * CB + lane];
+        // ---- aggregation into the resident state
+        {
+            const unsigned char* kbuf = smem + OFF_KV + (2 * buf) * KV_BYTES;
+            const unsigned char* vbuf = kbuf + KV_BYTES;
+            const int jl = 32 * hh + li;
+#pragma unroll
+            for (int ks = 0; ks < CB / 16; ++ks) {
+                const int rb0 = 16 * ks + 8 * lg, rb1 = rb0 + 4;
+                bf16x8 ak[2], av[2];
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    ak[rr] = tr_frag(kbuf, rb0, rb1, 32 * (rt0 + rr), lane);
+                    av[rr] = tr_frag(vbuf, rb0, rb1, 32 * (rt0 + rr), lane);
+                }
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const bf16x8 bm = *(const bf16x8*)(smem + dt_off(2 * m, jl, 2 * ks + lg));
+                    const bf16x8 bw = *(const bf16x8*)(smem + dt_off(2 * m + 1, jl, 2 * ks + lg));
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const bf16x8 x = (m < 2) ? ak[rr] : av[rr];
+                        acc[rr][2 * m] = mfma32(x, bm, acc[rr][2 * m]);
+                        acc[rr][2 * m + 1] = mfma32(x, bw, acc[rr][2 * m + 1]);
+                    }
+                }
             }
         }
-
-        // ---- aggregation into the resident state
-        aggregate_block(acc, L, lane, rt0, hh);
-        if (more && wave == 0) {
-            cbuf[(blk + 1) & 1][0][lane] = cm_n;
-            cbuf[(blk + 1) & 1][1][lane] = cw_n;
-        }
+        wait_vmem();  // this wave's share of the next block's K/V has landed
         __syncthreads();
     }
 
@@ -342,29 +369,28 @@ swiglu_loop_kernel(LoopArgs a) {
 
 // ---------------------------------------------------------------------------
 // apply: out = (silu(Q W1) * (Q W3)) W2 from the chunk-start snapshot.
-// Snapshot layout per (b, h, chunk), bf16: W1^T [Hd][D] | W3^T [Hd][D] | W2 [Hd][D].
-// One wavefront per 32 tokens; hidden units streamed through LDS 64 at a time.
-// Computed transposed (H^T = W1^T Q^T, out^T = W2^T U^T) so that U^T leaves
-// the first MFMA in exactly the register layout the second one consumes.
+// Snapshot layout per (b, h, chunk), bf16, all hidden-major:
+//   W1^T [Hd][D] | W3^T [Hd][D] | W2 [Hd][D].
+// One wavefront per 32 tokens; hidden units stream through LDS 32 at a time
+// (double-buffered, HBM -> LDS copies).  Computed transposed (H^T = W1^T Q^T,
+// out^T = W2^T U^T) so that U^T leaves the first MFMA in the register layout
+// the second one consumes; the W2^T operand comes from the hidden-major stage
+// through the transpose read.
 // ---------------------------------------------------------------------------
 struct ApplyArgs {
     const __bf16* q;
     const __bf16* snap;
     __bf16* out;
     int64_t T;
-    int Hd, C, nc, rbc;  // rbc: row blocks per chunk
+    int Hd, C, nc, rbc;  // rbc: workgroups per chunk
 };
 
-constexpr int HB = 64;
-constexpr int PA1 = D + 8;   // [HB][PA1] for W1^T / W3^T rows
-constexpr int PA2 = HB + 8;  // [D][PA2] for W2^T columns
+constexpr int HB = 32;                     // hidden units per stage
+constexpr int STAGE_BYTES = 3 * HB * 256;  // W1^T, W3^T, W2 rows of the stage
 
 template <int NWA>
 __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
-    __shared__ __bf16 lw1[HB][PA1];
-    __shared__ __bf16 lw3[HB][PA1];
-    __shared__ __bf16 lw2[D][PA2];
-    constexpr int NTA = 64 * NWA;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 31, lg = lane >> 5;
     const int64_t wg = blockIdx.x;
@@ -377,60 +403,59 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     const __bf16* sn = a.snap + (bh * a.nc + c) * P;
     const __bf16* qb = a.q + bh * a.T * D;
 
+    // stage hb -> buffer: 24 instructions of 4 rows (1 KB), spread over the waves
+    auto issue_stage = [&](int hb, int sbuf) {
+#pragma unroll
+        for (int i = wave; i < 24; i += NWA) {
+            const int m = i >> 3, r0 = 4 * (i & 7);
+            const int row = r0 + (lane >> 4);
+            const int cch = (lane & 15) ^ swz(row);
+            __builtin_amdgcn_global_load_lds((const void*)(sn + (int64_t)m * Hd * D + (int64_t)(hb + row) * D + 8 * cch),
+                                             (lds_void_t*)(smem + sbuf * STAGE_BYTES + m * HB * 256 + r0 * 256), 16,
+                                             0, 0);
+        }
+    };
+
+    issue_stage(0, 0);
     bf16x8 qf[8];  // Q^T as B operand: col = token, k = d
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)&qb[(t0 + li) * D + 16 * ks + 8 * lg];
+    wait_vmem();
+    __syncthreads();
 
     f32x16 oacc[4] = {};
-    for (int hb = 0; hb < Hd; hb += HB) {
-        // stage W1^T, W3^T rows [hb, hb+64) and W2^T columns [hb, hb+64)
-        for (int i = tid; i < HB * (D / 8); i += NTA) {
-            const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
-            *(bf16x8*)&lw1[r][c8] = *(const bf16x8*)&sn[(int64_t)(hb + r) * D + c8];
-            *(bf16x8*)&lw3[r][c8] = *(const bf16x8*)&sn[(int64_t)Hd * D + (int64_t)(hb + r) * D + c8];
+    const int nhb = Hd / HB;
+    for (int ih = 0; ih < nhb; ++ih) {
+        const int sbuf = ih & 1;
+        if (ih + 1 < nhb) issue_stage((ih + 1) * HB, sbuf ^ 1);
+        const unsigned char* st = smem + sbuf * STAGE_BYTES;
+        f32x16 x1 = {}, x3 = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int ch = (2 * ks + lg) ^ swz(li);
+            x1 = mfma32(*(const bf16x8*)(st + li * 256 + 16 * ch), qf[ks], x1);
+            x3 = mfma32(*(const bf16x8*)(st + HB * 256 + li * 256 + 16 * ch), qf[ks], x3);
         }
-        // W2 rows [hb, hb+64) transposed into lw2[d][j]: lanes run over j so the
-        // 2-byte LDS writes of one instruction land in consecutive columns
-        for (int i = tid; i < HB * (D / 8); i += NTA) {
-            const int r = i % HB, c8 = (i / HB) * 8;
-            const bf16x8 w8 = *(const bf16x8*)&sn[2 * (int64_t)Hd * D + (int64_t)(hb + r) * D + c8];
+        // U^T tile: rows j = 8(r/4) + 4 lg + r%4, col = token
+        bf16x8 ub[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lw2[c8 + e][r] = w8[e];
-        }
-        __syncthreads();
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            f32x16 x1 = {}, x3 = {};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int kc = 16 * ks + 8 * lg;
-                x1 = mfma32(*(const bf16x8*)&lw1[32 * jt + li][kc], qf[ks], x1);
-                x3 = mfma32(*(const bf16x8*)&lw3[32 * jt + li][kc], qf[ks], x3);
+            for (int e = 0; e < 8; ++e) {
+                const int r = 8 * s + e;
+                const float h = x1[r];
+                ub[s][e] = (__bf16)(h * fast_sigmoid(h) * x3[r]);
             }
-            // U^T tile: rows j = 32 jt + 8(r/4) + 4 lg + r%4, col = token
-            bf16x8 ub[2];
+        // k-step s covers j = 16 s + {0..15}; lane group lg holds j offsets
+        // {4lg..4lg+3, 8+4lg..8+4lg+3}; the transpose read fetches W2 rows in that order.
+        const unsigned char* w2 = st + 2 * HB * 256;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
+            const int jb = 16 * s + 4 * lg;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * s + e;
-                    const float h = x1[r];
-                    ub[s][e] = (__bf16)(h * sigm(h) * x3[r]);
-                }
-            // k-step s covers j = 32 jt + 16 s + {0..15}; lane group lg holds
-            // j offsets {4lg..4lg+3, 8+4lg..8+4lg+3}; the A operand matches it.
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int jb = 32 * jt + 16 * s + 4 * lg;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const u32x2 lo = *(const u32x2*)&lw2[32 * dt + li][jb];
-                    const u32x2 hi = *(const u32x2*)&lw2[32 * dt + li][jb + 8];
-                    u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, av), ub[s], oacc[dt]);
-                }
-            }
+            for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(tr_frag(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
         }
+        wait_vmem();
         __syncthreads();
     }
     __bf16* ob = a.out + bh * a.T * D;
@@ -486,12 +511,16 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.Hd = (int)d.Hd;
     aa.C = (int)d.chunk;
     aa.nc = (int)(d.T / d.chunk);
-    if (d.chunk % 128 == 0) {
+    const unsigned nck = (unsigned)(BH * aa.nc);
+    if (d.chunk % 256 == 0) {
+        aa.rbc = (int)(d.chunk / 256);
+        hipLaunchKernelGGL(swiglu_apply_kernel<8>, dim3(nck * aa.rbc), dim3(512), 0, s, aa);
+    } else if (d.chunk % 128 == 0) {
         aa.rbc = (int)(d.chunk / 128);
-        hipLaunchKernelGGL(swiglu_apply_kernel<4>, dim3((unsigned)(BH * aa.nc * aa.rbc)), dim3(256), 0, s, aa);
+        hipLaunchKernelGGL(swiglu_apply_kernel<4>, dim3(nck * aa.rbc), dim3(256), 0, s, aa);
     } else {
         aa.rbc = (int)(d.chunk / 64);
-        hipLaunchKernelGGL(swiglu_apply_kernel<2>, dim3((unsigned)(BH * aa.nc * aa.rbc)), dim3(128), 0, s, aa);
+        hipLaunchKernelGGL(swiglu_apply_kernel<2>, dim3(nck * aa.rbc), dim3(128), 0, s, aa);
     }
     return hipGetLastError();
 }
