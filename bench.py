@@ -84,8 +84,9 @@ def measured_traffic(loop_launch_bytes_alg: float):
 
 
 def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
-    """The fp64 oracle on a bounded sample of the same workload (whole batch
-    rows: every head of one sequence), timed on the host cores."""
+    """The fp64 oracle on a bounded sample of the same workload: whole batch
+    rows (every head of one sequence), cycling over the batch until about
+    budget_s seconds of host work have been timed."""
     import numpy as np
     import oracle
     try:
@@ -96,19 +97,18 @@ def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
     x = synth.make_inputs(cfg, seed=0)
     f = lambda t: t.double().numpy()
     rows, wall = 0, 0.0
-    for b in range(cfg.B):
+    while wall < budget_s:
+        b = rows % cfg.B
         sl = {n: f(t[b:b + 1]) for n, t in x.items()}
         t0 = time.perf_counter()
         oracle.chunk_forward(cfg.kind, cfg.loss, sl["q"], sl["k"], sl["v"], sl["eta"], sl["alpha"], sl["beta"],
                              sl["W0"], sl["M0"], cfg.chunk, cfg.Hd)
         wall += time.perf_counter() - t0
         rows += 1
-        if wall >= budget_s:
-            break
     tokens = rows * cfg.T
     return {"value": tokens / wall, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} of {cfg.B} batch rows (all {cfg.H} heads x {cfg.T} tokens each), "
-                      f"fp64 numpy closed form, {wall:.1f} s"}
+            "sample": f"{rows} batch rows of {cfg.H} heads x {cfg.T} tokens (cycling over the {cfg.B} rows of "
+                      f"the workload), fp64 numpy closed form, {wall:.1f} s"}
 
 
 def main() -> int:
@@ -118,7 +118,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="swiglu_1p3b", choices=list(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MiB",
+                    help="first run a plain fp32 copy kernel over MiB of data (3 launches), so that a counter "
+                         "profile of this command holds the HBM counters of a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -129,6 +132,15 @@ def main() -> int:
     import torch
     import chunk_weight_rnn_amd as e2
     lib = e2.library()
+
+    if args.copy_calibrate > 0:
+        n = args.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = synth.CONFIGS[args.config]
     x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
