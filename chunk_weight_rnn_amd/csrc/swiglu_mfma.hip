@@ -103,6 +103,20 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* buf, int rbase0, 
     return r;
 }
 
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (__bf16)lo[e];
+        r[4 + e] = (__bf16)hi[e];
+    }
+    return r;
+}
+
 struct LoopArgs {
     const __bf16* k;
     const __bf16* v;
@@ -118,87 +132,123 @@ struct LoopArgs {
     int Hd, C, nc, nsl, nwg, xcd_map;
 };
 
-// LDS of the loop kernel (bytes): exactly the 160 KB of a gfx950 CU
-constexpr int KV_BYTES = 64 * 256;             // one [64 tokens][128] bf16 matrix
-constexpr int OFF_KV = 0;                      // [2 buffers][K, V]
-constexpr int OFF_DT = OFF_KV + 4 * KV_BYTES;  // [6][64 hidden][64 tokens] bf16 scaled factors
-constexpr int DT_BYTES = 6 * 64 * 128;
-constexpr int OFF_WS = OFF_DT + DT_BYTES;      // [3][64 hidden][128 d] bf16 chunk-start weights
-constexpr int LOOP_LDS = OFF_WS + 3 * 64 * 256;
-static_assert(LOOP_LDS == 160 * 1024, "loop kernel LDS budget");
+// LDS of the loop kernel: two buffers of one token block each,
+//   K [64 tokens][128] bf16 | V [64][128] bf16 | cM [64] f32 | cW [64] f32 |
+//   (A, Bb, gamma, -) of the block's chunk.
+// Rows are 256 bytes; 16-byte chunk c of row t sits at physical chunk
+// c ^ swz3(t).  swz3 spreads the 8 rows read at one chunk by ds_read_b128
+// over 8 bank groups, and the 4 rows x 4 chunks of one 16-lane transpose
+// read (all in one 8-byte half) over all 16 eight-byte bank slots.
+constexpr int KV_BYTES = 64 * 256;
+constexpr int CO_BYTES = 2 * 64 * 4 + 16;
+constexpr int BUF_BYTES = 2 * KV_BYTES + CO_BYTES;
+constexpr int LOOP_LDS = 2 * BUF_BYTES;
 
-__device__ __forceinline__ int kv_off(int buf, int mat, int t, int chunk) {
-    return OFF_KV + (2 * buf + mat) * KV_BYTES + t * 256 + 16 * (chunk ^ swz(t));
-}
-// scaled factors: row j holds 64 tokens = 8 chunks, swizzled by j
-__device__ __forceinline__ int dt_off(int ty, int j, int chunk) {
-    return OFF_DT + ty * 8192 + j * 128 + 16 * (chunk ^ (j & 7));
-}
-// chunk-start weight slices W1^T, W3^T, W2 rows: [3][64 hidden][128 d], swizzled by j
-__device__ __forceinline__ int ws_off(int m, int j, int chunk) {
-    return OFF_WS + m * 16384 + j * 256 + 16 * (chunk ^ (j & 7));
-}
+__device__ __forceinline__ int swz3(int t) { return (t & 1) | ((t & 2) << 1) | ((t & 4) >> 1); }
 
-// tile element (lane l, register r) of a 32x32 MFMA accumulator:
-//   col = l % 32, row = 8*(r/4) + 4*(l/32) + r%4
-//
-// State ownership: wave w owns row tiles {rt0, rt0+1} (rt0 = 2(w&1)) of D
-// and hidden half hh = w>>1 of the slice, for all three matrices:
-// acc[rr][2m] / acc[rr][2m+1] are the M / W parts of matrix m
-// (0: W1, 1: W3, 2: W2 held transposed as [d][j]).
+__device__ __forceinline__ int row_off(int t, int chunk) { return t * 256 + 16 * (chunk ^ swz3(t)); }
+
+// Row permutation of the state tiles.  Accumulator tile i (16 rows of d)
+// holds, in its row 4g + r (lane group g, register r),
+//   d = 32(i/2) + 8g + 4((g & 1) ^ (i & 1)) + r.
+// Tiles 2kk and 2kk+1 together give lane group g exactly d = 32kk + 8g + 0..7,
+// which is the k-slot order of a natural 16x16x32 operand: the chunk-start
+// weights become grad operands by a conversion in registers, while the
+// aggregation's K^T / V^T operands pick the same d order in the transpose read.
+__device__ __forceinline__ int state_d(int i, int g) { return 32 * (i >> 1) + 8 * g + 4 * ((g & 1) ^ (i & 1)); }
+
+// K^T / V^T aggregation operand for state tile i and the 32 tokens tb..tb+31 of
+// the LDS block: operand row rho = l%16 is d = state_d(i, rho/4) + rho%4,
+// k-slot e < 4 is token tb + 4(l/16) + e, e >= 4 is token tb + 16 + 4(l/16) + e-4.
+// ds_read_b64_tr_b16: within a 16-lane group lane p fetches 4 values of
+// token row p/4 at d quad p%4, and lane i receives 4 token rows of quad
+// i/4, element i%4.
+__device__ __forceinline__ bf16x8 trT(const unsigned char* buf, int i, int tb, int lane) {
+    const int p = lane & 15, g = lane >> 4, q = p & 3;
+    const int dq = 32 * (i >> 1) + 8 * q + 4 * ((q & 1) ^ (i & 1));
+    const int chunk = dq >> 3, half = (dq >> 2) & 1;
+    const int r0 = tb + 4 * g + (p >> 2), r1 = r0 + 16;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swz3(r0)) + 8 * half));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swz3(r1)) + 8 * half));
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[4 + e] = hi[e];
+    }
+    return r;
+}
 
 // State tiles <-> packed fp32 parameters (W1 [D][Hd] | W3 [D][Hd] | W2 [Hd][D]).
+// acc[m][0] / acc[m][1] are the M / W parts of matrix m (0: W1, 1: W3, 2: W2
+// held transposed as [d][j]); tile element (i, r) of lane (jl, g) is
+// d = state_d(i, g) + r, hidden unit j = j0 + jl.
 template <bool STORE>
-__device__ __forceinline__ void state_io(f32x16 (&acc)[2][6], float* W, float* M, int rt0, int h, int j0, int Hd,
-                                         unsigned laneA, unsigned laneB) {
+__device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float* M, int64_t j, int g, int Hd) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
+    for (int m = 0; m < 3; ++m) {
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
+        for (int i = 0; i < 8; ++i) {
+            const int64_t d = state_d(i, g);
+            if (m < 2) {
+                const int64_t o = (int64_t)m * D * Hd + d * Hd + j;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dr = 32 * (rt0 + rr) + 8 * (r / 4) + (r % 4);  // uniform part of d
-                float* wb;
-                float* mb;
-                unsigned lo;
-                if (p < 2) {
-                    const int64_t ub = (int64_t)p * D * Hd + (int64_t)dr * Hd + j0 + 32 * h;
-                    wb = W + ub;
-                    mb = M + ub;
-                    lo = laneA;
-                } else {
-                    const int64_t ub = 2 * (int64_t)D * Hd + (int64_t)(j0 + 32 * h) * D + dr;
-                    wb = W + ub;
-                    mb = M + ub;
-                    lo = laneB;
+                for (int r = 0; r < 4; ++r) {
+                    if (STORE) {
+                        M[o + r * Hd] = acc[m][0][i][r];
+                        W[o + r * Hd] = acc[m][1][i][r];
+                    } else {
+                        acc[m][0][i][r] = M[o + r * Hd];
+                        acc[m][1][i][r] = W[o + r * Hd];
+                    }
                 }
+            } else {
+                const int64_t o = 2 * (int64_t)D * Hd + j * D + d;
                 if (STORE) {
-                    mb[lo] = acc[rr][2 * p][r];
-                    wb[lo] = acc[rr][2 * p + 1][r];
+                    *(f32x4*)&M[o] = acc[m][0][i];
+                    *(f32x4*)&W[o] = acc[m][1][i];
                 } else {
-                    acc[rr][2 * p][r] = mb[lo];
-                    acc[rr][2 * p + 1][r] = wb[lo];
+                    acc[m][0][i] = *(const f32x4*)&M[o];
+                    acc[m][1][i] = *(const f32x4*)&W[o];
                 }
             }
         }
     }
 }
 
+// One workgroup = one (b, h, 64-unit hidden slice) for the whole sequence.
+// Wavefront w owns hidden units j0 + 16w .. +15 of the slice in all three
+// matrices: their fp32 M and W (6 x 128 x 16 per wave) stay in accumulator
+// registers, and the chunk-start weights as bf16 grad operands.  Per 64-token
+// block every wave
+//   grad:      H1, H3 = K W1, K W3 and HV = V W2^T for its 16 units
+//              (16x16x32 MFMA, K/V rows from LDS),
+//   backward:  the six coefficient-scaled factors, converted in registers
+//              straight into the aggregation's B operand,
+//   aggregate: state += K^T F1, K^T F3, V^T F2 (K^T, V^T by transpose reads),
+// so the only data the waves share is the K/V/coefficient block in LDS, and
+// one barrier per block guards its double buffer.
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 swiglu_loop_kernel(LoopArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LOOP_LDS];
+    // Two LDS buffers as separate arrays: the compiler can then tell the
+    // next block's in-flight HBM->LDS copies from this block's LDS reads and
+    // need not wait for the copies before every transpose read.
+    __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int li = lane & 31, lg = lane >> 5;
+    const int jl = lane & 15, g = lane >> 4;
 
     // XCD-aware placement: consecutive workgroup ids go to different XCDs, so
     // remap to keep the slices of one head (which read the same K/V) on one XCD.
     int L_id = blockIdx.x;
     if (a.xcd_map) L_id = (blockIdx.x % 8) * (a.nwg / 8) + blockIdx.x / 8;
     const int64_t bh = L_id / a.nsl;
-    const int j0 = (L_id % a.nsl) * S;
     const int Hd = a.Hd;
+    const int64_t j = (int64_t)(L_id % a.nsl) * S + 16 * wave + jl;  // this lane's hidden unit
     const int64_t T = a.T;
     const int64_t P = 3 * (int64_t)D * Hd;
 
@@ -207,164 +257,150 @@ swiglu_loop_kernel(LoopArgs a) {
     const float* cMb = a.cM + bh * T;
     const float* cWb = a.cW + bh * T;
 
-    const int rt0 = 2 * (wave & 1), hh = wave >> 1;  // state / aggregation ownership
-    const int gr = wave >> 1, gc = wave & 1;         // grad: token rows 32gr.., hidden cols 32gc..
-
-    // HBM -> LDS copy of one token block's K and V rows: wave w moves rows
-    // [16w, 16w+16) of both, 4 rows (1 KB) per instruction; lane L writes row
-    // r0 + L/16 at physical chunk L%16, which holds logical chunk (L%16)^swz(row).
-    auto issue_kv = [&](int blk, int buf) {
-        const int64_t tb = (int64_t)blk * CB;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const __bf16* src = m == 0 ? kb : vb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r0 = 16 * wave + 4 * i;
-                const int row = r0 + (lane >> 4);
-                const int c = (lane & 15) ^ swz(row);
-                __builtin_amdgcn_global_load_lds((const void*)(src + (tb + row) * D + 8 * c),
-                                                 (lds_void_t*)(smem + OFF_KV + (2 * buf + m) * KV_BYTES + r0 * 256),
-                                                 16, 0, 0);
-            }
-        }
-    };
-
-    f32x16 acc[2][6];
-    const unsigned laneA = (unsigned)(4 * lg * Hd + li);
-    const unsigned laneB = (unsigned)(li * D + 4 * lg);
-    state_io<false>(acc, (float*)a.W0 + bh * P, (float*)a.M0 + bh * P, rt0, hh, j0, Hd, laneA, laneB);
-
+    // HBM -> LDS copy of one token block: wave w moves K and V rows
+    // [16w, 16w+16), 4 rows (1 KB) per instruction; lane L writes row r0 + L/16
+    // at physical chunk L%16, which holds logical chunk (L%16) ^ swz3(row).
+    // Wave 0 also moves the block's cM (lanes 0..15), cW (lanes 16..31) and
+    // the (A, Bb, gamma) of the block's chunk (lane 32).
     const int nblk = (int)(T / CB);
     const int bpc = a.C / CB;
 
-    issue_kv(0, 0);
+    // Per-lane byte offsets of the copy (uniform block base + 32-bit lane
+    // offset keeps the addresses in scalar registers).
+    unsigned koff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        koff[i] = (unsigned)(row * D + 8 * ((lane & 15) ^ swz3(row))) * 2u;
+    }
+    const unsigned coff = 16u * (unsigned)(lane & 15);
+    auto issue_block = [&](int blk, unsigned char* dst) {
+        const int64_t tb = (int64_t)blk * CB;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const char* src = (const char*)((m == 0 ? kb : vb) + tb * D);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
+                                                 (lds_void_t*)(dst + m * KV_BYTES + (16 * wave + 4 * i) * 256), 16,
+                                                 0, 0);
+        }
+        if (wave == 0 && lane <= 32) {
+            const char* src = lane < 32 ? (const char*)((lane < 16 ? cMb : cWb) + tb) + coff
+                                        : (const char*)(a.scal + (bh * a.nc + blk / bpc) * 4);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + 2 * KV_BYTES), 16, 0, 0);
+        }
+    };
+
+    f32x4 acc[3][2][8];
+    state_io<false>(acc, (float*)a.W0 + bh * P, (float*)a.M0 + bh * P, j, g, Hd);
+
+    const bool godd = (g & 1) != 0;
+    bf16x8 wb[3][4];  // chunk-start weights as grad B operands: k-slot e of lane group g is d = 32kk + 8g + e
+
+    issue_block(0, lds0);
     wait_vmem();
     __syncthreads();
 
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int buf = blk & 1;
-        const bool more = blk + 1 < nblk;
+    auto block = [&](int blk, const unsigned char* kbuf, unsigned char* next) {
+        const unsigned char* vbuf = kbuf + KV_BYTES;
+        const float* cob = (const float*)(kbuf + 2 * KV_BYTES);
         if (blk % bpc == 0) {
-            // ---- chunk start: bf16 weights -> LDS operand slices + global snapshot; rescale state
+            // ---- chunk start: grad operands + bf16 snapshot from W, then rescale the state
             const int c = blk / bpc;
-            const float* sc = a.scal + (bh * a.nc + c) * 4;
+            const f32x4 sc = *(const f32x4*)&cob[128];
             const float A = sc[0], Bb = sc[1], gamma = sc[2];
-            __bf16* snap = a.snap + (bh * a.nc + c) * P;
-            const int jl = 32 * hh + li;
+            __bf16* snap = a.snap + (bh * a.nc + c) * P + j * D + 8 * g;
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
-                __bf16* base = snap + (int64_t)m * Hd * D + (int64_t)(j0 + 32 * hh) * D + 32 * rt0 + li * D + 4 * lg;
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const f32x16 w = acc[rr][2 * m + 1];
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const bf16x4 v4 = pack4(w[4 * qd], w[4 * qd + 1], w[4 * qd + 2], w[4 * qd + 3]);
-                        *(bf16x4*)(smem + ws_off(m, jl, 4 * (rt0 + rr) + qd) + 8 * lg) = v4;
-                        *(bf16x4*)&base[32 * rr + 8 * qd] = v4;
-                    }
-                    const f32x16 mm = acc[rr][2 * m];
-                    acc[rr][2 * m + 1] = A * w - gamma * mm;
-                    acc[rr][2 * m] = Bb * mm;
-                }
-            }
-            __syncthreads();
-        }
-
-        // ---- next block's K/V copy runs behind this block's work
-        if (more) issue_kv(blk + 1, buf ^ 1);
-        // ---- this block's coefficients (cM, cW of the lane's 16 tokens)
-        f32x4 cm4[4], cw4[4];
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int64_t t = (int64_t)blk * CB + 32 * gr + 8 * qd + 4 * lg;
-            cm4[qd] = *(const f32x4*)&cMb[t];
-            cw4[qd] = *(const f32x4*)&cWb[t];
-        }
-
-        // ---- grad: H1, H3, V W2^T for token rows gr, hidden cols gc
-        f32x16 h1 = {}, h3 = {}, hv = {};
-        {
-            const int t = 32 * gr + li;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int jw = 32 * gc + li;
-                const bf16x8 ak = *(const bf16x8*)(smem + kv_off(buf, 0, t, 2 * ks + lg));
-                const bf16x8 av = *(const bf16x8*)(smem + kv_off(buf, 1, t, 2 * ks + lg));
-                h1 = mfma32(ak, *(const bf16x8*)(smem + ws_off(0, jw, 2 * ks + lg)), h1);
-                h3 = mfma32(ak, *(const bf16x8*)(smem + ws_off(1, jw, 2 * ks + lg)), h3);
-                hv = mfma32(av, *(const bf16x8*)(smem + ws_off(2, jw, 2 * ks + lg)), hv);
-            }
-        }
-        // ---- elementwise backward and coefficient scaling -> LDS (hidden-major)
-        // du = -hv: 1M = -cm*a, 1W = cw*a, 3M = -cm*b, 3W = cw*b, 2M = -cm*u,
-        // 2W = cw*u, where a = hv*h3*silu'(h1), b = hv*silu(h1)
-        {
-            const int jl = 32 * gc + li;
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                float o[6][4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * qd + e;
-                    const float x1 = h1[r], x3 = h3[r], y = hv[r];
-                    const float sg = fast_sigmoid(x1);
-                    const float s1 = x1 * sg;
-                    const float u = s1 * x3;
-                    const float ds = sg + s1 * (1.f - sg);
-                    const float av = y * x3 * ds;
-                    const float bv = y * s1;
-                    const float ncm = -cm4[qd][e], cw = cw4[qd][e];
-                    o[0][e] = ncm * av;
-                    o[1][e] = cw * av;
-                    o[2][e] = ncm * bv;
-                    o[3][e] = cw * bv;
-                    o[4][e] = ncm * u;
-                    o[5][e] = cw * u;
+                for (int kk = 0; kk < 4; ++kk) {
+                    const f32x4 t0 = acc[m][1][2 * kk], t1 = acc[m][1][2 * kk + 1];
+                    wb[m][kk] = godd ? pack8(t1, t0) : pack8(t0, t1);
+                    *(bf16x8*)&snap[(int64_t)m * Hd * D + 32 * kk] = wb[m][kk];
                 }
 #pragma unroll
-                for (int ty = 0; ty < 6; ++ty)
-                    *(bf16x4*)(smem + dt_off(ty, jl, 4 * gr + qd) + 8 * lg) =
-                        pack4(o[ty][0], o[ty][1], o[ty][2], o[ty][3]);
+                for (int i = 0; i < 8; ++i) {
+                    const f32x4 mm = acc[m][0][i];
+                    acc[m][1][i] = A * acc[m][1][i] - gamma * mm;
+                    acc[m][0][i] = Bb * mm;
+                }
             }
         }
-        __syncthreads();
+
+        // ---- next block's K/V/coefficients copy runs behind this block's work
+        if (blk + 1 < nblk) issue_block(blk + 1, next);
+
+        // ---- grad + backward per 16-token tile; factors go straight into B operands
+        // f[x][kk]: x = 1M, 1W, 3M, 3W, 2M, 2W; kk = 32-token half of the block
+        bf16x8 f[6][2];
+        f32x4 lo[6];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            f32x4 h1 = {0.f, 0.f, 0.f, 0.f}, h3 = h1, hv = h1;
+            const int t = 16 * ti + jl;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 ak = *(const bf16x8*)(kbuf + row_off(t, 4 * kk + g));
+                const bf16x8 av = *(const bf16x8*)(vbuf + row_off(t, 4 * kk + g));
+                h1 = mfma16(ak, wb[0][kk], h1);
+                h3 = mfma16(ak, wb[1][kk], h3);
+                hv = mfma16(av, wb[2][kk], hv);
+            }
+            // lane (jl, g) register r: token 16ti + 4g + r, hidden unit j
+            const f32x4 cm = *(const f32x4*)&cob[16 * ti + 4 * g];
+            const f32x4 cw = *(const f32x4*)&cob[64 + 16 * ti + 4 * g];
+            f32x4 o[6];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x1 = h1[r], x3 = h3[r], y = hv[r];
+                const float sg = fast_sigmoid(x1);
+                const float s1 = x1 * sg;
+                const float u = s1 * x3;
+                const float ds = sg + s1 * (1.f - sg);
+                const float av = y * x3 * ds;
+                const float bv = y * s1;
+                const float ncm = -cm[r], cwr = cw[r];
+                o[0][r] = ncm * av;
+                o[1][r] = cwr * av;
+                o[2][r] = ncm * bv;
+                o[3][r] = cwr * bv;
+                o[4][r] = ncm * u;
+                o[5][r] = cwr * u;
+            }
+            if (ti & 1) {
+#pragma unroll
+                for (int x = 0; x < 6; ++x) f[x][ti >> 1] = pack8(lo[x], o[x]);
+            } else {
+#pragma unroll
+                for (int x = 0; x < 6; ++x) lo[x] = o[x];
+            }
+        }
 
         // ---- aggregation into the resident state
-        {
-            const unsigned char* kbuf = smem + OFF_KV + (2 * buf) * KV_BYTES;
-            const unsigned char* vbuf = kbuf + KV_BYTES;
-            const int jl = 32 * hh + li;
 #pragma unroll
-            for (int ks = 0; ks < CB / 16; ++ks) {
-                const int rb0 = 16 * ks + 8 * lg, rb1 = rb0 + 4;
-                bf16x8 ak[2], av[2];
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    ak[rr] = tr_frag(kbuf, rb0, rb1, 32 * (rt0 + rr), lane);
-                    av[rr] = tr_frag(vbuf, rb0, rb1, 32 * (rt0 + rr), lane);
-                }
-#pragma unroll
-                for (int m = 0; m < 3; ++m) {
-                    const bf16x8 bm = *(const bf16x8*)(smem + dt_off(2 * m, jl, 2 * ks + lg));
-                    const bf16x8 bw = *(const bf16x8*)(smem + dt_off(2 * m + 1, jl, 2 * ks + lg));
-#pragma unroll
-                    for (int rr = 0; rr < 2; ++rr) {
-                        const bf16x8 x = (m < 2) ? ak[rr] : av[rr];
-                        acc[rr][2 * m] = mfma32(x, bm, acc[rr][2 * m]);
-                        acc[rr][2 * m + 1] = mfma32(x, bw, acc[rr][2 * m + 1]);
-                    }
-                }
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 kt = trT(kbuf, i, 32 * kk, lane);
+                const bf16x8 vt = trT(vbuf, i, 32 * kk, lane);
+                acc[0][0][i] = mfma16(kt, f[0][kk], acc[0][0][i]);
+                acc[0][1][i] = mfma16(kt, f[1][kk], acc[0][1][i]);
+                acc[1][0][i] = mfma16(kt, f[2][kk], acc[1][0][i]);
+                acc[1][1][i] = mfma16(kt, f[3][kk], acc[1][1][i]);
+                acc[2][0][i] = mfma16(vt, f[4][kk], acc[2][0][i]);
+                acc[2][1][i] = mfma16(vt, f[5][kk], acc[2][1][i]);
             }
         }
-        wait_vmem();  // this wave's share of the next block's K/V has landed
+        wait_vmem();  // this wave's share of the next block has landed
         __syncthreads();
+    };
+    for (int blk = 0; blk < nblk; blk += 2) {
+        block(blk, lds0, lds1);
+        if (blk + 1 < nblk) block(blk + 1, lds1, lds0);
     }
 
-    float* We = a.W_end + bh * P;
-    float* Me = a.M_end + bh * P;
-    state_io<true>(acc, We, Me, rt0, hh, j0, Hd, laneA, laneB);
+    state_io<true>(acc, a.W_end + bh * P, a.M_end + bh * P, j, g, Hd);
 }
 
 // ---------------------------------------------------------------------------
