@@ -70,6 +70,9 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
+// dword 3 of a raw buffer resource (gfx9 family: 32-bit data format, no swizzle)
+constexpr int RSRC_W3 = 0x00020000;
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // 16-byte chunk swizzle of a 256-byte row t (row-major [t][128] bf16): the 8
@@ -136,17 +139,21 @@ struct LoopArgs {
 //   K [64 tokens][128] bf16 | V [64][128] bf16 | cM [64] f32 | cW [64] f32 |
 //   (A, Bb, gamma, -) of the block's chunk.
 // Rows are 256 bytes; 16-byte chunk c of row t sits at physical chunk
-// c ^ swz3(t).  swz3 spreads the 8 rows read at one chunk by ds_read_b128
-// over 8 bank groups, and the 4 rows x 4 chunks of one 16-lane transpose
-// read (all in one 8-byte half) over all 16 eight-byte bank slots.
+// c ^ swz4(t).  The LDS has 64 four-byte banks (256 bytes per clock):
+// ds_read_b128 serves 16 lanes at a time, here 16 consecutive rows at one
+// chunk, which swz4 (a permutation of the 16 chunks over t mod 16) spreads
+// over all 64 banks; ds_read_b64_tr_b16 serves 32 lanes at a time, here 8
+// consecutive rows x 4 chunks x one 8-byte half per chunk pair, which swz4
+// (bits 0, 2, 3 of the permutation taken from the row, bit 1 from row bit 3)
+// also spreads over all 64 banks.
 constexpr int KV_BYTES = 64 * 256;
 constexpr int CO_BYTES = 2 * 64 * 4 + 16;
 constexpr int BUF_BYTES = 2 * KV_BYTES + CO_BYTES;
 constexpr int LOOP_LDS = 2 * BUF_BYTES;
 
-__device__ __forceinline__ int swz3(int t) { return (t & 1) | ((t & 2) << 1) | ((t & 4) >> 1); }
+__device__ __forceinline__ int swz4(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
 
-__device__ __forceinline__ int row_off(int t, int chunk) { return t * 256 + 16 * (chunk ^ swz3(t)); }
+__device__ __forceinline__ int row_off(int t, int chunk) { return t * 256 + 16 * (chunk ^ swz4(t)); }
 
 // Row permutation of the state tiles.  Accumulator tile i (16 rows of d)
 // holds, in its row 4g + r (lane group g, register r),
@@ -169,9 +176,9 @@ __device__ __forceinline__ bf16x8 trT(const unsigned char* buf, int i, int tb, i
     const int chunk = dq >> 3, half = (dq >> 2) & 1;
     const int r0 = tb + 4 * g + (p >> 2), r1 = r0 + 16;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swz3(r0)) + 8 * half));
+        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swz4(r0)) + 8 * half));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swz3(r1)) + 8 * half));
+        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swz4(r1)) + 8 * half));
     bf16x8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -259,36 +266,48 @@ swiglu_loop_kernel(LoopArgs a) {
 
     // HBM -> LDS copy of one token block: wave w moves K and V rows
     // [16w, 16w+16), 4 rows (1 KB) per instruction; lane L writes row r0 + L/16
-    // at physical chunk L%16, which holds logical chunk (L%16) ^ swz3(row).
+    // at physical chunk L%16, which holds logical chunk (L%16) ^ swz4(row).
     // Wave 0 also moves the block's cM (lanes 0..15), cW (lanes 16..31) and
-    // the (A, Bb, gamma) of the block's chunk (lane 32).
+    // the (A, Bb, gamma) of the block's chunk (lane 32); lane L of a copy
+    // writes 16 bytes at destination + 16 L.
     const int nblk = (int)(T / CB);
     const int bpc = a.C / CB;
 
-    // Per-lane byte offsets of the copy (uniform block base + 32-bit lane
-    // offset keeps the addresses in scalar registers).
+    // The copies use the buffer (MUBUF) form of the direct HBM->LDS load:
+    // unlike the global form it is not a FLAT instruction, so while it is in
+    // flight the compiler can still wait for individual LDS reads instead of
+    // draining all of them.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, (int)(T * D * 2), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, (int)(T * D * 2), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc((void*)cMb, 0, (int)(T * 4), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)cWb, 0, (int)(T * 4), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.scal + bh * a.nc * 4), 0, a.nc * 16, RSRC_W3);
     unsigned koff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * wave + 4 * i + (lane >> 4);
-        koff[i] = (unsigned)(row * D + 8 * ((lane & 15) ^ swz3(row))) * 2u;
+        koff[i] = (unsigned)(row * D + 8 * ((lane & 15) ^ swz4(row))) * 2u;
     }
     const unsigned coff = 16u * (unsigned)(lane & 15);
     auto issue_block = [&](int blk, unsigned char* dst) {
-        const int64_t tb = (int64_t)blk * CB;
+        const unsigned tbb = (unsigned)blk * CB * D * 2;  // byte offset of the block in K / V
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const char* src = (const char*)((m == 0 ? kb : vb) + tb * D);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
-                                                 (lds_void_t*)(dst + m * KV_BYTES + (16 * wave + 4 * i) * 256), 16,
-                                                 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(dst + (16 * wave + 4 * i) * 256), 16, koff[i],
+                                                     tbb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(dst + KV_BYTES + (16 * wave + 4 * i) * 256), 16,
+                                                     koff[i], tbb, 0, 0);
         }
-        if (wave == 0 && lane <= 32) {
-            const char* src = lane < 32 ? (const char*)((lane < 16 ? cMb : cWb) + tb) + coff
-                                        : (const char*)(a.scal + (bh * a.nc + blk / bpc) * 4);
-            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + 2 * KV_BYTES), 16, 0, 0);
+        if (wave == 0) {
+            lds_void_t* cdst = (lds_void_t*)(dst + 2 * KV_BYTES);
+            const unsigned cb = (unsigned)blk * CB * 4;
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, cdst, 16, coff, cb, 0, 0);
+            else if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, cdst, 16, coff, cb, 0, 0);
+            else if (lane == 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, cdst, 16, 0, (unsigned)(blk / bpc) * 16, 0, 0);
         }
     };
 
@@ -331,21 +350,53 @@ swiglu_loop_kernel(LoopArgs a) {
         // ---- next block's K/V/coefficients copy runs behind this block's work
         if (blk + 1 < nblk) issue_block(blk + 1, next);
 
-        // ---- grad + backward per 16-token tile; factors go straight into B operands
-        // f[x][kk]: x = 1M, 1W, 3M, 3W, 2M, 2W; kk = 32-token half of the block
+        // ---- grad + backward per 16-token tile; factors go straight into B
+        // operands.  The aggregation of the first 32 tokens is interleaved with
+        // the grad of the last two tiles; every LDS fragment is read one step
+        // before the MFMAs that use it.
+        // f[x][h]: x = 1M, 1W, 3M, 3W, 2M, 2W; h = 32-token half of the block
         bf16x8 f[6][2];
         f32x4 lo[6];
+        auto gfrag = [&](const unsigned char* b, int s) {
+            return *(const bf16x8*)(b + row_off(16 * (s >> 2) + jl, 4 * (s & 3) + g));
+        };
+        bf16x8 gk = gfrag(kbuf, 0), gv = gfrag(vbuf, 0);  // grad step s = 4 ti + kk
+        bf16x8 tk, tv;                                      // aggregation step u = 8 h + i
+        auto agg = [&](int u, bf16x8 kt, bf16x8 vt) {
+            const int h = u >> 3, i = u & 7;
+            acc[0][0][i] = mfma16(kt, f[0][h], acc[0][0][i]);
+            acc[0][1][i] = mfma16(kt, f[1][h], acc[0][1][i]);
+            acc[1][0][i] = mfma16(kt, f[2][h], acc[1][0][i]);
+            acc[1][1][i] = mfma16(kt, f[3][h], acc[1][1][i]);
+            acc[2][0][i] = mfma16(vt, f[4][h], acc[2][0][i]);
+            acc[2][1][i] = mfma16(vt, f[5][h], acc[2][1][i]);
+        };
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             f32x4 h1 = {0.f, 0.f, 0.f, 0.f}, h3 = h1, hv = h1;
-            const int t = 16 * ti + jl;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 ak = *(const bf16x8*)(kbuf + row_off(t, 4 * kk + g));
-                const bf16x8 av = *(const bf16x8*)(vbuf + row_off(t, 4 * kk + g));
+                const bf16x8 ak = gk, av = gv;
+                const int s = 4 * ti + kk + 1;
+                if (s < 16) {
+                    gk = gfrag(kbuf, s);
+                    gv = gfrag(vbuf, s);
+                }
+                bf16x8 ck = tk, cv = tv;
+                const int u = 4 * (ti - 2) + kk;  // aggregation step run in this grad step
+                if (ti == 1 && kk == 3) {
+                    tk = trT(kbuf, 0, 0, lane);
+                    tv = trT(vbuf, 0, 0, lane);
+                } else if (ti >= 2) {
+                    tk = trT(kbuf, (u + 1) & 7, 32 * ((u + 1) >> 3), lane);
+                    tv = trT(vbuf, (u + 1) & 7, 32 * ((u + 1) >> 3), lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 h1 = mfma16(ak, wb[0][kk], h1);
                 h3 = mfma16(ak, wb[1][kk], h3);
                 hv = mfma16(av, wb[2][kk], hv);
+                if (ti >= 2) agg(u, ck, cv);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // lane (jl, g) register r: token 16ti + 4g + r, hidden unit j
             const f32x4 cm = *(const f32x4*)&cob[16 * ti + 4 * g];
@@ -377,20 +428,17 @@ swiglu_loop_kernel(LoopArgs a) {
             }
         }
 
-        // ---- aggregation into the resident state
+        // ---- aggregation of the second 32 tokens
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 kt = trT(kbuf, i, 32 * kk, lane);
-                const bf16x8 vt = trT(vbuf, i, 32 * kk, lane);
-                acc[0][0][i] = mfma16(kt, f[0][kk], acc[0][0][i]);
-                acc[0][1][i] = mfma16(kt, f[1][kk], acc[0][1][i]);
-                acc[1][0][i] = mfma16(kt, f[2][kk], acc[1][0][i]);
-                acc[1][1][i] = mfma16(kt, f[3][kk], acc[1][1][i]);
-                acc[2][0][i] = mfma16(vt, f[4][kk], acc[2][0][i]);
-                acc[2][1][i] = mfma16(vt, f[5][kk], acc[2][1][i]);
+        for (int u = 8; u < 16; ++u) {
+            const bf16x8 ck = tk, cv = tv;
+            if (u + 1 < 16) {
+                tk = trT(kbuf, (u + 1) & 7, 32, lane);
+                tv = trT(vbuf, (u + 1) & 7, 32, lane);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            agg(u, ck, cv);
+            __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmem();  // this wave's share of the next block has landed
         __syncthreads();
