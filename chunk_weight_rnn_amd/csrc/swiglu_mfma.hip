@@ -45,6 +45,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -135,9 +136,9 @@ struct LoopArgs {
     int Hd, C, nc, nsl, nwg, xcd_map;
 };
 
-// LDS of the loop kernel: two buffers of one token block each,
-//   K [64 tokens][128] bf16 | V [64][128] bf16 | cM [64] f32 | cW [64] f32 |
-//   (A, Bb, gamma, -) of the block's chunk.
+// LDS of the loop kernel: two buffers of one token block each (TBK = 64 SB
+// tokens): K [TBK][128] bf16 | V [TBK][128] bf16 | cM [TBK] f32 | cW [TBK] f32
+// (| unused up to 1 KB) | (A, Bb, gamma, -) of the block's chunk.
 // Rows are 256 bytes; 16-byte chunk c of row t sits at physical chunk
 // c ^ swz4(t).  The LDS has 64 four-byte banks (256 bytes per clock):
 // ds_read_b128 serves 16 lanes at a time, here 16 consecutive rows at one
@@ -146,11 +147,6 @@ struct LoopArgs {
 // consecutive rows x 4 chunks x one 8-byte half per chunk pair, which swz4
 // (bits 0, 2, 3 of the permutation taken from the row, bit 1 from row bit 3)
 // also spreads over all 64 banks.
-constexpr int KV_BYTES = 64 * 256;
-constexpr int CO_BYTES = 2 * 64 * 4 + 16;
-constexpr int BUF_BYTES = 2 * KV_BYTES + CO_BYTES;
-constexpr int LOOP_LDS = 2 * BUF_BYTES;
-
 __device__ __forceinline__ int swz4(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
 
 __device__ __forceinline__ int row_off(int t, int chunk) { return t * 256 + 16 * (chunk ^ swz4(t)); }
@@ -228,8 +224,8 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 // One workgroup = one (b, h, 64-unit hidden slice) for the whole sequence.
 // Wavefront w owns hidden units j0 + 16w .. +15 of the slice in all three
 // matrices: their fp32 M and W (6 x 128 x 16 per wave) stay in accumulator
-// registers, and the chunk-start weights as bf16 grad operands.  Per 64-token
-// block every wave
+// registers, and the chunk-start weights as bf16 grad operands.  Tokens go
+// through LDS in blocks of SB sub-blocks of 64; per sub-block every wave runs
 //   grad:      H1, H3 = K W1, K W3 and HV = V W2^T for its 16 units
 //              (16x16x32 MFMA, K/V rows from LDS),
 //   backward:  the six coefficient-scaled factors, converted in registers
@@ -237,13 +233,30 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 //   aggregate: state += K^T F1, K^T F3, V^T F2 (K^T, V^T by transpose reads),
 // so the only data the waves share is the K/V/coefficient block in LDS, and
 // one barrier per block guards its double buffer.
+//
+// Within a block the three stages run as one software pipeline of
+// 16 SB + 12 steps; sub-block s occupies local steps ls = step - 16 s:
+//   ls  0..15  grad of tile ls/4, k-step ls%4       (3 MFMA)
+//   ls  4..19  backward of tile ls/4 - 1, row ls%4 (VALU)
+//   ls 12..27  aggregation step u = ls - 12         (6 MFMA)
+// so the MFMA-only head of one sub-block overlaps the backward of the
+// previous one.  sched_barrier keeps every step's work together; grad
+// fragments are read one step ahead, aggregation fragments two, and the next
+// block's HBM->LDS copies are spread over the first steps.
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 swiglu_loop_kernel(LoopArgs a) {
+    constexpr int SB = 1;                        // 64-token sub-blocks per LDS block
+    constexpr int TBK = CB * SB;                 // tokens per LDS block
+    constexpr int KVB = TBK * 256;               // one [TBK][128] bf16 matrix
+    constexpr int COB = 1024 + 16;               // cM | cW (| unused) | (A, Bb, gamma, -)
+    constexpr int BUFB = 2 * KVB + COB;
+    constexpr int NSTEP = 16 * SB + 12;
+    constexpr int NKV = 4 * SB;                  // copy instructions per matrix per wave
+    constexpr int AGG_AHEAD = SB == 1 ? 2 : 1;   // aggregation fragments are read this many steps ahead
     // Two LDS buffers as separate arrays: the compiler can then tell the
-    // next block's in-flight HBM->LDS copies from this block's LDS reads and
-    // need not wait for the copies before every transpose read.
-    __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
+    // next block's in-flight HBM->LDS copies from this block's LDS reads.
+    __shared__ __attribute__((aligned(16))) unsigned char lds0[BUFB];
+    __shared__ __attribute__((aligned(16))) unsigned char lds1[BUFB];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -258,57 +271,55 @@ swiglu_loop_kernel(LoopArgs a) {
     const int64_t j = (int64_t)(L_id % a.nsl) * S + 16 * wave + jl;  // this lane's hidden unit
     const int64_t T = a.T;
     const int64_t P = 3 * (int64_t)D * Hd;
+    const int nblk = (int)(T / TBK);
+    const int bpc = a.C / TBK;
 
+    // HBM -> LDS copies of one block (buffer / MUBUF form of the direct
+    // load: unlike the global form it is not a FLAT instruction, so while it
+    // is in flight the compiler still waits for individual LDS reads).  Lane L
+    // of a copy writes 16 bytes at destination + 16 L.  Wave w moves K and V
+    // rows [TBK/4 w, TBK/4 (w+1)), 4 rows per instruction: lane L loads
+    // row r0 + L/16, chunk (L%16) ^ swz4(row), which lands at physical chunk
+    // L%16.  Wave 0 also moves the block's cM and cW (one instruction; cM and
+    // cW are addressed from one resource based at cM) and the (A, Bb, gamma)
+    // of the block's chunk.  Copies past the end of the sequence (the block
+    // after the last) fall outside the resources' ranges and read zeros.
     const __bf16* kb = a.k + bh * T * D;
     const __bf16* vb = a.v + bh * T * D;
     const float* cMb = a.cM + bh * T;
-    const float* cWb = a.cW + bh * T;
-
-    // HBM -> LDS copy of one token block: wave w moves K and V rows
-    // [16w, 16w+16), 4 rows (1 KB) per instruction; lane L writes row r0 + L/16
-    // at physical chunk L%16, which holds logical chunk (L%16) ^ swz4(row).
-    // Wave 0 also moves the block's cM (lanes 0..15), cW (lanes 16..31) and
-    // the (A, Bb, gamma) of the block's chunk (lane 32); lane L of a copy
-    // writes 16 bytes at destination + 16 L.
-    const int nblk = (int)(T / CB);
-    const int bpc = a.C / CB;
-
-    // The copies use the buffer (MUBUF) form of the direct HBM->LDS load:
-    // unlike the global form it is not a FLAT instruction, so while it is in
-    // flight the compiler can still wait for individual LDS reads instead of
-    // draining all of them.
+    const unsigned cw_rel = (unsigned)((const char*)(a.cW + bh * T) - (const char*)cMb);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, (int)(T * D * 2), RSRC_W3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, (int)(T * D * 2), RSRC_W3);
-    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc((void*)cMb, 0, (int)(T * 4), RSRC_W3);
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)cWb, 0, (int)(T * 4), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t crs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cMb, 0, (int)(cw_rel + T * 4), RSRC_W3);
     const __amdgpu_buffer_rsrc_t srs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.scal + bh * a.nc * 4), 0, a.nc * 16, RSRC_W3);
-    unsigned koff[4];
+    unsigned koff[NKV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < NKV; ++i) {
+        const int row = (TBK / 4) * wave + 4 * i + (lane >> 4);
         koff[i] = (unsigned)(row * D + 8 * ((lane & 15) ^ swz4(row))) * 2u;
     }
-    const unsigned coff = 16u * (unsigned)(lane & 15);
-    auto issue_block = [&](int blk, unsigned char* dst) {
-        const unsigned tbb = (unsigned)blk * CB * D * 2;  // byte offset of the block in K / V
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(dst + (16 * wave + 4 * i) * 256), 16, koff[i],
-                                                     tbb, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(dst + KV_BYTES + (16 * wave + 4 * i) * 256), 16,
-                                                     koff[i], tbb, 0, 0);
+    const unsigned coff = lane < 16 * SB ? 16u * lane
+                        : lane < 32 * SB ? cw_rel + 16u * (lane - 16 * SB)
+                                         : 16u * (lane - 32 * SB);
+    // copy instruction n (0 <= n < 2 NKV + 1) of block blk into dst
+    auto issue = [&](int n, int blk, unsigned char* dst) {
+        const unsigned tbb = (unsigned)blk * TBK * D * 2;
+        if (n < 2 * NKV) {
+            const int m = n & 1, i = n >> 1;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? vrs : krs,
+                                                     (lds_void_t*)(dst + m * KVB + ((TBK / 4) * wave + 4 * i) * 256),
+                                                     16, koff[i], tbb, 0, 0);
+        } else if (wave == 0) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (lds_void_t*)(dst + 2 * KVB), 16, coff,
+                                                     (unsigned)blk * TBK * 4, 0, 0);
         }
-        if (wave == 0) {
-            lds_void_t* cdst = (lds_void_t*)(dst + 2 * KV_BYTES);
-            const unsigned cb = (unsigned)blk * CB * 4;
-            if (lane < 16)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, cdst, 16, coff, cb, 0, 0);
-            else if (lane < 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, cdst, 16, coff, cb, 0, 0);
-            else if (lane == 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, cdst, 16, 0, (unsigned)(blk / bpc) * 16, 0, 0);
-        }
+    };
+    auto issue_scal = [&](int blk, unsigned char* dst) {
+        if (wave == 0 && lane == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void_t*)(dst + 2 * KVB + 1024), 16, 0,
+                                                     (unsigned)(blk / bpc) * 16, 0, 0);
     };
 
     f32x4 acc[3][2][8];
@@ -317,26 +328,38 @@ swiglu_loop_kernel(LoopArgs a) {
     const bool godd = (g & 1) != 0;
     bf16x8 wb[3][4];  // chunk-start weights as grad B operands: k-slot e of lane group g is d = 32kk + 8g + e
 
-    issue_block(0, lds0);
+#pragma unroll
+    for (int n = 0; n < 2 * NKV + 1; ++n) issue(n, 0, lds0);
+    issue_scal(0, lds0);
     wait_vmem();
     __syncthreads();
 
     auto block = [&](int blk, const unsigned char* kbuf, unsigned char* next) {
-        const unsigned char* vbuf = kbuf + KV_BYTES;
-        const float* cob = (const float*)(kbuf + 2 * KV_BYTES);
+        const unsigned char* vbuf = kbuf + KVB;
+        const float* cob = (const float*)(kbuf + 2 * KVB);
         if (blk % bpc == 0) {
             // ---- chunk start: grad operands + bf16 snapshot from W, then rescale the state
             const int c = blk / bpc;
-            const f32x4 sc = *(const f32x4*)&cob[128];
+            const f32x4 sc = *(const f32x4*)&cob[256];
             const float A = sc[0], Bb = sc[1], gamma = sc[2];
             __bf16* snap = a.snap + (bh * a.nc + c) * P + j * D + 8 * g;
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const f32x4 t0 = acc[m][1][2 * kk], t1 = acc[m][1][2 * kk + 1];
-                    wb[m][kk] = godd ? pack8(t1, t0) : pack8(t0, t1);
-                    *(bf16x8*)&snap[(int64_t)m * Hd * D + 32 * kk] = wb[m][kk];
+                    const bf16x4 t0 = pack4(acc[m][1][2 * kk][0], acc[m][1][2 * kk][1], acc[m][1][2 * kk][2],
+                                            acc[m][1][2 * kk][3]);
+                    const bf16x4 t1 = pack4(acc[m][1][2 * kk + 1][0], acc[m][1][2 * kk + 1][1],
+                                            acc[m][1][2 * kk + 1][2], acc[m][1][2 * kk + 1][3]);
+                    const bf16x4 lo = godd ? t1 : t0, hi = godd ? t0 : t1;
+                    bf16x8 w8;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        w8[e] = lo[e];
+                        w8[4 + e] = hi[e];
+                    }
+                    wb[m][kk] = w8;
+                    *(bf16x8*)&snap[(int64_t)m * Hd * D + 32 * kk] = w8;
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -346,98 +369,118 @@ swiglu_loop_kernel(LoopArgs a) {
                 }
             }
         }
+        issue_scal(blk + 1, next);
 
-        // ---- next block's K/V/coefficients copy runs behind this block's work
-        if (blk + 1 < nblk) issue_block(blk + 1, next);
-
-        // ---- grad + backward per 16-token tile; factors go straight into B
-        // operands.  The aggregation of the first 32 tokens is interleaved with
-        // the grad of the last two tiles; every LDS fragment is read one step
-        // before the MFMAs that use it.
-        // f[x][h]: x = 1M, 1W, 3M, 3W, 2M, 2W; h = 32-token half of the block
-        bf16x8 f[6][2];
-        f32x4 lo[6];
-        auto gfrag = [&](const unsigned char* b, int s) {
-            return *(const bf16x8*)(b + row_off(16 * (s >> 2) + jl, 4 * (s & 3) + g));
+        // f[s][x][h]: factors of sub-block s; x = 1M, 1W, 3M, 3W, 2M, 2W; h = 32-token half
+        bf16x8 f[SB][6][2];
+        f32x4 hg[SB][4][3];     // grad accumulators per sub-block and tile
+        float ob[SB][6];        // backward outputs of the last even token row
+        bf16x2 pr[SB][6][4];    // packed factor pairs of the current tile pair
+        f32x4 cm[SB], cw[SB];   // coefficients of the tile being processed
+        auto gfrag = [&](const unsigned char* b, int gs) {  // grad step gs = 16 s + 4 ti + kk
+            const int s = gs >> 4, l = gs & 15;
+            return *(const bf16x8*)(b + row_off(64 * s + 16 * (l >> 2) + jl, 4 * (l & 3) + g));
         };
-        bf16x8 gk = gfrag(kbuf, 0), gv = gfrag(vbuf, 0);  // grad step s = 4 ti + kk
-        bf16x8 tk, tv;                                      // aggregation step u = 8 h + i
-        auto agg = [&](int u, bf16x8 kt, bf16x8 vt) {
+        auto afrag = [&](const unsigned char* b, int s, int u) { return trT(b, u & 7, 64 * s + 32 * (u >> 3), lane); };
+        // backward for token row r of tile ti of sub-block s:
+        // du = -hv: 1M = -cm*a, 1W = cw*a, 3M = -cm*b, 3W = cw*b, 2M = -cm*u,
+        // 2W = cw*u, where a = hv*h3*silu'(h1), b = hv*silu(h1)
+        auto backward = [&](int s, int ti, int r) {
+            if (r == 0) {
+                cm[s] = *(const f32x4*)&cob[64 * s + 16 * ti + 4 * g];
+                cw[s] = *(const f32x4*)&cob[64 * SB + 64 * s + 16 * ti + 4 * g];
+            }
+            const float x1 = hg[s][ti][0][r], x3 = hg[s][ti][1][r], y = hg[s][ti][2][r];
+            const float sg = fast_sigmoid(x1);
+            const float s1 = x1 * sg;
+            const float u = s1 * x3;
+            const float ds = sg + s1 * (1.f - sg);
+            const float av = y * x3 * ds;
+            const float bv = y * s1;
+            const float ncm = -cm[s][r], cwr = cw[s][r];
+            float o[6];
+            o[0] = ncm * av;
+            o[1] = cwr * av;
+            o[2] = ncm * bv;
+            o[3] = cwr * bv;
+            o[4] = ncm * u;
+            o[5] = cwr * u;
+            if ((r & 1) == 0) {
+#pragma unroll
+                for (int x = 0; x < 6; ++x) ob[s][x] = o[x];
+                return;
+            }
+            // rows r-1, r of the tile -> bf16 pair at position r/2 of the tile's half
+#pragma unroll
+            for (int x = 0; x < 6; ++x) {
+                bf16x2 p2;
+                p2[0] = (__bf16)ob[s][x];
+                p2[1] = (__bf16)o[x];
+                pr[s][x][(ti & 1) * 2 + (r >> 1)] = p2;
+            }
+            if (r == 3 && (ti & 1)) {
+#pragma unroll
+                for (int x = 0; x < 6; ++x) {
+                    bf16x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v8[2 * e] = pr[s][x][e][0];
+                        v8[2 * e + 1] = pr[s][x][e][1];
+                    }
+                    f[s][x][ti >> 1] = v8;
+                }
+            }
+        };
+        auto agg = [&](int s, int u, bf16x8 kt, bf16x8 vt) {
             const int h = u >> 3, i = u & 7;
-            acc[0][0][i] = mfma16(kt, f[0][h], acc[0][0][i]);
-            acc[0][1][i] = mfma16(kt, f[1][h], acc[0][1][i]);
-            acc[1][0][i] = mfma16(kt, f[2][h], acc[1][0][i]);
-            acc[1][1][i] = mfma16(kt, f[3][h], acc[1][1][i]);
-            acc[2][0][i] = mfma16(vt, f[4][h], acc[2][0][i]);
-            acc[2][1][i] = mfma16(vt, f[5][h], acc[2][1][i]);
+            acc[0][0][i] = mfma16(kt, f[s][0][h], acc[0][0][i]);
+            acc[0][1][i] = mfma16(kt, f[s][1][h], acc[0][1][i]);
+            acc[1][0][i] = mfma16(kt, f[s][2][h], acc[1][0][i]);
+            acc[1][1][i] = mfma16(kt, f[s][3][h], acc[1][1][i]);
+            acc[2][0][i] = mfma16(vt, f[s][4][h], acc[2][0][i]);
+            acc[2][1][i] = mfma16(vt, f[s][5][h], acc[2][1][i]);
         };
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            f32x4 h1 = {0.f, 0.f, 0.f, 0.f}, h3 = h1, hv = h1;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 ak = gk, av = gv;
-                const int s = 4 * ti + kk + 1;
-                if (s < 16) {
-                    gk = gfrag(kbuf, s);
-                    gv = gfrag(vbuf, s);
-                }
-                bf16x8 ck = tk, cv = tv;
-                const int u = 4 * (ti - 2) + kk;  // aggregation step run in this grad step
-                if (ti == 1 && kk == 3) {
-                    tk = trT(kbuf, 0, 0, lane);
-                    tv = trT(vbuf, 0, 0, lane);
-                } else if (ti >= 2) {
-                    tk = trT(kbuf, (u + 1) & 7, 32 * ((u + 1) >> 3), lane);
-                    tv = trT(vbuf, (u + 1) & 7, 32 * ((u + 1) >> 3), lane);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                h1 = mfma16(ak, wb[0][kk], h1);
-                h3 = mfma16(ak, wb[1][kk], h3);
-                hv = mfma16(av, wb[2][kk], hv);
-                if (ti >= 2) agg(u, ck, cv);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // lane (jl, g) register r: token 16ti + 4g + r, hidden unit j
-            const f32x4 cm = *(const f32x4*)&cob[16 * ti + 4 * g];
-            const f32x4 cw = *(const f32x4*)&cob[64 + 16 * ti + 4 * g];
-            f32x4 o[6];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x1 = h1[r], x3 = h3[r], y = hv[r];
-                const float sg = fast_sigmoid(x1);
-                const float s1 = x1 * sg;
-                const float u = s1 * x3;
-                const float ds = sg + s1 * (1.f - sg);
-                const float av = y * x3 * ds;
-                const float bv = y * s1;
-                const float ncm = -cm[r], cwr = cw[r];
-                o[0][r] = ncm * av;
-                o[1][r] = cwr * av;
-                o[2][r] = ncm * bv;
-                o[3][r] = cwr * bv;
-                o[4][r] = ncm * u;
-                o[5][r] = cwr * u;
-            }
-            if (ti & 1) {
-#pragma unroll
-                for (int x = 0; x < 6; ++x) f[x][ti >> 1] = pack8(lo[x], o[x]);
-            } else {
-#pragma unroll
-                for (int x = 0; x < 6; ++x) lo[x] = o[x];
-            }
-        }
 
-        // ---- aggregation of the second 32 tokens
+        bf16x8 gk = gfrag(kbuf, 0), gv = gfrag(vbuf, 0);
+        bf16x8 tk[3], tv[3];  // aggregation fragments, ring of 3
 #pragma unroll
-        for (int u = 8; u < 16; ++u) {
-            const bf16x8 ck = tk, cv = tv;
-            if (u + 1 < 16) {
-                tk = trT(kbuf, (u + 1) & 7, 32, lane);
-                tv = trT(vbuf, (u + 1) & 7, 32, lane);
+        for (int st = 0; st < NSTEP; ++st) {
+            // ---- copies for the next block, LDS reads for later steps
+            if (st < 2 * NKV + 1) issue(st, blk + 1, next);
+            const bf16x8 ak = gk, av = gv;
+            if (st + 1 < 16 * SB) {
+                gk = gfrag(kbuf, st + 1);
+                gv = gfrag(vbuf, st + 1);
+            }
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+                const int ur = st + AGG_AHEAD - 16 * s - 12;
+                if (ur >= 0 && ur < 16) {
+                    tk[(16 * s + ur) % 3] = afrag(kbuf, s, ur);
+                    tv[(16 * s + ur) % 3] = afrag(vbuf, s, ur);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
-            agg(u, ck, cv);
+            // ---- grad MFMAs
+            if (st < 16 * SB) {
+                const int s = st >> 4, ti = (st >> 2) & 3, kk = st & 3;
+                if (kk == 0) {
+                    hg[s][ti][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    hg[s][ti][1] = hg[s][ti][0];
+                    hg[s][ti][2] = hg[s][ti][0];
+                }
+                hg[s][ti][0] = mfma16(ak, wb[0][kk], hg[s][ti][0]);
+                hg[s][ti][1] = mfma16(ak, wb[1][kk], hg[s][ti][1]);
+                hg[s][ti][2] = mfma16(av, wb[2][kk], hg[s][ti][2]);
+            }
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+                const int ls = st - 16 * s;
+                // ---- aggregation MFMAs
+                if (ls >= 12 && ls < 28) agg(s, ls - 12, tk[(ls + 16 * s - 12) % 3], tv[(ls + 16 * s - 12) % 3]);
+                // ---- backward of the previous tile, one token row per step
+                if (ls >= 4 && ls < 20) backward(s, (ls >> 2) - 1, ls & 3);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmem();  // this wave's share of the next block has landed
