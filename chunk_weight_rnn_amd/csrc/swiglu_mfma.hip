@@ -499,10 +499,10 @@ swiglu_loop_kernel(LoopArgs a) {
 // Snapshot layout per (b, h, chunk), bf16, all hidden-major:
 //   W1^T [Hd][D] | W3^T [Hd][D] | W2 [Hd][D].
 // One wavefront per 32 tokens; hidden units stream through LDS 32 at a time
-// (double-buffered, HBM -> LDS copies).  Computed transposed (H^T = W1^T Q^T,
-// out^T = W2^T U^T) so that U^T leaves the first MFMA in the register layout
-// the second one consumes; the W2^T operand comes from the hidden-major stage
-// through the transpose read.
+// in a ring of three stages (two copies in flight while one is consumed).
+// Computed transposed (H^T = W1^T Q^T, out^T = W2^T U^T) so that U^T leaves
+// the first MFMA in the register layout the second one consumes; the W2^T
+// operand comes from the hidden-major stage through the transpose read.
 // ---------------------------------------------------------------------------
 struct ApplyArgs {
     const __bf16* q;
@@ -515,9 +515,51 @@ struct ApplyArgs {
 constexpr int HB = 32;                     // hidden units per stage
 constexpr int STAGE_BYTES = 3 * HB * 256;  // W1^T, W3^T, W2 rows of the stage
 
+// Stage rows are 256 bytes with 16-byte chunk c of row t at physical chunk
+// c ^ swza(t).  The grad-style row reads (16 consecutive rows at one chunk)
+// see a permutation of all 16 chunks, and each 32-lane half of a 32x32
+// transpose fragment (4 consecutive rows x 4 chunks x 2 halves) sees four
+// disjoint 4-chunk groups: conflict-free on the 64 four-byte banks.
+__device__ __forceinline__ int swza(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+// 32x16 MFMA operand fragment transposed out of a swizzled row-major
+// [rows][128] bf16 stage: operand row = source column col0 + lane%32,
+// operand k 0..3 = source rows rbase0..+3, k 4..7 = source rows rbase1..+3.
+__device__ __forceinline__ bf16x8 tr_frag_a(const unsigned char* buf, int rbase0, int rbase1, int col0, int lane) {
+    const int p = lane & 15, G = lane >> 4;
+    const int col = col0 + 16 * (G & 1) + 4 * (p & 3);
+    const int chunk = col >> 3;
+    const int half = p & 1;
+    const int r0 = rbase0 + (p >> 2);
+    const int r1 = rbase1 + (p >> 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swza(r0)) + 8 * half));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swza(r1)) + 8 * half));
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[4 + e] = hi[e];
+    }
+    return r;
+}
+
+// direct HBM->LDS copy of 16 bytes per lane (buffer form; lane L writes
+// dst + 16 L); offsets at or past num_bytes read zeros
+__device__ __forceinline__ void lds_copy16(const void* base, int num_bytes, unsigned char* dst, unsigned voff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, num_bytes, RSRC_W3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, 0, 0, 0);
+}
+
 template <int NWA>
 __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
+    // three stage buffers as separate arrays, so the compiler can tell copies
+    // in flight from the reads of the stage being consumed
+    __shared__ __attribute__((aligned(16))) unsigned char sb0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sb1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sb2[STAGE_BYTES];
+    constexpr int NI = 24 / NWA;  // copy instructions per wave per stage
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 31, lg = lane >> 5;
     const int64_t wg = blockIdx.x;
@@ -529,37 +571,40 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     const int64_t P = 3 * (int64_t)D * Hd;
     const __bf16* sn = a.snap + (bh * a.nc + c) * P;
     const __bf16* qb = a.q + bh * a.T * D;
+    const int nhb = Hd / HB;
 
-    // stage hb -> buffer: 24 instructions of 4 rows (1 KB), spread over the waves
-    auto issue_stage = [&](int hb, int sbuf) {
+    // stage ih -> buffer: 24 copies of 4 rows (1 KB), NI per wave; the two
+    // stages past the last read zeros or rows of this snapshot (never consumed)
+    unsigned voff[NI];
+    int mrow[NI];
 #pragma unroll
-        for (int i = wave; i < 24; i += NWA) {
-            const int m = i >> 3, r0 = 4 * (i & 7);
-            const int row = r0 + (lane >> 4);
-            const int cch = (lane & 15) ^ swz(row);
-            __builtin_amdgcn_global_load_lds((const void*)(sn + (int64_t)m * Hd * D + (int64_t)(hb + row) * D + 8 * cch),
-                                             (lds_void_t*)(smem + sbuf * STAGE_BYTES + m * HB * 256 + r0 * 256), 16,
-                                             0, 0);
-        }
+    for (int n = 0; n < NI; ++n) {
+        const int i = wave + NWA * n;
+        const int m = i >> 3, r0 = 4 * (i & 7);
+        const int row = r0 + (lane >> 4);
+        voff[n] = (unsigned)((m * Hd * D + row * D + 8 * ((lane & 15) ^ swza(row))) * 2);
+        mrow[n] = m * HB * 256 + r0 * 256;
+    }
+    auto issue_stage = [&](int ih, unsigned char* buf) {
+#pragma unroll
+        for (int n = 0; n < NI; ++n) lds_copy16(sn, (int)(P * 2), buf + mrow[n], voff[n] + (unsigned)(ih * HB * D * 2));
     };
 
-    issue_stage(0, 0);
     bf16x8 qf[8];  // Q^T as B operand: col = token, k = d
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)&qb[(t0 + li) * D + 16 * ks + 8 * lg];
-    wait_vmem();
-    __syncthreads();
+    issue_stage(0, sb0);
+    issue_stage(1, sb1);
 
     f32x16 oacc[4] = {};
-    const int nhb = Hd / HB;
-    for (int ih = 0; ih < nhb; ++ih) {
-        const int sbuf = ih & 1;
-        if (ih + 1 < nhb) issue_stage((ih + 1) * HB, sbuf ^ 1);
-        const unsigned char* st = smem + sbuf * STAGE_BYTES;
+    auto stage = [&](int ih, const unsigned char* st, unsigned char* refill) {
+        __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | 0x0F70);  // this stage's copies landed
+        __syncthreads();
+        issue_stage(ih + 2, refill);  // refill = buffer of stage ih - 1, free after the barrier
         f32x16 x1 = {}, x3 = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const int ch = (2 * ks + lg) ^ swz(li);
+            const int ch = (2 * ks + lg) ^ swza(li);
             x1 = mfma32(*(const bf16x8*)(st + li * 256 + 16 * ch), qf[ks], x1);
             x3 = mfma32(*(const bf16x8*)(st + HB * 256 + li * 256 + 16 * ch), qf[ks], x3);
         }
@@ -580,11 +625,16 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         for (int s = 0; s < 2; ++s) {
             const int jb = 16 * s + 4 * lg;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(tr_frag(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
+            for (int dt = 0; dt < 4; ++dt)
+                oacc[dt] = mfma32(tr_frag_a(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
         }
-        wait_vmem();
-        __syncthreads();
+    };
+    for (int ih = 0; ih < nhb; ih += 3) {
+        stage(ih, sb0, sb2);
+        if (ih + 1 < nhb) stage(ih + 1, sb1, sb0);
+        if (ih + 2 < nhb) stage(ih + 2, sb2, sb1);
     }
+    wait_vmem();  // copies of the stages past the last (zeros) before the LDS goes away
     __bf16* ob = a.out + bh * a.T * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
