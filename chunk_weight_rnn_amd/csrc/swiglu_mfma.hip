@@ -241,8 +241,8 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 //   ls 12..27  aggregation step u = ls - 12         (6 MFMA)
 // so the MFMA-only head of one sub-block overlaps the backward of the
 // previous one.  sched_barrier keeps every step's work together; grad
-// fragments are read one step ahead, aggregation fragments two, and the next
-// block's HBM->LDS copies are spread over the first steps.
+// fragments are read two steps ahead, aggregation fragments two, coefficients
+// one, and the next block's HBM->LDS copies are spread over the first steps.
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 swiglu_loop_kernel(LoopArgs a) {
     constexpr int SB = 1;                        // 64-token sub-blocks per LDS block
@@ -250,7 +250,9 @@ swiglu_loop_kernel(LoopArgs a) {
     constexpr int KVB = TBK * 256;               // one [TBK][128] bf16 matrix
     constexpr int COB = 1024 + 16;               // cM | cW (| unused) | (A, Bb, gamma, -)
     constexpr int BUFB = 2 * KVB + COB;
-    constexpr int NSTEP = 16 * SB + 12;
+    constexpr int BOFF = 5;                      // backward of tile t starts at local step 4 t + BOFF
+    constexpr int AOFF = 4 + 2 * 4 + BOFF - 4;   // aggregation step u runs at local step AOFF + u
+    constexpr int NSTEP = 16 * (SB - 1) + AOFF + 16;
     constexpr int NKV = 4 * SB;                  // copy instructions per matrix per wave
     constexpr int AGG_AHEAD = SB == 1 ? 2 : 1;   // aggregation fragments are read this many steps ahead
     // Two LDS buffers as separate arrays: the compiler can then tell the
@@ -377,6 +379,7 @@ swiglu_loop_kernel(LoopArgs a) {
         float ob[SB][6];        // backward outputs of the last even token row
         bf16x2 pr[SB][6][4];    // packed factor pairs of the current tile pair
         f32x4 cm[SB], cw[SB];   // coefficients of the tile being processed
+        f32x4 cmn[SB], cwn[SB]; // ... and of the next one (read a step early)
         auto gfrag = [&](const unsigned char* b, int gs) {  // grad step gs = 16 s + 4 ti + kk
             const int s = gs >> 4, l = gs & 15;
             return *(const bf16x8*)(b + row_off(64 * s + 16 * (l >> 2) + jl, 4 * (l & 3) + g));
@@ -387,8 +390,8 @@ swiglu_loop_kernel(LoopArgs a) {
         // 2W = cw*u, where a = hv*h3*silu'(h1), b = hv*silu(h1)
         auto backward = [&](int s, int ti, int r) {
             if (r == 0) {
-                cm[s] = *(const f32x4*)&cob[64 * s + 16 * ti + 4 * g];
-                cw[s] = *(const f32x4*)&cob[64 * SB + 64 * s + 16 * ti + 4 * g];
+                cm[s] = cmn[s];
+                cw[s] = cwn[s];
             }
             const float x1 = hg[s][ti][0][r], x3 = hg[s][ti][1][r], y = hg[s][ti][2][r];
             const float sg = fast_sigmoid(x1);
@@ -442,19 +445,31 @@ swiglu_loop_kernel(LoopArgs a) {
         };
 
         bf16x8 gk = gfrag(kbuf, 0), gv = gfrag(vbuf, 0);
+        bf16x8 gk2 = gfrag(kbuf, 1), gv2 = gfrag(vbuf, 1);
         bf16x8 tk[3], tv[3];  // aggregation fragments, ring of 3
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             // ---- copies for the next block, LDS reads for later steps
             if (st < 2 * NKV + 1) issue(st, blk + 1, next);
             const bf16x8 ak = gk, av = gv;
-            if (st + 1 < 16 * SB) {
-                gk = gfrag(kbuf, st + 1);
-                gv = gfrag(vbuf, st + 1);
+            gk = gk2;
+            gv = gv2;
+            if (st + 2 < 16 * SB) {
+                gk2 = gfrag(kbuf, st + 2);
+                gv2 = gfrag(vbuf, st + 2);
             }
 #pragma unroll
             for (int s = 0; s < SB; ++s) {
-                const int ur = st + AGG_AHEAD - 16 * s - 12;
+                const int ls = st - 16 * s;  // coefficients of tile ls/4 one step before its backward
+                const int lb = ls + 1 - BOFF;
+                if (lb >= 0 && lb < 16 && (lb & 3) == 0) {
+                    cmn[s] = *(const f32x4*)&cob[64 * s + 16 * (lb >> 2) + 4 * g];
+                    cwn[s] = *(const f32x4*)&cob[64 * SB + 64 * s + 16 * (lb >> 2) + 4 * g];
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+                const int ur = st + AGG_AHEAD - 16 * s - AOFF;
                 if (ur >= 0 && ur < 16) {
                     tk[(16 * s + ur) % 3] = afrag(kbuf, s, ur);
                     tv[(16 * s + ur) % 3] = afrag(vbuf, s, ur);
@@ -477,9 +492,17 @@ swiglu_loop_kernel(LoopArgs a) {
             for (int s = 0; s < SB; ++s) {
                 const int ls = st - 16 * s;
                 // ---- aggregation MFMAs
-                if (ls >= 12 && ls < 28) agg(s, ls - 12, tk[(ls + 16 * s - 12) % 3], tv[(ls + 16 * s - 12) % 3]);
+                if (ls >= AOFF && ls < AOFF + 16)
+                    agg(s, ls - AOFF, tk[(ls + 16 * s - AOFF) % 3], tv[(ls + 16 * s - AOFF) % 3]);
                 // ---- backward of the previous tile, one token row per step
-                if (ls >= 4 && ls < 20) backward(s, (ls >> 2) - 1, ls & 3);
+                if (ls >= BOFF && ls < BOFF + 16) backward(s, (ls - BOFF) >> 2, (ls - BOFF) & 3);
+            }
+            // issue order within the step: each MFMA followed by up to three
+            // VALU instructions, which run while the MFMA executes
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
