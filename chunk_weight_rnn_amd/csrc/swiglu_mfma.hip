@@ -532,7 +532,8 @@ struct ApplyArgs {
     const __bf16* snap;
     __bf16* out;
     int64_t T;
-    int Hd, C, nc, rbc;  // rbc: workgroups per chunk
+    int Hd, C, nc, rbc;  // rbc: items per chunk
+    int nb;              // B H
 };
 
 constexpr int HB = 32;                     // hidden units per stage
@@ -575,6 +576,10 @@ __device__ __forceinline__ void lds_copy16(const void* base, int num_bytes, unsi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, 0, 0, 0);
 }
 
+// Persistent: every workgroup walks a list of items (an item = 32 NWA tokens
+// of one chunk) so the stage copies never stop between items.  Each
+// wavefront copies its own 32 query rows of the next item into its own LDS
+// rows while the current item runs.
 template <int NWA>
 __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     // three stage buffers as separate arrays, so the compiler can tell copies
@@ -582,22 +587,39 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char sb0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char sb1[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char sb2[STAGE_BYTES];
-    constexpr int NI = 24 / NWA;  // copy instructions per wave per stage
+    __shared__ __attribute__((aligned(16))) unsigned char qs[NWA * 32 * 256];  // [wave][32 tokens][128] bf16
+    constexpr int NI = 24 / NWA;  // stage copy instructions per wave per stage
+    constexpr int NQ = 8;         // query copy instructions per wave per item (32 rows, 4 per copy)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 31, lg = lane >> 5;
-    const int64_t wg = blockIdx.x;
-    const int64_t bh = wg / ((int64_t)a.nc * a.rbc);
-    const int rem = (int)(wg % ((int64_t)a.nc * a.rbc));
-    const int c = rem / a.rbc, rb = rem % a.rbc;
     const int Hd = a.Hd;
-    const int64_t t0 = (int64_t)c * a.C + (int64_t)rb * 32 * NWA + 32 * wave;
     const int64_t P = 3 * (int64_t)D * Hd;
-    const __bf16* sn = a.snap + (bh * a.nc + c) * P;
-    const __bf16* qb = a.q + bh * a.T * D;
     const int nhb = Hd / HB;
+    const int64_t nitems = (int64_t)a.nb * a.nc * a.rbc;
+    // items of this workgroup: blockIdx.x + k gridDim.x
+    const int nmine = (int)((nitems - blockIdx.x + gridDim.x - 1) / gridDim.x);
+    unsigned char* qw = qs + wave * 32 * 256;
 
-    // stage ih -> buffer: 24 copies of 4 rows (1 KB), NI per wave; the two
-    // stages past the last read zeros or rows of this snapshot (never consumed)
+    struct Item {
+        const __bf16* sn;  // snapshot of the item's chunk
+        int64_t tok;       // first token (global row in q / out) of this wave
+        int nrec;          // bytes the copies may read (0 past the last item: zeros)
+    };
+    auto item = [&](int k) {
+        Item it;
+        const int64_t x = blockIdx.x + (int64_t)k * gridDim.x;
+        const bool ok = k < nmine;
+        const int64_t xx = ok ? x : 0;
+        const int64_t bh = xx / ((int64_t)a.nc * a.rbc);
+        const int rem = (int)(xx % ((int64_t)a.nc * a.rbc));
+        const int c = rem / a.rbc, rb = rem % a.rbc;
+        it.sn = a.snap + (bh * a.nc + c) * P;
+        it.tok = bh * a.T + (int64_t)c * a.C + (int64_t)rb * 32 * NWA + 32 * wave;
+        it.nrec = ok ? (int)(P * 2) : 0;
+        return it;
+    };
+
+    // stage copies: 24 copies of 4 rows (1 KB), NI per wave
     unsigned voff[NI];
     int mrow[NI];
 #pragma unroll
@@ -608,22 +630,49 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         voff[n] = (unsigned)((m * Hd * D + row * D + 8 * ((lane & 15) ^ swza(row))) * 2);
         mrow[n] = m * HB * 256 + r0 * 256;
     }
-    auto issue_stage = [&](int ih, unsigned char* buf) {
+    // global stage index gs = k nhb + ih
+    auto issue_stage = [&](int gs, unsigned char* buf) {
+        const Item it = item(gs / nhb);
+        const unsigned ho = (unsigned)((gs % nhb) * HB * D * 2);
 #pragma unroll
-        for (int n = 0; n < NI; ++n) lds_copy16(sn, (int)(P * 2), buf + mrow[n], voff[n] + (unsigned)(ih * HB * D * 2));
+        for (int n = 0; n < NI; ++n) lds_copy16(it.sn, it.nrec, buf + mrow[n], voff[n] + ho);
+    };
+    // the wave's 32 query rows of item k, row-major with the stage swizzle
+    auto issue_q = [&](int k) {
+        const Item it = item(k);
+        const int qrec = k < nmine ? 32 * D * 2 : 0;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int row = 4 * n + (lane >> 4);
+            const unsigned vo = (unsigned)((row * D + 8 * ((lane & 15) ^ swza(row))) * 2);
+            lds_copy16(a.q + it.tok * D, qrec, qw + 4 * n * 256, vo);
+        }
     };
 
     bf16x8 qf[8];  // Q^T as B operand: col = token, k = d
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)&qb[(t0 + li) * D + 16 * ks + 8 * lg];
+    f32x16 oacc[4] = {};
+    issue_q(0);
     issue_stage(0, sb0);
     issue_stage(1, sb1);
 
-    f32x16 oacc[4] = {};
-    auto stage = [&](int ih, const unsigned char* st, unsigned char* refill) {
-        __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | 0x0F70);  // this stage's copies landed
+    auto stage = [&](int gs, const unsigned char* st, unsigned char* refill) {
+        const int ih = gs % nhb;
+        // this stage's copies (and, at an item start, the item's queries)
+        // landed: the loads issued after them are the next stage's copies and,
+        // within two stages of an item start, the next item's queries.  (Loads
+        // complete in order; a count that ignores later stores only waits longer.)
+        if (ih == 1 || ih == 2)
+            __builtin_amdgcn_s_waitcnt(((NI + NQ) & 15) | (((NI + NQ) >> 4) << 14) | 0x0F70);
+        else
+            __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | 0x0F70);
         __syncthreads();
-        issue_stage(ih + 2, refill);  // refill = buffer of stage ih - 1, free after the barrier
+        issue_stage(gs + 2, refill);  // refill = buffer of stage gs - 1, free after the barrier
+        if (ih == 0) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qw + li * 256 + 16 * ((2 * ks + lg) ^ swza(li)));
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the query rows are in registers
+            issue_q(gs / nhb + 1);
+        }
         f32x16 x1 = {}, x3 = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -651,22 +700,28 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
             for (int dt = 0; dt < 4; ++dt)
                 oacc[dt] = mfma32(tr_frag_a(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
         }
-    };
-    for (int ih = 0; ih < nhb; ih += 3) {
-        stage(ih, sb0, sb2);
-        if (ih + 1 < nhb) stage(ih + 1, sb1, sb0);
-        if (ih + 2 < nhb) stage(ih + 2, sb2, sb1);
-    }
-    wait_vmem();  // copies of the stages past the last (zeros) before the LDS goes away
-    __bf16* ob = a.out + bh * a.T * D;
+        if (ih == nhb - 1) {
+            const int64_t tok = item(gs / nhb).tok;
+            __bf16* ob = a.out + tok * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int d = 32 * dt + 8 * qd + 4 * lg;
-            *(bf16x4*)&ob[(t0 + li) * D + d] =
-                pack4(oacc[dt][4 * qd], oacc[dt][4 * qd + 1], oacc[dt][4 * qd + 2], oacc[dt][4 * qd + 3]);
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int d = 32 * dt + 8 * qd + 4 * lg;
+                    *(bf16x4*)&ob[li * D + d] =
+                        pack4(oacc[dt][4 * qd], oacc[dt][4 * qd + 1], oacc[dt][4 * qd + 2], oacc[dt][4 * qd + 3]);
+                }
+                oacc[dt] = f32x16{};
+            }
         }
+    };
+    const int nst = nmine * nhb;
+    for (int gs = 0; gs < nst; gs += 3) {
+        stage(gs, sb0, sb2);
+        if (gs + 1 < nst) stage(gs + 1, sb1, sb0);
+        if (gs + 2 < nst) stage(gs + 2, sb2, sb1);
+    }
+    wait_vmem();  // copies past the last item (zeros) land before the LDS goes away
 }
 
 }  // namespace
@@ -711,16 +766,22 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.Hd = (int)d.Hd;
     aa.C = (int)d.chunk;
     aa.nc = (int)(d.T / d.chunk);
-    const unsigned nck = (unsigned)(BH * aa.nc);
+    aa.nb = (int)BH;
+    // persistent grid: one workgroup per compute unit (the LDS of one fills it)
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t nck = BH * aa.nc;
+    auto grid = [&](int64_t items) { return dim3((unsigned)(items < ncu ? items : ncu)); };
     if (d.chunk % 256 == 0) {
         aa.rbc = (int)(d.chunk / 256);
-        hipLaunchKernelGGL(swiglu_apply_kernel<8>, dim3(nck * aa.rbc), dim3(512), 0, s, aa);
+        hipLaunchKernelGGL(swiglu_apply_kernel<8>, grid(nck * aa.rbc), dim3(512), 0, s, aa);
     } else if (d.chunk % 128 == 0) {
         aa.rbc = (int)(d.chunk / 128);
-        hipLaunchKernelGGL(swiglu_apply_kernel<4>, dim3(nck * aa.rbc), dim3(256), 0, s, aa);
+        hipLaunchKernelGGL(swiglu_apply_kernel<4>, grid(nck * aa.rbc), dim3(256), 0, s, aa);
     } else {
         aa.rbc = (int)(d.chunk / 64);
-        hipLaunchKernelGGL(swiglu_apply_kernel<2>, dim3(nck * aa.rbc), dim3(128), 0, s, aa);
+        hipLaunchKernelGGL(swiglu_apply_kernel<2>, grid(nck * aa.rbc), dim3(128), 0, s, aa);
     }
     return hipGetLastError();
 }
