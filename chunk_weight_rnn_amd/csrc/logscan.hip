@@ -20,7 +20,10 @@
 //
 // Mapping: one 64-lane wavefront per chunk, 4 chunks per 256-thread block.
 // Lane l owns the contiguous tokens [l*npl, (l+1)*npl); lane-local sequential
-// passes plus wavefront shuffle scans combine them.
+// passes plus wavefront shuffle scans combine them.  For chunks of up to 1024
+// tokens (16 per lane) the lane's gates stay in registers and the logs are
+// base-2 hardware log / exp; longer chunks use a variant that re-reads its
+// tokens and uses natural-log library functions.
 #include <math.h>
 
 #include "e2ttt_internal.h"
@@ -28,13 +31,136 @@
 namespace e2ttt {
 namespace {
 
+// Everything below works in base-2 logs with the hardware log2 / exp2
+// (v_log_f32 / v_exp_f32): l = log2(x), so products become sums and
+// logaddexp becomes m + log2(1 + 2^(min - m)).
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_add_exp2(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m == -INFINITY) return -INFINITY;
+    return m + lg2(1.f + ex2(fminf(a, b) - m));
+}
+
+constexpr int MAXNPL = 16;  // tokens per lane: chunks up to 1024 tokens
+
+__global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int64_t nc, int64_t T, int C,
+                                                      int npl, const float* __restrict__ eta,
+                                                      const float* __restrict__ alpha,
+                                                      const float* __restrict__ beta, float* __restrict__ cM,
+                                                      float* __restrict__ cW, float* __restrict__ scal) {
+    const int lane = threadIdx.x & 63;
+    const int64_t gc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gc >= total_chunks) return;  // uniform per wavefront
+    const int64_t bh = gc / nc, c = gc % nc;
+    const size_t base = (size_t)bh * T + (size_t)c * C;
+    const int lo = lane * npl;
+
+    // the lane's tokens: log2 alpha, log2 beta (beta of the next token too), eta
+    float la[MAXNPL], lb[MAXNPL], lbn[MAXNPL], et[MAXNPL];
+#pragma unroll
+    for (int u = 0; u < MAXNPL; ++u) {
+        if (u < npl && lo + u < C) {
+            la[u] = lg2(alpha[base + lo + u]);
+            lb[u] = lg2(beta[base + lo + u]);
+            et[u] = eta[base + lo + u];
+        } else {
+            la[u] = 0.f;
+            lb[u] = 0.f;
+            et[u] = 0.f;
+        }
+    }
+    // log2 beta of token t+1 (the first token of the next lane for the last one)
+    const float lb_next_lane = __shfl_down(lb[0], 1, 64);
+#pragma unroll
+    for (int u = 0; u < MAXNPL; ++u) {
+        if (u + 1 < npl) lbn[u] = lb[u + 1];
+        else lbn[u] = lb_next_lane;
+        if (lo + u + 1 >= C) lbn[u] = -INFINITY;  // the chunk's last token has no successor
+    }
+
+    // pass 1: lane sums, then the inclusive reverse scan over lanes
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int u = 0; u < MAXNPL; ++u) {
+        sa += la[u];
+        sb += lb[u];
+    }
+    float ra = sa, rb = sb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float oa = __shfl_down(ra, off, 64);
+        const float ob = __shfl_down(rb, off, 64);
+        if (lane + off < 64) {
+            ra += oa;
+            rb += ob;
+        }
+    }
+    const float tot_a = __shfl(ra, 0, 64);
+    const float tot_b = __shfl(rb, 0, 64);
+    float base_a = __shfl_down(ra, 1, 64);  // sum over lanes > lane
+    float base_b = __shfl_down(rb, 1, 64);
+    if (lane == 63) base_a = base_b = 0.f;
+
+    // pass 2: compose the lane's maps f_t(z) = Sa_t (+) (log2 beta_{t+1} + z), last token first
+    float X = -INFINITY, Y = 0.f;  // identity map
+    {
+        float Sa = base_a;
+#pragma unroll
+        for (int u = MAXNPL - 1; u >= 0; --u) {
+            if (u < npl && lo + u < C) {
+                X = log2_add_exp2(Sa, lbn[u] + X);
+                Y = lbn[u] + Y;
+                Sa += la[u];
+            }
+        }
+    }
+    // inclusive reverse scan of the maps: R_lane = F_lane o F_lane+1 o ... o F_63
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float oX = __shfl_down(X, off, 64);
+        const float oY = __shfl_down(Y, off, 64);
+        if (lane + off < 64) {
+            X = log2_add_exp2(X, Y + oX);
+            Y = Y + oY;
+        }
+    }
+    // lw at the first token of the next lane; the chunk's last map is constant,
+    // so applying the right-hand composition to -inf gives its x component
+    float z = __shfl_down(X, 1, 64);
+    if (lane == 63) z = -INFINITY;
+
+    // pass 3: per-token coefficients
+    float Sa = base_a, Sb = base_b;
+#pragma unroll
+    for (int u = MAXNPL - 1; u >= 0; --u) {
+        if (u < npl && lo + u < C) {
+            const float lw = log2_add_exp2(Sa, lbn[u] + z);
+            z = lw;
+            cM[base + lo + u] = ex2(Sb) * et[u];
+            cW[base + lo + u] = ex2(lw) * et[u];
+            Sa += la[u];
+            Sb += lb[u];
+            if (lo + u == 0) {
+                float* sp = scal + gc * 4;
+                sp[0] = ex2(tot_a);
+                sp[1] = ex2(tot_b);
+                sp[2] = ex2(lb[0] + lw);  // gamma = beta_first * w_first
+                sp[3] = 0.f;
+            }
+        }
+    }
+}
+
+// Any chunk length (tokens per lane not bounded): the same three passes with
+// the lane's tokens re-read from memory and natural-log libm functions.
 __device__ __forceinline__ float log_add_exp(float a, float b) {
     const float m = fmaxf(a, b);
     if (m == -INFINITY) return -INFINITY;
     return m + log1pf(expf(fminf(a, b) - m));
 }
 
-__global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int64_t nc, int64_t T, int C,
+__global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, int64_t nc, int64_t T, int C,
                                                       int npl, const float* __restrict__ eta,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ cM,
@@ -129,8 +255,12 @@ hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, const float* eta
     if (total == 0) return hipSuccess;
     const int npl = (int)((chunk + 63) / 64);
     const int64_t blocks = (total + 3) / 4;
-    hipLaunchKernelGGL(logscan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk, npl,
-                       eta, alpha, beta, cM, cW, scal);
+    if (npl <= MAXNPL)
+        hipLaunchKernelGGL(logscan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk, npl,
+                           eta, alpha, beta, cM, cW, scal);
+    else
+        hipLaunchKernelGGL(logscan_kernel_any, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk,
+                           npl, eta, alpha, beta, cM, cW, scal);
     return hipGetLastError();
 }
 
