@@ -27,7 +27,7 @@ METRIC = "E2-TTT chunk-update tokens/sec at 1 GPU + % of MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / packed VALU)
 PEAK_HBM_GBS = 8000.0
-LOOP_SRC = os.path.join(ROOT, "chunk_weight_rnn_amd", "csrc", "swiglu_mfma.hip")
+LOOP_SRC = os.path.join(ROOT, "chunk_weight_rnn_amd", "csrc", "swiglu_loop.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_loop_1p3b.json")
 
 

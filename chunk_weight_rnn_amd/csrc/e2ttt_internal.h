@@ -34,6 +34,10 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
 
 // SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
 bool swiglu_mfma_supported(const e2ttt_desc& d);
+// Chunk loop of the SwiGLU path: final state and the bf16 chunk-start snapshots.
+hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
+                              const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
+                              void* snap, hipStream_t s);
 // ev_mid (may be null) is recorded between the chunk-loop and output launches.
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
                               const float* cM, const float* cW, const float* scal, const float* W0,
