@@ -54,10 +54,27 @@ Fast weights and losses (per token, k and v are D-vectors):
 Packing of the per-(b, h) parameter vector P (fp32 on the device, fp64
 here): linear W; mlp W1 | W2; swiglu W1 | W3 | W2, each row-major.
 
+Variants (flags of ``chunk_forward``):
+
+* ``momentum=False``: the recurrence without momentum,
+  W_t = alpha_t * W_{t-1} - eta_t * g_t (beta and M0 are not used).  The
+  pages name no-momentum token weights among the official code's functions;
+  the plainest reading is the momentum rule with M removed.  Closed form:
+  w_i = prod_{s=i+1..C} alpha_s, A = prod alpha, W_C = A W0 - sum_i w_i eta_i g_i.
+* ``chunk_avg=True``: the chunk-averaged variant the pages report as an
+  ablation (atlas, "Surprising findings": per-token factors collapsed to chunk
+  scalars).  Reading: the per-token kernel values m_i and w_i are replaced by
+  their mean over the chunk, the per-token learning rate eta_i is kept, and
+  the chunk scalars A, Bb, gamma are unchanged.  It is defined by this closed
+  form (there is no per-token recurrence behind it).
+
 Parity status: every public function is pinned by ``tests/test_oracle_pins.py``
 (brute force, limits alpha=beta=1, beta=0 and C=1 with autograd gradients,
 geometric-sum closed forms, semigroup, resume, finite differences,
-linearity).  No function here is "parity unpinned".
+linearity; for the variants: the no-momentum brute force and autograd SGD,
+and for the chunk average its C=1 and equal-token reductions to the
+per-token form and its alpha=beta=1 closed form).  No function here is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -233,6 +250,23 @@ def chunk_coefficients(alpha: np.ndarray, beta: np.ndarray):
     return m, w, A, Bb, gamma
 
 
+def chunk_coefficients_nomomentum(alpha: np.ndarray):
+    """Weight kernel w and chunk decay A of the no-momentum recurrence
+    W_t = alpha_t W_{t-1} - eta_t g_t: w_i = prod_{s>i} alpha_s, A = prod alpha."""
+    alpha = np.asarray(alpha, dtype=np.float64)
+    C = alpha.shape[-1]
+    w = np.ones_like(alpha)
+    for i in range(C - 1):
+        w[..., i] = np.prod(alpha[..., i + 1:], axis=-1)
+    return w, np.prod(alpha, axis=-1)
+
+
+def chunk_mean(x: np.ndarray) -> np.ndarray:
+    """Mean over the chunk (last axis), broadcast back to every token."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.broadcast_to(np.mean(x, axis=-1, keepdims=True), x.shape).copy()
+
+
 # ----------------------------------------------------------------------------
 # closed-form transition and the chunk loop
 # ----------------------------------------------------------------------------
@@ -253,13 +287,18 @@ def _flatten(q, k, v, eta, alpha, beta, W0, M0):
     return (B, H, T, D), [f(x) for x in (q, k, v, eta, alpha, beta, W0, M0)]
 
 
-def chunk_forward(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, keep=False):
+def chunk_forward(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, keep=False,
+                  momentum=True, chunk_avg=False):
     """Closed-form chunk update over a whole sequence.
 
     q, k, v: [B, H, T, D]; eta, alpha, beta: [B, H, T]; W0, M0: [B, H, P].
     Returns (out [B,H,T,D], W_end [B,H,P], M_end [B,H,P]) in fp64, plus a
-    per-chunk list of intermediates when ``keep``.
+    per-chunk list of intermediates when ``keep``.  With ``momentum=False``
+    beta and M0 may be None and M_end is None.
     """
+    if not momentum:
+        beta = np.zeros(np.shape(eta))
+        M0 = np.zeros(np.shape(W0))
     (B, H, T, D), (q, k, v, eta, alpha, beta, W, M) = _flatten(q, k, v, eta, alpha, beta, W0, M0)
     if chunk <= 0 or T % chunk:
         raise ValueError("T must be a positive multiple of the chunk size")
@@ -275,7 +314,15 @@ def chunk_forward(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, ke
         # 2. per-token backward factors at the chunk-start weights
         fac = grad_factors(kind, loss, mats, k[:, sl], v[:, sl])
         # 3. scalar kernels
-        m, w, A, Bb, gamma = chunk_coefficients(alpha[:, sl], beta[:, sl])
+        if momentum:
+            m, w, A, Bb, gamma = chunk_coefficients(alpha[:, sl], beta[:, sl])
+        else:
+            w, A = chunk_coefficients_nomomentum(alpha[:, sl])
+            m = np.zeros_like(w)
+            Bb = np.zeros_like(A)
+            gamma = np.zeros_like(A)
+        if chunk_avg:
+            m, w = chunk_mean(m), chunk_mean(w)
         cM = m * eta[:, sl]
         cW = w * eta[:, sl]
         # 4. the two weighted gradient aggregations
@@ -288,15 +335,19 @@ def chunk_forward(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, ke
             inter.append(dict(m=m, w=w, A=A, Bb=Bb, gamma=gamma, cM=cM, cW=cW, GM=GM, GW=GW))
         W, M = W_new, M_new
     P = W.shape[-1]
-    res = (out.reshape(B, H, T, D), W.reshape(B, H, P), M.reshape(B, H, P))
+    res = (out.reshape(B, H, T, D), W.reshape(B, H, P), M.reshape(B, H, P) if momentum else None)
     return (res + (inter,)) if keep else res
 
 
-def brute_force(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0):
-    """The definition: per-token recurrence with gradients frozen at chunk start.
+def brute_force(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, momentum=True):
+    """The definition: per-token recurrence with gradients frozen at chunk start
+    (``momentum=False``: W_t = alpha_t W_{t-1} - eta_t g_t, M_end None).
 
     For small inputs only (materialises every per-token gradient).
     """
+    if not momentum:
+        beta = np.zeros(np.shape(eta))
+        M0 = np.zeros(np.shape(W0))
     (B, H, T, D), (q, k, v, eta, alpha, beta, W, M) = _flatten(q, k, v, eta, alpha, beta, W0, M0)
     if chunk <= 0 or T % chunk:
         raise ValueError("T must be a positive multiple of the chunk size")
@@ -310,10 +361,13 @@ def brute_force(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0):
         g = pack(kind, token_grads(kind, loss, mats, k[:, sl], v[:, sl]))  # [BH, C, P]
         for i in range(chunk):
             t = c0 + i
-            M = beta[:, t, None] * M + eta[:, t, None] * g[:, i]
-            W = alpha[:, t, None] * W - M
+            if momentum:
+                M = beta[:, t, None] * M + eta[:, t, None] * g[:, i]
+                W = alpha[:, t, None] * W - M
+            else:
+                W = alpha[:, t, None] * W - eta[:, t, None] * g[:, i]
     P = W.shape[-1]
-    return out.reshape(B, H, T, D), W.reshape(B, H, P), M.reshape(B, H, P)
+    return out.reshape(B, H, T, D), W.reshape(B, H, P), M.reshape(B, H, P) if momentum else None
 
 
 def rel_err(x, ref) -> float:
