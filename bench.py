@@ -34,18 +34,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_loop_1p3b.json")
 def flops_per_token_head(cfg: synth.Config) -> dict:
     """Algorithmic MFMA-able flops per token per head, split by stage."""
     D, Hd = cfg.D, cfg.Hd
+    sets = 2 if cfg.momentum else 1  # weighted aggregations: G^M and G^W, or G^W alone
     if cfg.kind == "swiglu":
-        return {"grad": 6 * D * Hd, "aggregate": 12 * D * Hd, "apply": 6 * D * Hd}
+        return {"grad": 6 * D * Hd, "aggregate": 6 * sets * D * Hd, "apply": 6 * D * Hd}
     if cfg.kind == "mlp":
         fwd = 4 * D * Hd if cfg.loss == "mse" else 2 * D * Hd
-        return {"grad": fwd + 2 * D * Hd, "aggregate": 8 * D * Hd, "apply": 4 * D * Hd}
-    return {"grad": 2 * D * D, "aggregate": 4 * D * D, "apply": 2 * D * D}
+        return {"grad": fwd + 2 * D * Hd, "aggregate": 4 * sets * D * Hd, "apply": 4 * D * Hd}
+    return {"grad": 2 * D * D, "aggregate": 2 * sets * D * D, "apply": 2 * D * D}
 
 
 def alg_bytes(cfg: synth.Config) -> int:
     es = 2 if cfg.io_dtype == "bf16" else 4
     BH = cfg.B * cfg.H
-    return BH * cfg.T * cfg.D * es * 4 + BH * cfg.T * 4 * 3 + BH * cfg.P * 4 * 4
+    states = 4 if cfg.momentum else 2  # W0, M0 read + W_end, M_end written (no momentum: W only)
+    gates = 3 if cfg.momentum else 2
+    return BH * cfg.T * cfg.D * es * 4 + BH * cfg.T * 4 * gates + BH * cfg.P * 4 * states
 
 
 class HipEvents:
@@ -102,7 +105,7 @@ def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
         sl = {n: f(t[b:b + 1]) for n, t in x.items()}
         t0 = time.perf_counter()
         oracle.chunk_forward(cfg.kind, cfg.loss, sl["q"], sl["k"], sl["v"], sl["eta"], sl["alpha"], sl["beta"],
-                             sl["W0"], sl["M0"], cfg.chunk, cfg.Hd)
+                             sl["W0"], sl["M0"], cfg.chunk, cfg.Hd, momentum=cfg.momentum, chunk_avg=cfg.chunk_avg)
         wall += time.perf_counter() - t0
         rows += 1
     tokens = rows * cfg.T
@@ -147,7 +150,8 @@ def main() -> int:
     out = torch.empty_like(x["q"])
     W = torch.empty_like(x["W0"])
     M = torch.empty_like(x["M0"])
-    desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
+    desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk,
+                             cfg.flags)
     ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -208,7 +212,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "kind": cfg.kind, "loss": cfg.loss, "B": cfg.B,
                    "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk, "io": cfg.io_dtype,
-                   "state": "f32"},
+                   "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg},
         "roofline": {"bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
                      "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,
                      "traffic": traffic,

@@ -10,7 +10,9 @@ Method: "Rethinking Expressivity and Efficiency in Test-Time Training"
 chunk-start weights feed a closed-form transition that reproduces the
 chunk-end weights W and momentum M of the per-token recurrence
 M_t = beta_t M_{t-1} + eta_t g_t, W_t = alpha_t W_{t-1} - M_t, and the chunk
-output comes from the chunk-start weights.
+output comes from the chunk-start weights.  Variants: ``momentum=False``
+(W_t = alpha_t W_{t-1} - eta_t g_t) and ``chunk_avg=True`` (the per-token
+kernels replaced by their chunk means).
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import E2TTTError, FLAG_FORCE_GENERIC, make_desc
+from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, make_desc
 
 __all__ = ["chunk_forward", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
@@ -68,16 +70,23 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 
 def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
-                  out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False, stream=None):
+                  out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False,
+                  momentum: bool = True, chunk_avg: bool = False, stream=None):
     """Run the chunk update; returns (out, W_end, M_end).
 
     q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
     eta, alpha, beta: [B, H, T] float32; W0, M0: [B, H, P] float32.
-    ``W_end=W0`` / ``M_end=M0`` update the state in place.
+    ``W_end=W0`` / ``M_end=M0`` update the state in place.  With
+    ``momentum=False`` beta and M0 are ignored (may be None) and M_end is None.
     """
     lib = library()
+    if not momentum:
+        beta = M0 = None
+        M_end = None
     for name, t in (("q", q), ("k", k), ("v", v), ("eta", eta), ("alpha", alpha), ("beta", beta),
                     ("W0", W0), ("M0", M0)):
+        if t is None:
+            continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
         if not t.is_contiguous():
@@ -86,15 +95,16 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     for name, t in (("eta", eta), ("alpha", alpha), ("beta", beta), ("W0", W0), ("M0", M0)):
-        if t.dtype != torch.float32:
+        if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     B, H, T, D = q.shape
-    flags = FLAG_FORCE_GENERIC if force_generic else 0
+    flags = (FLAG_FORCE_GENERIC if force_generic else 0) | (0 if momentum else FLAG_NO_MOMENTUM) | \
+        (FLAG_CHUNK_AVG if chunk_avg else 0)
     desc = make_desc(kind, loss, io, B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
-    if tuple(W0.shape) != (B, H, P) or tuple(M0.shape) != (B, H, P):
+    if tuple(W0.shape) != (B, H, P) or (M0 is not None and tuple(M0.shape) != (B, H, P)):
         raise ValueError(f"W0/M0 must have shape {(B, H, P)}")
-    if tuple(eta.shape) != (B, H, T) or alpha.shape != eta.shape or beta.shape != eta.shape:
+    if tuple(eta.shape) != (B, H, T) or alpha.shape != eta.shape or (beta is not None and beta.shape != eta.shape):
         raise ValueError(f"eta/alpha/beta must have shape {(B, H, T)}")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one shape")
@@ -102,7 +112,7 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
         out = torch.empty_like(q)
     if W_end is None:
         W_end = torch.empty_like(W0)
-    if M_end is None:
+    if M_end is None and momentum:
         M_end = torch.empty_like(M0)
     ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
     if ws_bytes == ctypes.c_size_t(-1).value:
@@ -117,10 +127,16 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
     return out, W_end, M_end
 
 
-def logscan(eta, alpha, beta, *, chunk: int, stream=None):
-    """The scalar-kernel step alone: returns (cM, cW, scal[B, H, T/chunk, 4])."""
+def logscan(eta, alpha, beta, *, chunk: int, momentum: bool = True, chunk_avg: bool = False, stream=None):
+    """The scalar-kernel step alone: returns (cM, cW, scal[B, H, T/chunk, 4]).
+    ``momentum=False`` takes beta = 0 (beta may be None); ``chunk_avg`` replaces
+    the per-token kernels by their chunk means."""
     lib = library()
+    if not momentum:
+        beta = None
     for name, t in (("eta", eta), ("alpha", alpha), ("beta", beta)):
+        if t is None:
+            continue
         if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
     B, H, T = eta.shape
@@ -129,7 +145,8 @@ def logscan(eta, alpha, beta, *, chunk: int, stream=None):
     cM = torch.empty_like(eta)
     cW = torch.empty_like(eta)
     scal = torch.empty(B, H, T // chunk, 4, dtype=torch.float32, device=eta.device)
-    desc = make_desc("linear", "mse", "f32", B, H, T, 1, 0, chunk)
+    flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0)
+    desc = make_desc("linear", "mse", "f32", B, H, T, 1, 0, chunk, flags)
     st = lib.e2ttt_logscan(ctypes.byref(desc), _ptr(eta), _ptr(alpha), _ptr(beta), _ptr(cM), _ptr(cW),
                            _ptr(scal), _stream_handle(stream))
     if st != 0:

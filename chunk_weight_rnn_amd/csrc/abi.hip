@@ -14,6 +14,7 @@ static bool desc_ok(const e2ttt_desc* d) {
     if (d->io_dtype < E2TTT_F32 || d->io_dtype > E2TTT_BF16) return false;
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->D < 1 || d->chunk < 1) return false;
     if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
+    if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG)) return false;
     if (d->T % d->chunk != 0) return false;
     // keep every product used for indexing far from int64 overflow
     const int64_t lim = (int64_t)1 << 40;
@@ -93,10 +94,11 @@ int e2ttt_validate(const e2ttt_desc* d, const void* const ptrs[11]) {
     const size_t BH = (size_t)(d->B * d->H);
     const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
     const size_t P = (size_t)e2ttt_param_count(d);
+    const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);  // beta, M0, M_end unused without momentum
     const size_t bytes[11] = {BH * d->T * d->D * es, BH * d->T * d->D * es, BH * d->T * d->D * es,
-                              BH * d->T * 4,         BH * d->T * 4,         BH * d->T * 4,
-                              BH * P * 4,            BH * P * 4,            BH * d->T * d->D * es,
-                              BH * P * 4,            BH * P * 4};
+                              BH * d->T * 4,         BH * d->T * 4,         mom ? BH * d->T * 4 : 0,
+                              BH * P * 4,            mom ? BH * P * 4 : 0,  BH * d->T * d->D * es,
+                              BH * P * 4,            mom ? BH * P * 4 : 0};
     const size_t align[11] = {16, 16, 16, 4, 4, 4, 16, 16, 16, 16, 16};
     for (int i = 0; i < 11; ++i) {
         if (bytes[i] == 0) continue;
@@ -140,9 +142,11 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
         const size_t BH = (size_t)(d->B * d->H);
         const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
         const size_t P = (size_t)e2ttt_param_count(d);
+        const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
         const size_t bytes[11] = {BH * d->T * d->D * es, BH * d->T * d->D * es, BH * d->T * d->D * es,
-                                  BH * d->T * 4, BH * d->T * 4, BH * d->T * 4, BH * P * 4, BH * P * 4,
-                                  BH * d->T * d->D * es, BH * P * 4, BH * P * 4};
+                                  BH * d->T * 4, BH * d->T * 4, mom ? BH * d->T * 4 : 0, BH * P * 4,
+                                  mom ? BH * P * 4 : 0, BH * d->T * d->D * es, BH * P * 4,
+                                  mom ? BH * P * 4 : 0};
         for (int i = 0; i < 11; ++i)
             if (bytes[i] && overlap(wr, Range{(uintptr_t)ptrs[i], (uintptr_t)ptrs[i] + bytes[i]}))
                 return E2TTT_ERR_ALIAS;
@@ -154,7 +158,8 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (d->T == 0) {
         if (W_end != W0 && hipMemcpyAsync(W_end, W0, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return E2TTT_ERR_HIP;
-        if (M_end != M0 && hipMemcpyAsync(M_end, M0, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        if (!(d->flags & E2TTT_FLAG_NO_MOMENTUM) && M_end != M0 &&
+            hipMemcpyAsync(M_end, M0, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return E2TTT_ERR_HIP;
         return E2TTT_OK;
     }
@@ -166,7 +171,8 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (events)
         for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
     if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
-    if (launch_logscan(BH, d->T, d->chunk, eta, alpha, beta, cM, cW, scal, s) != hipSuccess) return E2TTT_ERR_HIP;
+    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, scal, s) != hipSuccess)
+        return E2TTT_ERR_HIP;
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
     if (path == 1) {
@@ -184,8 +190,10 @@ int e2ttt_logscan(const e2ttt_desc* d, const float* eta, const float* alpha, con
     if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1 || d->T % d->chunk) return E2TTT_ERR_INVALID_ARG;
     const int64_t BH = d->B * d->H;
     if (BH * d->T == 0) return E2TTT_OK;
-    if (!eta || !alpha || !beta || !cM || !cW || !scal) return E2TTT_ERR_INVALID_ARG;
-    return launch_logscan(BH, d->T, d->chunk, eta, alpha, beta, cM, cW, scal, (hipStream_t)stream) == hipSuccess
+    if (!eta || !alpha || !cM || !cW || !scal) return E2TTT_ERR_INVALID_ARG;
+    if (!beta && !(d->flags & E2TTT_FLAG_NO_MOMENTUM)) return E2TTT_ERR_INVALID_ARG;
+    return launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, scal, (hipStream_t)stream) ==
+                   hipSuccess
                ? E2TTT_OK
                : E2TTT_ERR_HIP;
 }

@@ -24,7 +24,7 @@ struct Workspace {
 Workspace workspace_layout(const e2ttt_desc& d, int path);
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, const float* eta, const float* alpha,
+hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,
                           const float* beta, float* cM, float* cW, float* scal, hipStream_t s);
 
 hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v,

@@ -27,6 +27,7 @@ constexpr int NT = 256;
 struct GenericArgs {
     int64_t T, D, Hd, C, nc, P;
     int loss, TB;
+    int nomom;  // no momentum: M0 / M are not used (the scalar kernels already have beta = 0)
     const void* q;
     const void* k;
     const void* v;
@@ -74,20 +75,19 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     float* cws = cms + TB;        // [TB]
 
     float* W = a.W + bh * P;
-    float* M = a.M + bh * P;
+    float* M = a.nomom ? nullptr : a.M + bh * P;
     float* GM = a.gacc + bh * 2 * P;
     float* GW = GM + P;
     const float* W0 = a.W0 + bh * P;
-    const float* M0 = a.M0 + bh * P;
+    const float* M0 = a.nomom ? nullptr : a.M0 + bh * P;
     const TIO* q = (const TIO*)a.q + bh * a.T * D;
     const TIO* k = (const TIO*)a.k + bh * a.T * D;
     const TIO* v = (const TIO*)a.v + bh * a.T * D;
     TIO* out = (TIO*)a.out + bh * a.T * D;
 
     for (int64_t p = tid; p < P; p += NT) {
-        const float w0 = W0[p], m0 = M0[p];
-        W[p] = w0;
-        M[p] = m0;
+        W[p] = W0[p];
+        if (M) M[p] = M0[p];
         GM[p] = 0.f;
         GW[p] = 0.f;
     }
@@ -298,9 +298,9 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
         const float* sc = a.scal + (bh * a.nc + c) * 4;
         const float A = sc[0], Bb = sc[1], gamma = sc[2];
         for (int64_t p = tid; p < P; p += NT) {
-            const float w = W[p], m = M[p];
+            const float w = W[p], m = M ? M[p] : 0.f;
             W[p] = A * w - gamma * m - GW[p];
-            M[p] = Bb * m + GM[p];
+            if (M) M[p] = Bb * m + GM[p];
             GM[p] = 0.f;
             GW[p] = 0.f;
         }
@@ -339,6 +339,7 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
     a.P = e2ttt_param_count(&d);
     a.loss = d.loss;
     a.TB = generic_token_block(d);
+    a.nomom = (d.flags & E2TTT_FLAG_NO_MOMENTUM) ? 1 : 0;
     a.q = q;
     a.k = k;
     a.v = v;

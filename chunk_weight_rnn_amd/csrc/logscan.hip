@@ -24,6 +24,13 @@
 // tokens (16 per lane) the lane's gates stay in registers and the logs are
 // base-2 hardware log / exp; longer chunks use a variant that re-reads its
 // tokens and uses natural-log library functions.
+//
+// Variants (flags):
+//   no momentum: W_t = alpha_t W_{t-1} - eta_t g_t, i.e. beta = 0 throughout:
+//     m_i = [i = C-1], w_i = exp(Sa_i), Bb = gamma = 0 (beta is not read);
+//   chunk average (the pages' chunk-averaged ablation, atlas summary
+//     "Surprising findings"): m_i and w_i are replaced by their mean over the
+//     chunk before the multiplication by eta_i; A, Bb, gamma are unchanged.
 #include <math.h>
 
 #include "e2ttt_internal.h"
@@ -45,7 +52,7 @@ __device__ __forceinline__ float log2_add_exp2(float a, float b) {
 constexpr int MAXNPL = 16;  // tokens per lane: chunks up to 1024 tokens
 
 __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int64_t nc, int64_t T, int C,
-                                                      int npl, const float* __restrict__ eta,
+                                                      int npl, int nomom, int avg, const float* __restrict__ eta,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ cM,
                                                       float* __restrict__ cW, float* __restrict__ scal) {
@@ -62,7 +69,7 @@ __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int6
     for (int u = 0; u < MAXNPL; ++u) {
         if (u < npl && lo + u < C) {
             la[u] = lg2(alpha[base + lo + u]);
-            lb[u] = lg2(beta[base + lo + u]);
+            lb[u] = nomom ? -INFINITY : lg2(beta[base + lo + u]);
             et[u] = eta[base + lo + u];
         } else {
             la[u] = 0.f;
@@ -130,15 +137,19 @@ __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int6
     float z = __shfl_down(X, 1, 64);
     if (lane == 63) z = -INFINITY;
 
-    // pass 3: per-token coefficients
-    float Sa = base_a, Sb = base_b;
+    // pass 3: per-token kernels m, w
+    float mv[MAXNPL], wv[MAXNPL];
+    float Sa = base_a, Sb = base_b, sum_m = 0.f, sum_w = 0.f;
 #pragma unroll
     for (int u = MAXNPL - 1; u >= 0; --u) {
+        mv[u] = wv[u] = 0.f;
         if (u < npl && lo + u < C) {
             const float lw = log2_add_exp2(Sa, lbn[u] + z);
             z = lw;
-            cM[base + lo + u] = ex2(Sb) * et[u];
-            cW[base + lo + u] = ex2(lw) * et[u];
+            mv[u] = ex2(Sb);
+            wv[u] = ex2(lw);
+            sum_m += mv[u];
+            sum_w += wv[u];
             Sa += la[u];
             Sb += lb[u];
             if (lo + u == 0) {
@@ -148,6 +159,26 @@ __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int6
                 sp[2] = ex2(lb[0] + lw);  // gamma = beta_first * w_first
                 sp[3] = 0.f;
             }
+        }
+    }
+    if (avg) {  // chunk means of m and w for every token
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sum_m += __shfl_xor(sum_m, off, 64);
+            sum_w += __shfl_xor(sum_w, off, 64);
+        }
+#pragma unroll
+        for (int u = 0; u < MAXNPL; ++u) {
+            mv[u] = sum_m / (float)C;
+            wv[u] = sum_w / (float)C;
+        }
+    }
+    // coefficients cM = m eta, cW = w eta
+#pragma unroll
+    for (int u = 0; u < MAXNPL; ++u) {
+        if (u < npl && lo + u < C) {
+            cM[base + lo + u] = mv[u] * et[u];
+            cW[base + lo + u] = wv[u] * et[u];
         }
     }
 }
@@ -161,7 +192,7 @@ __device__ __forceinline__ float log_add_exp(float a, float b) {
 }
 
 __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, int64_t nc, int64_t T, int C,
-                                                      int npl, const float* __restrict__ eta,
+                                                      int npl, int nomom, int avg, const float* __restrict__ eta,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ cM,
                                                       float* __restrict__ cW, float* __restrict__ scal) {
@@ -171,7 +202,8 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
     const int64_t bh = gc / nc, c = gc % nc;
     const size_t base = (size_t)bh * T + (size_t)c * C;
     const float* al = alpha + base;
-    const float* be = beta + base;
+    const float* be = nomom ? nullptr : beta + base;
+    auto logb = [&](int t) { return nomom ? -INFINITY : logf(be[t]); };
     const float* et = eta + base;
     const int lo = lane * npl;
     const int hi = min(lo + npl, C);
@@ -180,7 +212,7 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
     float sa = 0.f, sb = 0.f;
     for (int t = lo; t < hi; ++t) {
         sa += logf(al[t]);
-        sb += logf(be[t]);
+        sb += logb(t);
     }
     // inclusive reverse scan over lanes: ra = sum over lanes >= lane
     float ra = sa, rb = sb;
@@ -204,7 +236,7 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
     {
         float Sa = base_a;
         for (int t = hi - 1; t >= lo; --t) {
-            const float y = (t + 1 < C) ? logf(be[t + 1]) : -INFINITY;
+            const float y = (t + 1 < C) ? logb(t + 1) : -INFINITY;
             X = log_add_exp(Sa, y + X);
             Y = y + Y;
             Sa += logf(al[t]);
@@ -225,31 +257,50 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
     float z = __shfl_down(X, 1, 64);
     if (lane == 63) z = -INFINITY;
 
-    // pass 3: per-token coefficients
-    float Sa = base_a, Sb = base_b;
+    // pass 3: per-token coefficients (with the chunk average: their sums)
+    float Sa = base_a, Sb = base_b, sum_m = 0.f, sum_w = 0.f;
     for (int t = hi - 1; t >= lo; --t) {
-        const float y = (t + 1 < C) ? logf(be[t + 1]) : -INFINITY;
+        const float y = (t + 1 < C) ? logb(t + 1) : -INFINITY;
         const float lw = log_add_exp(Sa, y + z);
         z = lw;
         const float e = et[t];
-        cM[base + t] = expf(Sb) * e;
-        cW[base + t] = expf(lw) * e;
+        const float mt = expf(Sb), wt = expf(lw);
+        sum_m += mt;
+        sum_w += wt;
+        if (!avg) {
+            cM[base + t] = mt * e;
+            cW[base + t] = wt * e;
+        }
         Sa += logf(al[t]);
-        Sb += logf(be[t]);
+        Sb += logb(t);
         if (t == 0) {
             float* s = scal + gc * 4;
             s[0] = expf(tot_a);
             s[1] = expf(tot_b);
-            s[2] = expf(logf(be[0]) + lw);  // gamma = beta_first * w_first
+            s[2] = expf(logb(0) + lw);  // gamma = beta_first * w_first
             s[3] = 0.f;
+        }
+    }
+    if (avg) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sum_m += __shfl_xor(sum_m, off, 64);
+            sum_w += __shfl_xor(sum_w, off, 64);
+        }
+        const float mm = sum_m / (float)C, mw = sum_w / (float)C;
+        for (int t = lo; t < hi; ++t) {
+            cM[base + t] = mm * et[t];
+            cW[base + t] = mw * et[t];
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, const float* eta, const float* alpha,
+hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,
                           const float* beta, float* cM, float* cW, float* scal, hipStream_t s) {
+    const int nomom = (flags & E2TTT_FLAG_NO_MOMENTUM) ? 1 : 0;
+    const int avg = (flags & E2TTT_FLAG_CHUNK_AVG) ? 1 : 0;
     const int64_t nc = T / chunk;
     const int64_t total = BH * nc;
     if (total == 0) return hipSuccess;
@@ -257,10 +308,10 @@ hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, const float* eta
     const int64_t blocks = (total + 3) / 4;
     if (npl <= MAXNPL)
         hipLaunchKernelGGL(logscan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk, npl,
-                           eta, alpha, beta, cM, cW, scal);
+                           nomom, avg, eta, alpha, beta, cM, cW, scal);
     else
         hipLaunchKernelGGL(logscan_kernel_any, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk,
-                           npl, eta, alpha, beta, cM, cW, scal);
+                           npl, nomom, avg, eta, alpha, beta, cM, cW, scal);
     return hipGetLastError();
 }
 

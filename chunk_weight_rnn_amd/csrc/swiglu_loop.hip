@@ -159,8 +159,8 @@ struct LoopArgs {
 // State tiles <-> packed fp32 parameters (W1 [D][Hd] | W3 [D][Hd] | W2 [Hd][D]).
 // acc[m][0] / acc[m][1] are the M / W parts of matrix m (0: W1, 1: W3, 2: W2
 // held transposed as [d][j]); tile element (i, r) of lane (jl, g) is
-// d = state_d(i, g) + r, hidden unit j.
-template <bool STORE>
+// d = state_d(i, g) + r, hidden unit j.  Without momentum M is not touched.
+template <bool STORE, bool MOM>
 __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float* M, int64_t j, int g, int Hd) {
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
@@ -172,20 +172,20 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (STORE) {
-                        M[o + r * Hd] = acc[m][0][i][r];
+                        if (MOM) M[o + r * Hd] = acc[m][0][i][r];
                         W[o + r * Hd] = acc[m][1][i][r];
                     } else {
-                        acc[m][0][i][r] = M[o + r * Hd];
+                        acc[m][0][i][r] = MOM ? M[o + r * Hd] : 0.f;
                         acc[m][1][i][r] = W[o + r * Hd];
                     }
                 }
             } else {
                 const int64_t o = 2 * (int64_t)D * Hd + j * D + d;
                 if (STORE) {
-                    *(f32x4*)&M[o] = acc[m][0][i];
+                    if (MOM) *(f32x4*)&M[o] = acc[m][0][i];
                     *(f32x4*)&W[o] = acc[m][1][i];
                 } else {
-                    acc[m][0][i] = *(const f32x4*)&M[o];
+                    acc[m][0][i] = MOM ? *(const f32x4*)&M[o] : f32x4{0.f, 0.f, 0.f, 0.f};
                     acc[m][1][i] = *(const f32x4*)&W[o];
                 }
             }
@@ -193,8 +193,12 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
     }
 }
 
+template <bool MOM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 swiglu_loop_kernel(LoopArgs a) {
+    // MOM = false: the recurrence without momentum; the scalar kernels then
+    // have beta = 0 (cM unused, gamma = Bb = 0) and the M half of the state,
+    // its aggregation MFMAs and its HBM traffic are compiled out.
     __shared__ __attribute__((aligned(16))) unsigned char kvs[NBUF * KVBUF];
     __shared__ __attribute__((aligned(16))) unsigned char xch[4 * XW];
     const int tid = threadIdx.x;
@@ -282,7 +286,7 @@ swiglu_loop_kernel(LoopArgs a) {
         issue_block(0);
         if (nblk > 1) issue_block(1);
         f32x4 acc[3][2][8];
-        state_io<false>(acc, (float*)a.W0 + bh * P, (float*)a.M0 + bh * P, j, g, Hd);
+        state_io<false, MOM>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd);
 
         // chunk-start weights -> grad operands (exchange area) + bf16 snapshot
         const bool godd = (g & 1) != 0;
@@ -316,9 +320,13 @@ swiglu_loop_kernel(LoopArgs a) {
             for (int m = 0; m < 3; ++m) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const f32x4 mm = acc[m][0][i];
-                    acc[m][1][i] = A * acc[m][1][i] - gamma * mm;
-                    acc[m][0][i] = Bb * mm;
+                    if (MOM) {
+                        const f32x4 mm = acc[m][0][i];
+                        acc[m][1][i] = A * acc[m][1][i] - gamma * mm;
+                        acc[m][0][i] = Bb * mm;
+                    } else {
+                        acc[m][1][i] = A * acc[m][1][i];
+                    }
                 }
             }
         };
@@ -362,9 +370,9 @@ swiglu_loop_kernel(LoopArgs a) {
             for (int i = 0; i < 8; ++i) {
                 // the fragment of tile i + 1 is read while tile i's MFMAs run
                 const bf16x8 tn = i + 1 < 8 ? frag(i + 1, 0) : frag(0, 1);
-                acc[0][0][i] = mfma16(t, f[0], acc[0][0][i]);
+                if (MOM) acc[0][0][i] = mfma16(t, f[0], acc[0][0][i]);
                 acc[0][1][i] = mfma16(t, f[1], acc[0][1][i]);
-                acc[1][0][i] = mfma16(t, f[2], acc[1][0][i]);
+                if (MOM) acc[1][0][i] = mfma16(t, f[2], acc[1][0][i]);
                 acc[1][1][i] = mfma16(t, f[3], acc[1][1][i]);
                 if (i == 7) scale(*(const bf16x8*)(fb + 2 * 1024), f[0], f[1]);
                 t = tn;
@@ -374,7 +382,7 @@ swiglu_loop_kernel(LoopArgs a) {
             for (int i = 0; i < 8; ++i) {
                 bf16x8 tn = t;
                 if (i + 1 < 8) tn = frag(i + 1, 1);
-                acc[2][0][i] = mfma16(t, f[0], acc[2][0][i]);
+                if (MOM) acc[2][0][i] = mfma16(t, f[0], acc[2][0][i]);
                 acc[2][1][i] = mfma16(t, f[1], acc[2][1][i]);
                 t = tn;
                 __builtin_amdgcn_sched_barrier(0);
@@ -408,7 +416,7 @@ swiglu_loop_kernel(LoopArgs a) {
         // lane indices re-derived here so that no prologue address survives the loop
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
-        state_io<true>(acc, a.W_end + bh * P, a.M_end + bh * P, (int64_t)(L_id % a.nsl) * S + 16 * u + (lane_e & 15),
+        state_io<true, MOM>(acc, a.W_end + bh * P, MOM ? a.M_end + bh * P : nullptr, (int64_t)(L_id % a.nsl) * S + 16 * u + (lane_e & 15),
                        lane_e >> 4, Hd);
     } else {
         // ------------------------------------------------------------ gradient wave
@@ -545,7 +553,10 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.nsl = (int)(d.Hd / S);
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(swiglu_loop_kernel, dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+    if (d.flags & E2TTT_FLAG_NO_MOMENTUM)
+        hipLaunchKernelGGL(swiglu_loop_kernel<false>, dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+    else
+        hipLaunchKernelGGL(swiglu_loop_kernel<true>, dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
     return hipGetLastError();
 }
 

@@ -67,6 +67,18 @@ typedef enum {
 
 /* flags */
 #define E2TTT_FLAG_FORCE_GENERIC 1 /* run the portable fp32 kernel even where the MFMA path applies */
+/* No momentum: the recurrence W_t = alpha_t W_{t-1} - eta_t g_t (the official
+ * code's token weights without momentum, as named on the codewithpapers page
+ * of "Rethinking Expressivity and Efficiency in Test-Time Training").  beta,
+ * M0 and M_end are not used and may be NULL; the chunk transition is
+ * W_end = prod(alpha) W0 - sum_t alpha(t:end] eta_t g_t. */
+#define E2TTT_FLAG_NO_MOMENTUM 2
+/* Chunk average: the chunk-averaged ablation of the same paper (atlas summary,
+ * "Surprising findings": per-token factors collapsed to chunk scalars).  The
+ * per-token momentum and weight kernels m_t, w_t are replaced by their mean
+ * over the chunk; each token keeps its own eta_t, and the chunk scalars
+ * prod alpha, prod beta, gamma are unchanged.  Combines with NO_MOMENTUM. */
+#define E2TTT_FLAG_CHUNK_AVG 4
 
 typedef struct {
     int32_t kind;     /* e2ttt_kind */
@@ -97,7 +109,8 @@ E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
  *   - sizes: B, H, T >= 0; D >= 1; chunk >= 1; T % chunk == 0; Hd >= 1 for
  *     MLP / SWIGLU; enums in range (E2TTT_ERR_INVALID_ARG);
  *   - pointers: non-null when the tensor is non-empty, 16-byte aligned
- *     (eta, alpha, beta: 4-byte aligned) (E2TTT_ERR_INVALID_ARG);
+ *     (eta, alpha, beta: 4-byte aligned) (E2TTT_ERR_INVALID_ARG); with
+ *     E2TTT_FLAG_NO_MOMENTUM, beta, M0 and M_end are not checked;
  *   - shape support: E2TTT_ERR_UNSUPPORTED when neither device path handles
  *     the shape (portable path: D <= 256 and Hd <= 1024);
  *   - aliasing: W_end may equal W0 and M_end may equal M0 exactly (in-place
@@ -148,7 +161,9 @@ E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
  *   cW[b][h][t] = eta_t * w_t,  w_t = sum_{tau >= t} alpha(tau:end] * beta(t:tau]
  *   scal[b][h][c][0..3] = { prod alpha, prod beta, gamma = beta_first * w_first, 0 }
  * eta, alpha, beta, cM, cW: [B][H][T] fp32; scal: [B][H][T/chunk][4] fp32.
- * Only desc->B, H, T and chunk are read.
+ * Only desc->B, H, T, chunk and flags are read: E2TTT_FLAG_NO_MOMENTUM takes
+ * beta = 0 (beta may be NULL), E2TTT_FLAG_CHUNK_AVG replaces m_t and w_t by
+ * their chunk means.
  */
 E2TTT_API int e2ttt_logscan(const e2ttt_desc* desc, const float* eta, const float* alpha, const float* beta,
                   float* cM, float* cW, float* scal, void* stream);

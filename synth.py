@@ -57,6 +57,15 @@ class Config:
     chunk: int
     io_dtype: str  # "f32" or "bf16"
     notes: str = ""
+    flags: int = 0  # variant flags of the C ABI: 2 = no momentum, 4 = chunk-averaged kernels
+
+    @property
+    def momentum(self) -> bool:
+        return not (self.flags & 2)
+
+    @property
+    def chunk_avg(self) -> bool:
+        return bool(self.flags & 4)
 
     @property
     def P(self) -> int:
@@ -90,6 +99,11 @@ CONFIGS = {
                                 "1.3B-shaped TTT branch, chunk 1024"),
     "swiglu_16k": Config("swiglu_16k", "swiglu", "negdot", 1, 16, 16384, 128, 256, 256, "bf16",
                          "16K length extrapolation, state carried over 64 chunks"),
+    # the variants on the 1.3B-shaped workload
+    "swiglu_1p3b_nomom": Config("swiglu_1p3b_nomom", "swiglu", "negdot", 8, 16, 2048, 128, 256, 256, "bf16",
+                                "1.3B-shaped TTT branch, chunk 256, no momentum", flags=2),
+    "swiglu_1p3b_avg": Config("swiglu_1p3b_avg", "swiglu", "negdot", 8, 16, 2048, 128, 256, 256, "bf16",
+                              "1.3B-shaped TTT branch, chunk 256, chunk-averaged kernels", flags=4),
 }
 
 

@@ -42,25 +42,29 @@ def to_dev(x: dict) -> dict:
     return {n: t.cuda() for n, t in x.items()}
 
 
-def run_gpu(cfg: synth.Config, x: dict, force_generic=False, in_place=False):
+def run_gpu(cfg: synth.Config, x: dict, force_generic=False, in_place=False, momentum=None, chunk_avg=None):
     import chunk_weight_rnn_amd as e2
+    momentum = cfg.momentum if momentum is None else momentum
+    chunk_avg = cfg.chunk_avg if chunk_avg is None else chunk_avg
     d = to_dev(x)
     kw = {}
     if in_place:
-        kw = dict(W_end=d["W0"], M_end=d["M0"])
+        kw = dict(W_end=d["W0"], M_end=d["M0"] if momentum else None)
     out, W, M = e2.chunk_forward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
                                  chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd,
-                                 force_generic=force_generic, **kw)
+                                 force_generic=force_generic, momentum=momentum, chunk_avg=chunk_avg, **kw)
     torch.cuda.synchronize()
-    return out.float().cpu(), W.cpu(), M.cpu()
+    return out.float().cpu(), W.cpu(), (M.cpu() if M is not None else None)
 
 
-def run_oracle(cfg: synth.Config, x: dict, keep=False):
+def run_oracle(cfg: synth.Config, x: dict, keep=False, momentum=None, chunk_avg=None):
+    momentum = cfg.momentum if momentum is None else momentum
+    chunk_avg = cfg.chunk_avg if chunk_avg is None else chunk_avg
     f = lambda t: t.double().numpy()
     with np.errstate(over="ignore", invalid="ignore"):
         return oracle.chunk_forward(cfg.kind, cfg.loss, f(x["q"]), f(x["k"]), f(x["v"]), f(x["eta"]),
                                     f(x["alpha"]), f(x["beta"]), f(x["W0"]), f(x["M0"]), cfg.chunk, cfg.Hd,
-                                    keep=keep)
+                                    keep=keep, momentum=momentum, chunk_avg=chunk_avg)
 
 
 def _diverged(r) -> bool:
@@ -70,8 +74,9 @@ def _diverged(r) -> bool:
 def errors(cfg: synth.Config, got, ref, W0) -> dict:
     """Per-tensor errors: every W / M matrix, the update W_end - W0, and the
     output chunk by chunk (key out[c]).  Diverged references map to None."""
-    out_g, W_g, M_g = [np.asarray(t, dtype=np.float64) for t in got]
+    out_g, W_g, M_g = [None if t is None else np.asarray(t, dtype=np.float64) for t in got]
     out_r, W_r, M_r = ref
+    assert (M_g is None) == (M_r is None), "momentum output present on one side only"
     W0 = np.asarray(W0, dtype=np.float64)
     e = {}
     for c in range(cfg.T // cfg.chunk):
@@ -79,7 +84,7 @@ def errors(cfg: synth.Config, got, ref, W0) -> dict:
         r = out_r[:, :, sl]
         e[f"out[{c}]"] = None if _diverged(r) else err(out_g[:, :, sl], r)
     with np.errstate(invalid="ignore", over="ignore"):
-        pairs = [("W", W_g, W_r), ("M", M_g, M_r), ("dW", W_g - W0, W_r - W0)]
+        pairs = [("W", W_g, W_r), ("dW", W_g - W0, W_r - W0)] + ([("M", M_g, M_r)] if M_r is not None else [])
     for tag, g, r in pairs:
         mg = oracle.unpack(cfg.kind, g, cfg.D, cfg.Hd)
         mr = oracle.unpack(cfg.kind, r, cfg.D, cfg.Hd)

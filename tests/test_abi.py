@@ -167,3 +167,32 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         e2.logscan(x["eta"], x["alpha"], x["beta"], chunk=16)
     assert isinstance(torch.__version__, str)
+
+
+def test_validate_variant_flags(lib):
+    # no momentum: beta (5), M0 (7) and M_end (10) are not used and may be null
+    d = _desc(flags=2)
+    p = _ptrs(d)
+    p[5] = p[7] = p[10] = 0
+    assert _validate(lib, d, p) == 0
+    # ... and may then overlap anything (they are not read or written)
+    p = _ptrs(d)
+    p[10] = p[9]
+    assert _validate(lib, d, p) == 0
+    # the other pointers are still required
+    p = _ptrs(d)
+    p[9] = 0
+    assert _validate(lib, d, p) == 1
+    # with momentum they are required
+    d = _desc(flags=4)
+    p = _ptrs(d)
+    p[7] = 0
+    assert _validate(lib, d, p) == 1
+    # both variants together, and with the portable path
+    for f in (2 | 4, 1 | 2 | 4):
+        d = _desc(flags=f)
+        assert _validate(lib, d, _ptrs(d)) == 0
+    # unknown flag bits are rejected
+    d = _desc(flags=8)
+    assert _validate(lib, d, _ptrs(d)) == 1
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
