@@ -61,6 +61,10 @@ Variants (flags of ``chunk_forward``):
   pages name no-momentum token weights among the official code's functions;
   the plainest reading is the momentum rule with M removed.  Closed form:
   w_i = prod_{s=i+1..C} alpha_s, A = prod alpha, W_C = A W0 - sum_i w_i eta_i g_i.
+* a ragged tail (T % chunk != 0): the last chunk holds the remaining
+  T mod chunk tokens and takes the same closed form over them (the pages
+  name a tail-length helper among the official code's functions; the
+  plainest reading is a shorter last chunk).
 * ``chunk_avg=True``: the chunk-averaged variant the pages report as an
   ablation (atlas, "Surprising findings": per-token factors collapsed to chunk
   scalars).  Reading: the per-token kernel values m_i and w_i are replaced by
@@ -71,7 +75,8 @@ Variants (flags of ``chunk_forward``):
 Parity status: every public function is pinned by ``tests/test_oracle_pins.py``
 (brute force, limits alpha=beta=1, beta=0 and C=1 with autograd gradients,
 geometric-sum closed forms, semigroup, resume, finite differences,
-linearity; for the variants: the no-momentum brute force and autograd SGD,
+linearity; a ragged tail against the brute force and against a separate
+call on the remainder; for the variants: the no-momentum brute force and autograd SGD,
 and for the chunk average its C=1 and equal-token reductions to the
 per-token form and its alpha=beta=1 closed form).  No function here is
 "parity unpinned".
@@ -300,14 +305,14 @@ def chunk_forward(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, ke
         beta = np.zeros(np.shape(eta))
         M0 = np.zeros(np.shape(W0))
     (B, H, T, D), (q, k, v, eta, alpha, beta, W, M) = _flatten(q, k, v, eta, alpha, beta, W0, M0)
-    if chunk <= 0 or T % chunk:
-        raise ValueError("T must be a positive multiple of the chunk size")
+    if chunk <= 0:
+        raise ValueError("the chunk size must be positive")
     W = W.copy()
     M = M.copy()
     out = np.zeros_like(q)
     inter = []
     for c0 in range(0, T, chunk):
-        sl = slice(c0, c0 + chunk)
+        sl = slice(c0, min(c0 + chunk, T))  # the last chunk may be shorter
         mats = unpack(kind, W, D, Hd)
         # 1. chunk output from the chunk-start weights
         out[:, sl] = fast_weight_forward(kind, mats, q[:, sl])
@@ -349,17 +354,17 @@ def brute_force(kind, loss, q, k, v, eta, alpha, beta, W0, M0, chunk, Hd=0, mome
         beta = np.zeros(np.shape(eta))
         M0 = np.zeros(np.shape(W0))
     (B, H, T, D), (q, k, v, eta, alpha, beta, W, M) = _flatten(q, k, v, eta, alpha, beta, W0, M0)
-    if chunk <= 0 or T % chunk:
-        raise ValueError("T must be a positive multiple of the chunk size")
+    if chunk <= 0:
+        raise ValueError("the chunk size must be positive")
     W = W.copy()
     M = M.copy()
     out = np.zeros_like(q)
     for c0 in range(0, T, chunk):
         mats = unpack(kind, W, D, Hd)
-        sl = slice(c0, c0 + chunk)
+        sl = slice(c0, min(c0 + chunk, T))  # the last chunk may be shorter
         out[:, sl] = fast_weight_forward(kind, mats, q[:, sl])
         g = pack(kind, token_grads(kind, loss, mats, k[:, sl], v[:, sl]))  # [BH, C, P]
-        for i in range(chunk):
+        for i in range(sl.stop - c0):
             t = c0 + i
             if momentum:
                 M = beta[:, t, None] * M + eta[:, t, None] * g[:, i]

@@ -39,9 +39,9 @@ def _rand_inputs(kind, B, H, T, D, Hd, seed, m0=0.3, gates="random"):
     return dict(q=q, k=k, v=v, eta=eta, alpha=alpha, beta=beta, W0=W0, M0=M0)
 
 
-def _run(fn, kind, loss, x, chunk, Hd):
+def _run(fn, kind, loss, x, chunk, Hd, **kw):
     return fn(kind, loss, x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"],
-              x["W0"], x["M0"], chunk, Hd)
+              x["W0"], x["M0"], chunk, Hd, **kw)
 
 
 # --------------------------------------------------------------------------
@@ -295,7 +295,51 @@ def test_pack_unpack_roundtrip():
         assert np.array_equal(oracle.pack(kind, oracle.unpack(kind, p, 4, 6)), p)
 
 
-def test_rejects_ragged_chunk():
+def test_rejects_bad_chunk():
     x = _rand_inputs("linear", 1, 1, 10, 3, 0, seed=0)
     with pytest.raises(ValueError):
-        _run(oracle.chunk_forward, "linear", "mse", x, 4, 0)
+        _run(oracle.chunk_forward, "linear", "mse", x, 0, 0)
+
+
+# --------------------------------------------------------------------------
+# Ragged tail (T % C != 0): the last chunk holds the remaining tokens
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,loss", CASES)
+@pytest.mark.parametrize("C,r", [(4, 1), (4, 3), (16, 5), (7, 6)])
+@pytest.mark.parametrize("momentum", [True, False])
+def test_tail_closed_form_equals_brute_force(kind, loss, C, r, momentum):
+    D, Hd = 5, 7
+    x = _rand_inputs(kind, 1, 2, 2 * C + r, D, Hd, seed=C * 10 + r)
+    ref = oracle.brute_force(kind, loss, x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"],
+                             x["M0"], C, Hd, momentum=momentum)
+    got = _run(oracle.chunk_forward, kind, loss, x, C, Hd, momentum=momentum)
+    for a, b in zip(got, ref):
+        if b is not None:
+            assert oracle.rel_err(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("kind,loss", CASES)
+@pytest.mark.parametrize("C,r", [(4, 3), (16, 9)])
+def test_tail_equals_separate_call_on_the_remainder(kind, loss, C, r):
+    """n whole chunks then a call with chunk = r on the remaining r tokens,
+    state carried between the calls, is the ragged call."""
+    D, Hd, n = 5, 6, 3
+    x = _rand_inputs(kind, 1, 2, n * C + r, D, Hd, seed=C + r + 50)
+    out, W, M = _run(oracle.chunk_forward, kind, loss, x, C, Hd)
+    cut = lambda d, lo, hi: {k: (v[:, :, lo:hi] if v.ndim >= 3 and k not in ("W0", "M0") else v) for k, v in d.items()}
+    a = cut(x, 0, n * C)
+    o1, W1, M1 = _run(oracle.chunk_forward, kind, loss, a, C, Hd)
+    b = cut(x, n * C, n * C + r)
+    b["W0"], b["M0"] = W1, M1
+    o2, W2, M2 = _run(oracle.chunk_forward, kind, loss, b, r, Hd)
+    assert oracle.rel_err(out, np.concatenate([o1, o2], axis=2)) < 1e-13
+    assert oracle.rel_err(W, W2) < 1e-13
+    assert oracle.rel_err(M, M2) < 1e-13
+
+
+def test_chunk_longer_than_sequence_is_one_chunk():
+    x = _rand_inputs("swiglu", 1, 2, 13, 4, 5, seed=61)
+    a = _run(oracle.chunk_forward, "swiglu", "negdot", x, 64, 5)
+    b = _run(oracle.chunk_forward, "swiglu", "negdot", x, 13, 5)
+    for u, v in zip(a, b):
+        assert oracle.rel_err(u, v) == 0.0
