@@ -140,11 +140,11 @@ def logscan(eta, alpha, beta, *, chunk: int, momentum: bool = True, chunk_avg: b
         if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
     B, H, T = eta.shape
-    if chunk < 1 or T % chunk:
-        raise ValueError("T must be a multiple of chunk")
+    if chunk < 1:
+        raise ValueError("chunk must be positive")
     cM = torch.empty_like(eta)
     cW = torch.empty_like(eta)
-    scal = torch.empty(B, H, T // chunk, 4, dtype=torch.float32, device=eta.device)
+    scal = torch.empty(B, H, (T + chunk - 1) // chunk, 4, dtype=torch.float32, device=eta.device)
     flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0)
     desc = make_desc("linear", "mse", "f32", B, H, T, 1, 0, chunk, flags)
     st = lib.e2ttt_logscan(ctypes.byref(desc), _ptr(eta), _ptr(alpha), _ptr(beta), _ptr(cM), _ptr(cW),

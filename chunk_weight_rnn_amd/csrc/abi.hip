@@ -15,7 +15,6 @@ static bool desc_ok(const e2ttt_desc* d) {
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->D < 1 || d->chunk < 1) return false;
     if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
     if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG)) return false;
-    if (d->T % d->chunk != 0) return false;
     // keep every product used for indexing far from int64 overflow
     const int64_t lim = (int64_t)1 << 40;
     if (d->B > lim || d->H > lim || d->T > lim || d->D > 65536 || d->Hd > 65536) return false;
@@ -38,13 +37,16 @@ Workspace workspace_layout(const e2ttt_desc& d, int path) {
     Workspace w{};
     const size_t BH = (size_t)(d.B * d.H);
     const size_t T = (size_t)d.T;
-    const size_t nc = (size_t)(d.T / d.chunk);
+    const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     const size_t P = (size_t)e2ttt_param_count(&d);
+    w.ldc = (d.T + 63) / 64 * 64;
+    const size_t ldc = (size_t)w.ldc;
+    (void)T;
     size_t off = 0;
     w.cM = off;
-    off += align_up(BH * T * sizeof(float));
+    off += align_up(BH * ldc * sizeof(float));
     w.cW = off;
-    off += align_up(BH * T * sizeof(float));
+    off += align_up(BH * ldc * sizeof(float));
     w.scal = off;
     off += align_up(BH * nc * 4 * sizeof(float));
     w.gacc = w.snap = off;
@@ -171,14 +173,15 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (events)
         for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
     if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
-    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, scal, s) != hipSuccess)
+    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
         return E2TTT_ERR_HIP;
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
     if (path == 1) {
-        e = launch_swiglu_mfma(*d, q, k, v, cM, cW, scal, W0, M0, out, W_end, M_end, wsb + ws.snap, s, ev[2]);
+        e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap, s, ev[2]);
     } else {
-        e = launch_generic(*d, q, k, v, cM, cW, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc), s);
+        e = launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc),
+                           s);
         if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
     }
     if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
@@ -187,12 +190,12 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
 
 int e2ttt_logscan(const e2ttt_desc* d, const float* eta, const float* alpha, const float* beta, float* cM,
                   float* cW, float* scal, void* stream) {
-    if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1 || d->T % d->chunk) return E2TTT_ERR_INVALID_ARG;
+    if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1) return E2TTT_ERR_INVALID_ARG;
     const int64_t BH = d->B * d->H;
     if (BH * d->T == 0) return E2TTT_OK;
     if (!eta || !alpha || !cM || !cW || !scal) return E2TTT_ERR_INVALID_ARG;
     if (!beta && !(d->flags & E2TTT_FLAG_NO_MOMENTUM)) return E2TTT_ERR_INVALID_ARG;
-    return launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, scal, (hipStream_t)stream) ==
+    return launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, d->T, scal, (hipStream_t)stream) ==
                    hipSuccess
                ? E2TTT_OK
                : E2TTT_ERR_HIP;

@@ -15,7 +15,8 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Byte offsets of the workspace sections for one call.
 struct Workspace {
-    size_t cM, cW, scal;  // logscan outputs (fp32)
+    size_t cM, cW, scal;  // logscan outputs (fp32; cM / cW rows of ldc tokens)
+    int64_t ldc;          // T rounded up to a whole 64-token block
     size_t gacc;          // portable path: per-head gradient accumulators (fp32, 2*P)
     size_t snap;          // MFMA path: bf16 chunk-start weight snapshots (B*H*nc*P)
     size_t total;
@@ -24,11 +25,12 @@ struct Workspace {
 Workspace workspace_layout(const e2ttt_desc& d, int path);
 
 // Launchers (return hipError_t of the launch).
+// cM / cW rows have stride ldc >= T; entries T .. ldc-1 are written as zeros.
 hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,
-                          const float* beta, float* cM, float* cW, float* scal, hipStream_t s);
+                          const float* beta, float* cM, float* cW, int64_t ldc, float* scal, hipStream_t s);
 
 hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v,
-                          const float* cM, const float* cW, const float* scal, const float* W0,
+                          const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
                           const float* M0, void* out, float* W_end, float* M_end, float* gacc,
                           hipStream_t s);
 
@@ -36,11 +38,11 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
 bool swiglu_mfma_supported(const e2ttt_desc& d);
 // Chunk loop of the SwiGLU path: final state and the bf16 chunk-start snapshots.
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
-                              const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
+                              int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
                               void* snap, hipStream_t s);
 // ev_mid (may be null) is recorded between the chunk-loop and output launches.
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
-                              const float* cM, const float* cW, const float* scal, const float* W0,
+                              const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
                               const float* M0, void* out, float* W_end, float* M_end, void* snap,
                               hipStream_t s, hipEvent_t ev_mid);
 

@@ -26,6 +26,7 @@ constexpr int NT = 256;
 
 struct GenericArgs {
     int64_t T, D, Hd, C, nc, P;
+    int64_t ldc;  // row stride of cM / cW (tokens, >= T)
     int loss, TB;
     int nomom;  // no momentum: M0 / M are not used (the scalar kernels already have beta = 0)
     const void* q;
@@ -102,9 +103,10 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
 
     for (int64_t c = 0; c < a.nc; ++c) {
         const int64_t t0 = c * a.C;
+        const int64_t Cc = min(a.C, a.T - t0);  // the last chunk may be shorter
         // ---- 1. outputs from the chunk-start weights
-        for (int64_t b0 = 0; b0 < a.C; b0 += TB) {
-            const int nt = (int)min((int64_t)TB, a.C - b0);
+        for (int64_t b0 = 0; b0 < Cc; b0 += TB) {
+            const int nt = (int)min((int64_t)TB, Cc - b0);
             for (int i = tid; i < nt * D; i += NT) xs[i] = to_f32(q[(t0 + b0) * D + i]);
             __syncthreads();
             if (KIND == E2TTT_LINEAR) {
@@ -151,15 +153,15 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
         }
 
         // ---- 2-3. backward factors at the chunk-start weights, aggregated into G
-        for (int64_t b0 = 0; b0 < a.C; b0 += TB) {
-            const int nt = (int)min((int64_t)TB, a.C - b0);
+        for (int64_t b0 = 0; b0 < Cc; b0 += TB) {
+            const int nt = (int)min((int64_t)TB, Cc - b0);
             for (int i = tid; i < nt * D; i += NT) {
                 xs[i] = to_f32(k[(t0 + b0) * D + i]);
                 vs[i] = to_f32(v[(t0 + b0) * D + i]);
             }
             for (int i = tid; i < TB; i += NT) {
-                cms[i] = i < nt ? a.cM[bh * a.T + t0 + b0 + i] : 0.f;
-                cws[i] = i < nt ? a.cW[bh * a.T + t0 + b0 + i] : 0.f;
+                cms[i] = i < nt ? a.cM[bh * a.ldc + t0 + b0 + i] : 0.f;
+                cws[i] = i < nt ? a.cW[bh * a.ldc + t0 + b0 + i] : 0.f;
             }
             __syncthreads();
             if (KIND == E2TTT_LINEAR) {
@@ -328,14 +330,15 @@ int generic_token_block(const e2ttt_desc& d) {
 }
 
 hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
-                          const float* cW, const float* scal, const float* W0, const float* M0, void* out,
+                          const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
                           float* W_end, float* M_end, float* gacc, hipStream_t s) {
     GenericArgs a;
     a.T = d.T;
     a.D = d.D;
     a.Hd = d.kind == E2TTT_LINEAR ? 0 : d.Hd;
     a.C = d.chunk;
-    a.nc = d.T / d.chunk;
+    a.nc = (d.T + d.chunk - 1) / d.chunk;
+    a.ldc = ldc;
     a.P = e2ttt_param_count(&d);
     a.loss = d.loss;
     a.TB = generic_token_block(d);

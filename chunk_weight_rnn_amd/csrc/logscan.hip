@@ -18,6 +18,8 @@
 // "ratio" form exp(Sb_i) * sum exp(Sa - Sb) is avoided: it overflows fp32 once
 // sum log(alpha/beta) exceeds ~88, which chunks of 1024 tokens reach.
 //
+// A ragged last chunk (T % C != 0) takes the same passes over its tokens.
+//
 // Mapping: one 64-lane wavefront per chunk, 4 chunks per 256-thread block.
 // Lane l owns the contiguous tokens [l*npl, (l+1)*npl); lane-local sequential
 // passes plus wavefront shuffle scans combine them.  For chunks of up to 1024
@@ -55,12 +57,19 @@ __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int6
                                                       int npl, int nomom, int avg, const float* __restrict__ eta,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ cM,
-                                                      float* __restrict__ cW, float* __restrict__ scal) {
+                                                      float* __restrict__ cW, int64_t ldc,
+                                                      float* __restrict__ scal) {
     const int lane = threadIdx.x & 63;
     const int64_t gc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (gc >= total_chunks) return;  // uniform per wavefront
     const int64_t bh = gc / nc, c = gc % nc;
-    const size_t base = (size_t)bh * T + (size_t)c * C;
+    const size_t base = (size_t)bh * T + (size_t)c * C;     // inputs: rows of T tokens
+    const size_t obase = (size_t)bh * ldc + (size_t)c * C;  // outputs: rows of ldc tokens
+    if (c == nc - 1 && T + lane < ldc) {                    // zero padding after the sequence
+        cM[(size_t)bh * ldc + T + lane] = 0.f;
+        cW[(size_t)bh * ldc + T + lane] = 0.f;
+    }
+    C = (int)min((int64_t)C, T - c * (int64_t)C);  // this chunk's length (the last may be shorter)
     const int lo = lane * npl;
 
     // the lane's tokens: log2 alpha, log2 beta (beta of the next token too), eta
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(256) void logscan_kernel(int64_t total_chunks, int6
 #pragma unroll
     for (int u = 0; u < MAXNPL; ++u) {
         if (u < npl && lo + u < C) {
-            cM[base + lo + u] = mv[u] * et[u];
-            cW[base + lo + u] = wv[u] * et[u];
+            cM[obase + lo + u] = mv[u] * et[u];
+            cW[obase + lo + u] = wv[u] * et[u];
         }
     }
 }
@@ -195,12 +204,19 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
                                                       int npl, int nomom, int avg, const float* __restrict__ eta,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ cM,
-                                                      float* __restrict__ cW, float* __restrict__ scal) {
+                                                      float* __restrict__ cW, int64_t ldc,
+                                                      float* __restrict__ scal) {
     const int lane = threadIdx.x & 63;
     const int64_t gc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (gc >= total_chunks) return;  // uniform per wavefront
     const int64_t bh = gc / nc, c = gc % nc;
-    const size_t base = (size_t)bh * T + (size_t)c * C;
+    const size_t base = (size_t)bh * T + (size_t)c * C;     // inputs: rows of T tokens
+    const size_t obase = (size_t)bh * ldc + (size_t)c * C;  // outputs: rows of ldc tokens
+    if (c == nc - 1 && T + lane < ldc) {                    // zero padding after the sequence
+        cM[(size_t)bh * ldc + T + lane] = 0.f;
+        cW[(size_t)bh * ldc + T + lane] = 0.f;
+    }
+    C = (int)min((int64_t)C, T - c * (int64_t)C);  // this chunk's length (the last may be shorter)
     const float* al = alpha + base;
     const float* be = nomom ? nullptr : beta + base;
     auto logb = [&](int t) { return nomom ? -INFINITY : logf(be[t]); };
@@ -268,8 +284,8 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
         sum_m += mt;
         sum_w += wt;
         if (!avg) {
-            cM[base + t] = mt * e;
-            cW[base + t] = wt * e;
+            cM[obase + t] = mt * e;
+            cW[obase + t] = wt * e;
         }
         Sa += logf(al[t]);
         Sb += logb(t);
@@ -289,8 +305,8 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
         }
         const float mm = sum_m / (float)C, mw = sum_w / (float)C;
         for (int t = lo; t < hi; ++t) {
-            cM[base + t] = mm * et[t];
-            cW[base + t] = mw * et[t];
+            cM[obase + t] = mm * et[t];
+            cW[obase + t] = mw * et[t];
         }
     }
 }
@@ -298,20 +314,20 @@ __global__ __launch_bounds__(256) void logscan_kernel_any(int64_t total_chunks, 
 }  // namespace
 
 hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,
-                          const float* beta, float* cM, float* cW, float* scal, hipStream_t s) {
+                          const float* beta, float* cM, float* cW, int64_t ldc, float* scal, hipStream_t s) {
     const int nomom = (flags & E2TTT_FLAG_NO_MOMENTUM) ? 1 : 0;
     const int avg = (flags & E2TTT_FLAG_CHUNK_AVG) ? 1 : 0;
-    const int64_t nc = T / chunk;
+    const int64_t nc = (T + chunk - 1) / chunk;  // the last chunk may be shorter
     const int64_t total = BH * nc;
     if (total == 0) return hipSuccess;
     const int npl = (int)((chunk + 63) / 64);
     const int64_t blocks = (total + 3) / 4;
     if (npl <= MAXNPL)
         hipLaunchKernelGGL(logscan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk, npl,
-                           nomom, avg, eta, alpha, beta, cM, cW, scal);
+                           nomom, avg, eta, alpha, beta, cM, cW, ldc, scal);
     else
         hipLaunchKernelGGL(logscan_kernel_any, dim3((unsigned)blocks), dim3(256), 0, s, total, nc, T, (int)chunk,
-                           npl, nomom, avg, eta, alpha, beta, cM, cW, scal);
+                           npl, nomom, avg, eta, alpha, beta, cM, cW, ldc, scal);
     return hipGetLastError();
 }
 

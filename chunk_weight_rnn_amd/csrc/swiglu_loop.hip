@@ -153,6 +153,7 @@ struct LoopArgs {
     float* M_end;
     __bf16* snap;
     int64_t T;
+    int64_t ldc;  // row stride of cM / cW (T rounded up to a whole block, zero padded)
     int Hd, C, nc, nsl, nwg, xcd_map;
 };
 
@@ -216,8 +217,11 @@ swiglu_loop_kernel(LoopArgs a) {
     const int64_t j = (int64_t)(L_id % a.nsl) * S + 16 * u + jl;  // this lane's hidden unit
     const int64_t T = a.T;
     const int64_t P = 3 * (int64_t)D * Hd;
-    const int nblk = (int)(T / CB);
-    const int nh = a.C / 32;   // half-blocks per chunk
+    const int nblk = (int)((T + CB - 1) / CB);  // the last block may be partial (rows past T read as zeros)
+    const int nh = a.C / 32;                     // half-blocks per chunk
+    // half-blocks of chunk c: nh, except a shorter last chunk
+    const int nh_last = (int)((T - (int64_t)(a.nc - 1) * a.C + 31) / 32);
+    auto halves = [&](int c) { return c == a.nc - 1 ? nh_last : nh; };
     const int nc = a.nc;
     unsigned char* const xw = xch + u * XW;  // this unit group's exchange area
     const int xl = 16 * lane;                // this lane's 16 bytes in an exchange fragment
@@ -246,11 +250,11 @@ swiglu_loop_kernel(LoopArgs a) {
         // cW (one resource based at cM).
         const __bf16* kbase = a.k + bh * T * D;
         const __bf16* vbase = a.v + bh * T * D;
-        const float* cMb = a.cM + bh * T;
-        const unsigned cw_rel = (unsigned)((const char*)(a.cW + bh * T) - (const char*)cMb);
+        const float* cMb = a.cM + bh * a.ldc;
+        const unsigned cw_rel = (unsigned)((const char*)(a.cW + bh * a.ldc) - (const char*)cMb);
         const u32x4 krs = buffer_rsrc(kbase, (unsigned)(T * D * 2));
         const u32x4 vrs = buffer_rsrc(vbase, (unsigned)(T * D * 2));
-        const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(T * 4));
+        const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(a.ldc * 4));
         const unsigned kvs_lds = lds_addr(kvs);
         auto issue_block = [&](int X) {
             // per-lane offsets recomputed here rather than kept in registers
@@ -403,12 +407,13 @@ swiglu_loop_kernel(LoopArgs a) {
             rescale(c);
             copy_step(c * nh);
             slot_barrier();
-            for (int k = 1; k < nh; ++k) {
+            const int nhc = halves(c);
+            for (int k = 1; k < nhc; ++k) {
                 aggregate(c * nh + k - 1);
                 copy_step(c * nh + k);
                 slot_barrier();
             }
-            aggregate(c * nh + nh - 1);
+            aggregate(c * nh + nhc - 1);
             if (c + 1 == nc) break;
             grad_operands(c + 1);
             slot_barrier();
@@ -501,7 +506,8 @@ swiglu_loop_kernel(LoopArgs a) {
                 grad_read(c * nh, fr);
                 grad_mfma(fr, hg);
             }
-            for (int k = 0; k + 1 < nh; ++k) {
+            const int nhc = halves(c);
+            for (int k = 0; k + 1 < nhc; ++k) {
                 const int hh = c * nh + k;
                 // next half-block's fragments, this one's backward with the next
                 // one's MFMAs slotted in between its VALU work, factor writes last
@@ -523,7 +529,7 @@ swiglu_loop_kernel(LoopArgs a) {
 #pragma unroll
                     for (int m = 0; m < 3; ++m) hg[ti][m] = hn[ti][m];
             }
-            backward(c * nh + nh - 1, hg);
+            backward(c * nh + nhc - 1, hg);
             slot_barrier();
         }
     }
@@ -532,7 +538,7 @@ swiglu_loop_kernel(LoopArgs a) {
 }  // namespace
 
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
-                              const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
+                              int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
                               void* snap, hipStream_t s) {
     const int64_t BH = d.B * d.H;
     LoopArgs la;
@@ -549,7 +555,8 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.T = d.T;
     la.Hd = (int)d.Hd;
     la.C = (int)d.chunk;
-    la.nc = (int)(d.T / d.chunk);
+    la.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
+    la.ldc = ldc;
     la.nsl = (int)(d.Hd / S);
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         const __bf16* sn;  // snapshot of the item's chunk
         int64_t tok;       // first token (global row in q / out) of this wave
         int nrec;          // bytes the copies may read (0 past the last item: zeros)
+        int nrows;         // rows of this wave inside the sequence (a short last chunk has fewer)
     };
     auto item = [&](int k) {
         Item it;
@@ -146,8 +147,10 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         const int rem = (int)(xx % ((int64_t)a.nc * a.rbc));
         const int c = rem / a.rbc, rb = rem % a.rbc;
         it.sn = a.snap + (bh * a.nc + c) * P;
-        it.tok = bh * a.T + (int64_t)c * a.C + (int64_t)rb * 32 * NWA + 32 * wave;
+        const int64_t tl = (int64_t)c * a.C + (int64_t)rb * 32 * NWA + 32 * wave;  // token within the sequence
+        it.tok = bh * a.T + tl;
         it.nrec = ok ? (int)(P * 2) : 0;
+        it.nrows = ok ? (int)(a.T - tl < 0 ? 0 : (a.T - tl > 32 ? 32 : a.T - tl)) : 0;
         return it;
     };
 
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     // the wave's 32 query rows of item k, row-major with the stage swizzle
     auto issue_q = [&](int k) {
         const Item it = item(k);
-        const int qrec = k < nmine ? 32 * D * 2 : 0;
+        const int qrec = it.nrows * D * 2;  // rows past the sequence read zeros
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
             const int row = 4 * n + (lane >> 4);
@@ -233,15 +236,17 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
                 oacc[dt] = mfma32(tr_frag_a(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
         }
         if (ih == nhb - 1) {
-            const int64_t tok = item(gs / nhb).tok;
-            __bf16* ob = a.out + tok * D;
+            const Item it = item(gs / nhb);
+            __bf16* ob = a.out + it.tok * D;
+            const bool row_ok = li < it.nrows;  // no stores past the sequence
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
                     const int d = 32 * dt + 8 * qd + 4 * lg;
-                    *(bf16x4*)&ob[li * D + d] =
-                        pack4(oacc[dt][4 * qd], oacc[dt][4 * qd + 1], oacc[dt][4 * qd + 2], oacc[dt][4 * qd + 3]);
+                    if (row_ok)
+                        *(bf16x4*)&ob[li * D + d] =
+                            pack4(oacc[dt][4 * qd], oacc[dt][4 * qd + 1], oacc[dt][4 * qd + 2], oacc[dt][4 * qd + 3]);
                 }
                 oacc[dt] = f32x16{};
             }
@@ -264,10 +269,10 @@ bool swiglu_mfma_supported(const e2ttt_desc& d) {
 }
 
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
-                              const float* cW, const float* scal, const float* W0, const float* M0, void* out,
+                              const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
                               float* W_end, float* M_end, void* snap, hipStream_t s, hipEvent_t ev_mid) {
     const int64_t BH = d.B * d.H;
-    hipError_t e = launch_swiglu_loop(d, k, v, cM, cW, scal, W0, M0, W_end, M_end, snap, s);
+    hipError_t e = launch_swiglu_loop(d, k, v, cM, cW, ldc, scal, W0, M0, W_end, M_end, snap, s);
     if (e != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, s)) != hipSuccess) return e;
 
@@ -278,7 +283,7 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.T = d.T;
     aa.Hd = (int)d.Hd;
     aa.C = (int)d.chunk;
-    aa.nc = (int)(d.T / d.chunk);
+    aa.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     aa.nb = (int)BH;
     // persistent grid: one workgroup per compute unit (the LDS of one fills it)
     int dev = 0, ncu = 0;

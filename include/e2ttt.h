@@ -58,7 +58,7 @@ typedef enum { E2TTT_F32 = 0, E2TTT_BF16 = 1 } e2ttt_dtype; /* dtype of q, k, v,
 
 typedef enum {
     E2TTT_OK = 0,
-    E2TTT_ERR_INVALID_ARG = 1, /* bad enum, negative size, T % chunk != 0, null or misaligned pointer */
+    E2TTT_ERR_INVALID_ARG = 1, /* bad enum or flag, negative size, null or misaligned pointer */
     E2TTT_ERR_UNSUPPORTED = 2, /* shape outside what any kernel handles (e.g. D > 256, Hd > 1024) */
     E2TTT_ERR_ALIAS = 3,       /* an output overlaps an input or another output */
     E2TTT_ERR_WORKSPACE = 4,   /* workspace null or smaller than e2ttt_workspace_size() */
@@ -88,7 +88,7 @@ typedef struct {
     int64_t B, H, T;  /* batch, heads, tokens per sequence */
     int64_t D;        /* head dim (k, q, v, out width) */
     int64_t Hd;       /* hidden width of MLP / SwiGLU fast weights; ignored for LINEAR */
-    int64_t chunk;    /* tokens per chunk; T must be a multiple */
+    int64_t chunk;    /* tokens per chunk; the last chunk holds the remaining T mod chunk tokens */
 } e2ttt_desc;
 
 /* Floats per (b, h) in the packed fast-weight vector; -1 for a bad desc. */
@@ -106,8 +106,8 @@ E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
  * Host-only validation of a call, touching no device memory (usable without
  * a GPU).  ptrs[] holds, in order: q, k, v, eta, alpha, beta, W0, M0, out,
  * W_end, M_end.  Returns E2TTT_OK or the first problem found:
- *   - sizes: B, H, T >= 0; D >= 1; chunk >= 1; T % chunk == 0; Hd >= 1 for
- *     MLP / SWIGLU; enums in range (E2TTT_ERR_INVALID_ARG);
+ *   - sizes: B, H, T >= 0; D >= 1; chunk >= 1; Hd >= 1 for MLP / SWIGLU;
+ *     enums and flags in range (E2TTT_ERR_INVALID_ARG);
  *   - pointers: non-null when the tensor is non-empty, 16-byte aligned
  *     (eta, alpha, beta: 4-byte aligned) (E2TTT_ERR_INVALID_ARG); with
  *     E2TTT_FLAG_NO_MOMENTUM, beta, M0 and M_end are not checked;
@@ -129,7 +129,9 @@ E2TTT_API int e2ttt_validate(const e2ttt_desc* desc, const void* const ptrs[11])
  *   workspace device scratch of >= e2ttt_workspace_size(desc) bytes, 256-byte
  *             aligned; clobbered.
  * T == 0 copies W0 -> W_end and M0 -> M_end; B*H == 0 does nothing.
- * Ragged tails (T % chunk != 0) are rejected with E2TTT_ERR_INVALID_ARG.
+ * A ragged tail (T % chunk != 0) is a shorter last chunk of T mod chunk
+ * tokens with the same closed form over its tokens (the official code's
+ * tail-length helper, named on the codewithpapers page, suggests one).
  */
 E2TTT_API int e2ttt_chunk_forward(const e2ttt_desc* desc,
                         const void* q, const void* k, const void* v,
@@ -160,7 +162,8 @@ E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
  *   cM[b][h][t] = eta_t * m_t,  m_t = prod_{s after t in its chunk} beta_s
  *   cW[b][h][t] = eta_t * w_t,  w_t = sum_{tau >= t} alpha(tau:end] * beta(t:tau]
  *   scal[b][h][c][0..3] = { prod alpha, prod beta, gamma = beta_first * w_first, 0 }
- * eta, alpha, beta, cM, cW: [B][H][T] fp32; scal: [B][H][T/chunk][4] fp32.
+ * eta, alpha, beta, cM, cW: [B][H][T] fp32; scal: [B][H][ceil(T/chunk)][4] fp32
+ * (a shorter last chunk takes the same sums over its tokens).
  * Only desc->B, H, T, chunk and flags are read: E2TTT_FLAG_NO_MOMENTUM takes
  * beta = 0 (beta may be NULL), E2TTT_FLAG_CHUNK_AVG replaces m_t and w_t by
  * their chunk means.

@@ -104,6 +104,12 @@ CONFIGS = {
                                 "1.3B-shaped TTT branch, chunk 256, no momentum", flags=2),
     "swiglu_1p3b_avg": Config("swiglu_1p3b_avg", "swiglu", "negdot", 8, 16, 2048, 128, 256, 256, "bf16",
                               "1.3B-shaped TTT branch, chunk 256, chunk-averaged kernels", flags=4),
+    # streaming: one 256-token chunk per call, state carried in from the previous call
+    "swiglu_1p3b_stream": Config("swiglu_1p3b_stream", "swiglu", "negdot", 8, 16, 256, 128, 256, 256, "bf16",
+                                 "1.3B-shaped TTT branch, streaming: one chunk per call"),
+    # a ragged sequence: 7 whole chunks and a 208-token tail
+    "swiglu_1p3b_tail": Config("swiglu_1p3b_tail", "swiglu", "negdot", 8, 16, 2000, 128, 256, 256, "bf16",
+                               "1.3B-shaped TTT branch, T = 7 x 256 + 208"),
 }
 
 

@@ -79,8 +79,8 @@ def errors(cfg: synth.Config, got, ref, W0) -> dict:
     assert (M_g is None) == (M_r is None), "momentum output present on one side only"
     W0 = np.asarray(W0, dtype=np.float64)
     e = {}
-    for c in range(cfg.T // cfg.chunk):
-        sl = slice(c * cfg.chunk, (c + 1) * cfg.chunk)
+    for c in range(-(-cfg.T // cfg.chunk)):  # the last chunk may be shorter
+        sl = slice(c * cfg.chunk, min((c + 1) * cfg.chunk, cfg.T))
         r = out_r[:, :, sl]
         e[f"out[{c}]"] = None if _diverged(r) else err(out_g[:, :, sl], r)
     with np.errstate(invalid="ignore", over="ignore"):

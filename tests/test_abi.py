@@ -52,8 +52,9 @@ def test_workspace_size_rules(lib):
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 0
     d = _desc(T=0)
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 0
+    # a ragged tail is a shorter last chunk: two chunks, coefficient rows padded to 128
     d = _desc(T=100, chunk=64)
-    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == lib.e2ttt_workspace_size(ctypes.byref(_desc(T=128, chunk=64)))
     # MFMA path needs the snapshots: grows with the number of chunks
     a = lib.e2ttt_workspace_size(ctypes.byref(_desc(chunk=64)))
     b = lib.e2ttt_workspace_size(ctypes.byref(_desc(chunk=256)))
@@ -88,9 +89,10 @@ def test_validate_bad_desc(lib, field, value):
     assert _validate(lib, d, _ptrs(d)) == 1
 
 
-def test_validate_ragged_tail_rejected(lib):
-    d = _desc(T=100, chunk=64)
-    assert _validate(lib, d, _ptrs(d)) == 1
+def test_validate_ragged_tail_accepted(lib):
+    for T, C in ((100, 64), (1, 64), (65, 64), (7, 3)):
+        d = _desc(T=T, chunk=C)
+        assert _validate(lib, d, _ptrs(d)) == 0
 
 
 def test_validate_null_and_misaligned(lib):
@@ -137,7 +139,7 @@ def test_validate_unsupported_shape(lib):
 
 
 def test_chunk_forward_rejects_before_launch(lib):
-    d = _desc(T=100, chunk=64)
+    d = _desc(flags=8)  # unknown flag
     v = ctypes.c_void_p
     args = [v(1 << 40)] * 11
     assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 1

@@ -32,5 +32,5 @@ def test_bf16_and_distributions():
 
 def test_config_table():
     for cfg in synth.CONFIGS.values():
-        assert cfg.T % cfg.chunk == 0
+        assert cfg.T >= 1 and cfg.chunk >= 1
         assert cfg.P == synth.param_count(cfg.kind, cfg.D, cfg.Hd)
