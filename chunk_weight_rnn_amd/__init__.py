@@ -12,7 +12,8 @@ chunk-end weights W and momentum M of the per-token recurrence
 M_t = beta_t M_{t-1} + eta_t g_t, W_t = alpha_t W_{t-1} - M_t, and the chunk
 output comes from the chunk-start weights.  Variants: ``momentum=False``
 (W_t = alpha_t W_{t-1} - eta_t g_t) and ``chunk_avg=True`` (the per-token
-kernels replaced by their chunk means).
+kernels replaced by their chunk means).  ``chunk_backward`` is the
+vector-Jacobian product of ``chunk_forward`` (SwiGLU MFMA path).
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, make_desc
 
-__all__ = ["chunk_forward", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
+__all__ = ["chunk_forward", "chunk_backward", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
 
 
@@ -125,6 +126,58 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
     if st != 0:
         raise E2TTTError("e2ttt_chunk_forward", st)
     return out, W_end, M_end
+
+
+def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, chunk: int, Hd: int,
+                   kind: str = "swiglu", loss: str = "negdot", momentum: bool = True, chunk_avg: bool = False,
+                   workspace=None, stream=None):
+    """Gradients of <dout, out> + <dW_end, W_end> + <dM_end, M_end> through
+    ``chunk_forward``; returns a dict with keys q, k, v (bf16), eta, alpha,
+    beta, W0, M0 (float32).  Without momentum beta, M0 and dM_end are ignored
+    and the beta / M0 gradients are None."""
+    lib = library()
+    if not momentum:
+        beta = M0 = dM_end = None
+    named = (("q", q), ("k", k), ("v", v), ("eta", eta), ("alpha", alpha), ("beta", beta), ("W0", W0),
+             ("M0", M0), ("dout", dout), ("dW_end", dW_end), ("dM_end", dM_end))
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in named:
+        want = q.dtype if name in ("q", "k", "v", "dout") else torch.float32
+        if t is not None and t.dtype != want:
+            raise TypeError(f"{name} must be {want}")
+    B, H, T, D = q.shape
+    flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0)
+    desc = make_desc(kind, loss, _io_name(q), B, H, T, D, Hd, chunk, flags)
+    P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("dout", dout, q.shape),
+                         ("eta", eta, (B, H, T)), ("alpha", alpha, (B, H, T)), ("beta", beta, (B, H, T)),
+                         ("W0", W0, (B, H, P)), ("M0", M0, (B, H, P)), ("dW_end", dW_end, (B, H, P)),
+                         ("dM_end", dM_end, (B, H, P))):
+        if t is not None and tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} must have shape {tuple(shp)}")
+    g = {"q": torch.empty_like(q), "k": torch.empty_like(k), "v": torch.empty_like(v),
+         "eta": torch.empty_like(eta), "alpha": torch.empty_like(alpha),
+         "beta": torch.empty_like(beta) if momentum else None, "W0": torch.empty_like(W0),
+         "M0": torch.empty_like(M0) if momentum else None}
+    ws_bytes = int(lib.e2ttt_backward_workspace_size(ctypes.byref(desc)))
+    if ws_bytes == ctypes.c_size_t(-1).value:
+        raise E2TTTError("e2ttt_backward_workspace_size", 1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.e2ttt_chunk_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha),
+                                  _ptr(beta), _ptr(W0), _ptr(M0), _ptr(dout), _ptr(dW_end), _ptr(dM_end),
+                                  _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["eta"]), _ptr(g["alpha"]),
+                                  _ptr(g["beta"]), _ptr(g["W0"]), _ptr(g["M0"]), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel()), _stream_handle(stream))
+    if st != 0:
+        raise E2TTTError("e2ttt_chunk_backward", st)
+    return g
 
 
 def logscan(eta, alpha, beta, *, chunk: int, momentum: bool = True, chunk_avg: bool = False, stream=None):

@@ -17,7 +17,9 @@ STATUS = {0: "E2TTT_OK", 1: "E2TTT_ERR_INVALID_ARG", 2: "E2TTT_ERR_UNSUPPORTED",
           4: "E2TTT_ERR_WORKSPACE", 5: "E2TTT_ERR_HIP"}
 
 EXPORTS = ("e2ttt_param_count", "e2ttt_workspace_size", "e2ttt_path", "e2ttt_validate",
-           "e2ttt_chunk_forward", "e2ttt_chunk_forward_events", "e2ttt_logscan", "e2ttt_status_string")
+           "e2ttt_chunk_forward", "e2ttt_chunk_forward_events", "e2ttt_logscan", "e2ttt_status_string",
+           "e2ttt_backward_workspace_size", "e2ttt_validate_backward", "e2ttt_chunk_backward",
+           "e2ttt_chunk_backward_events")
 
 
 class Desc(ctypes.Structure):
@@ -60,6 +62,14 @@ def load() -> ctypes.CDLL:
     lib.e2ttt_chunk_forward_events.restype = ctypes.c_int
     lib.e2ttt_logscan.argtypes = [pd] + [vp] * 6 + [vp]
     lib.e2ttt_logscan.restype = ctypes.c_int
+    lib.e2ttt_backward_workspace_size.argtypes = [pd]
+    lib.e2ttt_backward_workspace_size.restype = sz
+    lib.e2ttt_validate_backward.argtypes = [pd, ctypes.POINTER(vp)]
+    lib.e2ttt_validate_backward.restype = ctypes.c_int
+    lib.e2ttt_chunk_backward.argtypes = [pd] + [vp] * 19 + [vp, sz, vp]
+    lib.e2ttt_chunk_backward.restype = ctypes.c_int
+    lib.e2ttt_chunk_backward_events.argtypes = [pd] + [vp] * 19 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.e2ttt_chunk_backward_events.restype = ctypes.c_int
     lib.e2ttt_status_string.argtypes = [ctypes.c_int]
     lib.e2ttt_status_string.restype = ctypes.c_char_p
     _lib = lib

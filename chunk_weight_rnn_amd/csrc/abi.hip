@@ -64,6 +64,62 @@ struct Range {
 
 static bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// ---------------------------------------------------------------- backward
+static bool backward_supported(const e2ttt_desc& d) {
+    if (d.flags & E2TTT_FLAG_FORCE_GENERIC) return false;
+    if (!swiglu_mfma_supported(d) || d.chunk > 2048) return false;
+    // 32-bit byte offsets of the buffer copies
+    return d.T * d.D * 2 < ((int64_t)1 << 31) && 6 * d.Hd * d.D * 2 < ((int64_t)1 << 31);
+}
+
+struct BwdWorkspace {
+    size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, total;
+    int64_t ldc;
+};
+
+static BwdWorkspace bwd_workspace_layout(const e2ttt_desc& d) {
+    BwdWorkspace w{};
+    const size_t BH = (size_t)(d.B * d.H);
+    const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);
+    const size_t P = (size_t)e2ttt_param_count(&d);
+    const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
+    w.ldc = (d.T + 63) / 64 * 64;
+    const size_t ldc = (size_t)w.ldc;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    w.cM = take(BH * ldc * 4);
+    w.cW = take(BH * ldc * 4);
+    w.scal = take(BH * nc * 4 * 4);
+    w.snapW = take(BH * nc * P * 2);
+    w.snapM = mom ? take(BH * nc * P * 2) : 0;
+    w.lamW = take(BH * P * 4);
+    w.lamM = mom ? take(BH * P * 4) : 0;
+    w.lam = take(BH * 2 * P * 2);
+    w.inter = take(BH * (size_t)swiglu_bwd_inter_elems(d) * 2);
+    w.dcM = take(BH * ldc * 4);
+    w.dcW = take(BH * ldc * 4);
+    w.dpart = take(BH * nc * (size_t)(d.Hd / 64) * 4 * 4);
+    w.total = (BH * (size_t)d.T == 0) ? 0 : off;
+    return w;
+}
+
+// byte sizes of the backward's 19 tensors: q, k, v, eta, alpha, beta, W0, M0,
+// dout, dW_end, dM_end (inputs), dq, dk, dv, deta, dalpha, dbeta, dW0, dM0
+static void bwd_sizes(const e2ttt_desc& d, size_t bytes[19]) {
+    const size_t BH = (size_t)(d.B * d.H);
+    const size_t es = d.io_dtype == E2TTT_BF16 ? 2 : 4;
+    const size_t P = (size_t)e2ttt_param_count(&d);
+    const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
+    const size_t x = BH * d.T * d.D * es, g = BH * d.T * 4, st = BH * P * 4;
+    const size_t tmp[19] = {x, x, x, g, g, mom ? g : 0, st, mom ? st : 0, x, st, mom ? st : 0,
+                            x, x, x, g, g, mom ? g : 0, st, mom ? st : 0};
+    for (int i = 0; i < 19; ++i) bytes[i] = tmp[i];
+}
+
 }  // namespace e2ttt
 
 using namespace e2ttt;
@@ -184,6 +240,125 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
                            s);
         if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
     }
+    if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
+    return e == hipSuccess ? E2TTT_OK : E2TTT_ERR_HIP;
+}
+
+size_t e2ttt_backward_workspace_size(const e2ttt_desc* d) {
+    if (!desc_ok(d)) return (size_t)-1;
+    return bwd_workspace_layout(*d).total;
+}
+
+int e2ttt_validate_backward(const e2ttt_desc* d, const void* const ptrs[19]) {
+    if (!desc_ok(d) || !ptrs) return E2TTT_ERR_INVALID_ARG;
+    if (!backward_supported(*d)) return E2TTT_ERR_UNSUPPORTED;
+    size_t bytes[19];
+    bwd_sizes(*d, bytes);
+    for (int i = 0; i < 19; ++i) {
+        if (bytes[i] == 0) continue;
+        if (!ptrs[i]) return E2TTT_ERR_INVALID_ARG;
+        const bool scalar = (i >= 3 && i <= 5) || (i >= 14 && i <= 16);  // [B][H][T] fp32
+        if ((uintptr_t)ptrs[i] % (scalar ? 4 : 16)) return E2TTT_ERR_INVALID_ARG;
+    }
+    for (int o = 11; o < 19; ++o) {
+        if (bytes[o] == 0) continue;
+        const Range ro{(uintptr_t)ptrs[o], (uintptr_t)ptrs[o] + bytes[o]};
+        for (int i = 0; i < 19; ++i) {
+            if (i == o || bytes[i] == 0) continue;
+            if (overlap(ro, Range{(uintptr_t)ptrs[i], (uintptr_t)ptrs[i] + bytes[i]})) return E2TTT_ERR_ALIAS;
+        }
+    }
+    return E2TTT_OK;
+}
+
+int e2ttt_chunk_backward(const e2ttt_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                         const float* alpha, const float* beta, const float* W0, const float* M0, const void* dout,
+                         const float* dW_end, const float* dM_end, void* dq, void* dk, void* dv, float* deta,
+                         float* dalpha, float* dbeta, float* dW0, float* dM0, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    return e2ttt_chunk_backward_events(d, q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, dq, dk, dv, deta,
+                                       dalpha, dbeta, dW0, dM0, workspace, workspace_bytes, stream, nullptr);
+}
+
+int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                                const float* alpha, const float* beta, const float* W0, const float* M0,
+                                const void* dout, const float* dW_end, const float* dM_end, void* dq, void* dk,
+                                void* dv, float* deta, float* dalpha, float* dbeta, float* dW0, float* dM0,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const events[4]) {
+    const void* ptrs[19] = {q,  k,  v,  eta,  alpha,  beta,  W0,  M0,  dout, dW_end,
+                            dM_end, dq, dk, dv, deta, dalpha, dbeta, dW0, dM0};
+    const int st = e2ttt_validate_backward(d, ptrs);
+    if (st != E2TTT_OK) return st;
+    const BwdWorkspace ws = bwd_workspace_layout(*d);
+    if (ws.total > 0) {
+        if (!workspace || workspace_bytes < ws.total || (uintptr_t)workspace % kAlign) return E2TTT_ERR_WORKSPACE;
+        const Range wr{(uintptr_t)workspace, (uintptr_t)workspace + ws.total};
+        size_t bytes[19];
+        bwd_sizes(*d, bytes);
+        for (int i = 0; i < 19; ++i)
+            if (bytes[i] && overlap(wr, Range{(uintptr_t)ptrs[i], (uintptr_t)ptrs[i] + bytes[i]}))
+                return E2TTT_ERR_ALIAS;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t BH = d->B * d->H;
+    if (BH == 0) return E2TTT_OK;
+    const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
+    const size_t P = (size_t)e2ttt_param_count(d);
+    if (d->T == 0) {  // the state passes through unchanged
+        if (hipMemcpyAsync(dW0, dW_end, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess) return E2TTT_ERR_HIP;
+        if (mom && hipMemcpyAsync(dM0, dM_end, BH * P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        return E2TTT_OK;
+    }
+    char* wsb = (char*)workspace;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+        for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
+    if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
+    // forward recompute: scalar kernels and the chunk loop (chunk-start
+    // snapshots of W and M); its end state goes to dW0 / dM0, which the
+    // backward overwrites
+    float* cM = (float*)(wsb + ws.cM);
+    float* cW = (float*)(wsb + ws.cW);
+    float* scal = (float*)(wsb + ws.scal);
+    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
+        return E2TTT_ERR_HIP;
+    if (launch_swiglu_loop(*d, k, v, cM, cW, ws.ldc, scal, W0, M0, dW0, dM0, wsb + ws.snapW,
+                           mom ? wsb + ws.snapM : nullptr, s) != hipSuccess)
+        return E2TTT_ERR_HIP;
+    if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
+    BwdBuffers b;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.dout = dout;
+    b.eta = eta;
+    b.alpha = alpha;
+    b.beta = beta;
+    b.cM = cM;
+    b.cW = cW;
+    b.scal = scal;
+    b.snapW = wsb + ws.snapW;
+    b.snapM = mom ? wsb + ws.snapM : nullptr;
+    b.dW_end = dW_end;
+    b.dM_end = dM_end;
+    b.lamW = (float*)(wsb + ws.lamW);
+    b.lamM = mom ? (float*)(wsb + ws.lamM) : nullptr;
+    b.lam = wsb + ws.lam;
+    b.inter = wsb + ws.inter;
+    b.dcM = (float*)(wsb + ws.dcM);
+    b.dcW = (float*)(wsb + ws.dcW);
+    b.dpart = (float*)(wsb + ws.dpart);
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.deta = deta;
+    b.dalpha = dalpha;
+    b.dbeta = dbeta;
+    b.dW0 = dW0;
+    b.dM0 = dM0;
+    b.ldc = ws.ldc;
+    hipError_t e = launch_swiglu_backward(*d, b, s, ev[2]);
     if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
     return e == hipSuccess ? E2TTT_OK : E2TTT_ERR_HIP;
 }

@@ -36,14 +36,38 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
 
 // SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
 bool swiglu_mfma_supported(const e2ttt_desc& d);
-// Chunk loop of the SwiGLU path: final state and the bf16 chunk-start snapshots.
+// Chunk loop of the SwiGLU path: final state and the bf16 chunk-start weight
+// snapshots [BH][nc][W1^T | W3^T | W2] (each [Hd][D]); with snapM non-null
+// (momentum only) also the chunk-start momentum snapshots in the same layout.
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
-                              void* snap, hipStream_t s);
+                              void* snap, void* snapM, hipStream_t s);
 // ev_mid (may be null) is recorded between the chunk-loop and output launches.
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
                               const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
                               const float* M0, void* out, float* W_end, float* M_end, void* snap,
                               hipStream_t s, hipEvent_t ev_mid);
+
+// Backward pass of the SwiGLU path (same shape support, chunk <= 2048).
+struct BwdBuffers {
+    const void *q, *k, *v, *dout;      // [BH][T][D] bf16
+    const float *eta, *alpha, *beta;   // [BH][T]
+    const float *cM, *cW, *scal;       // scalar-kernel outputs of the recompute
+    const void *snapW, *snapM;         // bf16 chunk-start snapshots of the recompute
+    const float *dW_end, *dM_end;      // [BH][P] state cotangents
+    float *lamW, *lamM;                // [BH][P] fp32 working state cotangents (hidden-major)
+    void* lam;                         // [BH][2P] bf16 copies
+    void* inter;                       // [BH][6][Hd][chunk] bf16 per-chunk terms
+    float *dcM, *dcW;                  // [BH][ldc]
+    float* dpart;                      // [BH][nc][Hd/64][4]
+    void *dq, *dk, *dv;                // [BH][T][D] bf16
+    float *deta, *dalpha, *dbeta;      // [BH][T]
+    float *dW0, *dM0;                  // [BH][P]
+    int64_t ldc;
+};
+// ev_loop (may be null) is recorded after the reverse chunk loop, before the
+// scalar kernels' backward.
+hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipStream_t s, hipEvent_t ev_loop);
+int64_t swiglu_bwd_inter_elems(const e2ttt_desc& d);  // per (b, h)
 
 }  // namespace e2ttt

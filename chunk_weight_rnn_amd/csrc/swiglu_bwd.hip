@@ -1,0 +1,785 @@
+// SwiGLU fast weight, negative-dot loss, bf16 q/k/v: the backward pass of the
+// E2-TTT chunk update on CDNA4 (gfx950).
+//
+// Method: "Rethinking Expressivity and Efficiency in Test-Time Training"
+// (abstract; atlas summary "Approach"): the forward pass takes, per chunk,
+// gradients at the chunk-start weights W_c, two weighted aggregations with the
+// per-token coefficients cM = eta*m, cW = eta*w, and the transition
+//   M_{c+1} = Bb M_c + sum_t cM_t g_t,   W_{c+1} = A W_c - gamma M_c - sum_t cW_t g_t,
+// and emits out_t = f_{W_c}(q_t).  This file is its vector-Jacobian product.
+//
+// Reverse over chunks with the state cotangents (lW, lM) of (W_{c+1}, M_{c+1})
+// (initially dW_end, dM_end).  Per token t and hidden unit j of chunk c, at
+// W_c (row vectors; W1, W3 [D x Hd], W2 [Hd x D]):
+//   h1 = k W1, h3 = k W3, du = -v W2^T, a = silu(h1), s = silu'(h1),
+//   s2 = silu''(h1), u = a h3, dh1 = du h3 s, dh3 = du a;
+//   projections of the cotangents: pX1 = k lX1, pX3 = k lX3, pX2 = v lX2^T
+//   (X in {W, M}), combined P = cM pM - cW pW;
+//   E  = P1 h3 s + P3 a                          (d/d du)
+//   F1 = du P1 h3 s2 + (du P3 - h3 P2) s          (d/d h1)
+//   F3 = du P1 s - a P2                           (d/d h3)
+//   dcM_t = sum_j pM1 dh1 + pM3 dh3 - u pM2,   dcW_t = -(same with pW)
+//   dk_t = sum_j F1 W1[:,j] + F3 W3[:,j] + dh1 (cM lM1 - cW lW1)[:,j]
+//                                        + dh3 (cM lM3 - cW lW3)[:,j]
+//   dv_t = sum_j -E W2[j,:] - u (cM lM2 - cW lW2)[j,:]
+//   output path: hq1 = q W1, hq3 = q W3, hdo = do W2^T, uq = silu(hq1) hq3,
+//   dhq1 = hdo hq3 silu'(hq1), dhq3 = hdo silu(hq1),
+//   dq_t = sum_j dhq1 W1[:,j] + dhq3 W3[:,j]
+// and per chunk
+//   dW1 = sum_t k_t^T F1 + q_t^T dhq1,  dW3 = sum_t k_t^T F3 + q_t^T dhq3,
+//   dW2 = sum_t -E^T v_t + uq^T do_t,
+//   lW <- A lW + dW,   lM <- Bb lM - gamma lW_old,
+//   dA = <lW_old, W_c>,  dBb = <lM_old, M_c>,  dgamma = -<lW_old, M_c>.
+// The chunk-start states come from a forward recompute (bf16 snapshots of W_c
+// and M_c); the scalar kernels' backward turns dcM, dcW, dA, dBb, dgamma into
+// d eta, d alpha, d beta.
+//
+// Kernels, per chunk from the last to the first:
+//   token kernel  (one workgroup per 64 tokens): projections at W_c and the
+//                 cotangents (16x16x32 MFMA, hidden units 16 at a time through
+//                 LDS), the elementwise terms, and dk, dv, dq, dcM, dcW summed
+//                 over all hidden units (16x16x16 MFMA); E, F1, F3, dhq1, dhq3,
+//                 uq go to a per-chunk buffer for
+//   weight kernel (one workgroup per 64 hidden units): the chunk's dW by a
+//                 contraction over its tokens (16x16x32 MFMA, token rows
+//                 through LDS and the gfx950 transpose read) and the state
+//                 cotangent update, in fp32, with bf16 copies for the next
+//                 token kernel;
+// then one scalar kernel for the whole sequence.
+#include "e2ttt_internal.h"
+
+namespace e2ttt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+constexpr int D = 128;             // head dim
+constexpr int NT = 256;            // 4 wavefronts per workgroup
+constexpr int US = 16;             // hidden units per token-kernel step
+constexpr int TB = 64;             // tokens per token-kernel workgroup
+constexpr int ROWB = D * 2;        // one bf16 row of D
+constexpr int STEPB = US * ROWB;   // one matrix's rows of a token-kernel step (4 KB)
+constexpr int NMAT = 9;            // W1^T, W3^T, W2, lW1^T, lW3^T, lW2, lM1^T, lM3^T, lM2
+constexpr int WS = 64;             // hidden units per weight-kernel workgroup
+constexpr int KT = 32;             // tokens per weight-kernel step
+constexpr int KTB = KT * ROWB;     // one token matrix's rows of a weight-kernel step (8 KB)
+constexpr int NQ = 6;              // per (token, unit) terms handed to the weight kernel
+constexpr int RSRC_W3 = 0x00020000;  // dword 3 of a raw buffer resource (32-bit format, no swizzle)
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x16: A lane (row l%16, k 4(l/16)..+3), B lane (column l%16, same k)
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                      0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+// 16-byte chunk swizzle of 256-byte rows: logical chunk c of row t sits at
+// physical chunk c ^ swz4(t) (a bijection of 0..15 in t, so 16 consecutive
+// rows read at one logical chunk cover all 64 banks).
+__device__ __forceinline__ int swz4(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
+
+// (base and size must be the same in every lane; the words are read from
+// the first lane so that the descriptor lives in scalar registers)
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, unsigned num_bytes) {
+    const unsigned long long p = (unsigned long long)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+    r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
+    r[3] = RSRC_W3;
+    return r;
+}
+
+// HBM -> LDS copy of 16 bytes per lane: lane L reads base + voff (zeros at or
+// past the resource's size) and writes LDS byte lds + 16 L.  Its completion is
+// waited for explicitly with wait_vm; the instruction writes no register.
+__device__ __forceinline__ void copy16(u32x4 rsrc, unsigned lds, unsigned voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// B fragment of a 16x16x16 MFMA from a hidden-major [16 units][D] stage
+// (swizzled rows): lane (p, g) gets rows 4g + e (e = 0..3), column d0 + p,
+// by the transpose read (lane p's result slot e comes from the 8 bytes that
+// lane 4e + p/4 of its 16-lane group addresses, element p%4).
+__device__ __forceinline__ bf16x4 tr_units(const unsigned char* stage, int lane, int n) {
+    const int p = lane & 15, g = lane >> 4;
+    const int row = 4 * g + (p >> 2);
+    const int q = p & 3;
+    const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz4(row)) + 8 * (q & 1);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
+}
+
+// B fragment of a 16x16x32 MFMA from a token-major [32 tokens][D] stage:
+// lane (p, g) gets tokens 8g + e (e = 0..7), column 16 n + p.
+__device__ __forceinline__ bf16x8 tr_tokens(const unsigned char* stage, int lane, int n) {
+    const int p = lane & 15, g = lane >> 4;
+    const int q = p & 3;
+    bf16x8 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 8 * g + 4 * h + (p >> 2);
+        const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz4(row & 15)) + 8 * (q & 1);
+        const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 * h + e] = v[e];
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// token kernel
+struct TokArgs {
+    const __bf16 *k, *v, *q, *dout;  // [BH][T][D]
+    const float *cM, *cW;            // [BH][ldc]
+    const __bf16* snapW;             // [BH][nc][3][Hd][D]: W1^T, W3^T, W2 of each chunk start
+    const __bf16* lam;               // [BH][6][Hd][D]: lW1^T, lW3^T, lW2, lM1^T, lM3^T, lM2
+    __bf16* inter;                   // [BH][6][Hd][C]: F1, F3, -E, dhq1, dhq3, uq
+    __bf16 *dq, *dk, *dv;            // [BH][T][D]
+    float *dcM, *dcW;                // [BH][ldc]
+    int64_t T, ldc;
+    int Hd, C, nc, c, nb;            // nb: 64-token blocks of chunk c
+};
+
+template <bool MOM>
+__global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char stage[2 * NMAT * STEPB];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tl = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / a.nb;
+    const int blk = blockIdx.x % a.nb;
+    const int64_t T = a.T;
+    const int Hd = a.Hd;
+    const int64_t P = 3 * (int64_t)D * Hd;
+    const int64_t tc0 = (int64_t)a.c * a.C + blk * TB + 16 * w;  // the wave's first token
+    const int64_t t = tc0 + tl;                                  // this lane's token (projections)
+    const bool tin = t < T;
+    const int tcl = blk * TB + 16 * w + tl;                      // ... within the chunk
+    constexpr int nmat = MOM ? NMAT : 6;
+
+    const u32x4 wrs = buffer_rsrc(a.snapW + (bh * a.nc + a.c) * P, (unsigned)(P * 2));
+    const u32x4 lrs = buffer_rsrc(a.lam + bh * 2 * P, (unsigned)(2 * P * 2));
+    const unsigned stage_lds = lds_addr(stage);
+    // rows j0 .. j0+15 of matrices 0 .. nm-1 into stage buffer b: 4 copies per
+    // matrix (4 rows each), spread over the 4 waves
+    auto issue = [&](int j0, int b, int nm) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        for (int ii = w; ii < 4 * nm; ii += 4) {
+            const int mi = ii >> 2, rq = ii & 3;
+            const int row = 4 * rq + (ln >> 4);
+            const unsigned off = (unsigned)((mi < 3 ? mi : mi - 3) * Hd * D + (j0 + row) * D) * 2u +
+                                 16u * (unsigned)((ln & 15) ^ swz4(row));
+            copy16(mi < 3 ? wrs : lrs, stage_lds + (unsigned)((b * NMAT + mi) * STEPB + 4 * rq * ROWB), off);
+        }
+    };
+    // A fragment of a projection: row j0 + tl of matrix mi, d = 32 kk + 8 g .. +7
+    auto afrag = [&](const unsigned char* sb, int mi, int kk) {
+        return *(const bf16x8*)(sb + mi * STEPB + tl * ROWB + 16 * ((4 * kk + g) ^ swz4(tl)));
+    };
+    auto load_tok = [&](const __bf16* X, bf16x8 (&f)[4]) {
+        const __bf16* row = X + (bh * T + (tin ? t : 0)) * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            f[kk] = *(const bf16x8*)(row + 32 * kk);
+            if (!tin) f[kk] = bf16x8{};
+        }
+    };
+    __bf16* const inter = a.inter + bh * NQ * (int64_t)Hd * a.C;
+    auto put_inter = [&](int qi, int j0, const float (&x)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) inter[((int64_t)qi * Hd + j0 + 4 * g + r) * a.C + tcl] = (__bf16)x[r];
+    };
+    auto store_tok = [&](__bf16* X, const f32x4 (&acc)[8]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t tt = tc0 + 4 * g + r;
+            if (tt < T) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) X[(bh * T + tt) * D + 16 * n + tl] = (__bf16)acc[n][r];
+            }
+        }
+    };
+    const int nsteps = Hd / US;
+
+    // ---------------- pass A: k / v side (needs W_c and the cotangents)
+    {
+        const float cm = MOM ? a.cM[bh * a.ldc + tcl + (int64_t)a.c * a.C] : 0.f;
+        const float cw = a.cW[bh * a.ldc + tcl + (int64_t)a.c * a.C];
+        bf16x8 xk[4], xv[4];
+        load_tok(a.k, xk);
+        load_tok(a.v, xv);
+        f32x4 dk[8], dv[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) dk[n] = dv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float sM = 0.f, sW = 0.f;
+        issue(0, 0, nmat);
+        for (int js = 0; js < nsteps; ++js) {
+            wait_vm0();
+            barrier_lds();
+            if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, nmat);
+            const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
+            const int j0 = US * js;
+            f32x4 pr[NMAT];
+#pragma unroll
+            for (int mi = 0; mi < nmat; ++mi) pr[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int mi = 0; mi < nmat; ++mi) {
+                    const bool vside = (mi == 2 || mi == 5 || mi == 8);
+                    pr[mi] = mfma32(afrag(sb, mi, kk), vside ? xv[kk] : xk[kk], pr[mi]);
+                }
+            }
+            // elementwise: lane holds units j0 + 4g + r of token tl
+            float F1[4], F3[4], nE[4];
+            bf16x4 aF1, aF3, aW1, aW3, aM1, aM3, anE, aW2, aM2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float h1 = pr[0][r], h3 = pr[1][r], du = -pr[2][r];
+                const float sg = fast_sigmoid(h1);
+                const float act = h1 * sg;
+                const float s1 = sg * (1.f + h1 * (1.f - sg));
+                const float s2 = sg * (1.f - sg) * (2.f + h1 * (1.f - 2.f * sg));
+                const float u = act * h3, dh1 = du * h3 * s1, dh3 = du * act;
+                float P1 = -cw * pr[3][r], P3 = -cw * pr[4][r], P2 = -cw * pr[5][r];
+                if (MOM) {
+                    P1 += cm * pr[6][r];
+                    P3 += cm * pr[7][r];
+                    P2 += cm * pr[8][r];
+                }
+                const float E = P1 * h3 * s1 + P3 * act;
+                F1[r] = du * P1 * h3 * s2 + (du * P3 - h3 * P2) * s1;
+                F3[r] = du * P1 * s1 - act * P2;
+                nE[r] = -E;
+                sW -= pr[3][r] * dh1 + pr[4][r] * dh3 - u * pr[5][r];
+                if (MOM) sM += pr[6][r] * dh1 + pr[7][r] * dh3 - u * pr[8][r];
+                aF1[r] = (__bf16)F1[r];
+                aF3[r] = (__bf16)F3[r];
+                anE[r] = (__bf16)nE[r];
+                aW1[r] = (__bf16)(-cw * dh1);
+                aW3[r] = (__bf16)(-cw * dh3);
+                aW2[r] = (__bf16)(cw * u);
+                aM1[r] = (__bf16)(cm * dh1);
+                aM3[r] = (__bf16)(cm * dh3);
+                aM2[r] = (__bf16)(-cm * u);
+            }
+            put_inter(0, j0, F1);
+            put_inter(1, j0, F3);
+            put_inter(2, j0, nE);
+            // token side: contraction over the step's 16 units, the B fragments
+            // of column tile n + 1 read while tile n's MFMAs run
+            bf16x4 bf[NMAT];
+#pragma unroll
+            for (int mi = 0; mi < nmat; ++mi) bf[mi] = tr_units(sb + mi * STEPB, lane, 0);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                bf16x4 cur[NMAT];
+#pragma unroll
+                for (int mi = 0; mi < nmat; ++mi) cur[mi] = bf[mi];
+                if (n + 1 < 8) {
+#pragma unroll
+                    for (int mi = 0; mi < nmat; ++mi) bf[mi] = tr_units(sb + mi * STEPB, lane, n + 1);
+                }
+                dk[n] = mfma16(aF1, cur[0], dk[n]);
+                dk[n] = mfma16(aF3, cur[1], dk[n]);
+                dk[n] = mfma16(aW1, cur[3], dk[n]);
+                dk[n] = mfma16(aW3, cur[4], dk[n]);
+                dv[n] = mfma16(anE, cur[2], dv[n]);
+                dv[n] = mfma16(aW2, cur[5], dv[n]);
+                if (MOM) {
+                    dk[n] = mfma16(aM1, cur[6], dk[n]);
+                    dk[n] = mfma16(aM3, cur[7], dk[n]);
+                    dv[n] = mfma16(aM2, cur[8], dv[n]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        store_tok(a.dk, dk);
+        store_tok(a.dv, dv);
+        sW += __shfl_xor(sW, 16);
+        sW += __shfl_xor(sW, 32);
+        if (MOM) {
+            sM += __shfl_xor(sM, 16);
+            sM += __shfl_xor(sM, 32);
+        }
+        if (g == 0) {
+            const int64_t o = bh * a.ldc + (int64_t)a.c * a.C + tcl;
+            a.dcW[o] = sW;
+            if (MOM) a.dcM[o] = sM;
+        }
+    }
+    barrier_lds();  // every wave is done with the stage buffers
+
+    // ---------------- pass B: output path (needs W_c only)
+    {
+        bf16x8 xq[4], xd[4];
+        load_tok(a.q, xq);
+        load_tok(a.dout, xd);
+        f32x4 dq[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        issue(0, 0, 3);
+        for (int js = 0; js < nsteps; ++js) {
+            wait_vm0();
+            barrier_lds();
+            if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, 3);
+            const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
+            const int j0 = US * js;
+            f32x4 pr[3];
+#pragma unroll
+            for (int mi = 0; mi < 3; ++mi) pr[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                pr[0] = mfma32(afrag(sb, 0, kk), xq[kk], pr[0]);
+                pr[1] = mfma32(afrag(sb, 1, kk), xq[kk], pr[1]);
+                pr[2] = mfma32(afrag(sb, 2, kk), xd[kk], pr[2]);
+            }
+            float d1[4], d3[4], uq[4];
+            bf16x4 a1, a3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float h1 = pr[0][r], h3 = pr[1][r], hdo = pr[2][r];
+                const float sg = fast_sigmoid(h1);
+                const float act = h1 * sg;
+                const float s1 = sg * (1.f + h1 * (1.f - sg));
+                d1[r] = hdo * h3 * s1;
+                d3[r] = hdo * act;
+                uq[r] = act * h3;
+                a1[r] = (__bf16)d1[r];
+                a3[r] = (__bf16)d3[r];
+            }
+            put_inter(3, j0, d1);
+            put_inter(4, j0, d3);
+            put_inter(5, j0, uq);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                dq[n] = mfma16(a1, tr_units(sb + 0 * STEPB, lane, n), dq[n]);
+                dq[n] = mfma16(a3, tr_units(sb + 1 * STEPB, lane, n), dq[n]);
+                if (n & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        store_tok(a.dq, dq);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// weight kernel
+struct WtArgs {
+    const __bf16 *k, *v, *q, *dout;  // [BH][T][D]
+    const __bf16* inter;             // [BH][6][Hd][C]
+    const __bf16 *snapW, *snapM;     // [BH][nc][3][Hd][D]
+    const float* scal;               // [BH][nc][4]: A, Bb, gamma
+    float *lamW, *lamM;              // [BH][3][Hd][D] fp32 state cotangents, hidden-major
+    __bf16* lam;                     // [BH][6][Hd][D] bf16 copies (token kernel operands)
+    float* dpart;                    // [BH][nc][nsl][4]: partial dA, dBb, dgamma
+    float *dW0, *dM0;                // packed [BH][P], written for chunk 0
+    int64_t T;
+    int Hd, C, nc, c, nsl, nsteps;   // nsteps: 32-token steps of chunk c (whole 64-token blocks)
+};
+
+// packed-parameter index of hidden-major element (m, j, d)
+__device__ __forceinline__ int64_t packed_index(int m, int64_t j, int d, int Hd) {
+    return m < 2 ? (int64_t)m * D * Hd + (int64_t)d * Hd + j : 2 * (int64_t)D * Hd + j * D + d;
+}
+
+template <bool MOM>
+__global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char stage[2 * 4 * KTB];
+    __shared__ float red[4][4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / a.nsl;
+    const int sl = blockIdx.x % a.nsl;
+    const int Hd = a.Hd;
+    const int64_t T = a.T;
+    const int64_t P = 3 * (int64_t)D * Hd;
+    const int j0 = WS * sl + 16 * w;  // the wave's 16 hidden units
+    const unsigned xbytes = (unsigned)(T * D * 2);
+    const u32x4 rs[4] = {buffer_rsrc(a.k + bh * T * D, xbytes), buffer_rsrc(a.q + bh * T * D, xbytes),
+                         buffer_rsrc(a.v + bh * T * D, xbytes), buffer_rsrc(a.dout + bh * T * D, xbytes)};
+    const unsigned stage_lds = lds_addr(stage);
+    const int64_t tbase = (int64_t)a.c * a.C;
+    // token rows of step s (32 rows of k, q, v, do) into buffer b: 8 copies
+    // per matrix (4 rows each), spread over the waves
+    auto issue = [&](int s, int b) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int x8 = 0; x8 < 8; ++x8) {
+            const int mat = x8 >> 1, rq = 4 * (x8 & 1) + w;  // (matrix index stays compile-time)
+            const int row = 4 * rq + (ln >> 4);
+            const unsigned off = (unsigned)((tbase + KT * s + row) * D) * 2u + 16u * (unsigned)((ln & 15) ^ swz4(row & 15));
+            copy16(rs[mat], stage_lds + (unsigned)((b * 4 + mat) * KTB + 4 * rq * ROWB), off);
+        }
+    };
+    const __bf16* const inter = a.inter + (bh * NQ * Hd + j0 + p) * (int64_t)a.C + 8 * g;
+    auto afrag = [&](int qi, int s) {
+        return *(const bf16x8*)(inter + (int64_t)qi * Hd * a.C + KT * s);
+    };
+    f32x4 acc[3][8];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    for (int s = 0; s < a.nsteps; ++s) {
+        bf16x8 fa[NQ];
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) fa[qi] = afrag(qi, s);
+        wait_vm0();
+        barrier_lds();
+        if (s + 1 < a.nsteps) issue(s + 1, (s + 1) & 1);
+        const unsigned char* sb = stage + (s & 1) * 4 * KTB;
+        bf16x8 nb4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) nb4[x] = tr_tokens(sb + x * KTB, lane, 0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            const bf16x8 bk = nb4[0], bq = nb4[1], bv = nb4[2], bd = nb4[3];
+            if (n + 1 < 8) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) nb4[x] = tr_tokens(sb + x * KTB, lane, n + 1);
+            }
+            acc[0][n] = mfma32(fa[0], bk, acc[0][n]);
+            acc[0][n] = mfma32(fa[3], bq, acc[0][n]);
+            acc[1][n] = mfma32(fa[1], bk, acc[1][n]);
+            acc[1][n] = mfma32(fa[4], bq, acc[1][n]);
+            acc[2][n] = mfma32(fa[2], bv, acc[2][n]);
+            acc[2][n] = mfma32(fa[5], bd, acc[2][n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // state cotangents: lane holds units j0 + 4g + r, d = 16 n + p
+    const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + a.c) * 4);
+    const float A = sc[0], Bb = sc[1], gam = sc[2];
+    const __bf16* snw = a.snapW + (bh * a.nc + a.c) * P;
+    const __bf16* snm = MOM ? a.snapM + (bh * a.nc + a.c) * P : nullptr;
+    float sA = 0.f, sB = 0.f, sG = 0.f;
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t j = j0 + 4 * g + r;
+                const int d = 16 * n + p;
+                const int64_t hm = ((int64_t)m * Hd + j) * D + d;  // hidden-major index within a head
+                const float lw = a.lamW[bh * P + hm];
+                sA += lw * (float)snw[hm];
+                const float nw = A * lw + acc[m][n][r];
+                float nm = 0.f;
+                if (MOM) {
+                    const float lm = a.lamM[bh * P + hm];
+                    const float mc = (float)snm[hm];
+                    sB += lm * mc;
+                    sG -= lw * mc;
+                    nm = Bb * lm - gam * lw;
+                }
+                if (a.c > 0) {
+                    a.lamW[bh * P + hm] = nw;
+                    a.lam[bh * 2 * P + hm] = (__bf16)nw;
+                    if (MOM) {
+                        a.lamM[bh * P + hm] = nm;
+                        a.lam[bh * 2 * P + P + hm] = (__bf16)nm;
+                    }
+                } else {
+                    const int64_t pi = packed_index(m, j, d, Hd);
+                    a.dW0[bh * P + pi] = nw;
+                    if (MOM) a.dM0[bh * P + pi] = nm;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        sA += __shfl_xor(sA, o);
+        sB += __shfl_xor(sB, o);
+        sG += __shfl_xor(sG, o);
+    }
+    if (lane == 0) {
+        red[w][0] = sA;
+        red[w][1] = sB;
+        red[w][2] = sG;
+    }
+    __syncthreads();
+    if (tid < 3) {
+        const float v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+        a.dpart[((bh * a.nc + a.c) * a.nsl + sl) * 4 + tid] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// initial state cotangents: dW_end, dM_end (packed) -> hidden-major fp32 + bf16
+struct InitArgs {
+    const float *dW, *dM;
+    float *lamW, *lamM;
+    __bf16* lam;
+    int Hd, nsl;
+};
+
+template <bool MOM>
+__global__ void __launch_bounds__(NT) bwd_init_kernel(InitArgs a) {
+    const int64_t bh = blockIdx.x / a.nsl;
+    const int sl = blockIdx.x % a.nsl;
+    const int Hd = a.Hd;
+    const int64_t P = 3 * (int64_t)D * Hd;
+    for (int e = threadIdx.x; e < 3 * WS * D; e += NT) {
+        const int m = e / (WS * D);
+        const int64_t j = (int64_t)WS * sl + (e / D) % WS;
+        const int d = e % D;
+        const int64_t hm = ((int64_t)m * Hd + j) * D + d;
+        const int64_t pi = packed_index(m, j, d, Hd);
+        const float lw = a.dW[bh * P + pi];
+        a.lamW[bh * P + hm] = lw;
+        a.lam[bh * 2 * P + hm] = (__bf16)lw;
+        if (MOM) {
+            const float lm = a.dM[bh * P + pi];
+            a.lamM[bh * P + hm] = lm;
+            a.lam[bh * 2 * P + P + hm] = (__bf16)lm;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scalar kernels' backward, one workgroup (one wavefront) per (b, h, chunk).
+// With a_i = prod_{s>i} alpha_s, m_i = prod_{s>i} beta_s and
+// w_i = a_i + beta_{i+1} w_{i+1} (w_last = 1), A = alpha_0 a_0, Bb = beta_0 m_0,
+// gamma = beta_0 w_0, the adjoints run forward through the chunk:
+//   Wb_0 = dw_0 + beta_0 dgamma,  Mb_0 = dm_0 + beta_0 dBb,  Ab_0 = Wb_0 + alpha_0 dA
+//   Wb_i = dw_i + beta_i Wb_{i-1}, Mb_i = dm_i + beta_i Mb_{i-1}, Ab_i = Wb_i + alpha_i Ab_{i-1}
+//   dalpha_0 = dA a_0,  dbeta_0 = dBb m_0 + dgamma w_0,
+//   dalpha_i = Ab_{i-1} a_i,  dbeta_i = Wb_{i-1} w_i + Mb_{i-1} m_i   (i > 0)
+// with dm_i = eta_i dcM_i, dw_i = eta_i dcW_i and deta_i = m_i dcM_i + w_i dcW_i
+// (chunk average: m_i, w_i replaced by their means mb, wb; then
+// deta_i = mb dcM_i + wb dcW_i and dm_i = sum_t eta_t dcM_t / C for every i).
+struct ScalArgs {
+    const float *eta, *alpha, *beta;  // [BH][T]
+    const float *dcM, *dcW;           // [BH][ldc]
+    const float* dpart;               // [BH][nc][nsl][4]
+    float *deta, *dalpha, *dbeta;     // [BH][T]
+    int64_t T, ldc;
+    int C, nc, nsl, mom, avg;
+};
+
+__global__ void __launch_bounds__(64) bwd_scalar_kernel(ScalArgs a) {
+    extern __shared__ float sh[];
+    const int C = a.C;
+    float* al = sh;
+    float* be = sh + C;
+    float* et = sh + 2 * C;
+    float* gm = sh + 3 * C;  // dcM, then d eta
+    float* gw = sh + 4 * C;  // dcW
+    float* va = sh + 5 * C;  // a_i, then d alpha
+    float* vm = sh + 6 * C;  // m_i, then d beta
+    float* vw = sh + 7 * C;  // w_i
+    const int64_t bh = blockIdx.x / a.nc;
+    const int c = blockIdx.x % a.nc;
+    const int lane = threadIdx.x;
+    const int64_t t0 = (int64_t)c * C;
+    const int Cc = (int)((a.T - t0) < C ? (a.T - t0) : C);
+    const int64_t base = bh * a.T + t0;
+    const int64_t cb = bh * a.ldc + t0;
+    for (int i = lane; i < Cc; i += 64) {
+        al[i] = a.alpha[base + i];
+        be[i] = a.mom ? a.beta[base + i] : 0.f;
+        et[i] = a.eta[base + i];
+        gm[i] = a.mom ? a.dcM[cb + i] : 0.f;
+        gw[i] = a.dcW[cb + i];
+    }
+    __syncthreads();
+    if (lane == 0) {
+        float dA = 0.f, dB = 0.f, dG = 0.f;
+        const float* dp = a.dpart + (bh * a.nc + c) * a.nsl * 4;
+        for (int s = 0; s < a.nsl; ++s) {
+            dA += dp[4 * s];
+            dB += dp[4 * s + 1];
+            dG += dp[4 * s + 2];
+        }
+        float av = 1.f, mv = 1.f, wv = 1.f;
+        float msum = 0.f, wsum = 0.f;
+        for (int i = Cc - 1; i >= 0; --i) {
+            if (i < Cc - 1) {
+                av = al[i + 1] * av;
+                mv = be[i + 1] * mv;
+                wv = av + be[i + 1] * wv;
+            }
+            va[i] = av;
+            vm[i] = mv;
+            vw[i] = wv;
+            msum += mv;
+            wsum += wv;
+        }
+        const float mb = msum / (float)Cc, wb = wsum / (float)Cc;
+        float dmb = 0.f, dwb = 0.f;
+        if (a.avg) {
+            for (int i = 0; i < Cc; ++i) {
+                dmb += et[i] * gm[i];
+                dwb += et[i] * gw[i];
+            }
+            dmb /= (float)Cc;
+            dwb /= (float)Cc;
+        }
+        float Wb = 0.f, Mb = 0.f, Ab = 0.f;
+        for (int i = 0; i < Cc; ++i) {
+            const float dm = a.avg ? dmb : et[i] * gm[i];
+            const float dw = a.avg ? dwb : et[i] * gw[i];
+            const float de = a.avg ? mb * gm[i] + wb * gw[i] : vm[i] * gm[i] + vw[i] * gw[i];
+            float da, db;
+            if (i == 0) {
+                da = dA * va[0];
+                db = dB * vm[0] + dG * vw[0];
+                Wb = dw + be[0] * dG;
+                Mb = dm + be[0] * dB;
+                Ab = Wb + al[0] * dA;
+            } else {
+                da = Ab * va[i];
+                db = Wb * vw[i] + Mb * vm[i];
+                Wb = dw + be[i] * Wb;
+                Mb = dm + be[i] * Mb;
+                Ab = Wb + al[i] * Ab;
+            }
+            gm[i] = de;
+            va[i] = da;
+            vm[i] = db;
+        }
+    }
+    __syncthreads();
+    for (int i = lane; i < Cc; i += 64) {
+        a.deta[base + i] = gm[i];
+        a.dalpha[base + i] = va[i];
+        if (a.mom) a.dbeta[base + i] = vm[i];
+    }
+}
+
+}  // namespace
+
+int64_t swiglu_bwd_inter_elems(const e2ttt_desc& d) { return (int64_t)NQ * d.Hd * d.chunk; }
+
+hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipStream_t s, hipEvent_t ev_loop) {
+    const int64_t BH = d.B * d.H;
+    const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
+    const int Hd = (int)d.Hd, C = (int)d.chunk;
+    const int nc = (int)((d.T + d.chunk - 1) / d.chunk);
+    const int nsl = Hd / WS;
+    {
+        InitArgs ia{b.dW_end, b.dM_end, b.lamW, b.lamM, (__bf16*)b.lam, Hd, nsl};
+        if (mom)
+            hipLaunchKernelGGL(bwd_init_kernel<true>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, ia);
+        else
+            hipLaunchKernelGGL(bwd_init_kernel<false>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, ia);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    for (int c = nc - 1; c >= 0; --c) {
+        const int Cc = (int)((d.T - (int64_t)c * C) < C ? (d.T - (int64_t)c * C) : C);
+        const int nb = (Cc + TB - 1) / TB;
+        TokArgs ta;
+        ta.k = (const __bf16*)b.k;
+        ta.v = (const __bf16*)b.v;
+        ta.q = (const __bf16*)b.q;
+        ta.dout = (const __bf16*)b.dout;
+        ta.cM = b.cM;
+        ta.cW = b.cW;
+        ta.snapW = (const __bf16*)b.snapW;
+        ta.lam = (const __bf16*)b.lam;
+        ta.inter = (__bf16*)b.inter;
+        ta.dq = (__bf16*)b.dq;
+        ta.dk = (__bf16*)b.dk;
+        ta.dv = (__bf16*)b.dv;
+        ta.dcM = b.dcM;
+        ta.dcW = b.dcW;
+        ta.T = d.T;
+        ta.ldc = b.ldc;
+        ta.Hd = Hd;
+        ta.C = C;
+        ta.nc = nc;
+        ta.c = c;
+        ta.nb = nb;
+        if (mom)
+            hipLaunchKernelGGL(bwd_tok_kernel<true>, dim3((unsigned)(BH * nb)), dim3(NT), 0, s, ta);
+        else
+            hipLaunchKernelGGL(bwd_tok_kernel<false>, dim3((unsigned)(BH * nb)), dim3(NT), 0, s, ta);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        WtArgs wa;
+        wa.k = (const __bf16*)b.k;
+        wa.v = (const __bf16*)b.v;
+        wa.q = (const __bf16*)b.q;
+        wa.dout = (const __bf16*)b.dout;
+        wa.inter = (const __bf16*)b.inter;
+        wa.snapW = (const __bf16*)b.snapW;
+        wa.snapM = (const __bf16*)b.snapM;
+        wa.scal = b.scal;
+        wa.lamW = b.lamW;
+        wa.lamM = b.lamM;
+        wa.lam = (__bf16*)b.lam;
+        wa.dpart = b.dpart;
+        wa.dW0 = b.dW0;
+        wa.dM0 = b.dM0;
+        wa.T = d.T;
+        wa.Hd = Hd;
+        wa.C = C;
+        wa.nc = nc;
+        wa.c = c;
+        wa.nsl = nsl;
+        wa.nsteps = nb * (TB / KT);
+        if (mom)
+            hipLaunchKernelGGL(bwd_wt_kernel<true>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, wa);
+        else
+            hipLaunchKernelGGL(bwd_wt_kernel<false>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, wa);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
+    ScalArgs sa;
+    sa.eta = b.eta;
+    sa.alpha = b.alpha;
+    sa.beta = b.beta;
+    sa.dcM = b.dcM;
+    sa.dcW = b.dcW;
+    sa.dpart = b.dpart;
+    sa.deta = b.deta;
+    sa.dalpha = b.dalpha;
+    sa.dbeta = b.dbeta;
+    sa.T = d.T;
+    sa.ldc = b.ldc;
+    sa.C = C;
+    sa.nc = nc;
+    sa.nsl = nsl;
+    sa.mom = mom ? 1 : 0;
+    sa.avg = (d.flags & E2TTT_FLAG_CHUNK_AVG) ? 1 : 0;
+    hipLaunchKernelGGL(bwd_scalar_kernel, dim3((unsigned)(BH * nc)), dim3(64), (size_t)8 * C * sizeof(float), s, sa);
+    return hipGetLastError();
+}
+
+}  // namespace e2ttt

@@ -152,6 +152,7 @@ struct LoopArgs {
     float* W_end;
     float* M_end;
     __bf16* snap;
+    __bf16* snapM;  // bf16 chunk-start momentum snapshots (SAVEM instantiation only)
     int64_t T;
     int64_t ldc;  // row stride of cM / cW (T rounded up to a whole block, zero padded)
     int Hd, C, nc, nsl, nwg, xcd_map;
@@ -194,12 +195,14 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
     }
 }
 
-template <bool MOM>
+template <bool MOM, bool SAVEM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 swiglu_loop_kernel(LoopArgs a) {
     // MOM = false: the recurrence without momentum; the scalar kernels then
     // have beta = 0 (cM unused, gamma = Bb = 0) and the M half of the state,
     // its aggregation MFMAs and its HBM traffic are compiled out.
+    // SAVEM: also write a bf16 snapshot of every chunk's start momentum, in
+    // the layout of the weight snapshot (for the backward pass).
     __shared__ __attribute__((aligned(16))) unsigned char kvs[NBUF * KVBUF];
     __shared__ __attribute__((aligned(16))) unsigned char xch[4 * XW];
     const int tid = threadIdx.x;
@@ -312,6 +315,18 @@ swiglu_loop_kernel(LoopArgs a) {
                     }
                     *(bf16x8*)(xw + (4 * m + kk) * 1024 + xl) = w8;
                     *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
+                    if (SAVEM) {
+                        unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
+                        const bf16x4 s0 = pack4(acc[m][0][2 * kk]), s1 = pack4(acc[m][0][2 * kk + 1]);
+                        const bf16x4 mlo = godd ? s1 : s0, mhi = godd ? s0 : s1;
+                        bf16x8 m8;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            m8[e] = mlo[e];
+                            m8[4 + e] = mhi[e];
+                        }
+                        *(bf16x8*)(snapm + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = m8;
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -539,7 +554,7 @@ swiglu_loop_kernel(LoopArgs a) {
 
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
-                              void* snap, hipStream_t s) {
+                              void* snap, void* snapM, hipStream_t s) {
     const int64_t BH = d.B * d.H;
     LoopArgs la;
     la.k = (const __bf16*)k;
@@ -552,6 +567,7 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.W_end = W_end;
     la.M_end = M_end;
     la.snap = (__bf16*)snap;
+    la.snapM = (__bf16*)snapM;
     la.T = d.T;
     la.Hd = (int)d.Hd;
     la.C = (int)d.chunk;
@@ -561,9 +577,11 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
     if (d.flags & E2TTT_FLAG_NO_MOMENTUM)
-        hipLaunchKernelGGL(swiglu_loop_kernel<false>, dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+        hipLaunchKernelGGL((swiglu_loop_kernel<false, false>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+    else if (snapM)
+        hipLaunchKernelGGL((swiglu_loop_kernel<true, true>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
     else
-        hipLaunchKernelGGL(swiglu_loop_kernel<true>, dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+        hipLaunchKernelGGL((swiglu_loop_kernel<true, false>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
     return hipGetLastError();
 }
 

@@ -171,6 +171,69 @@ E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
 E2TTT_API int e2ttt_logscan(const e2ttt_desc* desc, const float* eta, const float* alpha, const float* beta,
                   float* cM, float* cW, float* scal, void* stream);
 
+/*
+ * Backward pass of the chunk update (the gradients a training step needs).
+ * It is the vector-Jacobian product of e2ttt_chunk_forward: given cotangents
+ * dout, dW_end, dM_end of its outputs, it returns
+ *   dX = d/dX [ <dout, out> + <dW_end, W_end> + <dM_end, M_end> ]
+ * for X in q, k, v, eta, alpha, beta, W0, M0 -- the derivative of the chunk
+ * update that "Rethinking Expressivity and Efficiency in Test-Time Training"
+ * trains with (abstract; atlas summary "Approach").  The forward is
+ * recomputed inside the call (scalar kernels and chunk loop, keeping each
+ * chunk's start state); nothing needs to be saved from the forward call.
+ *
+ * Supported (else E2TTT_ERR_UNSUPPORTED): the SwiGLU MFMA path's shapes
+ * (SWIGLU, LOSS_NEGDOT, BF16 I/O, D == 128, Hd a multiple of 64 up to 4096,
+ * chunk a multiple of 64) with chunk <= 2048 and T*D*2 < 2^31;
+ * E2TTT_FLAG_NO_MOMENTUM and E2TTT_FLAG_CHUNK_AVG are honoured,
+ * E2TTT_FLAG_FORCE_GENERIC is not supported.  A ragged last chunk is allowed.
+ *
+ *   q, k, v, dout        [B][H][T][D] bf16 (dout: cotangent of out)
+ *   eta, alpha, beta     [B][H][T] fp32
+ *   W0, M0               [B][H][P] fp32 (the forward's initial state)
+ *   dW_end, dM_end       [B][H][P] fp32 cotangents of W_end, M_end
+ *   dq, dk, dv           [B][H][T][D] bf16 outputs
+ *   deta, dalpha, dbeta  [B][H][T] fp32 outputs
+ *   dW0, dM0             [B][H][P] fp32 outputs (packed like W0)
+ *   workspace            >= e2ttt_backward_workspace_size(desc) bytes,
+ *                        256-byte aligned; clobbered
+ * Without momentum, beta, M0, dM_end, dbeta and dM0 are not used (may be NULL).
+ * Every output must be disjoint from every other buffer (no in-place form).
+ * T == 0 copies dW_end -> dW0 and dM_end -> dM0; B*H == 0 does nothing.
+ */
+E2TTT_API size_t e2ttt_backward_workspace_size(const e2ttt_desc* desc);
+
+/* Host-only validation of a backward call; ptrs[] holds, in order: q, k, v,
+ * eta, alpha, beta, W0, M0, dout, dW_end, dM_end, dq, dk, dv, deta, dalpha,
+ * dbeta, dW0, dM0.  Same rules as e2ttt_validate (16-byte alignment; eta,
+ * alpha, beta, deta, dalpha, dbeta 4-byte), and no output may overlap any
+ * other tensor (E2TTT_ERR_ALIAS). */
+E2TTT_API int e2ttt_validate_backward(const e2ttt_desc* desc, const void* const ptrs[19]);
+
+E2TTT_API int e2ttt_chunk_backward(const e2ttt_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        const float* eta, const float* alpha, const float* beta,
+                        const float* W0, const float* M0,
+                        const void* dout, const float* dW_end, const float* dM_end,
+                        void* dq, void* dk, void* dv,
+                        float* deta, float* dalpha, float* dbeta,
+                        float* dW0, float* dM0,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* e2ttt_chunk_backward plus timing: `events` (4 hipEvent_t, or NULL) are
+ * recorded before the forward recompute, after it, after the reverse chunk
+ * loop and after the scalar kernels' backward. */
+E2TTT_API int e2ttt_chunk_backward_events(const e2ttt_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        const float* eta, const float* alpha, const float* beta,
+                        const float* W0, const float* M0,
+                        const void* dout, const float* dW_end, const float* dM_end,
+                        void* dq, void* dk, void* dv,
+                        float* deta, float* dalpha, float* dbeta,
+                        float* dW0, float* dM0,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const events[4]);
+
 /* Static, human-readable name of a status code. */
 E2TTT_API const char* e2ttt_status_string(int status);
 

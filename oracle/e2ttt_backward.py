@@ -103,30 +103,35 @@ def _weighted_sum(kind, fac, K, c):
     return {"W1": _T(K) @ (cc * fac["dh1"]), "W3": _T(K) @ (cc * fac["dh3"]), "W2": _T(cc * fac["u"]) @ fac["dy"]}
 
 
+def _excl_mask(C, dtype):
+    """mask[i, s] = 1 where s > i (the tokens after token i)."""
+    idx = torch.arange(C)
+    return (idx[None, :] > idx[:, None]).to(dtype)
+
+
 def _suffix_prod(x):
     """prod_{s>i} x_s for every i (last axis), as plain products."""
     C = x.shape[-1]
-    cols = [torch.prod(x[..., i + 1:], dim=-1) if i + 1 < C else torch.ones_like(x[..., 0]) for i in range(C)]
-    return torch.stack(cols, dim=-1)
+    mk = _excl_mask(C, x.dtype)
+    return torch.prod(mk * x[..., None, :] + (1.0 - mk), dim=-1)
 
 
 def _coefficients(alpha, beta):
     """Momentum kernel m, weight kernel w and A, Bb, gamma of one chunk, each a
-    plain product or sum of products of the gates (atlas summary, "Approach")."""
+    plain product or sum of products of the gates (atlas summary, "Approach"):
+    m_i = prod_{s>i} beta_s, w_i = sum_{tau>=i} prod_{s>tau} alpha_s prod_{i<s<=tau} beta_s,
+    A = prod alpha, Bb = prod beta, gamma = sum_tau prod_{s>tau} alpha_s prod_{s<=tau} beta_s."""
     C = alpha.shape[-1]
     a = _suffix_prod(alpha)
     m = _suffix_prod(beta)
-    w = []
-    for i in range(C):
-        # sum_{tau >= i} prod_{s>tau} alpha_s * prod_{i<s<=tau} beta_s
-        pb = [torch.prod(beta[..., i + 1:tau + 1], dim=-1) if tau > i else torch.ones_like(beta[..., 0])
-              for tau in range(i, C)]
-        w.append(torch.sum(a[..., i:] * torch.stack(pb, dim=-1), dim=-1))
-    w = torch.stack(w, dim=-1)
+    mk = _excl_mask(C, beta.dtype)
+    # bprod[i, tau] = prod_{i<s<=tau} beta_s (1 for tau <= i)
+    bprod = torch.cumprod(mk * beta[..., None, :] + (1.0 - mk), dim=-1)
+    upper = 1.0 - _excl_mask(C, beta.dtype).transpose(0, 1)  # [i, tau] = 1 where tau >= i
+    w = torch.sum(upper * bprod * a[..., None, :], dim=-1)
     A = torch.prod(alpha, dim=-1)
     Bb = torch.prod(beta, dim=-1)
-    pre = torch.stack([torch.prod(beta[..., :tau + 1], dim=-1) for tau in range(C)], dim=-1)
-    gamma = torch.sum(a * pre, dim=-1)
+    gamma = torch.sum(a * torch.cumprod(beta, dim=-1), dim=-1)
     return m, w, A, Bb, gamma
 
 

@@ -144,6 +144,19 @@ def make_inputs(cfg: Config, seed: int = 0, m0_scale: float = 0.0) -> dict:
     return dict(q=q, k=k, v=v, eta=eta, alpha=alpha, beta=beta, W0=W0, M0=M0)
 
 
+def make_cotangents(cfg: Config, seed: int = 1, state_scale: float = 1.0) -> dict:
+    """Seeded cotangents for the backward pass, as CPU tensors: dout
+    [B,H,T,D] ~ N(0, 1) in the I/O dtype (the gradient arriving at the chunk
+    outputs), dW_end and dM_end [B,H,P] ~ state_scale * N(0, 1/D) fp32 (the
+    gradient arriving at the final state; 0 when the final state is unused)."""
+    g = torch.Generator().manual_seed(seed)
+    io = torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
+    dout = torch.randn(cfg.B, cfg.H, cfg.T, cfg.D, generator=g).to(io).contiguous()
+    dW = (state_scale * torch.randn(cfg.B, cfg.H, cfg.P, generator=g) / (cfg.D ** 0.5)).contiguous()
+    dM = (state_scale * torch.randn(cfg.B, cfg.H, cfg.P, generator=g) / (cfg.D ** 0.5)).contiguous()
+    return dict(dout=dout, dW_end=dW, dM_end=dM)
+
+
 def head_slice(inputs: dict, heads: list[tuple[int, int]]) -> dict:
     """Select a list of (b, h) pairs as a new B=1, H=len(heads) input set."""
     out = {}

@@ -29,7 +29,7 @@ def _desc(kind="swiglu", loss="negdot", io="bf16", B=2, H=3, T=256, D=128, Hd=25
 
 def test_exports_every_declared_symbol(lib):
     names = set(re.findall(r"E2TTT_API[^;(]*?\b(e2ttt_\w+)\s*\(", open(HEADER).read()))
-    assert len(names) == 8
+    assert len(names) == 12
     from chunk_weight_rnn_amd import _lib
     assert names == set(_lib.EXPORTS)
     for n in names:
@@ -198,3 +198,56 @@ def test_validate_variant_flags(lib):
     d = _desc(flags=8)
     assert _validate(lib, d, _ptrs(d)) == 1
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+
+
+def _bwd_ptrs(d, momentum=True):
+    # 19 disjoint fake device addresses, 1 GiB apart
+    p = [(1 << 40) + i * (1 << 30) for i in range(19)]
+    if not momentum:
+        for i in (5, 7, 10, 16, 18):  # beta, M0, dM_end, dbeta, dM0
+            p[i] = 0
+    return p
+
+
+def _validate_bwd(lib, d, p):
+    arr = (ctypes.c_void_p * 19)(*[ctypes.c_void_p(x) for x in p])
+    return lib.e2ttt_validate_backward(ctypes.byref(d), arr)
+
+
+def test_backward_validation(lib):
+    d = _desc()
+    assert _validate_bwd(lib, d, _bwd_ptrs(d)) == 0
+    assert lib.e2ttt_backward_workspace_size(ctypes.byref(d)) > 0
+    # ragged tail, no momentum (unused pointers may be null), chunk average
+    d = _desc(T=200)
+    assert _validate_bwd(lib, d, _bwd_ptrs(d)) == 0
+    d = _desc(flags=2)
+    assert _validate_bwd(lib, d, _bwd_ptrs(d, momentum=False)) == 0
+    d = _desc(flags=4)
+    assert _validate_bwd(lib, d, _bwd_ptrs(d)) == 0
+    # shapes outside the SwiGLU MFMA path, the portable-path flag, long chunks
+    for bad in (_desc(kind="linear", loss="mse", io="f32", D=32, Hd=0), _desc(io="f32"), _desc(D=64),
+                _desc(Hd=96), _desc(chunk=96), _desc(chunk=4096, T=8192), _desc(flags=1)):
+        assert _validate_bwd(lib, bad, _bwd_ptrs(bad)) == 2
+    # every output must be disjoint from everything else (no in-place form)
+    d = _desc()
+    for o, i in ((17, 6), (18, 7), (11, 0), (14, 3), (12, 11)):
+        p = _bwd_ptrs(d)
+        p[o] = p[i]
+        assert _validate_bwd(lib, d, p) == 3, (o, i)
+    # null and misaligned pointers
+    p = _bwd_ptrs(d)
+    p[9] = 0
+    assert _validate_bwd(lib, d, p) == 1
+    p = _bwd_ptrs(d)
+    p[12] += 4
+    assert _validate_bwd(lib, d, p) == 1
+    p = _bwd_ptrs(d)
+    p[15] += 4  # dalpha needs 4-byte alignment only
+    assert _validate_bwd(lib, d, p) == 0
+    # the entry point validates before launching, and checks the workspace
+    v = ctypes.c_void_p
+    args = [v(x) for x in _bwd_ptrs(d)]
+    assert lib.e2ttt_chunk_backward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 4
+    bad = _desc(D=64)
+    assert lib.e2ttt_chunk_backward(ctypes.byref(bad), *args, v(0), ctypes.c_size_t(0), v(0)) == 2

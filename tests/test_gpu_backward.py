@@ -1,0 +1,108 @@
+"""GPU parity of the backward pass (e2ttt_chunk_backward through the C ABI)
+against the fp64 backward oracle (autograd of the closed form), gradient by
+gradient: dq, dk, dv, deta, dalpha, dbeta, dW0 (per matrix), dM0 (per matrix).
+
+Error measure as in the forward tests: max|x - r| / max|r| per tensor,
+bound 2e-2 for bf16 I/O (the forward's bound; the backward's operands are the
+same bf16-rounded chunk-start weights and per-token terms).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import err, note
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+SMALL = synth.Config("bwd_small", "swiglu", "negdot", 1, 2, 320, 128, 128, 128, "bf16",
+                     "2.5 chunks of 128 (ragged tail of 64)")
+
+
+def _gpu(cfg, x, c):
+    import chunk_weight_rnn_amd as e2
+    d = {n: t.cuda() for n, t in x.items()}
+    dc = {n: t.cuda() for n, t in c.items()}
+    g = e2.chunk_backward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
+                          dc["dout"], dc["dW_end"], dc["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd,
+                          momentum=cfg.momentum, chunk_avg=cfg.chunk_avg)
+    torch.cuda.synchronize()
+    return {n: (None if t is None else t.float().cpu().numpy()) for n, t in g.items()}
+
+
+def _oracle(cfg, x, c):
+    f = lambda t: t.double().numpy()
+    return oracle.chunk_backward(cfg.kind, cfg.loss, f(x["q"]), f(x["k"]), f(x["v"]), f(x["eta"]), f(x["alpha"]),
+                                 f(x["beta"]), f(x["W0"]), f(x["M0"]), f(c["dout"]), f(c["dW_end"]),
+                                 f(c["dM_end"]), cfg.chunk, cfg.Hd, momentum=cfg.momentum,
+                                 chunk_avg=cfg.chunk_avg)
+
+
+def _compare(cfg, got, ref, tol=TOL):
+    errs = {}
+    for n in ("q", "k", "v", "eta", "alpha", "beta"):
+        if ref[n] is None or not cfg.momentum and n == "beta":
+            assert got[n] is None
+            continue
+        errs["d" + n] = err(got[n], ref[n])
+    for n in ("W0", "M0"):
+        if not cfg.momentum and n == "M0":
+            continue
+        mg = oracle.unpack(cfg.kind, got[n], cfg.D, cfg.Hd)
+        mr = oracle.unpack(cfg.kind, ref[n], cfg.D, cfg.Hd)
+        for m in mg:
+            errs[f"d{n}.{m}"] = err(mg[m], mr[m])
+    note(f"  {cfg.name}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for n, t in got.items():
+        if t is not None:
+            assert np.all(np.isfinite(t)), n
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, f"{cfg.name}: tolerance exceeded: {bad}"
+
+
+@pytest.mark.parametrize("flags,state_scale", [(0, 1.0), (0, 0.0), (2, 1.0), (4, 1.0)],
+                         ids=["momentum", "zero_state_cotangent", "no_momentum", "chunk_avg"])
+def test_backward_small(flags, state_scale):
+    cfg = SMALL.with_(flags=flags, name=f"bwd_small_f{flags}_s{state_scale:g}")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=0, m0_scale=0.5 if cfg.momentum else 0.0)
+    c = synth.make_cotangents(cfg, seed=1, state_scale=state_scale)
+    _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
+@pytest.mark.parametrize("T,chunk", [(64, 64), (256, 64), (200, 128), (512, 256)])
+def test_backward_shapes(T, chunk):
+    cfg = SMALL.with_(T=T, chunk=chunk, Hd=256, name=f"bwd_T{T}_C{chunk}")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=2, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=3)
+    _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
+def test_backward_full_size_sampled_heads():
+    """The 1.3B-shaped workload (B=8, H=16, T=2048, chunk 256) in one call;
+    two (b, h) pairs checked against the oracle."""
+    cfg = synth.CONFIGS["swiglu_1p3b"]
+    note(f"case {cfg.name} backward")
+    x = synth.make_inputs(cfg, seed=0, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=1)
+    got = _gpu(cfg, x, c)
+    heads = [(0, 0), (5, 11)]
+    xs = synth.head_slice(x, heads)
+    cs = synth.head_slice(c, heads)
+    ref = _oracle(cfg.with_(B=1, H=len(heads)), xs, cs)
+    sub = {n: (None if t is None else np.stack([t[b, h] for b, h in heads])[None]) for n, t in got.items()}
+    _compare(cfg.with_(B=1, H=len(heads)), sub, ref)
+
+
+def test_backward_deterministic():
+    cfg = SMALL
+    x = synth.make_inputs(cfg, seed=4, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=5)
+    a = _gpu(cfg, x, c)
+    b = _gpu(cfg, x, c)
+    for n in a:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
