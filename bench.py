@@ -6,7 +6,11 @@ kernels, fast-weight forward/backward at the chunk-start weights, both
 gradient aggregations, state transition and chunk outputs for every chunk of
 every (batch, head)), inputs resident in HBM.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--backward]
+
+With --backward one step is one e2ttt_chunk_backward call instead (forward
+recompute, reverse chunk loop, scalar-kernel backward): the gradients of a
+training step for the same workload.
 """
 from __future__ import annotations
 
@@ -41,6 +45,18 @@ def flops_per_token_head(cfg: synth.Config) -> dict:
         fwd = 4 * D * Hd if cfg.loss == "mse" else 2 * D * Hd
         return {"grad": fwd + 2 * D * Hd, "aggregate": 4 * sets * D * Hd, "apply": 4 * D * Hd}
     return {"grad": 2 * D * D, "aggregate": 2 * sets * D * D, "apply": 2 * D * D}
+
+
+def bwd_flops_per_token_head(cfg: synth.Config) -> dict:
+    """MFMA-able flops per token per head of the backward (SwiGLU path), by kernel:
+    recompute = the forward chunk loop; token = projections of k, v at W_c and
+    the cotangents, dk and dv, and the output path's projections and dq;
+    weight = the chunk's dW contraction over its tokens."""
+    D, Hd = cfg.D, cfg.Hd
+    mom = cfg.momentum
+    token = (9 if mom else 6) * 2 * D * Hd + (6 if mom else 4) * 2 * D * Hd + (3 if mom else 2) * 2 * D * Hd \
+        + 3 * 2 * D * Hd + 2 * 2 * D * Hd
+    return {"recompute": 6 * D * Hd + 6 * (2 if mom else 1) * D * Hd, "token": token, "weight": 12 * D * Hd}
 
 
 def alg_bytes(cfg: synth.Config) -> int:
@@ -86,6 +102,98 @@ def measured_traffic(loop_launch_bytes_alg: float):
         return None
 
 
+def cpu_baseline_backward(cfg: synth.Config, budget_s: float) -> dict:
+    """The fp64 backward oracle (autograd of the closed form) on a bounded
+    sample: single (b, h) heads, cycling over the workload's heads, until
+    about budget_s seconds of host work have been timed."""
+    import torch
+    import oracle
+    cores = torch.get_num_threads()
+    x = synth.make_inputs(cfg, seed=0)
+    c = synth.make_cotangents(cfg, seed=1)
+    f = lambda t: t.double().numpy()
+    n, wall = 0, 0.0
+    while wall < budget_s:
+        b, h = (n // cfg.H) % cfg.B, n % cfg.H
+        xs = synth.head_slice(x, [(b, h)])
+        cs = synth.head_slice(c, [(b, h)])
+        t0 = time.perf_counter()
+        oracle.chunk_backward(cfg.kind, cfg.loss, f(xs["q"]), f(xs["k"]), f(xs["v"]), f(xs["eta"]),
+                              f(xs["alpha"]), f(xs["beta"]), f(xs["W0"]), f(xs["M0"]), f(cs["dout"]),
+                              f(cs["dW_end"]), f(cs["dM_end"]), cfg.chunk, cfg.Hd, momentum=cfg.momentum,
+                              chunk_avg=cfg.chunk_avg)
+        wall += time.perf_counter() - t0
+        n += 1
+    # tokens/s of the whole workload: each sampled head is 1/H of a sequence's work
+    return {"value": n * cfg.T / cfg.H / wall, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} single (b, h) heads x {cfg.T} tokens (one head = 1/{cfg.H} of a sequence), fp64 "
+                      f"torch autograd of the closed form, {wall:.1f} s"}
+
+
+def run_backward(args, cfg, lib, e2, torch) -> dict:
+    """Time e2ttt_chunk_backward on the workload; returns the JSON record."""
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=1).items()}
+    g = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")}
+    desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk,
+                             cfg.flags)
+    ws_bytes = int(lib.e2ttt_backward_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    hev = HipEvents(4 * max(args.steps, 1))
+
+    def step(i=None):
+        evs = None if i is None else (ctypes.c_void_p * 4)(*hev.ev[4 * i:4 * i + 4])
+        st = lib.e2ttt_chunk_backward_events(
+            ctypes.byref(desc), p(x["q"]), p(x["k"]), p(x["v"]), p(x["eta"]), p(x["alpha"]), p(x["beta"]),
+            p(x["W0"]), p(x["M0"]), p(c["dout"]), p(c["dW_end"]), p(c["dM_end"]), p(g["q"]), p(g["k"]),
+            p(g["v"]), p(g["eta"]), p(g["alpha"]), p(g["beta"]), p(g["W0"]), p(g["M0"]), p(ws),
+            ctypes.c_size_t(ws_bytes), hs, evs)
+        if st != 0:
+            raise e2.E2TTTError("e2ttt_chunk_backward_events", st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    st = {"recompute": [], "reverse_loop": [], "scalar": []}
+    for i in range(args.steps):
+        e = hev.ev[4 * i:4 * i + 4]
+        st["recompute"].append(hev.elapsed_ms(e[0], e[1]))
+        st["reverse_loop"].append(hev.elapsed_ms(e[1], e[2]))
+        st["scalar"].append(hev.elapsed_ms(e[2], e[3]))
+    st_ms = {k: sum(v) / len(v) for k, v in st.items()}
+    fpt = bwd_flops_per_token_head(cfg)
+    th = cfg.B * cfg.H * cfg.T
+    loop_flops = (fpt["token"] + fpt["weight"]) * th
+    loop_tflops = loop_flops / (st_ms["reverse_loop"] * 1e-3) / 1e12
+    call_tflops = sum(fpt.values()) * th / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "E2-TTT chunk-update backward (VJP) tokens/sec at 1 GPU + % of MFMA roofline",
+        "value": cfg.B * cfg.T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.notes}, backward", "kind": cfg.kind, "loss": cfg.loss,
+                   "B": cfg.B, "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk,
+                   "io": cfg.io_dtype, "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg},
+        "roofline": {"bound": "mfma", "kernel": "bwd_tok_kernel + bwd_wt_kernel (reverse chunk loop)",
+                     "achieved": loop_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": loop_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "per_launch": f"{fpt['token'] + fpt['weight']} flop/token/head x {th} token-heads = "
+                                   f"{loop_flops:.4g} flop over the reverse loop"},
+        "whole_call": {"tflops": call_tflops, "frac_of_peak": call_tflops / PEAK_BF16_TFLOPS},
+        "stages_ms": st_ms,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_budget)
+    return res
+
+
 def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole batch
     rows (every head of one sequence), cycling over the batch until about
@@ -121,6 +229,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="swiglu_1p3b", choices=list(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MiB",
                     help="first run a plain fp32 copy kernel over MiB of data (3 launches), so that a counter "
@@ -146,6 +255,9 @@ def main() -> int:
         del src, dst
 
     cfg = synth.CONFIGS[args.config]
+    if args.backward:
+        print(json.dumps(run_backward(args, cfg, lib, e2, torch)), flush=True)
+        return 0
     x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
     out = torch.empty_like(x["q"])
     W = torch.empty_like(x["W0"])

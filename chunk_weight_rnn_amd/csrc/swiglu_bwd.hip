@@ -123,6 +123,14 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// Workgroup id -> logical id such that consecutive logical ids (the slices or
+// token blocks of one head, which read the same operands) share an XCD:
+// hardware ids go round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_remap(int nwg, int on) {
+    const int b = blockIdx.x;
+    return on ? (b % 8) * (nwg / 8) + b / 8 : b;
+}
+
 // B fragment of a 16x16x16 MFMA from a hidden-major [16 units][D] stage
 // (swizzled rows): lane (p, g) gets rows 4g + e (e = 0..3), column d0 + p,
 // by the transpose read (lane p's result slot e comes from the 8 bytes that
@@ -164,6 +172,7 @@ struct TokArgs {
     float *dcM, *dcW;                // [BH][ldc]
     int64_t T, ldc;
     int Hd, C, nc, c, nb;            // nb: 64-token blocks of chunk c
+    int nwg, xcd_map;
 };
 
 template <bool MOM>
@@ -173,8 +182,9 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tl = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x / a.nb;
-    const int blk = blockIdx.x % a.nb;
+    const int lid = xcd_remap(a.nwg, a.xcd_map);
+    const int64_t bh = lid / a.nb;
+    const int blk = lid % a.nb;
     const int64_t T = a.T;
     const int Hd = a.Hd;
     const int64_t P = 3 * (int64_t)D * Hd;
@@ -397,18 +407,14 @@ struct WtArgs {
     const __bf16* inter;             // [BH][6][Hd][C]
     const __bf16 *snapW, *snapM;     // [BH][nc][3][Hd][D]
     const float* scal;               // [BH][nc][4]: A, Bb, gamma
-    float *lamW, *lamM;              // [BH][3][Hd][D] fp32 state cotangents, hidden-major
+    const float *linW, *linM;        // [BH][P] packed state cotangents of chunk c's end
+    float *loutW, *loutM;            // [BH][P] packed state cotangents of chunk c's start (may equal lin)
     __bf16* lam;                     // [BH][6][Hd][D] bf16 copies (token kernel operands)
     float* dpart;                    // [BH][nc][nsl][4]: partial dA, dBb, dgamma
-    float *dW0, *dM0;                // packed [BH][P], written for chunk 0
     int64_t T;
     int Hd, C, nc, c, nsl, nsteps;   // nsteps: 32-token steps of chunk c (whole 64-token blocks)
+    int nwg, xcd_map;
 };
-
-// packed-parameter index of hidden-major element (m, j, d)
-__device__ __forceinline__ int64_t packed_index(int m, int64_t j, int d, int Hd) {
-    return m < 2 ? (int64_t)m * D * Hd + (int64_t)d * Hd + j : 2 * (int64_t)D * Hd + j * D + d;
-}
 
 template <bool MOM>
 __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
@@ -418,8 +424,9 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int p = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x / a.nsl;
-    const int sl = blockIdx.x % a.nsl;
+    const int lid = xcd_remap(a.nwg, a.xcd_map);
+    const int64_t bh = lid / a.nsl;
+    const int sl = lid % a.nsl;
     const int Hd = a.Hd;
     const int64_t T = a.T;
     const int64_t P = 3 * (int64_t)D * Hd;
@@ -442,9 +449,12 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
             copy16(rs[mat], stage_lds + (unsigned)((b * 4 + mat) * KTB + 4 * rq * ROWB), off);
         }
     };
+    // A fragments: rows j0 + p of the six per-(token, unit) terms, tokens
+    // 32 s + 8 g .. +7
     const __bf16* const inter = a.inter + (bh * NQ * Hd + j0 + p) * (int64_t)a.C + 8 * g;
-    auto afrag = [&](int qi, int s) {
-        return *(const bf16x8*)(inter + (int64_t)qi * Hd * a.C + KT * s);
+    auto load_frags = [&](int s, bf16x8 (&f)[NQ]) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) f[qi] = *(const bf16x8*)(inter + (int64_t)qi * Hd * a.C + KT * s);
     };
     f32x4 acc[3][8];
 #pragma unroll
@@ -452,14 +462,17 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    bf16x8 fa[NQ];
+    load_frags(0, fa);
     issue(0, 0);
     for (int s = 0; s < a.nsteps; ++s) {
-        bf16x8 fa[NQ];
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) fa[qi] = afrag(qi, s);
         wait_vm0();
         barrier_lds();
-        if (s + 1 < a.nsteps) issue(s + 1, (s + 1) & 1);
+        bf16x8 fn[NQ];
+        if (s + 1 < a.nsteps) {
+            issue(s + 1, (s + 1) & 1);
+            load_frags(s + 1, fn);
+        }
         const unsigned char* sb = stage + (s & 1) * 4 * KTB;
         bf16x8 nb4[4];
 #pragma unroll
@@ -479,45 +492,84 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
             acc[2][n] = mfma32(fa[5], bd, acc[2][n]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (s + 1 < a.nsteps) {
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) fa[qi] = fn[qi];
+        }
     }
 
-    // state cotangents: lane holds units j0 + 4g + r, d = 16 n + p
+    // state cotangents: lane holds units j0 + 4g + r, d = 16 n + p.  Packed
+    // W1 / W3 [D][Hd] put units r = 0..3 side by side (one 16-byte access);
+    // W2 [Hd][D] and the hidden-major snapshots / copies take one row each.
     const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + a.c) * 4);
     const float A = sc[0], Bb = sc[1], gam = sc[2];
-    const __bf16* snw = a.snapW + (bh * a.nc + a.c) * P;
-    const __bf16* snm = MOM ? a.snapM + (bh * a.nc + a.c) * P : nullptr;
+    // uniform bases + 32-bit unsigned byte offsets (scalar-base addressing)
+    const char* linW = (const char*)(a.linW + bh * P);
+    const char* linM = MOM ? (const char*)(a.linM + bh * P) : nullptr;
+    char* loutW = (char*)(a.loutW + bh * P);
+    char* loutM = MOM ? (char*)(a.loutM + bh * P) : nullptr;
+    const char* snw = (const char*)(a.snapW + (bh * a.nc + a.c) * P);
+    const char* snm = MOM ? (const char*)(a.snapM + (bh * a.nc + a.c) * P) : nullptr;
+    char* lamW = (char*)(a.lam + bh * 2 * P);
+    char* lamM = (char*)(a.lam + bh * 2 * P + P);
+    const bool copies = a.c > 0;  // chunk 0's cotangents are final: no token kernel reads them
     float sA = 0.f, sB = 0.f, sG = 0.f;
+    // The accumulators go through this wave's part of the (now idle) stage
+    // buffer one matrix at a time, so that the epilogue holds one tile in
+    // registers instead of all 24.
+    __syncthreads();
+    f32x4* park = (f32x4*)(stage + w * 8 * 64 * 16) + lane;
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
 #pragma unroll
+        for (int n = 0; n < 8; ++n) park[64 * n] = acc[m][n];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
         for (int n = 0; n < 8; ++n) {
+            const f32x4 an = park[64 * n];
+            unsigned jb = (unsigned)(j0 + 4 * g), d = (unsigned)(16 * n + p);
+            asm volatile("" : "+v"(jb), "+v"(d));  // offsets recomputed here, not kept live
+            const unsigned hm0 = ((unsigned)m * Hd + jb) * D + d;  // hidden-major index of r = 0
+            const unsigned pk = m < 2 ? (unsigned)m * D * Hd + d * Hd + jb : 2u * D * Hd + jb * D + d;
+            f32x4 lw, lm = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (m < 2) {
+                lw = *(const f32x4*)(linW + 4u * pk);
+                if (MOM) lm = *(const f32x4*)(linM + 4u * pk);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lw[r] = *(const float*)(linW + 4u * (pk + r * D));
+                    if (MOM) lm[r] = *(const float*)(linM + 4u * (pk + r * D));
+                }
+            }
+            f32x4 nw, nm;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t j = j0 + 4 * g + r;
-                const int d = 16 * n + p;
-                const int64_t hm = ((int64_t)m * Hd + j) * D + d;  // hidden-major index within a head
-                const float lw = a.lamW[bh * P + hm];
-                sA += lw * (float)snw[hm];
-                const float nw = A * lw + acc[m][n][r];
-                float nm = 0.f;
+                const float wc = (float)*(const __bf16*)(snw + 2u * (hm0 + r * D));
+                sA += lw[r] * wc;
+                nw[r] = A * lw[r] + an[r];
                 if (MOM) {
-                    const float lm = a.lamM[bh * P + hm];
-                    const float mc = (float)snm[hm];
-                    sB += lm * mc;
-                    sG -= lw * mc;
-                    nm = Bb * lm - gam * lw;
+                    const float mc = (float)*(const __bf16*)(snm + 2u * (hm0 + r * D));
+                    sB += lm[r] * mc;
+                    sG -= lw[r] * mc;
+                    nm[r] = Bb * lm[r] - gam * lw[r];
                 }
-                if (a.c > 0) {
-                    a.lamW[bh * P + hm] = nw;
-                    a.lam[bh * 2 * P + hm] = (__bf16)nw;
-                    if (MOM) {
-                        a.lamM[bh * P + hm] = nm;
-                        a.lam[bh * 2 * P + P + hm] = (__bf16)nm;
-                    }
-                } else {
-                    const int64_t pi = packed_index(m, j, d, Hd);
-                    a.dW0[bh * P + pi] = nw;
-                    if (MOM) a.dM0[bh * P + pi] = nm;
+            }
+            if (m < 2) {
+                *(f32x4*)(loutW + 4u * pk) = nw;
+                if (MOM) *(f32x4*)(loutM + 4u * pk) = nm;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    *(float*)(loutW + 4u * (pk + r * D)) = nw[r];
+                    if (MOM) *(float*)(loutM + 4u * (pk + r * D)) = nm[r];
+                }
+            }
+            if (copies) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    *(__bf16*)(lamW + 2u * (hm0 + r * D)) = (__bf16)nw[r];
+                    if (MOM) *(__bf16*)(lamM + 2u * (hm0 + r * D)) = (__bf16)nm[r];
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -542,34 +594,40 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// initial state cotangents: dW_end, dM_end (packed) -> hidden-major fp32 + bf16
+// bf16 hidden-major copies of the initial state cotangents dW_end, dM_end
+// (packed): W1 / W3 [D][Hd] are transposed through LDS 64 units at a time, W2
+// [Hd][D] is already hidden-major.
 struct InitArgs {
     const float *dW, *dM;
-    float *lamW, *lamM;
     __bf16* lam;
-    int Hd, nsl;
+    int Hd, nsl, nx;  // nx: 2 with momentum (W and M), else 1
 };
 
-template <bool MOM>
 __global__ void __launch_bounds__(NT) bwd_init_kernel(InitArgs a) {
-    const int64_t bh = blockIdx.x / a.nsl;
+    __shared__ float tile[D][WS + 1];
+    const int64_t bh = blockIdx.x / (a.nx * a.nsl);
+    const int x = (blockIdx.x / a.nsl) % a.nx;  // 0: W, 1: M
     const int sl = blockIdx.x % a.nsl;
     const int Hd = a.Hd;
     const int64_t P = 3 * (int64_t)D * Hd;
-    for (int e = threadIdx.x; e < 3 * WS * D; e += NT) {
-        const int m = e / (WS * D);
-        const int64_t j = (int64_t)WS * sl + (e / D) % WS;
-        const int d = e % D;
-        const int64_t hm = ((int64_t)m * Hd + j) * D + d;
-        const int64_t pi = packed_index(m, j, d, Hd);
-        const float lw = a.dW[bh * P + pi];
-        a.lamW[bh * P + hm] = lw;
-        a.lam[bh * 2 * P + hm] = (__bf16)lw;
-        if (MOM) {
-            const float lm = a.dM[bh * P + pi];
-            a.lamM[bh * P + hm] = lm;
-            a.lam[bh * 2 * P + P + hm] = (__bf16)lm;
+    const float* src = (x ? a.dM : a.dW) + bh * P;
+    __bf16* dst = a.lam + bh * 2 * P + x * P;
+    const int j0 = WS * sl;
+    for (int m = 0; m < 2; ++m) {
+        for (int e = threadIdx.x; e < D * WS; e += NT) {
+            const int d = e / WS, jj = e % WS;
+            tile[d][jj] = src[(int64_t)m * D * Hd + (int64_t)d * Hd + j0 + jj];
         }
+        __syncthreads();
+        for (int e = threadIdx.x; e < WS * D; e += NT) {
+            const int jj = e / D, d = e % D;
+            dst[((int64_t)m * Hd + j0 + jj) * D + d] = (__bf16)tile[d][jj];
+        }
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < WS * D; e += NT) {
+        const int64_t o = 2 * (int64_t)D * Hd + (int64_t)j0 * D + e;
+        dst[o] = (__bf16)src[o];
     }
 }
 
@@ -577,14 +635,17 @@ __global__ void __launch_bounds__(NT) bwd_init_kernel(InitArgs a) {
 // scalar kernels' backward, one workgroup (one wavefront) per (b, h, chunk).
 // With a_i = prod_{s>i} alpha_s, m_i = prod_{s>i} beta_s and
 // w_i = a_i + beta_{i+1} w_{i+1} (w_last = 1), A = alpha_0 a_0, Bb = beta_0 m_0,
-// gamma = beta_0 w_0, the adjoints run forward through the chunk:
-//   Wb_0 = dw_0 + beta_0 dgamma,  Mb_0 = dm_0 + beta_0 dBb,  Ab_0 = Wb_0 + alpha_0 dA
-//   Wb_i = dw_i + beta_i Wb_{i-1}, Mb_i = dm_i + beta_i Mb_{i-1}, Ab_i = Wb_i + alpha_i Ab_{i-1}
-//   dalpha_0 = dA a_0,  dbeta_0 = dBb m_0 + dgamma w_0,
-//   dalpha_i = Ab_{i-1} a_i,  dbeta_i = Wb_{i-1} w_i + Mb_{i-1} m_i   (i > 0)
+// gamma = beta_0 w_0, the adjoints run forward through the chunk from
+// Wb_{-1} = dgamma, Mb_{-1} = dBb, Ab_{-1} = dA:
+//   Wb_i = dw_i + beta_i Wb_{i-1},  Mb_i = dm_i + beta_i Mb_{i-1},  Ab_i = Wb_i + alpha_i Ab_{i-1},
+//   dalpha_i = Ab_{i-1} a_i,  dbeta_i = Wb_{i-1} w_i + Mb_{i-1} m_i,
 // with dm_i = eta_i dcM_i, dw_i = eta_i dcW_i and deta_i = m_i dcM_i + w_i dcW_i
 // (chunk average: m_i, w_i replaced by their means mb, wb; then
 // deta_i = mb dcM_i + wb dcW_i and dm_i = sum_t eta_t dcM_t / C for every i).
+// Every recurrence is affine, x_i = u_i + v_i x_{i-1} (or its mirror image for
+// the suffix quantities): each lane folds its segment of consecutive tokens
+// into one map, a log-step shuffle scan composes the maps across the wave,
+// and each lane then replays its segment from its incoming value.
 struct ScalArgs {
     const float *eta, *alpha, *beta;  // [BH][T]
     const float *dcM, *dcW;           // [BH][ldc]
@@ -593,6 +654,35 @@ struct ScalArgs {
     int64_t T, ldc;
     int C, nc, nsl, mom, avg;
 };
+
+// composition of affine maps x -> u + v x: (u, v) after (u', v')
+__device__ __forceinline__ void compose(float& u, float& v, float u2, float v2) {
+    u = u + v * u2;
+    v = v * v2;
+}
+
+// inclusive scan of maps over lanes: from the right (lane l gets
+// f_l o f_{l+1} o ... o f_63) or from the left (f_l o ... o f_0)
+template <bool RIGHT>
+__device__ __forceinline__ void scan_maps(float& u, float& v, int lane) {
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        float u2 = RIGHT ? __shfl_down(u, k) : __shfl_up(u, k);
+        float v2 = RIGHT ? __shfl_down(v, k) : __shfl_up(v, k);
+        const bool in = RIGHT ? lane + k < 64 : lane >= k;
+        if (!in) {
+            u2 = 0.f;
+            v2 = 1.f;
+        }
+        compose(u, v, u2, v2);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
 
 __global__ void __launch_bounds__(64) bwd_scalar_kernel(ScalArgs a) {
     extern __shared__ float sh[];
@@ -620,61 +710,119 @@ __global__ void __launch_bounds__(64) bwd_scalar_kernel(ScalArgs a) {
         gw[i] = a.dcW[cb + i];
     }
     __syncthreads();
-    if (lane == 0) {
-        float dA = 0.f, dB = 0.f, dG = 0.f;
-        const float* dp = a.dpart + (bh * a.nc + c) * a.nsl * 4;
-        for (int s = 0; s < a.nsl; ++s) {
-            dA += dp[4 * s];
-            dB += dp[4 * s + 1];
-            dG += dp[4 * s + 2];
+    float dA = 0.f, dB = 0.f, dG = 0.f;
+    const float* dp = a.dpart + (bh * a.nc + c) * a.nsl * 4;
+    for (int s = 0; s < a.nsl; ++s) {
+        dA += dp[4 * s];
+        dB += dp[4 * s + 1];
+        dG += dp[4 * s + 2];
+    }
+    const int L = (Cc + 63) / 64;  // tokens per lane
+    const int i0 = lane * L < Cc ? lane * L : Cc;
+    const int i1 = i0 + L < Cc ? i0 + L : Cc;
+    auto bnext = [&](int i) { return i + 1 < Cc ? be[i + 1] : 0.f; };
+
+    // a_i, m_i: suffix products (segment products scanned from the right)
+    float pa = 1.f, pb = 1.f;
+    for (int i = i0; i < i1; ++i) {
+        pa *= al[i];
+        pb *= be[i];
+    }
+    {
+        float u = 0.f, v = pa, u2 = 0.f, v2 = pb;  // products as maps x -> v x
+        scan_maps<true>(u, v, lane);
+        scan_maps<true>(u2, v2, lane);
+        float ra = __shfl_down(v, 1), rm = __shfl_down(v2, 1);
+        if (lane == 63) ra = rm = 1.f;
+        for (int i = i1 - 1; i >= i0; --i) {
+            va[i] = ra;
+            vm[i] = rm;
+            ra *= al[i];
+            rm *= be[i];
         }
-        float av = 1.f, mv = 1.f, wv = 1.f;
-        float msum = 0.f, wsum = 0.f;
-        for (int i = Cc - 1; i >= 0; --i) {
-            if (i < Cc - 1) {
-                av = al[i + 1] * av;
-                mv = be[i + 1] * mv;
-                wv = av + be[i + 1] * wv;
-            }
-            va[i] = av;
-            vm[i] = mv;
+    }
+    // w_i = a_i + beta_{i+1} w_{i+1}: the segment as w_{i0} = X + Y w_{i1}
+    {
+        float X = 0.f, Y = 1.f;
+        for (int i = i1 - 1; i >= i0; --i) {
+            const float bn = bnext(i);
+            X = va[i] + bn * X;
+            Y = bn * Y;
+        }
+        scan_maps<true>(X, Y, lane);
+        float wv = __shfl_down(X, 1);  // w of the next segment's first token (maps applied to 0)
+        if (lane == 63) wv = 0.f;
+        for (int i = i1 - 1; i >= i0; --i) {
+            wv = va[i] + bnext(i) * wv;
             vw[i] = wv;
-            msum += mv;
-            wsum += wv;
         }
-        const float mb = msum / (float)Cc, wb = wsum / (float)Cc;
-        float dmb = 0.f, dwb = 0.f;
-        if (a.avg) {
-            for (int i = 0; i < Cc; ++i) {
-                dmb += et[i] * gm[i];
-                dwb += et[i] * gw[i];
-            }
-            dmb /= (float)Cc;
-            dwb /= (float)Cc;
+    }
+    float mb = 0.f, wb = 0.f, dmb = 0.f, dwb = 0.f;
+    if (a.avg) {
+        float sm = 0.f, sw = 0.f, sdm = 0.f, sdw = 0.f;
+        for (int i = i0; i < i1; ++i) {
+            sm += vm[i];
+            sw += vw[i];
+            sdm += et[i] * gm[i];
+            sdw += et[i] * gw[i];
         }
-        float Wb = 0.f, Mb = 0.f, Ab = 0.f;
-        for (int i = 0; i < Cc; ++i) {
-            const float dm = a.avg ? dmb : et[i] * gm[i];
-            const float dw = a.avg ? dwb : et[i] * gw[i];
-            const float de = a.avg ? mb * gm[i] + wb * gw[i] : vm[i] * gm[i] + vw[i] * gw[i];
-            float da, db;
-            if (i == 0) {
-                da = dA * va[0];
-                db = dB * vm[0] + dG * vw[0];
-                Wb = dw + be[0] * dG;
-                Mb = dm + be[0] * dB;
-                Ab = Wb + al[0] * dA;
-            } else {
-                da = Ab * va[i];
-                db = Wb * vw[i] + Mb * vm[i];
-                Wb = dw + be[i] * Wb;
-                Mb = dm + be[i] * Mb;
-                Ab = Wb + al[i] * Ab;
-            }
-            gm[i] = de;
-            va[i] = da;
-            vm[i] = db;
+        const float inv = 1.f / (float)Cc;
+        mb = wave_sum(sm) * inv;
+        wb = wave_sum(sw) * inv;
+        dmb = wave_sum(sdm) * inv;
+        dwb = wave_sum(sdw) * inv;
+    }
+    auto dm_of = [&](int i) { return a.avg ? dmb : et[i] * gm[i]; };
+    auto dw_of = [&](int i) { return a.avg ? dwb : et[i] * gw[i]; };
+
+    // Wb, Mb: segment maps from the left, applied to dgamma / dBb
+    float Wi, Mi;  // Wb_{i0-1}, Mb_{i0-1}
+    {
+        float uw = 0.f, vwm = 1.f, um = 0.f, vmm = 1.f;
+        for (int i = i0; i < i1; ++i) {
+            uw = dw_of(i) + be[i] * uw;
+            vwm = be[i] * vwm;
+            um = dm_of(i) + be[i] * um;
+            vmm = be[i] * vmm;
         }
+        scan_maps<false>(uw, vwm, lane);
+        scan_maps<false>(um, vmm, lane);
+        float ue = __shfl_up(uw, 1), ve = __shfl_up(vwm, 1), ume = __shfl_up(um, 1), vme = __shfl_up(vmm, 1);
+        if (lane == 0) {
+            ue = ume = 0.f;
+            ve = vme = 1.f;
+        }
+        Wi = ue + ve * dG;
+        Mi = ume + vme * dB;
+    }
+    // Ab: Ab_i = Wb_i + alpha_i Ab_{i-1}, from dA
+    float Ai;  // Ab_{i0-1}
+    {
+        float ua = 0.f, vaa = 1.f, wbv = Wi;
+        for (int i = i0; i < i1; ++i) {
+            wbv = dw_of(i) + be[i] * wbv;
+            ua = wbv + al[i] * ua;
+            vaa = al[i] * vaa;
+        }
+        scan_maps<false>(ua, vaa, lane);
+        float ue = __shfl_up(ua, 1), ve = __shfl_up(vaa, 1);
+        if (lane == 0) {
+            ue = 0.f;
+            ve = 1.f;
+        }
+        Ai = ue + ve * dA;
+    }
+    // replay: gradients of every token of the segment
+    for (int i = i0; i < i1; ++i) {
+        const float de = a.avg ? mb * gm[i] + wb * gw[i] : vm[i] * gm[i] + vw[i] * gw[i];
+        const float da = Ai * va[i];
+        const float db = Wi * vw[i] + Mi * vm[i];
+        Wi = dw_of(i) + be[i] * Wi;
+        Mi = dm_of(i) + be[i] * Mi;
+        Ai = Wi + al[i] * Ai;
+        gm[i] = de;
+        va[i] = da;
+        vm[i] = db;
     }
     __syncthreads();
     for (int i = lane; i < Cc; i += 64) {
@@ -694,12 +842,10 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
     const int Hd = (int)d.Hd, C = (int)d.chunk;
     const int nc = (int)((d.T + d.chunk - 1) / d.chunk);
     const int nsl = Hd / WS;
-    {
-        InitArgs ia{b.dW_end, b.dM_end, b.lamW, b.lamM, (__bf16*)b.lam, Hd, nsl};
-        if (mom)
-            hipLaunchKernelGGL(bwd_init_kernel<true>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, ia);
-        else
-            hipLaunchKernelGGL(bwd_init_kernel<false>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, ia);
+    {  // the last chunk's token kernel reads bf16 copies of dW_end, dM_end
+        const int nx = mom ? 2 : 1;
+        InitArgs ia{b.dW_end, b.dM_end, (__bf16*)b.lam, Hd, nsl, nx};
+        hipLaunchKernelGGL(bwd_init_kernel, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, ia);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     for (int c = nc - 1; c >= 0; --c) {
@@ -727,10 +873,12 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         ta.nc = nc;
         ta.c = c;
         ta.nb = nb;
+        ta.nwg = (int)(BH * nb);
+        ta.xcd_map = ta.nwg % 8 == 0 ? 1 : 0;
         if (mom)
-            hipLaunchKernelGGL(bwd_tok_kernel<true>, dim3((unsigned)(BH * nb)), dim3(NT), 0, s, ta);
+            hipLaunchKernelGGL(bwd_tok_kernel<true>, dim3((unsigned)ta.nwg), dim3(NT), 0, s, ta);
         else
-            hipLaunchKernelGGL(bwd_tok_kernel<false>, dim3((unsigned)(BH * nb)), dim3(NT), 0, s, ta);
+            hipLaunchKernelGGL(bwd_tok_kernel<false>, dim3((unsigned)ta.nwg), dim3(NT), 0, s, ta);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         WtArgs wa;
         wa.k = (const __bf16*)b.k;
@@ -741,12 +889,14 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         wa.snapW = (const __bf16*)b.snapW;
         wa.snapM = (const __bf16*)b.snapM;
         wa.scal = b.scal;
-        wa.lamW = b.lamW;
-        wa.lamM = b.lamM;
+        // state cotangents, packed: read from dW_end at the last chunk, written
+        // to dW0 at the first, in place in the workspace in between
+        wa.linW = c == nc - 1 ? b.dW_end : b.lamW;
+        wa.linM = c == nc - 1 ? b.dM_end : b.lamM;
+        wa.loutW = c == 0 ? b.dW0 : b.lamW;
+        wa.loutM = c == 0 ? b.dM0 : b.lamM;
         wa.lam = (__bf16*)b.lam;
         wa.dpart = b.dpart;
-        wa.dW0 = b.dW0;
-        wa.dM0 = b.dM0;
         wa.T = d.T;
         wa.Hd = Hd;
         wa.C = C;
@@ -754,10 +904,12 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         wa.c = c;
         wa.nsl = nsl;
         wa.nsteps = nb * (TB / KT);
+        wa.nwg = (int)(BH * nsl);
+        wa.xcd_map = wa.nwg % 8 == 0 ? 1 : 0;
         if (mom)
-            hipLaunchKernelGGL(bwd_wt_kernel<true>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, wa);
+            hipLaunchKernelGGL(bwd_wt_kernel<true>, dim3((unsigned)wa.nwg), dim3(NT), 0, s, wa);
         else
-            hipLaunchKernelGGL(bwd_wt_kernel<false>, dim3((unsigned)(BH * nsl)), dim3(NT), 0, s, wa);
+            hipLaunchKernelGGL(bwd_wt_kernel<false>, dim3((unsigned)wa.nwg), dim3(NT), 0, s, wa);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
