@@ -112,6 +112,17 @@ __device__ __forceinline__ void copy16(u32x4 rsrc, unsigned lds, unsigned voff) 
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Wait for a step's stage copies but not for the kStoresAfterCopy global
+// stores each wave issues after them in the previous step (vector memory
+// operations complete in issue order, so vmcnt(k) leaves the last k pending).
+constexpr int kStoresAfterCopy = 12;  // three put_inter calls of four stores
+__device__ __forceinline__ void wait_stage(int step) {
+    if (step == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kStoresAfterCopy);  // vmcnt(12)
+}
+
 __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
@@ -252,7 +263,7 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
         float sM = 0.f, sW = 0.f;
         issue(0, 0, nmat);
         for (int js = 0; js < nsteps; ++js) {
-            wait_vm0();
+            wait_stage(js);
             barrier_lds();
             if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, nmat);
             const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
@@ -358,7 +369,7 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
         for (int n = 0; n < 8; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         issue(0, 0, 3);
         for (int js = 0; js < nsteps; ++js) {
-            wait_vm0();
+            wait_stage(js);
             barrier_lds();
             if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, 3);
             const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
@@ -407,8 +418,7 @@ struct WtArgs {
     const __bf16* inter;             // [BH][6][Hd][C]
     const __bf16 *snapW, *snapM;     // [BH][nc][3][Hd][D]
     const float* scal;               // [BH][nc][4]: A, Bb, gamma
-    const float *linW, *linM;        // [BH][P] packed state cotangents of chunk c's end
-    float *loutW, *loutM;            // [BH][P] packed state cotangents of chunk c's start (may equal lin)
+    float *lamW, *lamM;              // [BH][3][Hd][D] fp32 state cotangents, hidden-major, updated in place
     __bf16* lam;                     // [BH][6][Hd][D] bf16 copies (token kernel operands)
     float* dpart;                    // [BH][nc][nsl][4]: partial dA, dBb, dgamma
     int64_t T;
@@ -498,82 +508,68 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
         }
     }
 
-    // state cotangents: lane holds units j0 + 4g + r, d = 16 n + p.  Packed
-    // W1 / W3 [D][Hd] put units r = 0..3 side by side (one 16-byte access);
-    // W2 [Hd][D] and the hidden-major snapshots / copies take one row each.
+    // State cotangents, one matrix at a time: the accumulators (lane: units
+    // j0 + 4g + r, d = 16 n + p) are parked as a [64 units][D] fp32 tile in
+    // the idle stage buffer (row stride 132 floats: conflict-free), then the
+    // whole workgroup walks the tile row by row, 4 d per thread, so that every
+    // global access covers whole rows (fp32 cotangents 512 B, bf16 snapshots
+    // and copies 256 B per unit).
     const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + a.c) * 4);
     const float A = sc[0], Bb = sc[1], gam = sc[2];
-    // uniform bases + 32-bit unsigned byte offsets (scalar-base addressing)
-    const char* linW = (const char*)(a.linW + bh * P);
-    const char* linM = MOM ? (const char*)(a.linM + bh * P) : nullptr;
-    char* loutW = (char*)(a.loutW + bh * P);
-    char* loutM = MOM ? (char*)(a.loutM + bh * P) : nullptr;
-    const char* snw = (const char*)(a.snapW + (bh * a.nc + a.c) * P);
-    const char* snm = MOM ? (const char*)(a.snapM + (bh * a.nc + a.c) * P) : nullptr;
-    char* lamW = (char*)(a.lam + bh * 2 * P);
-    char* lamM = (char*)(a.lam + bh * 2 * P + P);
+    const int64_t ws0 = (int64_t)WS * sl;  // the workgroup's first unit
+    float* const lamW = a.lamW + bh * P;
+    float* const lamM = MOM ? a.lamM + bh * P : nullptr;
+    const __bf16* const snw = a.snapW + (bh * a.nc + a.c) * P;
+    const __bf16* const snm = MOM ? a.snapM + (bh * a.nc + a.c) * P : nullptr;
+    __bf16* const cpW = a.lam + bh * 2 * P;
+    __bf16* const cpM = a.lam + bh * 2 * P + P;
     const bool copies = a.c > 0;  // chunk 0's cotangents are final: no token kernel reads them
+    constexpr int TS = 132;       // parked tile row stride (floats)
+    float* const tile = (float*)stage;
     float sA = 0.f, sB = 0.f, sG = 0.f;
-    // The accumulators go through this wave's part of the (now idle) stage
-    // buffer one matrix at a time, so that the epilogue holds one tile in
-    // registers instead of all 24.
-    __syncthreads();
-    f32x4* park = (f32x4*)(stage + w * 8 * 64 * 16) + lane;
+    __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) park[64 * n] = acc[m][n];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-        for (int n = 0; n < 8; ++n) {
-            const f32x4 an = park[64 * n];
-            unsigned jb = (unsigned)(j0 + 4 * g), d = (unsigned)(16 * n + p);
-            asm volatile("" : "+v"(jb), "+v"(d));  // offsets recomputed here, not kept live
-            const unsigned hm0 = ((unsigned)m * Hd + jb) * D + d;  // hidden-major index of r = 0
-            const unsigned pk = m < 2 ? (unsigned)m * D * Hd + d * Hd + jb : 2u * D * Hd + jb * D + d;
-            f32x4 lw, lm = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (m < 2) {
-                lw = *(const f32x4*)(linW + 4u * pk);
-                if (MOM) lm = *(const f32x4*)(linM + 4u * pk);
-            } else {
+        for (int n = 0; n < 8; ++n)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    lw[r] = *(const float*)(linW + 4u * (pk + r * D));
-                    if (MOM) lm[r] = *(const float*)(linM + 4u * (pk + r * D));
-                }
+            for (int r = 0; r < 4; ++r) tile[(16 * w + 4 * g + r) * TS + 16 * n + p] = acc[m][n][r];
+        __syncthreads();
+#pragma unroll 2
+        for (int e = tid; e < WS * D / 4; e += NT) {
+            const int jj = e / (D / 4), d4 = 4 * (e % (D / 4));
+            const int64_t hm = ((int64_t)m * Hd + ws0 + jj) * D + d4;
+            const f32x4 an = *(const f32x4*)(tile + jj * TS + d4);
+            const f32x4 lw = *(const f32x4*)(lamW + hm);
+            const bf16x4 wc = *(const bf16x4*)(snw + hm);
+            f32x4 lm = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x4 mc = bf16x4{};
+            if (MOM) {
+                lm = *(const f32x4*)(lamM + hm);
+                mc = *(const bf16x4*)(snm + hm);
             }
             f32x4 nw, nm;
+            bf16x4 bw, bm;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float wc = (float)*(const __bf16*)(snw + 2u * (hm0 + r * D));
-                sA += lw[r] * wc;
+                sA += lw[r] * (float)wc[r];
                 nw[r] = A * lw[r] + an[r];
+                bw[r] = (__bf16)nw[r];
                 if (MOM) {
-                    const float mc = (float)*(const __bf16*)(snm + 2u * (hm0 + r * D));
-                    sB += lm[r] * mc;
-                    sG -= lw[r] * mc;
+                    sB += lm[r] * (float)mc[r];
+                    sG -= lw[r] * (float)mc[r];
                     nm[r] = Bb * lm[r] - gam * lw[r];
+                    bm[r] = (__bf16)nm[r];
                 }
             }
-            if (m < 2) {
-                *(f32x4*)(loutW + 4u * pk) = nw;
-                if (MOM) *(f32x4*)(loutM + 4u * pk) = nm;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    *(float*)(loutW + 4u * (pk + r * D)) = nw[r];
-                    if (MOM) *(float*)(loutM + 4u * (pk + r * D)) = nm[r];
-                }
-            }
+            *(f32x4*)(lamW + hm) = nw;
+            if (MOM) *(f32x4*)(lamM + hm) = nm;
             if (copies) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    *(__bf16*)(lamW + 2u * (hm0 + r * D)) = (__bf16)nw[r];
-                    if (MOM) *(__bf16*)(lamM + 2u * (hm0 + r * D)) = (__bf16)nm[r];
-                }
+                *(bf16x4*)(cpW + hm) = bw;
+                if (MOM) *(bf16x4*)(cpM + hm) = bm;
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
+        __syncthreads();  // the tile is rewritten for the next matrix
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -594,40 +590,79 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 hidden-major copies of the initial state cotangents dW_end, dM_end
-// (packed): W1 / W3 [D][Hd] are transposed through LDS 64 units at a time, W2
-// [Hd][D] is already hidden-major.
-struct InitArgs {
-    const float *dW, *dM;
-    __bf16* lam;
-    int Hd, nsl, nx;  // nx: 2 with momentum (W and M), else 1
+// Layout changes of the state cotangents between the packed parameter layout
+// (W1, W3 [D][Hd], W2 [Hd][D]) and the hidden-major working layout ([3][Hd][D]):
+// W1 / W3 are transposed through LDS 64 units at a time, W2 is hidden-major
+// already.  TO_HIDDEN: packed dW_end / dM_end -> fp32 working copy + bf16
+// copies; else the working copy -> packed dW0 / dM0.
+struct LayoutArgs {
+    const float *srcW, *srcM;  // [BH][P]
+    float *dstW, *dstM;        // [BH][P]
+    __bf16* cp;                // [BH][2P] bf16 copies (TO_HIDDEN only)
+    int Hd, nsl, nx;           // nx: 2 with momentum (W and M), else 1
 };
 
-__global__ void __launch_bounds__(NT) bwd_init_kernel(InitArgs a) {
+template <bool TO_HIDDEN>
+__global__ void __launch_bounds__(NT) bwd_layout_kernel(LayoutArgs a) {
     __shared__ float tile[D][WS + 1];
     const int64_t bh = blockIdx.x / (a.nx * a.nsl);
     const int x = (blockIdx.x / a.nsl) % a.nx;  // 0: W, 1: M
     const int sl = blockIdx.x % a.nsl;
     const int Hd = a.Hd;
     const int64_t P = 3 * (int64_t)D * Hd;
-    const float* src = (x ? a.dM : a.dW) + bh * P;
-    __bf16* dst = a.lam + bh * 2 * P + x * P;
+    const float* src = (x ? a.srcM : a.srcW) + bh * P;
+    float* dst = (x ? a.dstM : a.dstW) + bh * P;
+    __bf16* cp = TO_HIDDEN ? a.cp + bh * 2 * P + x * P : nullptr;
     const int j0 = WS * sl;
     for (int m = 0; m < 2; ++m) {
-        for (int e = threadIdx.x; e < D * WS; e += NT) {
-            const int d = e / WS, jj = e % WS;
-            tile[d][jj] = src[(int64_t)m * D * Hd + (int64_t)d * Hd + j0 + jj];
+        const int64_t pk = (int64_t)m * D * Hd + j0;            // packed: + d * Hd + j
+        const int64_t hmb = ((int64_t)m * Hd + j0) * D;         // hidden-major: + j * D + d
+        for (int e = threadIdx.x; e < D * WS / 4; e += NT) {
+            if (TO_HIDDEN) {  // 16-byte reads along the packed rows
+                const int d = e / (WS / 4), j4 = 4 * (e % (WS / 4));
+                const f32x4 v = *(const f32x4*)(src + pk + (int64_t)d * Hd + j4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tile[d][j4 + i] = v[i];
+            } else {  // 16-byte reads along the hidden-major rows
+                const int jj = e / (D / 4), d4 = 4 * (e % (D / 4));
+                const f32x4 v = *(const f32x4*)(src + hmb + (int64_t)jj * D + d4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tile[d4 + i][jj] = v[i];
+            }
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < WS * D; e += NT) {
-            const int jj = e / D, d = e % D;
-            dst[((int64_t)m * Hd + j0 + jj) * D + d] = (__bf16)tile[d][jj];
+        for (int e = threadIdx.x; e < D * WS / 4; e += NT) {
+            if (TO_HIDDEN) {  // 16-byte writes along the hidden-major rows
+                const int jj = e / (D / 4), d4 = 4 * (e % (D / 4));
+                f32x4 v;
+                bf16x4 b;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = tile[d4 + i][jj];
+                    b[i] = (__bf16)v[i];
+                }
+                *(f32x4*)(dst + hmb + (int64_t)jj * D + d4) = v;
+                *(bf16x4*)(cp + hmb + (int64_t)jj * D + d4) = b;
+            } else {  // 16-byte writes along the packed rows
+                const int d = e / (WS / 4), j4 = 4 * (e % (WS / 4));
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = tile[d][j4 + i];
+                *(f32x4*)(dst + pk + (int64_t)d * Hd + j4) = v;
+            }
         }
         __syncthreads();
     }
-    for (int e = threadIdx.x; e < WS * D; e += NT) {
-        const int64_t o = 2 * (int64_t)D * Hd + (int64_t)j0 * D + e;
-        dst[o] = (__bf16)src[o];
+    for (int e = threadIdx.x; e < WS * D / 4; e += NT) {
+        const int64_t o = 2 * (int64_t)D * Hd + (int64_t)j0 * D + 4 * e;
+        const f32x4 v = *(const f32x4*)(src + o);
+        *(f32x4*)(dst + o) = v;
+        if (TO_HIDDEN) {
+            bf16x4 b;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[i] = (__bf16)v[i];
+            *(bf16x4*)(cp + o) = b;
+        }
     }
 }
 
@@ -842,10 +877,10 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
     const int Hd = (int)d.Hd, C = (int)d.chunk;
     const int nc = (int)((d.T + d.chunk - 1) / d.chunk);
     const int nsl = Hd / WS;
-    {  // the last chunk's token kernel reads bf16 copies of dW_end, dM_end
-        const int nx = mom ? 2 : 1;
-        InitArgs ia{b.dW_end, b.dM_end, (__bf16*)b.lam, Hd, nsl, nx};
-        hipLaunchKernelGGL(bwd_init_kernel, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, ia);
+    const int nx = mom ? 2 : 1;
+    {  // working copy and bf16 copies of dW_end, dM_end
+        LayoutArgs la{b.dW_end, b.dM_end, b.lamW, b.lamM, (__bf16*)b.lam, Hd, nsl, nx};
+        hipLaunchKernelGGL(bwd_layout_kernel<true>, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, la);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     for (int c = nc - 1; c >= 0; --c) {
@@ -889,12 +924,8 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         wa.snapW = (const __bf16*)b.snapW;
         wa.snapM = (const __bf16*)b.snapM;
         wa.scal = b.scal;
-        // state cotangents, packed: read from dW_end at the last chunk, written
-        // to dW0 at the first, in place in the workspace in between
-        wa.linW = c == nc - 1 ? b.dW_end : b.lamW;
-        wa.linM = c == nc - 1 ? b.dM_end : b.lamM;
-        wa.loutW = c == 0 ? b.dW0 : b.lamW;
-        wa.loutM = c == 0 ? b.dM0 : b.lamM;
+        wa.lamW = b.lamW;
+        wa.lamM = b.lamM;
         wa.lam = (__bf16*)b.lam;
         wa.dpart = b.dpart;
         wa.T = d.T;
@@ -910,6 +941,11 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
             hipLaunchKernelGGL(bwd_wt_kernel<true>, dim3((unsigned)wa.nwg), dim3(NT), 0, s, wa);
         else
             hipLaunchKernelGGL(bwd_wt_kernel<false>, dim3((unsigned)wa.nwg), dim3(NT), 0, s, wa);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    {  // chunk 0's state cotangents -> packed dW0, dM0
+        LayoutArgs la{b.lamW, b.lamM, b.dW0, b.dM0, nullptr, Hd, nsl, nx};
+        hipLaunchKernelGGL(bwd_layout_kernel<false>, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, la);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
