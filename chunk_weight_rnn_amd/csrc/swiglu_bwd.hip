@@ -38,7 +38,8 @@
 //   token kernel  (one workgroup per 64 tokens): projections at W_c and the
 //                 cotangents (16x16x32 MFMA, hidden units 16 at a time through
 //                 LDS), the elementwise terms, and dk, dv, dq, dcM, dcW summed
-//                 over all hidden units (16x16x16 MFMA); E, F1, F3, dhq1, dhq3,
+//                 over all hidden units (pairs of 16-unit products as one
+//                 16x16x32 MFMA); E, F1, F3, dhq1, dhq3,
 //                 uq go to a per-chunk buffer for
 //   weight kernel (one workgroup per 64 hidden units): the chunk's dW by a
 //                 contraction over its tokens (16x16x32 MFMA, token rows
@@ -79,6 +80,18 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
                                                       0, 0, 0);
+}
+
+// Two K = 16 products into one 16x16x32 MFMA: k-slots 0..3 of lane group g
+// take a's and b's units 4g..4g+3, slots 4..7 the second pair's.
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[4 + e] = hi[e];
+    }
+    return r;
 }
 
 __device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -329,15 +342,12 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
 #pragma unroll
                     for (int mi = 0; mi < nmat; ++mi) bf[mi] = tr_units(sb + mi * STEPB, lane, n + 1);
                 }
-                dk[n] = mfma16(aF1, cur[0], dk[n]);
-                dk[n] = mfma16(aF3, cur[1], dk[n]);
-                dk[n] = mfma16(aW1, cur[3], dk[n]);
-                dk[n] = mfma16(aW3, cur[4], dk[n]);
-                dv[n] = mfma16(anE, cur[2], dv[n]);
-                dv[n] = mfma16(aW2, cur[5], dv[n]);
+                // pairs of K = 16 terms as one K = 32 product each
+                dk[n] = mfma32(cat8(aF1, aF3), cat8(cur[0], cur[1]), dk[n]);
+                dk[n] = mfma32(cat8(aW1, aW3), cat8(cur[3], cur[4]), dk[n]);
+                dv[n] = mfma32(cat8(anE, aW2), cat8(cur[2], cur[5]), dv[n]);
                 if (MOM) {
-                    dk[n] = mfma16(aM1, cur[6], dk[n]);
-                    dk[n] = mfma16(aM3, cur[7], dk[n]);
+                    dk[n] = mfma32(cat8(aM1, aM3), cat8(cur[6], cur[7]), dk[n]);
                     dv[n] = mfma16(aM2, cur[8], dv[n]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -402,8 +412,8 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
             put_inter(5, j0, uq);
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
-                dq[n] = mfma16(a1, tr_units(sb + 0 * STEPB, lane, n), dq[n]);
-                dq[n] = mfma16(a3, tr_units(sb + 1 * STEPB, lane, n), dq[n]);
+                dq[n] = mfma32(cat8(a1, a3), cat8(tr_units(sb + 0 * STEPB, lane, n), tr_units(sb + 1 * STEPB, lane, n)),
+                               dq[n]);
                 if (n & 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
