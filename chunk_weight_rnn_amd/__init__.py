@@ -130,11 +130,12 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
 
 def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, chunk: int, Hd: int,
                    kind: str = "swiglu", loss: str = "negdot", momentum: bool = True, chunk_avg: bool = False,
-                   workspace=None, stream=None):
+                   force_generic: bool = False, workspace=None, stream=None):
     """Gradients of <dout, out> + <dW_end, W_end> + <dM_end, M_end> through
-    ``chunk_forward``; returns a dict with keys q, k, v (bf16), eta, alpha,
-    beta, W0, M0 (float32).  Without momentum beta, M0 and dM_end are ignored
-    and the beta / M0 gradients are None."""
+    ``chunk_forward``; returns a dict with keys q, k, v (the I/O dtype), eta,
+    alpha, beta, W0, M0 (float32).  Without momentum beta, M0 and dM_end are
+    ignored and the beta / M0 gradients are None.  ``force_generic`` takes the
+    portable fp32 backward where the SwiGLU MFMA one applies."""
     lib = library()
     if not momentum:
         beta = M0 = dM_end = None
@@ -152,7 +153,8 @@ def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, c
         if t is not None and t.dtype != want:
             raise TypeError(f"{name} must be {want}")
     B, H, T, D = q.shape
-    flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0)
+    flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0) | \
+        (FLAG_FORCE_GENERIC if force_generic else 0)
     desc = make_desc(kind, loss, _io_name(q), B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
     for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("dout", dout, q.shape),

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libe2ttt.so")
-SOURCES = ["abi.hip", "logscan.hip", "generic.hip", "swiglu_loop.hip", "swiglu_mfma.hip", "swiglu_bwd.hip"]
+SOURCES = ["abi.hip", "logscan.hip", "generic.hip", "generic_bwd.hip", "swiglu_loop.hip", "swiglu_mfma.hip",
+           "swiglu_bwd.hip"]
 ARCH = "gfx950"
 
 

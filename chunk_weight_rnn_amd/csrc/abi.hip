@@ -65,20 +65,47 @@ struct Range {
 static bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // ---------------------------------------------------------------- backward
-static bool backward_supported(const e2ttt_desc& d) {
-    if (d.flags & E2TTT_FLAG_FORCE_GENERIC) return false;
-    if (!swiglu_mfma_supported(d) || d.chunk > 2048) return false;
-    // 32-bit byte offsets of the buffer copies
-    return d.T * d.D * 2 < ((int64_t)1 << 31) && 6 * d.Hd * d.D * 2 < ((int64_t)1 << 31);
+// 1: SwiGLU MFMA backward, 0: portable fp32 backward, -1: unsupported
+static int backward_path(const e2ttt_desc& d) {
+    if (d.chunk > 2048) return -1;  // the scalar backward stages one chunk in LDS
+    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d) &&
+        d.T * d.D * 2 < ((int64_t)1 << 31) && 6 * d.Hd * d.D * 2 < ((int64_t)1 << 31))  // 32-bit copy offsets
+        return 1;
+    if (generic_supported(d) && generic_bwd_token_block(d) > 0) return 0;
+    return -1;
 }
 
 struct BwdWorkspace {
     size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, total;
+    size_t save, gacc;  // portable path: chunk-start states, forward G accumulators / dJ/dW
     int64_t ldc;
 };
 
 static BwdWorkspace bwd_workspace_layout(const e2ttt_desc& d) {
     BwdWorkspace w{};
+    if (backward_path(d) == 0) {
+        const size_t BH = (size_t)(d.B * d.H);
+        const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);
+        const size_t P = (size_t)e2ttt_param_count(&d);
+        w.ldc = (d.T + 63) / 64 * 64;
+        const size_t ldc = (size_t)w.ldc;
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            const size_t o = off;
+            off += align_up(bytes);
+            return o;
+        };
+        w.cM = take(BH * ldc * 4);
+        w.cW = take(BH * ldc * 4);
+        w.scal = take(BH * nc * 4 * 4);
+        w.save = take(BH * nc * 2 * P * 4);
+        w.gacc = take(BH * 2 * P * 4);
+        w.dcM = take(BH * ldc * 4);
+        w.dcW = take(BH * ldc * 4);
+        w.dpart = take(BH * nc * 4 * 4);
+        w.total = (BH * (size_t)d.T == 0) ? 0 : off;
+        return w;
+    }
     const size_t BH = (size_t)(d.B * d.H);
     const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);
     const size_t P = (size_t)e2ttt_param_count(&d);
@@ -251,7 +278,7 @@ size_t e2ttt_backward_workspace_size(const e2ttt_desc* d) {
 
 int e2ttt_validate_backward(const e2ttt_desc* d, const void* const ptrs[19]) {
     if (!desc_ok(d) || !ptrs) return E2TTT_ERR_INVALID_ARG;
-    if (!backward_supported(*d)) return E2TTT_ERR_UNSUPPORTED;
+    if (backward_path(*d) < 0) return E2TTT_ERR_UNSUPPORTED;
     size_t bytes[19];
     bwd_sizes(*d, bytes);
     for (int i = 0; i < 19; ++i) {
@@ -315,6 +342,51 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
     if (events)
         for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
     if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
+    if (backward_path(*d) == 0) {
+        // portable path: recompute saving every chunk's start state (outputs
+        // into dq, end state into dW0 / dM0, both overwritten below)
+        float* cM = (float*)(wsb + ws.cM);
+        float* cW = (float*)(wsb + ws.cW);
+        float* scal = (float*)(wsb + ws.scal);
+        float* save = (float*)(wsb + ws.save);
+        if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        if (launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, (float*)(wsb + ws.gacc), s,
+                           save) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
+        GenericBwdBuffers g;
+        g.q = q;
+        g.k = k;
+        g.v = v;
+        g.dout = dout;
+        g.eta = eta;
+        g.alpha = alpha;
+        g.beta = beta;
+        g.cM = cM;
+        g.cW = cW;
+        g.scal = scal;
+        g.save = save;
+        g.dW_end = dW_end;
+        g.dM_end = dM_end;
+        g.dacc = (float*)(wsb + ws.gacc);
+        g.dcM = (float*)(wsb + ws.dcM);
+        g.dcW = (float*)(wsb + ws.dcW);
+        g.dpart = (float*)(wsb + ws.dpart);
+        g.dq = dq;
+        g.dk = dk;
+        g.dv = dv;
+        g.deta = deta;
+        g.dalpha = dalpha;
+        g.dbeta = dbeta;
+        g.dW0 = dW0;
+        g.dM0 = dM0;
+        g.ldc = ws.ldc;
+        hipError_t e = launch_generic_backward(*d, g, s);
+        if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
+        if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
+        return e == hipSuccess ? E2TTT_OK : E2TTT_ERR_HIP;
+    }
     // forward recompute: scalar kernels and the chunk loop (chunk-start
     // snapshots of W and M); its end state goes to dW0 / dM0, which the
     // backward overwrites

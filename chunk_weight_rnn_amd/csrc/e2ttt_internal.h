@@ -29,10 +29,11 @@ Workspace workspace_layout(const e2ttt_desc& d, int path);
 hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,
                           const float* beta, float* cM, float* cW, int64_t ldc, float* scal, hipStream_t s);
 
+// save (may be null): [BH][nc][2][P] fp32, every chunk's start W and M.
 hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v,
                           const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
                           const float* M0, void* out, float* W_end, float* M_end, float* gacc,
-                          hipStream_t s);
+                          hipStream_t s, float* save = nullptr);
 
 // SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
 bool swiglu_mfma_supported(const e2ttt_desc& d);
@@ -69,5 +70,28 @@ struct BwdBuffers {
 // scalar kernels' backward.
 hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipStream_t s, hipEvent_t ev_loop);
 int64_t swiglu_bwd_inter_elems(const e2ttt_desc& d);  // per (b, h)
+
+// Scalar kernels' backward: d eta, d alpha, d beta from dcM, dcW (per token)
+// and the partial dA, dBb, dgamma in dpart [BH][nc][nsl][4].
+hipError_t launch_bwd_scalar(const e2ttt_desc& d, const float* eta, const float* alpha, const float* beta,
+                             const float* dcM, const float* dcW, int64_t ldc, const float* dpart, int nsl,
+                             float* deta, float* dalpha, float* dbeta, hipStream_t s);
+
+// Backward of the portable path (every kind and loss).
+struct GenericBwdBuffers {
+    const void *q, *k, *v, *dout;
+    const float *eta, *alpha, *beta;
+    const float *cM, *cW, *scal;
+    const float* save;                // [BH][nc][2][P] chunk-start W, M
+    const float *dW_end, *dM_end;
+    float* dacc;                      // [BH][P]
+    float *dcM, *dcW;                 // [BH][ldc]
+    float* dpart;                     // [BH][nc][4]
+    void *dq, *dk, *dv;
+    float *deta, *dalpha, *dbeta, *dW0, *dM0;
+    int64_t ldc;
+};
+int generic_bwd_token_block(const e2ttt_desc& d);  // 0: the shape does not fit
+hipError_t launch_generic_backward(const e2ttt_desc& d, const GenericBwdBuffers& b, hipStream_t s);
 
 }  // namespace e2ttt

@@ -41,6 +41,7 @@ struct GenericArgs {
     float* W;
     float* M;
     float* gacc;
+    float* save;  // [BH][nc][2][P] chunk-start W, M (may be null)
 };
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -104,6 +105,13 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     for (int64_t c = 0; c < a.nc; ++c) {
         const int64_t t0 = c * a.C;
         const int64_t Cc = min(a.C, a.T - t0);  // the last chunk may be shorter
+        if (a.save) {  // chunk-start state for the backward pass
+            float* sv = a.save + (bh * a.nc + c) * 2 * P;
+            for (int64_t p = tid; p < P; p += NT) {
+                sv[p] = W[p];
+                sv[P + p] = M ? M[p] : 0.f;
+            }
+        }
         // ---- 1. outputs from the chunk-start weights
         for (int64_t b0 = 0; b0 < Cc; b0 += TB) {
             const int nt = (int)min((int64_t)TB, Cc - b0);
@@ -331,7 +339,7 @@ int generic_token_block(const e2ttt_desc& d) {
 
 hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
                           const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
-                          float* W_end, float* M_end, float* gacc, hipStream_t s) {
+                          float* W_end, float* M_end, float* gacc, hipStream_t s, float* save) {
     GenericArgs a;
     a.T = d.T;
     a.D = d.D;
@@ -355,6 +363,7 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
     a.W = W_end;
     a.M = M_end;
     a.gacc = gacc;
+    a.save = save;
     const size_t shmem = (size_t)(3 * a.D + 3 * a.Hd + 2) * a.TB * sizeof(float);
     switch (d.kind) {
         case E2TTT_LINEAR: return launch_kind<E2TTT_LINEAR>(d, a, shmem, s);

@@ -959,22 +959,32 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
+    return launch_bwd_scalar(d, b.eta, b.alpha, b.beta, b.dcM, b.dcW, b.ldc, b.dpart, nsl, b.deta, b.dalpha, b.dbeta,
+                             s);
+}
+
+hipError_t launch_bwd_scalar(const e2ttt_desc& d, const float* eta, const float* alpha, const float* beta,
+                             const float* dcM, const float* dcW, int64_t ldc, const float* dpart, int nsl,
+                             float* deta, float* dalpha, float* dbeta, hipStream_t s) {
+    const int64_t BH = d.B * d.H;
+    const int C = (int)d.chunk;
+    const int nc = (int)((d.T + d.chunk - 1) / d.chunk);
     ScalArgs sa;
-    sa.eta = b.eta;
-    sa.alpha = b.alpha;
-    sa.beta = b.beta;
-    sa.dcM = b.dcM;
-    sa.dcW = b.dcW;
-    sa.dpart = b.dpart;
-    sa.deta = b.deta;
-    sa.dalpha = b.dalpha;
-    sa.dbeta = b.dbeta;
+    sa.eta = eta;
+    sa.alpha = alpha;
+    sa.beta = beta;
+    sa.dcM = dcM;
+    sa.dcW = dcW;
+    sa.dpart = dpart;
+    sa.deta = deta;
+    sa.dalpha = dalpha;
+    sa.dbeta = dbeta;
     sa.T = d.T;
-    sa.ldc = b.ldc;
+    sa.ldc = ldc;
     sa.C = C;
     sa.nc = nc;
     sa.nsl = nsl;
-    sa.mom = mom ? 1 : 0;
+    sa.mom = (d.flags & E2TTT_FLAG_NO_MOMENTUM) ? 0 : 1;
     sa.avg = (d.flags & E2TTT_FLAG_CHUNK_AVG) ? 1 : 0;
     hipLaunchKernelGGL(bwd_scalar_kernel, dim3((unsigned)(BH * nc)), dim3(64), (size_t)8 * C * sizeof(float), s, sa);
     return hipGetLastError();

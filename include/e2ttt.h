@@ -182,17 +182,19 @@ E2TTT_API int e2ttt_logscan(const e2ttt_desc* desc, const float* eta, const floa
  * recomputed inside the call (scalar kernels and chunk loop, keeping each
  * chunk's start state); nothing needs to be saved from the forward call.
  *
- * Supported (else E2TTT_ERR_UNSUPPORTED): the SwiGLU MFMA path's shapes
+ * Paths, chosen like the forward's: the SwiGLU MFMA backward for its shapes
  * (SWIGLU, LOSS_NEGDOT, BF16 I/O, D == 128, Hd a multiple of 64 up to 4096,
- * chunk a multiple of 64) with chunk <= 2048 and T*D*2 < 2^31;
- * E2TTT_FLAG_NO_MOMENTUM and E2TTT_FLAG_CHUNK_AVG are honoured,
- * E2TTT_FLAG_FORCE_GENERIC is not supported.  A ragged last chunk is allowed.
+ * chunk a multiple of 64, T*D*2 < 2^31), else (or with
+ * E2TTT_FLAG_FORCE_GENERIC) a portable fp32 backward for every kind and loss
+ * with D <= 256, Hd <= 1024.  chunk <= 2048 on both (else
+ * E2TTT_ERR_UNSUPPORTED).  E2TTT_FLAG_NO_MOMENTUM and E2TTT_FLAG_CHUNK_AVG
+ * are honoured and a ragged last chunk is allowed.
  *
- *   q, k, v, dout        [B][H][T][D] bf16 (dout: cotangent of out)
+ *   q, k, v, dout        [B][H][T][D] io_dtype (dout: cotangent of out)
  *   eta, alpha, beta     [B][H][T] fp32
  *   W0, M0               [B][H][P] fp32 (the forward's initial state)
  *   dW_end, dM_end       [B][H][P] fp32 cotangents of W_end, M_end
- *   dq, dk, dv           [B][H][T][D] bf16 outputs
+ *   dq, dk, dv           [B][H][T][D] io_dtype outputs
  *   deta, dalpha, dbeta  [B][H][T] fp32 outputs
  *   dW0, dM0             [B][H][P] fp32 outputs (packed like W0)
  *   workspace            >= e2ttt_backward_workspace_size(desc) bytes,

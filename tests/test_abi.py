@@ -225,9 +225,13 @@ def test_backward_validation(lib):
     assert _validate_bwd(lib, d, _bwd_ptrs(d, momentum=False)) == 0
     d = _desc(flags=4)
     assert _validate_bwd(lib, d, _bwd_ptrs(d)) == 0
-    # shapes outside the SwiGLU MFMA path, the portable-path flag, long chunks
-    for bad in (_desc(kind="linear", loss="mse", io="f32", D=32, Hd=0), _desc(io="f32"), _desc(D=64),
-                _desc(Hd=96), _desc(chunk=96), _desc(chunk=4096, T=8192), _desc(flags=1)):
+    # the portable backward takes what the MFMA path does not
+    for ok in (_desc(kind="linear", loss="mse", io="f32", D=32, Hd=0), _desc(io="f32"), _desc(D=64),
+               _desc(Hd=96), _desc(chunk=96), _desc(flags=1), _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128)):
+        assert _validate_bwd(lib, ok, _bwd_ptrs(ok)) == 0
+    # long chunks, and shapes neither path handles
+    for bad in (_desc(chunk=4096, T=8192), _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=2048),
+                _desc(kind="linear", loss="mse", io="f32", D=512, Hd=0), _desc(D=256, Hd=2048)):
         assert _validate_bwd(lib, bad, _bwd_ptrs(bad)) == 2
     # every output must be disjoint from everything else (no in-place form)
     d = _desc()
@@ -249,5 +253,5 @@ def test_backward_validation(lib):
     v = ctypes.c_void_p
     args = [v(x) for x in _bwd_ptrs(d)]
     assert lib.e2ttt_chunk_backward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 4
-    bad = _desc(D=64)
+    bad = _desc(chunk=4096, T=8192)
     assert lib.e2ttt_chunk_backward(ctypes.byref(bad), *args, v(0), ctypes.c_size_t(0), v(0)) == 2

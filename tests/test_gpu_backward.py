@@ -21,13 +21,14 @@ SMALL = synth.Config("bwd_small", "swiglu", "negdot", 1, 2, 320, 128, 128, 128, 
                      "2.5 chunks of 128 (ragged tail of 64)")
 
 
-def _gpu(cfg, x, c):
+def _gpu(cfg, x, c, force_generic=False):
     import chunk_weight_rnn_amd as e2
     d = {n: t.cuda() for n, t in x.items()}
     dc = {n: t.cuda() for n, t in c.items()}
     g = e2.chunk_backward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
-                          dc["dout"], dc["dW_end"], dc["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd,
-                          momentum=cfg.momentum, chunk_avg=cfg.chunk_avg)
+                          dc["dout"], dc["dW_end"], dc["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd, kind=cfg.kind,
+                          loss=cfg.loss, momentum=cfg.momentum, chunk_avg=cfg.chunk_avg,
+                          force_generic=force_generic)
     torch.cuda.synchronize()
     return {n: (None if t is None else t.float().cpu().numpy()) for n, t in g.items()}
 
