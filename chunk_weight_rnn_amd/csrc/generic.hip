@@ -11,7 +11,7 @@
 //        G^M = sum_i cM_i g_i,   G^W = sum_i cW_i g_i   (cM, cW from logscan),
 //   4. M <- Bb*M + G^M,  W <- A*W - gamma*M_old - G^W.
 //
-// One 256-thread workgroup per (b, h).  The state lives in the W_end / M_end
+// One 1024-thread workgroup per (b, h).  The state lives in the W_end / M_end
 // buffers (fp32, L2-resident) and G^M, G^W in a per-head workspace slice.
 // Tokens are staged through LDS in blocks of TB; every contraction is a plain
 // fp32 dot product (no reassociation beyond the per-thread loop order).
@@ -22,13 +22,14 @@
 namespace e2ttt {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 1024;  // 16 wavefronts: the fp32 loops are latency-bound
 
 struct GenericArgs {
     int64_t T, D, Hd, C, nc, P;
     int64_t ldc;  // row stride of cM / cW (tokens, >= T)
     int loss, TB;
     int nomom;  // no momentum: M0 / M are not used (the scalar kernels already have beta = 0)
+    int wlds;   // 1: the chunk-start weights are copied to LDS after the token rows
     const void* q;
     const void* k;
     const void* v;
@@ -60,7 +61,7 @@ __device__ __forceinline__ float dsilu_f(float x) {
     return s * (1.f + x * (1.f - s));
 }
 
-template <int KIND, typename TIO>
+template <int KIND, typename TIO, bool WLDS>
 __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     extern __shared__ float smem[];
     const int64_t bh = blockIdx.x;
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     float* us = h3s + TB * Hd;    // [TB][Hd]
     float* cms = us + TB * Hd;    // [TB]
     float* cws = cms + TB;        // [TB]
+    float* wl = cws + TB;         // [P] chunk-start weights (when a.wlds)
 
     float* W = a.W + bh * P;
     float* M = a.nomom ? nullptr : a.M + bh * P;
@@ -95,12 +97,19 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     }
     __syncthreads();
 
-    // matrix views of the state
-    const float* Wl = W;                       // linear  [D][D]
-    const float* W1 = W;                       // mlp [Hd][D] ; swiglu [D][Hd]
-    const float* W3 = W + (int64_t)D * Hd;     // swiglu [D][Hd]
-    const float* W2m = W + (int64_t)D * Hd;    // mlp [D][Hd]
-    const float* W2s = W + 2 * (int64_t)D * Hd;  // swiglu [Hd][D]
+    // matrix views of the chunk-start weights: the LDS copy when it fits,
+    // else the state buffer itself (read-only until step 4).  The LDS copy
+    // pads every matrix row by one float, so that lanes reading one column of
+    // consecutive rows hit distinct banks (rows of D or Hd floats are a
+    // multiple of the 64 banks otherwise).
+    const int pad = WLDS ? 1 : 0;
+    const int64_t sD = D + pad, sH = Hd + pad;    // row strides of D- and Hd-wide rows
+    const float* Wr = WLDS ? wl : W;
+    const float* Wl = Wr;                         // linear  [D][D]     (rows of D)
+    const float* W1 = Wr;                         // mlp [Hd][D] (rows of D); swiglu [D][Hd] (rows of Hd)
+    const float* W3 = Wr + (int64_t)D * sH;       // swiglu [D][Hd]
+    const float* W2m = Wr + (int64_t)Hd * sD;     // mlp [D][Hd]         (rows of Hd)
+    const float* W2s = Wr + 2 * (int64_t)D * sH;  // swiglu [Hd][D]      (rows of D)
 
     for (int64_t c = 0; c < a.nc; ++c) {
         const int64_t t0 = c * a.C;
@@ -112,6 +121,22 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 sv[P + p] = M ? M[p] : 0.f;
             }
         }
+        if (WLDS) {  // packed index -> padded (row, column)
+            for (int64_t p = tid; p < P; p += NT) {
+                int64_t o;
+                if (KIND == E2TTT_LINEAR) {
+                    o = (p / D) * sD + p % D;
+                } else if (KIND == E2TTT_MLP) {
+                    const int64_t n1 = (int64_t)Hd * D;
+                    o = p < n1 ? (p / D) * sD + p % D : n1 + Hd + ((p - n1) / Hd) * sH + (p - n1) % Hd;
+                } else {
+                    const int64_t n1 = (int64_t)D * Hd;
+                    o = p < 2 * n1 ? (p / Hd) * sH + p % Hd : 2 * D * sH + ((p - 2 * n1) / D) * sD + (p - 2 * n1) % D;
+                }
+                wl[o] = W[p];
+            }
+            __syncthreads();
+        }
         // ---- 1. outputs from the chunk-start weights
         for (int64_t b0 = 0; b0 < Cc; b0 += TB) {
             const int nt = (int)min((int64_t)TB, Cc - b0);
@@ -121,31 +146,35 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, r = i % D;
                     float acc = 0.f;
-                    for (int d = 0; d < D; ++d) acc += Wl[(int64_t)r * D + d] * xs[t * D + d];
+                    #pragma unroll 4
+                    for (int d = 0; d < D; ++d) acc += Wl[r * sD + d] * xs[t * D + d];
                     out[(t0 + b0) * D + i] = from_f32<TIO>(acc);
                 }
             } else if (KIND == E2TTT_MLP) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float acc = 0.f;
-                    for (int d = 0; d < D; ++d) acc += W1[(int64_t)j * D + d] * xs[t * D + d];
+                    #pragma unroll 4
+                    for (int d = 0; d < D; ++d) acc += W1[j * sD + d] * xs[t * D + d];
                     us[t * Hd + j] = silu_f(acc);
                 }
                 __syncthreads();
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, r = i % D;
                     float acc = 0.f;
-                    for (int j = 0; j < Hd; ++j) acc += W2m[(int64_t)r * Hd + j] * us[t * Hd + j];
+                    #pragma unroll 4
+                    for (int j = 0; j < Hd; ++j) acc += W2m[r * sH + j] * us[t * Hd + j];
                     out[(t0 + b0) * D + i] = from_f32<TIO>(acc);
                 }
             } else {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float a1 = 0.f, a3 = 0.f;
+                    #pragma unroll 4
                     for (int d = 0; d < D; ++d) {
                         const float x = xs[t * D + d];
-                        a1 += x * W1[(int64_t)d * Hd + j];
-                        a3 += x * W3[(int64_t)d * Hd + j];
+                        a1 += x * W1[d * sH + j];
+                        a3 += x * W3[d * sH + j];
                     }
                     us[t * Hd + j] = silu_f(a1) * a3;
                 }
@@ -153,7 +182,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, r = i % D;
                     float acc = 0.f;
-                    for (int j = 0; j < Hd; ++j) acc += us[t * Hd + j] * W2s[(int64_t)j * D + r];
+                    #pragma unroll 4
+                    for (int j = 0; j < Hd; ++j) acc += us[t * Hd + j] * W2s[j * sD + r];
                     out[(t0 + b0) * D + i] = from_f32<TIO>(acc);
                 }
             }
@@ -178,7 +208,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                     float g = -vs[i];
                     if (a.loss == E2TTT_LOSS_MSE) {
                         float acc = 0.f;
-                        for (int d = 0; d < D; ++d) acc += Wl[(int64_t)r * D + d] * xs[t * D + d];
+                        #pragma unroll 4
+                        for (int d = 0; d < D; ++d) acc += Wl[r * sD + d] * xs[t * D + d];
                         g = acc - vs[i];
                     }
                     dys[i] = g;
@@ -187,6 +218,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int64_t p = tid; p < P; p += NT) {
                     const int r = (int)(p / D), d = (int)(p % D);
                     float gm = 0.f, gw = 0.f;
+                    #pragma unroll 4
                     for (int t = 0; t < nt; ++t) {
                         const float g = dys[t * D + r] * xs[t * D + d];
                         gm += cms[t] * g;
@@ -199,7 +231,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float acc = 0.f;
-                    for (int d = 0; d < D; ++d) acc += W1[(int64_t)j * D + d] * xs[t * D + d];
+                    #pragma unroll 4
+                    for (int d = 0; d < D; ++d) acc += W1[j * sD + d] * xs[t * D + d];
                     h1s[i] = acc;          // z
                     us[i] = silu_f(acc);   // a
                 }
@@ -209,7 +242,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                     float g = -vs[i];
                     if (a.loss == E2TTT_LOSS_MSE) {
                         float acc = 0.f;
-                        for (int j = 0; j < Hd; ++j) acc += W2m[(int64_t)r * Hd + j] * us[t * Hd + j];
+                        #pragma unroll 4
+                        for (int j = 0; j < Hd; ++j) acc += W2m[r * sH + j] * us[t * Hd + j];
                         g = acc - vs[i];
                     }
                     dys[i] = g;
@@ -218,7 +252,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float acc = 0.f;
-                    for (int r = 0; r < D; ++r) acc += W2m[(int64_t)r * Hd + j] * dys[t * D + r];
+                    #pragma unroll 4
+                    for (int r = 0; r < D; ++r) acc += W2m[r * sH + j] * dys[t * D + r];
                     h3s[i] = acc * dsilu_f(h1s[i]);  // dz
                 }
                 __syncthreads();
@@ -227,6 +262,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                     float gm = 0.f, gw = 0.f;
                     if (p < n1) {
                         const int j = (int)(p / D), d = (int)(p % D);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const float g = h3s[t * Hd + j] * xs[t * D + d];
                             gm += cms[t] * g;
@@ -234,6 +270,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                         }
                     } else {
                         const int r = (int)((p - n1) / Hd), j = (int)((p - n1) % Hd);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const float g = dys[t * D + r] * us[t * Hd + j];
                             gm += cms[t] * g;
@@ -247,10 +284,11 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float a1 = 0.f, a3 = 0.f;
+                    #pragma unroll 4
                     for (int d = 0; d < D; ++d) {
                         const float x = xs[t * D + d];
-                        a1 += x * W1[(int64_t)d * Hd + j];
-                        a3 += x * W3[(int64_t)d * Hd + j];
+                        a1 += x * W1[d * sH + j];
+                        a3 += x * W3[d * sH + j];
                     }
                     h1s[i] = a1;
                     h3s[i] = a3;
@@ -262,7 +300,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                     float g = -vs[i];
                     if (a.loss == E2TTT_LOSS_MSE) {
                         float acc = 0.f;
-                        for (int j = 0; j < Hd; ++j) acc += us[t * Hd + j] * W2s[(int64_t)j * D + r];
+                        #pragma unroll 4
+                        for (int j = 0; j < Hd; ++j) acc += us[t * Hd + j] * W2s[j * sD + r];
                         g = acc - vs[i];
                     }
                     dys[i] = g;
@@ -271,7 +310,8 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float du = 0.f;
-                    for (int r = 0; r < D; ++r) du += dys[t * D + r] * W2s[(int64_t)j * D + r];
+                    #pragma unroll 4
+                    for (int r = 0; r < D; ++r) du += dys[t * D + r] * W2s[j * sD + r];
                     const float x1 = h1s[i], x3 = h3s[i];
                     h1s[i] = du * x3 * dsilu_f(x1);  // dh1
                     h3s[i] = du * silu_f(x1);        // dh3
@@ -284,6 +324,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                         const float* fac = p < n1 ? h1s : h3s;
                         const int64_t pp = p < n1 ? p : p - n1;
                         const int d = (int)(pp / Hd), j = (int)(pp % Hd);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const float g = xs[t * D + d] * fac[t * Hd + j];
                             gm += cms[t] * g;
@@ -291,6 +332,7 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
                         }
                     } else {
                         const int j = (int)((p - 2 * n1) / D), r = (int)((p - 2 * n1) % D);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const float g = us[t * Hd + j] * dys[t * D + r];
                             gm += cms[t] * g;
@@ -318,15 +360,24 @@ __global__ __launch_bounds__(NT) void generic_kernel(GenericArgs a) {
     }
 }
 
-template <int KIND>
-hipError_t launch_kind(const e2ttt_desc& d, const GenericArgs& a, size_t shmem, hipStream_t s) {
-    const unsigned grid = (unsigned)(d.B * d.H);
-    if (d.io_dtype == E2TTT_BF16)
-        hipLaunchKernelGGL((generic_kernel<KIND, __bf16>), dim3(grid), dim3(NT), shmem, s, a);
-    else
-        hipLaunchKernelGGL((generic_kernel<KIND, float>), dim3(grid), dim3(NT), shmem, s, a);
+template <int KIND, typename TIO, bool WLDS>
+hipError_t launch_one(const e2ttt_desc& d, const GenericArgs& a, size_t shmem, hipStream_t s) {
+    const void* f = (const void*)generic_kernel<KIND, TIO, WLDS>;
+    if (shmem > 64 * 1024 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((generic_kernel<KIND, TIO, WLDS>), dim3((unsigned)(d.B * d.H)), dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
+
+template <int KIND>
+hipError_t launch_kind(const e2ttt_desc& d, const GenericArgs& a, size_t shmem, hipStream_t s) {
+    if (d.io_dtype == E2TTT_BF16)
+        return a.wlds ? launch_one<KIND, __bf16, true>(d, a, shmem, s) : launch_one<KIND, __bf16, false>(d, a, shmem, s);
+    return a.wlds ? launch_one<KIND, float, true>(d, a, shmem, s) : launch_one<KIND, float, false>(d, a, shmem, s);
+}
+
+// LDS the portable kernels may use per workgroup (of gfx950's 160 KB)
+constexpr size_t kLdsBudget = 144 * 1024;
 
 }  // namespace
 
@@ -364,7 +415,14 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
     a.M = M_end;
     a.gacc = gacc;
     a.save = save;
-    const size_t shmem = (size_t)(3 * a.D + 3 * a.Hd + 2) * a.TB * sizeof(float);
+    size_t shmem = (size_t)(3 * a.D + 3 * a.Hd + 2) * a.TB * sizeof(float);
+    // the weights with every row padded by one float
+    const int64_t Dd = a.D, H = a.Hd;
+    const int64_t Ppad = d.kind == E2TTT_LINEAR ? Dd * (Dd + 1)
+                         : d.kind == E2TTT_MLP  ? H * (Dd + 1) + Dd * (H + 1)
+                                                : 2 * Dd * (H + 1) + H * (Dd + 1);
+    a.wlds = shmem + (size_t)Ppad * sizeof(float) <= kLdsBudget ? 1 : 0;
+    if (a.wlds) shmem += (size_t)Ppad * sizeof(float);
     switch (d.kind) {
         case E2TTT_LINEAR: return launch_kind<E2TTT_LINEAR>(d, a, shmem, s);
         case E2TTT_MLP: return launch_kind<E2TTT_MLP>(d, a, shmem, s);

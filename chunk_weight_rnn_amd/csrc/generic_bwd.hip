@@ -36,7 +36,7 @@
 // ([...] only for the MSE loss) and the output path, the gradient of
 // <dout, f_W(q)>, as in any MLP backward.
 //
-// One 256-thread workgroup per (b, h); tokens in blocks through LDS; every
+// One 1024-thread workgroup per (b, h); tokens in blocks through LDS; every
 // contraction is a plain fp32 loop.  The cotangents are updated in place in
 // the dW0 / dM0 buffers; dJ/dW accumulates in a per-head workspace slice.
 #include <math.h>
@@ -46,7 +46,7 @@
 namespace e2ttt {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 1024;  // 16 wavefronts: the fp32 loops are latency-bound
 
 struct GBwdArgs {
     int64_t T, D, Hd, C, nc, P, ldc;
@@ -107,7 +107,26 @@ __device__ void block_sum3(float& a, float& b, float& c, float* red) {
 __host__ __device__ constexpr int rows_d(int kind) { return kind == E2TTT_LINEAR ? 8 : kind == E2TTT_MLP ? 8 : 6; }
 __host__ __device__ constexpr int rows_h(int kind) { return kind == E2TTT_LINEAR ? 0 : kind == E2TTT_MLP ? 7 : 13; }
 
-template <int KIND, typename TIO>
+// Packed parameter index -> index in the row-padded copy, and its size.
+template <int KIND>
+__device__ __forceinline__ int64_t padded_index(int64_t p, int64_t D, int64_t Hd) {
+    if (KIND == E2TTT_LINEAR) return (p / D) * (D + 1) + p % D;
+    if (KIND == E2TTT_MLP) {
+        const int64_t n1 = Hd * D;
+        return p < n1 ? (p / D) * (D + 1) + p % D : Hd * (D + 1) + ((p - n1) / Hd) * (Hd + 1) + (p - n1) % Hd;
+    }
+    const int64_t n1 = D * Hd;
+    return p < 2 * n1 ? (p / Hd) * (Hd + 1) + p % Hd : 2 * D * (Hd + 1) + ((p - 2 * n1) / D) * (D + 1) + (p - 2 * n1) % D;
+}
+template <int KIND>
+__host__ __device__ constexpr int64_t padded_count(int64_t D, int64_t Hd) {
+    return KIND == E2TTT_LINEAR ? D * (D + 1) : KIND == E2TTT_MLP ? Hd * (D + 1) + D * (Hd + 1) : 2 * D * (Hd + 1) + Hd * (D + 1);
+}
+
+// CACHE: 0 nothing in LDS, 1 W_c, 2 W_c and the cotangents lW, lM (copied per
+// chunk after the token rows, rows padded); the rest is read from global
+// memory.
+template <int KIND, typename TIO, int CACHE>
 __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
     extern __shared__ float smem[];
     __shared__ float red[3 * NT / 64];
@@ -124,6 +143,13 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
     auto RH = [&](int i) { return rh + i * TB * Hd; };
     float* cms = rh + rows_h(KIND) * TB * Hd;
     float* cws = cms + TB;
+    float* cache = cws + TB;  // W_c (CACHE >= 1), lW and lM (CACHE >= 2), rows padded
+    // Row strides of the weights (w*) and cotangents (l*): the LDS copies pad
+    // every row by one float, so that lanes reading one column of consecutive
+    // rows hit distinct banks.
+    const int64_t wD = D + (CACHE > 0), wH = Hd + (CACHE > 0);
+    const int64_t lD = D + (CACHE > 1), lH = Hd + (CACHE > 1);
+    const int64_t PP = padded_count<KIND>(D, Hd);
 
     const TIO* q = (const TIO*)a.q + bh * a.T * D;
     const TIO* k = (const TIO*)a.k + bh * a.T * D;
@@ -166,6 +192,18 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 dp[2] = sG;
             }
         }
+        if (CACHE > 0) {  // packed index -> padded (row, column), as in the portable forward
+            for (int64_t p = tid; p < P; p += NT) {
+                const int64_t o = padded_index<KIND>(p, D, Hd);
+                cache[o] = Wc[p];
+                if (CACHE > 1) cache[PP + o] = LW[p];
+                if (CACHE > 1 && mom) cache[2 * PP + o] = LM[p];
+            }
+            __syncthreads();
+        }
+        const float* Wr = CACHE > 0 ? cache : Wc;
+        const float* LWr = CACHE > 1 ? cache + PP : LW;
+        const float* LMr = CACHE > 1 ? cache + 2 * PP : LM;
         for (int64_t b0 = 0; b0 < Cc; b0 += TB) {
             const int nt = (int)min((int64_t)TB, Cc - b0);
             const int64_t tb = t0 + b0;  // first token of the block
@@ -194,11 +232,12 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, r = i % D;
                     float y = 0.f, pm = 0.f, pw = 0.f;
+                    #pragma unroll 4
                     for (int d = 0; d < D; ++d) {
                         const float x = xk[t * D + d];
-                        y += Wc[(int64_t)r * D + d] * x;
-                        pw += LW[(int64_t)r * D + d] * x;
-                        if (mom) pm += LM[(int64_t)r * D + d] * x;
+                        y += Wr[r * wD + d] * x;
+                        pw += LWr[r * lD + d] * x;
+                        if (mom) pm += LMr[r * lD + d] * x;
                     }
                     dy[i] = mse ? y - xv[i] : -xv[i];
                     sM[i] = pm;
@@ -207,6 +246,7 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 __syncthreads();
                 for (int t = tid; t < nt; t += NT) {
                     float gm = 0.f, gw = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
                         gm += sM[t * D + r] * dy[t * D + r];
                         gw += sW[t * D + r] * dy[t * D + r];
@@ -222,9 +262,10 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, d = i % D;
                     float gk = 0.f, gq = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
-                        const float w = Wc[(int64_t)r * D + d];
-                        const float lam = cms[t] * (mom ? LM[(int64_t)r * D + d] : 0.f) - cws[t] * LW[(int64_t)r * D + d];
+                        const float w = Wr[r * wD + d];
+                        const float lam = cms[t] * (mom ? LMr[r * lD + d] : 0.f) - cws[t] * LWr[r * lD + d];
                         gk += lam * dy[t * D + r] + (mse ? w * s[t * D + r] : 0.f);
                         gq += w * xo[t * D + r];
                     }
@@ -235,13 +276,15 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int64_t p = tid; p < P; p += NT) {
                     const int r = (int)(p / D), d = (int)(p % D);
                     float acc = 0.f;
+                    #pragma unroll 4
                     for (int t = 0; t < nt; ++t)
                         acc += (mse ? s[t * D + r] * xk[t * D + d] : 0.f) + xo[t * D + r] * xq[t * D + d];
                     DJ[p] += acc;
                 }
             } else if (KIND == E2TTT_MLP) {
                 // W1 [Hd][D] at 0, W2 [D][Hd] at Hd*D (column vectors)
-                const int64_t o2 = (int64_t)Hd * D;
+                const int64_t o2 = (int64_t)Hd * D;     // packed offset of W2
+                const int64_t w2o = Hd * wD, l2o = Hd * lD;  // ... in the (padded) weights / cotangents
                 float* dy = RD(4);
                 float* gy = RD(5);
                 float* p2M = RD(6);
@@ -256,12 +299,13 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float zz = 0.f, zzq = 0.f, pm = 0.f, pw = 0.f;
+                    #pragma unroll 4
                     for (int d = 0; d < D; ++d) {
-                        const float w1 = Wc[(int64_t)j * D + d];
+                        const float w1 = Wr[j * wD + d];
                         zz += w1 * xk[t * D + d];
                         zzq += w1 * xq[t * D + d];
-                        pw += LW[(int64_t)j * D + d] * xk[t * D + d];
-                        if (mom) pm += LM[(int64_t)j * D + d] * xk[t * D + d];
+                        pw += LWr[j * lD + d] * xk[t * D + d];
+                        if (mom) pm += LMr[j * lD + d] * xk[t * D + d];
                     }
                     z[i] = zz;
                     zq[i] = zzq;
@@ -272,11 +316,12 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, r = i % D;
                     float y = 0.f, pm = 0.f, pw = 0.f;
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
                         const float aj = silu_f(z[t * Hd + j]);
-                        y += Wc[o2 + (int64_t)r * Hd + j] * aj;
-                        pw += LW[o2 + (int64_t)r * Hd + j] * aj;
-                        if (mom) pm += LM[o2 + (int64_t)r * Hd + j] * aj;
+                        y += Wr[w2o + r * wH + j] * aj;
+                        pw += LWr[l2o + r * lH + j] * aj;
+                        if (mom) pm += LMr[l2o + r * lH + j] * aj;
                     }
                     dy[i] = mse ? y - xv[i] : -xv[i];
                     p2M[i] = pm;
@@ -286,8 +331,9 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float ee = 0.f, eq = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
-                        const float w2 = Wc[o2 + (int64_t)r * Hd + j];
+                        const float w2 = Wr[w2o + r * wH + j];
                         ee += w2 * dy[t * D + r];
                         eq += w2 * xo[t * D + r];
                     }
@@ -297,10 +343,12 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 __syncthreads();
                 for (int t = tid; t < nt; t += NT) {
                     float gm = 0.f, gw = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
                         gm += dy[t * D + r] * p2M[t * D + r];
                         gw += dy[t * D + r] * p2W[t * D + r];
                     }
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
                         const float dz = e[t * Hd + j] * dsilu_f(z[t * Hd + j]);
                         gm += dz * p1M[t * Hd + j];
@@ -325,18 +373,20 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {  // Gy = p2 + W2 (silu'(z) p1)
                     const int t = i / D, r = i % D;
                     float acc = p2[i];
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j)
-                        acc += Wc[o2 + (int64_t)r * Hd + j] * dsilu_f(z[t * Hd + j]) * p1[t * Hd + j];
+                        acc += Wr[w2o + r * wH + j] * dsilu_f(z[t * Hd + j]) * p1[t * Hd + j];
                     gy[i] = acc;
                 }
                 __syncthreads();
                 for (int i = tid; i < nt * Hd; i += NT) {  // Ja, Jz
                     const int t = i / Hd, j = i % Hd;
                     float ja = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
-                        const int64_t o = o2 + (int64_t)r * Hd + j;
-                        const float lam = cms[t] * (mom ? LM[o] : 0.f) - cws[t] * LW[o];
-                        ja += lam * dy[t * D + r] + (mse ? Wc[o] * gy[t * D + r] : 0.f);
+                        const int64_t ow = w2o + r * wH + j, ol = l2o + r * lH + j;
+                        const float lam = cms[t] * (mom ? LMr[ol] : 0.f) - cws[t] * LWr[ol];
+                        ja += lam * dy[t * D + r] + (mse ? Wr[ow] * gy[t * D + r] : 0.f);
                     }
                     const float zz = z[i];
                     jz[i] = e[i] * p1[i] * d2silu_f(zz) + ja * dsilu_f(zz);
@@ -345,12 +395,13 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, d = i % D;
                     float gk = 0.f, gq = 0.f;
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
-                        const int64_t o = (int64_t)j * D + d;
+                        const int64_t ow = j * wD + d, ol = j * lD + d;
                         const float dz = e[t * Hd + j] * dsilu_f(z[t * Hd + j]);
-                        const float lam = cms[t] * (mom ? LM[o] : 0.f) - cws[t] * LW[o];
-                        gk += lam * dz + Wc[o] * jz[t * Hd + j];
-                        gq += Wc[o] * dzq[t * Hd + j];
+                        const float lam = cms[t] * (mom ? LMr[ol] : 0.f) - cws[t] * LWr[ol];
+                        gk += lam * dz + Wr[ow] * jz[t * Hd + j];
+                        gq += Wr[ow] * dzq[t * Hd + j];
                     }
                     st(dk, tb * D + i, gk);
                     st(dv, tb * D + i, -gy[i]);
@@ -360,9 +411,11 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                     float acc = 0.f;
                     if (p < o2) {
                         const int j = (int)(p / D), d = (int)(p % D);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) acc += jz[t * Hd + j] * xk[t * D + d] + dzq[t * Hd + j] * xq[t * D + d];
                     } else {
                         const int r = (int)((p - o2) / Hd), j = (int)((p - o2) % Hd);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const float zz = z[t * Hd + j];
                             acc += dy[t * D + r] * dsilu_f(zz) * p1[t * Hd + j] + xo[t * D + r] * silu_f(zq[t * Hd + j]) +
@@ -373,7 +426,8 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 }
             } else {
                 // W1, W3 [D][Hd] at 0, D*Hd; W2 [Hd][D] at 2*D*Hd (row vectors)
-                const int64_t o3 = (int64_t)D * Hd, o2 = 2 * (int64_t)D * Hd;
+                const int64_t o3 = (int64_t)D * Hd, o2 = 2 * (int64_t)D * Hd;  // packed offsets of W3, W2
+                const int64_t w3o = D * wH, w2o = 2 * D * wH, l3o = D * lH, l2o = 2 * D * lH;
                 float* dy = RD(4);
                 float* gy = RD(5);
                 float* h1 = RH(0);
@@ -392,18 +446,19 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float a1 = 0.f, a3 = 0.f, q1 = 0.f, q3 = 0.f, m1 = 0.f, w1 = 0.f, m3 = 0.f, w3 = 0.f;
+                    #pragma unroll 4
                     for (int d = 0; d < D; ++d) {
-                        const int64_t o = (int64_t)d * Hd + j;
+                        const int64_t ow = d * wH + j, ol = d * lH + j;
                         const float x = xk[t * D + d], y = xq[t * D + d];
-                        a1 += x * Wc[o];
-                        a3 += x * Wc[o3 + o];
-                        q1 += y * Wc[o];
-                        q3 += y * Wc[o3 + o];
-                        w1 += x * LW[o];
-                        w3 += x * LW[o3 + o];
+                        a1 += x * Wr[ow];
+                        a3 += x * Wr[w3o + ow];
+                        q1 += y * Wr[ow];
+                        q3 += y * Wr[w3o + ow];
+                        w1 += x * LWr[ol];
+                        w3 += x * LWr[l3o + ol];
                         if (mom) {
-                            m1 += x * LM[o];
-                            m3 += x * LM[o3 + o];
+                            m1 += x * LMr[ol];
+                            m3 += x * LMr[l3o + ol];
                         }
                     }
                     h1[i] = a1;
@@ -420,21 +475,23 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                     const int t = i / D, r = i % D;
                     float y = 0.f;
                     if (mse)
+                        #pragma unroll 4
                         for (int j = 0; j < Hd; ++j)
-                            y += silu_f(h1[t * Hd + j]) * h3[t * Hd + j] * Wc[o2 + (int64_t)j * D + r];
+                            y += silu_f(h1[t * Hd + j]) * h3[t * Hd + j] * Wr[w2o + j * wD + r];
                     dy[i] = mse ? y - xv[i] : -xv[i];
                 }
                 __syncthreads();
                 for (int i = tid; i < nt * Hd; i += NT) {
                     const int t = i / Hd, j = i % Hd;
                     float u_ = 0.f, qm = 0.f, qw = 0.f, ho = 0.f;
+                    #pragma unroll 4
                     for (int r = 0; r < D; ++r) {
-                        const int64_t o = o2 + (int64_t)j * D + r;
+                        const int64_t ow = w2o + j * wD + r, ol = l2o + j * lD + r;
                         const float g = dy[t * D + r];
-                        u_ += g * Wc[o];
-                        qw += LW[o] * g;
-                        if (mom) qm += LM[o] * g;
-                        ho += xo[t * D + r] * Wc[o];
+                        u_ += g * Wr[ow];
+                        qw += LWr[ol] * g;
+                        if (mom) qm += LMr[ol] * g;
+                        ho += xo[t * D + r] * Wr[ow];
                     }
                     du[i] = u_;
                     Q2[i] = qm;
@@ -444,6 +501,7 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 __syncthreads();
                 for (int t = tid; t < nt; t += NT) {
                     float gm = 0.f, gw = 0.f;
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
                         const int i = t * Hd + j;
                         const float x1 = h1[i], x3 = h3[i];
@@ -470,10 +528,11 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {  // Gy = u Lam2 + E W2
                     const int t = i / D, r = i % D;
                     float acc = 0.f;
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
-                        const int64_t o = o2 + (int64_t)j * D + r;
-                        const float lam = cms[t] * (mom ? LM[o] : 0.f) - cws[t] * LW[o];
-                        acc += silu_f(h1[t * Hd + j]) * h3[t * Hd + j] * lam + E[t * Hd + j] * Wc[o];
+                        const int64_t ow = w2o + j * wD + r, ol = l2o + j * lD + r;
+                        const float lam = cms[t] * (mom ? LMr[ol] : 0.f) - cws[t] * LWr[ol];
+                        acc += silu_f(h1[t * Hd + j]) * h3[t * Hd + j] * lam + E[t * Hd + j] * Wr[ow];
                     }
                     gy[i] = acc;
                 }
@@ -482,7 +541,8 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                     const int t = i / Hd, j = i % Hd;
                     float ju = Q2[i];
                     if (mse)
-                        for (int r = 0; r < D; ++r) ju += gy[t * D + r] * Wc[o2 + (int64_t)j * D + r];
+                        #pragma unroll 4
+                        for (int r = 0; r < D; ++r) ju += gy[t * D + r] * Wr[w2o + j * wD + r];
                     const float x1 = h1[i], x3 = h3[i];
                     const float s1 = dsilu_f(x1), s2 = d2silu_f(x1), act = silu_f(x1);
                     Ju[i] = ju;
@@ -493,16 +553,17 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                 for (int i = tid; i < nt * D; i += NT) {
                     const int t = i / D, d = i % D;
                     float gk = 0.f, gq = 0.f;
+                    #pragma unroll 4
                     for (int j = 0; j < Hd; ++j) {
-                        const int64_t o = (int64_t)d * Hd + j;
+                        const int64_t ow = d * wH + j, ol = d * lH + j;
                         const int h = t * Hd + j;
                         const float x1 = h1[h], x3 = h3[h];
                         const float dh1 = du[h] * x3 * dsilu_f(x1), dh3 = du[h] * silu_f(x1);
-                        const float l1 = cms[t] * (mom ? LM[o] : 0.f) - cws[t] * LW[o];
-                        const float l3 = cms[t] * (mom ? LM[o3 + o] : 0.f) - cws[t] * LW[o3 + o];
-                        gk += Jh1[h] * Wc[o] + Jh3[h] * Wc[o3 + o] + dh1 * l1 + dh3 * l3;
+                        const float l1 = cms[t] * (mom ? LMr[ol] : 0.f) - cws[t] * LWr[ol];
+                        const float l3 = cms[t] * (mom ? LMr[l3o + ol] : 0.f) - cws[t] * LWr[l3o + ol];
+                        gk += Jh1[h] * Wr[ow] + Jh3[h] * Wr[w3o + ow] + dh1 * l1 + dh3 * l3;
                         const float y1 = hq1[h], y3 = hq3[h];
-                        gq += hdo[h] * y3 * dsilu_f(y1) * Wc[o] + hdo[h] * silu_f(y1) * Wc[o3 + o];
+                        gq += hdo[h] * y3 * dsilu_f(y1) * Wr[ow] + hdo[h] * silu_f(y1) * Wr[w3o + ow];
                     }
                     st(dk, tb * D + i, gk);
                     st(dv, tb * D + i, -gy[i]);
@@ -514,6 +575,7 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                         const bool three = p >= o3;
                         const int64_t pp = three ? p - o3 : p;
                         const int d = (int)(pp / Hd), j = (int)(pp % Hd);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const int h = t * Hd + j;
                             const float y1 = hq1[h], y3 = hq3[h];
@@ -522,6 +584,7 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
                         }
                     } else {
                         const int j = (int)((p - o2) / D), r = (int)((p - o2) % D);
+                        #pragma unroll 4
                         for (int t = 0; t < nt; ++t) {
                             const int h = t * Hd + j;
                             const float u_ = silu_f(h1[h]) * h3[h];
@@ -546,15 +609,32 @@ __global__ __launch_bounds__(NT) void generic_bwd_kernel(GBwdArgs a) {
     }
 }
 
-template <int KIND>
-hipError_t launch_bwd_kind(const e2ttt_desc& d, const GBwdArgs& a, size_t shmem, hipStream_t s) {
-    const unsigned grid = (unsigned)(d.B * d.H);
-    if (d.io_dtype == E2TTT_BF16)
-        hipLaunchKernelGGL((generic_bwd_kernel<KIND, __bf16>), dim3(grid), dim3(NT), shmem, s, a);
-    else
-        hipLaunchKernelGGL((generic_bwd_kernel<KIND, float>), dim3(grid), dim3(NT), shmem, s, a);
+template <int KIND, typename TIO, int CACHE>
+hipError_t launch_bwd_one(const e2ttt_desc& d, const GBwdArgs& a, size_t shmem, hipStream_t s) {
+    const void* f = (const void*)generic_bwd_kernel<KIND, TIO, CACHE>;
+    if (shmem > 64 * 1024 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((generic_bwd_kernel<KIND, TIO, CACHE>), dim3((unsigned)(d.B * d.H)), dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
+
+template <int KIND, typename TIO>
+hipError_t launch_bwd_cache(const e2ttt_desc& d, const GBwdArgs& a, int cache, size_t shmem, hipStream_t s) {
+    switch (cache) {
+        case 2: return launch_bwd_one<KIND, TIO, 2>(d, a, shmem, s);
+        case 1: return launch_bwd_one<KIND, TIO, 1>(d, a, shmem, s);
+        default: return launch_bwd_one<KIND, TIO, 0>(d, a, shmem, s);
+    }
+}
+
+template <int KIND>
+hipError_t launch_bwd_kind(const e2ttt_desc& d, const GBwdArgs& a, int cache, size_t shmem, hipStream_t s) {
+    if (d.io_dtype == E2TTT_BF16) return launch_bwd_cache<KIND, __bf16>(d, a, cache, shmem, s);
+    return launch_bwd_cache<KIND, float>(d, a, cache, shmem, s);
+}
+
+// LDS the portable kernels may use per workgroup (of gfx950's 160 KB)
+constexpr size_t kLdsBudget = 144 * 1024;
 
 int floats_per_token(const e2ttt_desc& d) {
     const int64_t Hd = d.kind == E2TTT_LINEAR ? 0 : d.Hd;
@@ -602,12 +682,28 @@ hipError_t launch_generic_backward(const e2ttt_desc& d, const GenericBwdBuffers&
     a.dcM = b.dcM;
     a.dcW = b.dcW;
     a.dpart = b.dpart;
-    const size_t shmem = (size_t)floats_per_token(d) * a.TB * sizeof(float);
+    size_t shmem = (size_t)floats_per_token(d) * a.TB * sizeof(float);
+    // cache as many of W_c, lW, lM as fit next to the token rows (a smaller
+    // token block would cost more than the cache saves: every block re-reads
+    // and re-writes the dJ/dW accumulators)
+    const int64_t Hd0 = d.kind == E2TTT_LINEAR ? 0 : d.Hd;
+    const int64_t PP = d.kind == E2TTT_LINEAR ? padded_count<E2TTT_LINEAR>(d.D, Hd0)
+                       : d.kind == E2TTT_MLP  ? padded_count<E2TTT_MLP>(d.D, Hd0)
+                                              : padded_count<E2TTT_SWIGLU>(d.D, Hd0);
+    int cache = 0;
+    for (int c = 2; c >= 1 && cache == 0; --c) {
+        const int arrays = c == 1 ? 1 : (a.mom ? 3 : 2);  // W_c; or W_c, lW (and lM)
+        const size_t need = ((size_t)floats_per_token(d) * a.TB + (size_t)arrays * PP) * sizeof(float);
+        if (need <= kLdsBudget) {
+            cache = c;
+            shmem = need;
+        }
+    }
     hipError_t e;
     switch (d.kind) {
-        case E2TTT_LINEAR: e = launch_bwd_kind<E2TTT_LINEAR>(d, a, shmem, s); break;
-        case E2TTT_MLP: e = launch_bwd_kind<E2TTT_MLP>(d, a, shmem, s); break;
-        default: e = launch_bwd_kind<E2TTT_SWIGLU>(d, a, shmem, s); break;
+        case E2TTT_LINEAR: e = launch_bwd_kind<E2TTT_LINEAR>(d, a, cache, shmem, s); break;
+        case E2TTT_MLP: e = launch_bwd_kind<E2TTT_MLP>(d, a, cache, shmem, s); break;
+        default: e = launch_bwd_kind<E2TTT_SWIGLU>(d, a, cache, shmem, s); break;
     }
     if (e != hipSuccess) return e;
     return launch_bwd_scalar(d, b.eta, b.alpha, b.beta, b.dcM, b.dcW, b.ldc, b.dpart, 1, b.deta, b.dalpha, b.dbeta,
