@@ -25,6 +25,7 @@ def _gpu(cfg, x, c, force_generic=False):
     import chunk_weight_rnn_amd as e2
     d = {n: t.cuda() for n, t in x.items()}
     dc = {n: t.cuda() for n, t in c.items()}
+    note(f"  gpu backward {cfg.name}: B={cfg.B} H={cfg.H} T={cfg.T} C={cfg.chunk} flags={cfg.flags}")
     g = e2.chunk_backward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
                           dc["dout"], dc["dW_end"], dc["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd, kind=cfg.kind,
                           loss=cfg.loss, momentum=cfg.momentum, chunk_avg=cfg.chunk_avg,
@@ -107,3 +108,59 @@ def test_backward_deterministic():
     for n in a:
         if a[n] is not None:
             assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 64), (63, 64), (64, 128), (130, 2048)], ids=lambda v: str(v))
+def test_backward_short_sequences(T, chunk):
+    """Sequences shorter than a block or than the chunk (one ragged chunk)."""
+    cfg = SMALL.with_(T=T, chunk=chunk, name=f"bwd_short_T{T}_C{chunk}")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=6, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=7)
+    _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
+def test_backward_empty_sequence_passes_state_through():
+    """T == 0: the state cotangents pass through unchanged; the others are empty."""
+    import chunk_weight_rnn_amd as e2
+    cfg = SMALL.with_(T=0, name="bwd_T0")
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=8, m0_scale=0.5).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=9).items()}
+    g = e2.chunk_backward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], c["dout"],
+                          c["dW_end"], c["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd)
+    torch.cuda.synchronize()
+    assert torch.equal(g["W0"], c["dW_end"]) and torch.equal(g["M0"], c["dM_end"])
+    assert g["q"].numel() == 0 and g["eta"].numel() == 0
+
+
+def test_backward_empty_batch():
+    import chunk_weight_rnn_amd as e2
+    cfg = SMALL.with_(B=0, name="bwd_B0")
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=8).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=9).items()}
+    g = e2.chunk_backward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], c["dout"],
+                          c["dW_end"], c["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd)
+    torch.cuda.synchronize()
+    assert all(t is None or t.numel() == 0 for t in g.values())
+
+
+def test_backward_rejects_aliased_output():
+    """An output that overlaps an input is refused before any launch."""
+    import chunk_weight_rnn_amd as e2
+    from chunk_weight_rnn_amd._lib import make_desc
+    import ctypes
+    cfg = SMALL
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=8).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=9).items()}
+    lib = e2.library()
+    d = make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
+    ws = torch.empty(int(lib.e2ttt_backward_workspace_size(ctypes.byref(d))), dtype=torch.uint8, device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    out = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")}
+    args = [p(x[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")] + \
+           [p(c["dout"]), p(c["dW_end"]), p(c["dM_end"])]
+    outs = [p(out[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")]
+    outs[6] = p(x["W0"])  # dW0 written over W0
+    st = lib.e2ttt_chunk_backward(ctypes.byref(d), *args, *outs, p(ws), ctypes.c_size_t(ws.numel()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 3
