@@ -96,10 +96,16 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 
 __device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-// 16-byte chunk swizzle of 256-byte rows: logical chunk c of row t sits at
-// physical chunk c ^ swz4(t) (a bijection of 0..15 in t, so 16 consecutive
-// rows read at one logical chunk cover all 64 banks).
-__device__ __forceinline__ int swz4(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
+// 16-byte chunk swizzles of 256-byte LDS rows: logical chunk c of row t sits
+// at physical chunk c ^ swz(t).  Each is a bijection of 0..15, so 16
+// consecutive rows read at one logical chunk (ds_read_b128, 16 lanes per
+// cycle) cover all 64 banks.  The transpose read serves 32 lanes per cycle:
+// 8 rows, each at the aligned chunk pair {2n, 2n+1}, which lands on the pair
+// n ^ (swz(t) >> 1); so swz(t) >> 1 must differ across the 8 rows of a cycle.
+//   swz_u: hidden-unit stage, rows 0..7 and 8..15 per cycle;
+//   swz_t: token stage, rows {0..3, 8..11} and {4..7, 12..15} per cycle.
+__device__ __forceinline__ int swz_u(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
+__device__ __forceinline__ int swz_t(int t) { return ((t & 3) << 1) | (t & 8) | ((t >> 2) & 1); }
 
 // (base and size must be the same in every lane; the words are read from
 // the first lane so that the descriptor lives in scalar registers)
@@ -163,7 +169,7 @@ __device__ __forceinline__ bf16x4 tr_units(const unsigned char* stage, int lane,
     const int p = lane & 15, g = lane >> 4;
     const int row = 4 * g + (p >> 2);
     const int q = p & 3;
-    const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz4(row)) + 8 * (q & 1);
+    const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz_u(row)) + 8 * (q & 1);
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
 }
 
@@ -176,7 +182,7 @@ __device__ __forceinline__ bf16x8 tr_tokens(const unsigned char* stage, int lane
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int row = 8 * g + 4 * h + (p >> 2);
-        const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz4(row & 15)) + 8 * (q & 1);
+        const unsigned char* a = stage + row * ROWB + 16 * ((2 * n + (q >> 1)) ^ swz_t(row & 15)) + 8 * (q & 1);
         const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[4 * h + e] = v[e];
@@ -230,13 +236,13 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
             const int mi = ii >> 2, rq = ii & 3;
             const int row = 4 * rq + (ln >> 4);
             const unsigned off = (unsigned)((mi < 3 ? mi : mi - 3) * Hd * D + (j0 + row) * D) * 2u +
-                                 16u * (unsigned)((ln & 15) ^ swz4(row));
+                                 16u * (unsigned)((ln & 15) ^ swz_u(row));
             copy16(mi < 3 ? wrs : lrs, stage_lds + (unsigned)((b * NMAT + mi) * STEPB + 4 * rq * ROWB), off);
         }
     };
     // A fragment of a projection: row j0 + tl of matrix mi, d = 32 kk + 8 g .. +7
     auto afrag = [&](const unsigned char* sb, int mi, int kk) {
-        return *(const bf16x8*)(sb + mi * STEPB + tl * ROWB + 16 * ((4 * kk + g) ^ swz4(tl)));
+        return *(const bf16x8*)(sb + mi * STEPB + tl * ROWB + 16 * ((4 * kk + g) ^ swz_u(tl)));
     };
     auto load_tok = [&](const __bf16* X, bf16x8 (&f)[4]) {
         const __bf16* row = X + (bh * T + (tin ? t : 0)) * D + 8 * g;
@@ -465,7 +471,7 @@ __global__ void __launch_bounds__(NT) bwd_wt_kernel(WtArgs a) {
         for (int x8 = 0; x8 < 8; ++x8) {
             const int mat = x8 >> 1, rq = 4 * (x8 & 1) + w;  // (matrix index stays compile-time)
             const int row = 4 * rq + (ln >> 4);
-            const unsigned off = (unsigned)((tbase + KT * s + row) * D) * 2u + 16u * (unsigned)((ln & 15) ^ swz4(row & 15));
+            const unsigned off = (unsigned)((tbase + KT * s + row) * D) * 2u + 16u * (unsigned)((ln & 15) ^ swz_t(row & 15));
             copy16(rs[mat], stage_lds + (unsigned)((b * 4 + mat) * KTB + 4 * rq * ROWB), off);
         }
     };
