@@ -264,8 +264,10 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
 }  // namespace
 
 bool swiglu_mfma_supported(const e2ttt_desc& d) {
+    // the chunk loop addresses each head's K / V rows through 32-bit buffer
+    // offsets, so one head's rows must stay below 2 GiB (T < 8M tokens)
     return d.kind == E2TTT_SWIGLU && d.loss == E2TTT_LOSS_NEGDOT && d.io_dtype == E2TTT_BF16 && d.D == D &&
-           d.Hd >= S && d.Hd % S == 0 && d.Hd <= 4096 && d.chunk % CB == 0;
+           d.Hd >= S && d.Hd % S == 0 && d.Hd <= 4096 && d.chunk % CB == 0 && d.T * D * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,

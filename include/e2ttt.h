@@ -99,7 +99,9 @@ E2TTT_API int64_t e2ttt_param_count(const e2ttt_desc* desc);
 E2TTT_API size_t e2ttt_workspace_size(const e2ttt_desc* desc);
 
 /* Which device path e2ttt_chunk_forward takes: 0 = portable fp32 kernel,
- * 1 = SwiGLU bf16 MFMA path; negative e2ttt_status for a bad desc. */
+ * 1 = SwiGLU bf16 MFMA path (SWIGLU, LOSS_NEGDOT, BF16, D == 128, Hd a
+ * multiple of 64 up to 4096, chunk a multiple of 64, T * D * 2 < 2^31);
+ * negative e2ttt_status for a bad desc. */
 E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
 
 /*

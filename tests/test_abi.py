@@ -255,3 +255,11 @@ def test_backward_validation(lib):
     assert lib.e2ttt_chunk_backward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 4
     bad = _desc(chunk=4096, T=8192)
     assert lib.e2ttt_chunk_backward(ctypes.byref(bad), *args, v(0), ctypes.c_size_t(0), v(0)) == 2
+
+
+def test_very_long_sequences_take_the_portable_path(lib):
+    """One head's K/V rows beyond 2 GiB leave the MFMA path (32-bit buffer offsets)."""
+    d = _desc(B=1, H=1, T=(1 << 23) - 64)
+    assert lib.e2ttt_path(ctypes.byref(d)) == 1
+    d = _desc(B=1, H=1, T=1 << 23)
+    assert lib.e2ttt_path(ctypes.byref(d)) == 0
