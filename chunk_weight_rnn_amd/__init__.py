@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, make_desc
 
-__all__ = ["chunk_forward", "chunk_backward", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
+__all__ = ["chunk_forward", "chunk_backward", "chunk_update", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
 
 
@@ -207,3 +207,43 @@ def logscan(eta, alpha, beta, *, chunk: int, momentum: bool = True, chunk_avg: b
     if st != 0:
         raise E2TTTError("e2ttt_logscan", st)
     return cM, cW, scal
+
+
+class _ChunkUpdate(torch.autograd.Function):
+    """chunk_forward with chunk_backward as its derivative (both through the C ABI)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, momentum, chunk_avg):
+        out, W, M = chunk_forward(q, k, v, eta, alpha, beta, W0, M0, chunk=chunk, kind=kind, loss=loss, Hd=Hd,
+                                  momentum=momentum, chunk_avg=chunk_avg)
+        ctx.save_for_backward(q, k, v, eta, alpha, beta, W0, M0)
+        ctx.opts = (chunk, kind, loss, Hd, momentum, chunk_avg)
+        if M is None:
+            M = torch.zeros_like(W0)  # no momentum: a placeholder output with no gradient path
+        return out, W, M
+
+    @staticmethod
+    def backward(ctx, dout, dW, dM):
+        q, k, v, eta, alpha, beta, W0, M0 = ctx.saved_tensors
+        chunk, kind, loss, Hd, momentum, chunk_avg = ctx.opts
+        dout = torch.zeros_like(q) if dout is None else dout.to(q.dtype).contiguous()
+        dW = torch.zeros_like(W0) if dW is None else dW.contiguous()
+        dM = (torch.zeros_like(W0) if dM is None else dM.contiguous()) if momentum else None
+        g = chunk_backward(q, k, v, eta, alpha, beta if momentum else None, W0, M0 if momentum else None, dout, dW, dM,
+                           chunk=chunk, Hd=Hd, kind=kind, loss=loss, momentum=momentum, chunk_avg=chunk_avg)
+        return (g["q"], g["k"], g["v"], g["eta"], g["alpha"], g["beta"], g["W0"], g["M0"],
+                None, None, None, None, None, None)
+
+
+def chunk_update(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str = "swiglu", loss: str = "negdot",
+                 Hd: int = 0, momentum: bool = True, chunk_avg: bool = False):
+    """The chunk update as a differentiable PyTorch op: (out, W_end, M_end),
+    with gradients for every input from ``chunk_backward``.  Without
+    momentum, beta and M0 may be None and M_end is None."""
+    if not momentum:
+        beta = M0 = None
+        dummy = torch.zeros((), device=q.device)  # keeps the argument list tensor-typed
+        out, W, _ = _ChunkUpdate.apply(q, k, v, eta, alpha, dummy, W0, dummy, chunk, kind, loss, Hd, False,
+                                       chunk_avg)
+        return out, W, None
+    return _ChunkUpdate.apply(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, True, chunk_avg)

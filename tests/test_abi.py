@@ -263,3 +263,11 @@ def test_very_long_sequences_take_the_portable_path(lib):
     assert lib.e2ttt_path(ctypes.byref(d)) == 1
     d = _desc(B=1, H=1, T=1 << 23)
     assert lib.e2ttt_path(ctypes.byref(d)) == 0
+
+
+def test_chunk_update_refuses_cpu_tensors(lib):
+    import chunk_weight_rnn_amd as e2
+    x = synth.make_inputs(synth.CONFIGS["tiny_linear"])
+    with pytest.raises(ValueError):
+        e2.chunk_update(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], chunk=16,
+                        kind="linear", loss="mse")
