@@ -10,7 +10,9 @@ every (batch, head)), inputs resident in HBM.  Prints one JSON line.
 
 With --backward one step is one e2ttt_chunk_backward call instead (forward
 recompute, reverse chunk loop, scalar-kernel backward): the gradients of a
-training step for the same workload.
+training step for the same workload.  With --train one step is a training
+step: e2ttt_chunk_forward with E2TTT_FLAG_SAVE_STATES, then
+e2ttt_chunk_backward on the same workspace (no recompute).
 """
 from __future__ import annotations
 
@@ -206,6 +208,67 @@ def run_backward(args, cfg, lib, e2, torch) -> dict:
     return res
 
 
+def run_train(args, cfg, lib, e2, torch) -> dict:
+    """Time forward (saving states) + backward (from them) on the workload."""
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=1).items()}
+    g = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")}
+    out, W, M = torch.empty_like(x["q"]), torch.empty_like(x["W0"]), torch.empty_like(x["M0"])
+    desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk,
+                             cfg.flags | e2._lib.FLAG_SAVE_STATES)
+    ws_bytes = int(lib.e2ttt_backward_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    hev = HipEvents(8 * max(args.steps, 1))
+    ins = [p(x[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")]
+
+    def step(i=None):
+        ef = eb = None
+        if i is not None:
+            ef = (ctypes.c_void_p * 4)(*hev.ev[8 * i:8 * i + 4])
+            eb = (ctypes.c_void_p * 4)(*hev.ev[8 * i + 4:8 * i + 8])
+        st = lib.e2ttt_chunk_forward_events(ctypes.byref(desc), *ins, p(out), p(W), p(M), p(ws),
+                                            ctypes.c_size_t(ws_bytes), hs, ef)
+        if st != 0:
+            raise e2.E2TTTError("e2ttt_chunk_forward_events", st)
+        st = lib.e2ttt_chunk_backward_events(
+            ctypes.byref(desc), *ins, p(c["dout"]), p(c["dW_end"]), p(c["dM_end"]),
+            *[p(g[n]) for n in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")], p(ws),
+            ctypes.c_size_t(ws_bytes), hs, eb)
+        if st != 0:
+            raise e2.E2TTTError("e2ttt_chunk_backward_events", st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    fw = [hev.elapsed_ms(hev.ev[8 * i], hev.ev[8 * i + 3]) for i in range(args.steps)]
+    bw = [hev.elapsed_ms(hev.ev[8 * i + 4], hev.ev[8 * i + 7]) for i in range(args.steps)]
+    th = cfg.B * cfg.H * cfg.T
+    f_fwd = sum(flops_per_token_head(cfg).values())
+    fb = bwd_flops_per_token_head(cfg)
+    f_bwd = fb["token"] + fb["weight"]
+    tflops = (f_fwd + f_bwd) * th / (ms_step * 1e-3) / 1e12
+    return {
+        "metric": "E2-TTT chunk-update training step (forward + backward) tokens/sec at 1 GPU",
+        "value": cfg.B * cfg.T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.io_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.notes}, forward + backward", "kind": cfg.kind, "loss": cfg.loss,
+                   "B": cfg.B, "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk,
+                   "io": cfg.io_dtype, "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg},
+        "whole_step": {"tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+                       "flop_model": f"forward {f_fwd} + backward (token and weight kernels) {f_bwd} flop per "
+                                     f"token and head"},
+        "stages_ms": {"forward": sum(fw) / len(fw), "backward": sum(bw) / len(bw)},
+    }
+
+
 def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole batch
     rows (every head of one sequence), cycling over the batch until about
@@ -242,6 +305,8 @@ def main() -> int:
     ap.add_argument("--config", default="swiglu_1p3b", choices=list(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: forward saving states, then backward from them")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MiB",
                     help="first run a plain fp32 copy kernel over MiB of data (3 launches), so that a counter "
@@ -269,6 +334,9 @@ def main() -> int:
     cfg = synth.CONFIGS[args.config]
     if args.backward:
         print(json.dumps(run_backward(args, cfg, lib, e2, torch)), flush=True)
+        return 0
+    if args.train:
+        print(json.dumps(run_train(args, cfg, lib, e2, torch)), flush=True)
         return 0
     x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=0).items()}
     out = torch.empty_like(x["q"])

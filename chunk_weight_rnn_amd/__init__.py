@@ -22,9 +22,9 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, make_desc
+from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, FLAG_SAVE_STATES, make_desc
 
-__all__ = ["chunk_forward", "chunk_backward", "chunk_update", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
+__all__ = ["chunk_forward", "chunk_backward", "chunk_update", "training_workspace", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
 
 
@@ -70,16 +70,34 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def training_workspace(q, *, chunk: int, kind: str = "swiglu", loss: str = "negdot", Hd: int = 0,
+                       momentum: bool = True, chunk_avg: bool = False, force_generic: bool = False):
+    """A workspace shared by chunk_forward(save_states=True) and the
+    chunk_backward(saved=True) that follows it (uint8 tensor on q's device)."""
+    B, H, T, D = q.shape
+    flags = FLAG_SAVE_STATES | (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0) | \
+        (FLAG_FORCE_GENERIC if force_generic else 0)
+    d = make_desc(kind, loss, _io_name(q), B, H, T, D, Hd, chunk, flags)
+    n = library().e2ttt_backward_workspace_size(ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise E2TTTError("e2ttt_backward_workspace_size", 1)
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=q.device)
+
+
 def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
                   out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False,
-                  momentum: bool = True, chunk_avg: bool = False, stream=None):
+                  momentum: bool = True, chunk_avg: bool = False, save_states: bool = False, stream=None):
     """Run the chunk update; returns (out, W_end, M_end).
 
     q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
     eta, alpha, beta: [B, H, T] float32; W0, M0: [B, H, P] float32.
     ``W_end=W0`` / ``M_end=M0`` update the state in place.  With
     ``momentum=False`` beta and M0 are ignored (may be None) and M_end is None.
+    ``save_states`` keeps in ``workspace`` (from training_workspace, required)
+    what chunk_backward(saved=True) needs, so that it skips its recompute.
     """
+    if save_states and workspace is None:
+        raise ValueError("save_states needs the shared workspace from training_workspace()")
     lib = library()
     if not momentum:
         beta = M0 = None
@@ -100,7 +118,7 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
             raise TypeError(f"{name} must be float32")
     B, H, T, D = q.shape
     flags = (FLAG_FORCE_GENERIC if force_generic else 0) | (0 if momentum else FLAG_NO_MOMENTUM) | \
-        (FLAG_CHUNK_AVG if chunk_avg else 0)
+        (FLAG_CHUNK_AVG if chunk_avg else 0) | (FLAG_SAVE_STATES if save_states else 0)
     desc = make_desc(kind, loss, io, B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
     if tuple(W0.shape) != (B, H, P) or (M0 is not None and tuple(M0.shape) != (B, H, P)):
@@ -130,12 +148,16 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
 
 def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, chunk: int, Hd: int,
                    kind: str = "swiglu", loss: str = "negdot", momentum: bool = True, chunk_avg: bool = False,
-                   force_generic: bool = False, workspace=None, stream=None):
+                   force_generic: bool = False, workspace=None, saved: bool = False, stream=None):
     """Gradients of <dout, out> + <dW_end, W_end> + <dM_end, M_end> through
     ``chunk_forward``; returns a dict with keys q, k, v (the I/O dtype), eta,
     alpha, beta, W0, M0 (float32).  Without momentum beta, M0 and dM_end are
     ignored and the beta / M0 gradients are None.  ``force_generic`` takes the
-    portable fp32 backward where the SwiGLU MFMA one applies."""
+    portable fp32 backward where the SwiGLU MFMA one applies.  ``saved``:
+    ``workspace`` holds the states a chunk_forward(save_states=True) call on
+    the same inputs left in it; the forward is then not recomputed."""
+    if saved and workspace is None:
+        raise ValueError("saved=True needs the workspace the forward call filled")
     lib = library()
     if not momentum:
         beta = M0 = dM_end = None
@@ -154,7 +176,7 @@ def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, c
             raise TypeError(f"{name} must be {want}")
     B, H, T, D = q.shape
     flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0) | \
-        (FLAG_FORCE_GENERIC if force_generic else 0)
+        (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_SAVE_STATES if saved else 0)
     desc = make_desc(kind, loss, _io_name(q), B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
     for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("dout", dout, q.shape),
@@ -214,9 +236,12 @@ class _ChunkUpdate(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, momentum, chunk_avg):
+        ws = training_workspace(q, chunk=chunk, kind=kind, loss=loss, Hd=Hd, momentum=momentum,
+                                chunk_avg=chunk_avg)
         out, W, M = chunk_forward(q, k, v, eta, alpha, beta, W0, M0, chunk=chunk, kind=kind, loss=loss, Hd=Hd,
-                                  momentum=momentum, chunk_avg=chunk_avg)
+                                  momentum=momentum, chunk_avg=chunk_avg, workspace=ws, save_states=True)
         ctx.save_for_backward(q, k, v, eta, alpha, beta, W0, M0)
+        ctx.ws = ws  # the chunk-start states for the backward
         ctx.opts = (chunk, kind, loss, Hd, momentum, chunk_avg)
         if M is None:
             M = torch.zeros_like(W0)  # no momentum: a placeholder output with no gradient path
@@ -230,7 +255,9 @@ class _ChunkUpdate(torch.autograd.Function):
         dW = torch.zeros_like(W0) if dW is None else dW.contiguous()
         dM = (torch.zeros_like(W0) if dM is None else dM.contiguous()) if momentum else None
         g = chunk_backward(q, k, v, eta, alpha, beta if momentum else None, W0, M0 if momentum else None, dout, dW, dM,
-                           chunk=chunk, Hd=Hd, kind=kind, loss=loss, momentum=momentum, chunk_avg=chunk_avg)
+                           chunk=chunk, Hd=Hd, kind=kind, loss=loss, momentum=momentum, chunk_avg=chunk_avg,
+                           workspace=ctx.ws, saved=True)
+        ctx.ws = None
         return (g["q"], g["k"], g["v"], g["eta"], g["alpha"], g["beta"], g["W0"], g["M0"],
                 None, None, None, None, None, None)
 

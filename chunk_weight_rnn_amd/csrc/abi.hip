@@ -14,7 +14,9 @@ static bool desc_ok(const e2ttt_desc* d) {
     if (d->io_dtype < E2TTT_F32 || d->io_dtype > E2TTT_BF16) return false;
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->D < 1 || d->chunk < 1) return false;
     if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
-    if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG)) return false;
+    if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG |
+                     E2TTT_FLAG_SAVE_STATES))
+        return false;
     // keep every product used for indexing far from int64 overflow
     const int64_t lim = (int64_t)1 << 40;
     if (d->B > lim || d->H > lim || d->T > lim || d->D > 65536 || d->Hd > 65536) return false;
@@ -32,37 +34,6 @@ static bool generic_supported(const e2ttt_desc& d) {
     if (d.kind != E2TTT_LINEAR && d.Hd > 1024) return false;
     return true;
 }
-
-Workspace workspace_layout(const e2ttt_desc& d, int path) {
-    Workspace w{};
-    const size_t BH = (size_t)(d.B * d.H);
-    const size_t T = (size_t)d.T;
-    const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
-    const size_t P = (size_t)e2ttt_param_count(&d);
-    w.ldc = (d.T + 63) / 64 * 64;
-    const size_t ldc = (size_t)w.ldc;
-    (void)T;
-    size_t off = 0;
-    w.cM = off;
-    off += align_up(BH * ldc * sizeof(float));
-    w.cW = off;
-    off += align_up(BH * ldc * sizeof(float));
-    w.scal = off;
-    off += align_up(BH * nc * 4 * sizeof(float));
-    w.gacc = w.snap = off;
-    if (path == 0)
-        off += align_up(BH * 2 * P * sizeof(float));
-    else
-        off += align_up(BH * nc * P * 2);
-    w.total = (BH * T == 0) ? 0 : off;
-    return w;
-}
-
-struct Range {
-    uintptr_t lo, hi;
-};
-
-static bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // ---------------------------------------------------------------- backward
 // 1: SwiGLU MFMA backward, 0: portable fp32 backward, -1: unsupported
@@ -147,6 +118,38 @@ static void bwd_sizes(const e2ttt_desc& d, size_t bytes[19]) {
     for (int i = 0; i < 19; ++i) bytes[i] = tmp[i];
 }
 
+
+Workspace workspace_layout(const e2ttt_desc& d, int path) {
+    Workspace w{};
+    const size_t BH = (size_t)(d.B * d.H);
+    const size_t T = (size_t)d.T;
+    const size_t nc = (size_t)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
+    const size_t P = (size_t)e2ttt_param_count(&d);
+    w.ldc = (d.T + 63) / 64 * 64;
+    const size_t ldc = (size_t)w.ldc;
+    (void)T;
+    size_t off = 0;
+    w.cM = off;
+    off += align_up(BH * ldc * sizeof(float));
+    w.cW = off;
+    off += align_up(BH * ldc * sizeof(float));
+    w.scal = off;
+    off += align_up(BH * nc * 4 * sizeof(float));
+    w.gacc = w.snap = off;
+    if (path == 0)
+        off += align_up(BH * 2 * P * sizeof(float));
+    else
+        off += align_up(BH * nc * P * 2);
+    w.total = (BH * T == 0) ? 0 : off;
+    return w;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+static bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
 }  // namespace e2ttt
 
 using namespace e2ttt;
@@ -165,6 +168,7 @@ int64_t e2ttt_param_count(const e2ttt_desc* d) {
 
 size_t e2ttt_workspace_size(const e2ttt_desc* d) {
     if (!desc_ok(d)) return (size_t)-1;
+    if (d->flags & E2TTT_FLAG_SAVE_STATES) return bwd_workspace_layout(*d).total;  // shared with the backward
     return workspace_layout(*d, path_of(*d)).total;
 }
 
@@ -176,6 +180,7 @@ int e2ttt_path(const e2ttt_desc* d) {
 int e2ttt_validate(const e2ttt_desc* d, const void* const ptrs[11]) {
     if (!desc_ok(d) || !ptrs) return E2TTT_ERR_INVALID_ARG;
     if (path_of(*d) == 0 && !generic_supported(*d)) return E2TTT_ERR_UNSUPPORTED;
+    if ((d->flags & E2TTT_FLAG_SAVE_STATES) && backward_path(*d) != path_of(*d)) return E2TTT_ERR_UNSUPPORTED;
     const size_t BH = (size_t)(d->B * d->H);
     const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
     const size_t P = (size_t)e2ttt_param_count(d);
@@ -220,7 +225,17 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     const int st = e2ttt_validate(d, ptrs);
     if (st != E2TTT_OK) return st;
     const int path = path_of(*d);
-    const Workspace ws = workspace_layout(*d, path);
+    const bool save = (d->flags & E2TTT_FLAG_SAVE_STATES) != 0;
+    Workspace ws = workspace_layout(*d, path);
+    const BwdWorkspace bws = bwd_workspace_layout(*d);
+    if (save) {  // the backward's layout: its leading sections are the forward's
+        ws.cM = bws.cM;
+        ws.cW = bws.cW;
+        ws.scal = bws.scal;
+        ws.snap = bws.snapW;
+        ws.gacc = bws.gacc;
+        ws.total = bws.total;
+    }
     if (ws.total > 0) {
         if (!workspace || workspace_bytes < ws.total || (uintptr_t)workspace % kAlign) return E2TTT_ERR_WORKSPACE;
         const Range wr{(uintptr_t)workspace, (uintptr_t)workspace + ws.total};
@@ -260,11 +275,13 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
         return E2TTT_ERR_HIP;
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
+    const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
     if (path == 1) {
-        e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap, s, ev[2]);
+        e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap,
+                               save && mom ? wsb + bws.snapM : nullptr, s, ev[2]);
     } else {
         e = launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc),
-                           s);
+                           s, save ? (float*)(wsb + bws.save) : nullptr);
         if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
     }
     if (e == hipSuccess && ev[3]) e = hipEventRecord(ev[3], s);
@@ -349,11 +366,13 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
         float* cW = (float*)(wsb + ws.cW);
         float* scal = (float*)(wsb + ws.scal);
         float* save = (float*)(wsb + ws.save);
-        if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
-            return E2TTT_ERR_HIP;
-        if (launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, (float*)(wsb + ws.gacc), s,
-                           save) != hipSuccess)
-            return E2TTT_ERR_HIP;
+        if (!(d->flags & E2TTT_FLAG_SAVE_STATES)) {  // else a forward call left them in the workspace
+            if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
+                return E2TTT_ERR_HIP;
+            if (launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, (float*)(wsb + ws.gacc), s,
+                               save) != hipSuccess)
+                return E2TTT_ERR_HIP;
+        }
         if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
         GenericBwdBuffers g;
         g.q = q;
@@ -393,11 +412,13 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
     float* cM = (float*)(wsb + ws.cM);
     float* cW = (float*)(wsb + ws.cW);
     float* scal = (float*)(wsb + ws.scal);
-    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
-        return E2TTT_ERR_HIP;
-    if (launch_swiglu_loop(*d, k, v, cM, cW, ws.ldc, scal, W0, M0, dW0, dM0, wsb + ws.snapW,
-                           mom ? wsb + ws.snapM : nullptr, s) != hipSuccess)
-        return E2TTT_ERR_HIP;
+    if (!(d->flags & E2TTT_FLAG_SAVE_STATES)) {  // else a forward call left them in the workspace
+        if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+        if (launch_swiglu_loop(*d, k, v, cM, cW, ws.ldc, scal, W0, M0, dW0, dM0, wsb + ws.snapW,
+                               mom ? wsb + ws.snapM : nullptr, s) != hipSuccess)
+            return E2TTT_ERR_HIP;
+    }
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     BwdBuffers b;
     b.q = q;

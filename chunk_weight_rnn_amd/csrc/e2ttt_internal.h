@@ -43,10 +43,11 @@ bool swiglu_mfma_supported(const e2ttt_desc& d);
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
                               void* snap, void* snapM, hipStream_t s);
-// ev_mid (may be null) is recorded between the chunk-loop and output launches.
+// ev_mid (may be null) is recorded between the chunk-loop and output launches;
+// snapM (may be null) receives the momentum snapshots.
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
                               const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
-                              const float* M0, void* out, float* W_end, float* M_end, void* snap,
+                              const float* M0, void* out, float* W_end, float* M_end, void* snap, void* snapM,
                               hipStream_t s, hipEvent_t ev_mid);
 
 // Backward pass of the SwiGLU path (same shape support, chunk <= 2048).

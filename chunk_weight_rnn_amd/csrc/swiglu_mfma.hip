@@ -272,9 +272,9 @@ bool swiglu_mfma_supported(const e2ttt_desc& d) {
 
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
                               const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
-                              float* W_end, float* M_end, void* snap, hipStream_t s, hipEvent_t ev_mid) {
+                              float* W_end, float* M_end, void* snap, void* snapM, hipStream_t s, hipEvent_t ev_mid) {
     const int64_t BH = d.B * d.H;
-    hipError_t e = launch_swiglu_loop(d, k, v, cM, cW, ldc, scal, W0, M0, W_end, M_end, snap, nullptr, s);
+    hipError_t e = launch_swiglu_loop(d, k, v, cM, cW, ldc, scal, W0, M0, W_end, M_end, snap, snapM, s);
     if (e != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, s)) != hipSuccess) return e;
 

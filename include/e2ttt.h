@@ -79,6 +79,14 @@ typedef enum {
  * over the chunk; each token keeps its own eta_t, and the chunk scalars
  * prod alpha, prod beta, gamma are unchanged.  Combines with NO_MOMENTUM. */
 #define E2TTT_FLAG_CHUNK_AVG 4
+/* Save states for the backward (training): with this flag the forward and
+ * the backward share one workspace, sized by e2ttt_workspace_size() ==
+ * e2ttt_backward_workspace_size() for the flagged desc.  The forward leaves
+ * in it what the backward needs (scalar kernels and every chunk's start
+ * state); a following e2ttt_chunk_backward with the same desc (flag
+ * included), the same inputs and the untouched workspace skips its forward
+ * recompute.  Unsupported (E2TTT_ERR_UNSUPPORTED) where the backward is. */
+#define E2TTT_FLAG_SAVE_STATES 8
 
 typedef struct {
     int32_t kind;     /* e2ttt_kind */

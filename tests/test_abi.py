@@ -139,7 +139,7 @@ def test_validate_unsupported_shape(lib):
 
 
 def test_chunk_forward_rejects_before_launch(lib):
-    d = _desc(flags=8)  # unknown flag
+    d = _desc(flags=16)  # unknown flag
     v = ctypes.c_void_p
     args = [v(1 << 40)] * 11
     assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 1
@@ -195,7 +195,7 @@ def test_validate_variant_flags(lib):
         d = _desc(flags=f)
         assert _validate(lib, d, _ptrs(d)) == 0
     # unknown flag bits are rejected
-    d = _desc(flags=8)
+    d = _desc(flags=16)
     assert _validate(lib, d, _ptrs(d)) == 1
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
@@ -271,3 +271,16 @@ def test_chunk_update_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         e2.chunk_update(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], chunk=16,
                         kind="linear", loss="mse")
+
+
+def test_save_states_flag(lib):
+    """With the save-states flag forward and backward share one workspace."""
+    for d in (_desc(flags=8), _desc(flags=8 | 2), _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=8)):
+        assert lib.e2ttt_workspace_size(ctypes.byref(d)) == lib.e2ttt_backward_workspace_size(ctypes.byref(d))
+        assert _validate(lib, d, _ptrs(d)) == 0
+    plain, saved = _desc(), _desc(flags=8)
+    assert lib.e2ttt_workspace_size(ctypes.byref(saved)) > lib.e2ttt_workspace_size(ctypes.byref(plain))
+    # where the backward is unsupported, so is saving for it
+    d = _desc(chunk=4096, T=8192, flags=8)
+    assert _validate(lib, d, _ptrs(d)) == 2
+    assert _validate(lib, _desc(chunk=4096, T=8192), _ptrs(_desc(chunk=4096, T=8192))) == 0

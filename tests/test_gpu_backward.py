@@ -164,3 +164,30 @@ def test_backward_rejects_aliased_output():
     st = lib.e2ttt_chunk_backward(ctypes.byref(d), *args, *outs, p(ws), ctypes.c_size_t(ws.numel()),
                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 3
+
+
+@pytest.mark.parametrize("case", ["swiglu_mfma", "swiglu_nomom", "mlp_portable", "linear_portable"])
+def test_backward_from_saved_forward_states(case):
+    """chunk_forward(save_states=True) then chunk_backward(saved=True) on one
+    shared workspace gives the recomputing backward's result bit for bit."""
+    import chunk_weight_rnn_amd as e2
+    cfg = {"swiglu_mfma": SMALL, "swiglu_nomom": SMALL.with_(flags=2),
+           "mlp_portable": synth.Config("saved_mlp", "mlp", "mse", 1, 2, 80, 16, 24, 32, "f32", ""),
+           "linear_portable": synth.Config("saved_lin", "linear", "negdot", 1, 2, 80, 16, 0, 32, "f32", "")}[case]
+    note(f"case saved {case}")
+    x = {n: t.cuda() for n, t in synth.make_inputs(cfg, seed=14, m0_scale=0.5 if cfg.momentum else 0.0).items()}
+    c = {n: t.cuda() for n, t in synth.make_cotangents(cfg, seed=15).items()}
+    kw = dict(chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd, momentum=cfg.momentum)
+    ws = e2.training_workspace(x["q"], **kw)
+    fo = e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], workspace=ws,
+                          save_states=True, **kw)
+    plain = e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], **kw)
+    gs = e2.chunk_backward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], c["dout"],
+                           c["dW_end"], c["dM_end"], workspace=ws, saved=True, **kw)
+    gr = e2.chunk_backward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], c["dout"],
+                           c["dW_end"], c["dM_end"], **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(fo, plain):
+        assert (a is None and b is None) or torch.equal(a, b)
+    for n in gs:
+        assert (gs[n] is None and gr[n] is None) or torch.equal(gs[n], gr[n]), n
