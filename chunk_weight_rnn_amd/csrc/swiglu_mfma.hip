@@ -12,6 +12,8 @@
 // on chip and writes a bf16 snapshot of every chunk's start weights; the
 // output needs all hidden units of a head, so this second, fully parallel
 // kernel computes every chunk's output from the snapshots.
+#include <type_traits>
+
 #include "e2ttt_internal.h"
 
 namespace e2ttt {
@@ -54,7 +56,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // Snapshot layout per (b, h, chunk), bf16, all hidden-major:
 //   W1^T [Hd][D] | W3^T [Hd][D] | W2 [Hd][D].
 // One wavefront per 32 tokens; hidden units stream through LDS 32 at a time
-// in a ring of three stages (two copies in flight while one is consumed).
+// in a ring of stages (all but one in flight while one is consumed).
 // Computed transposed (H^T = W1^T Q^T, out^T = W2^T U^T) so that U^T leaves
 // the first MFMA in the register layout the second one consumes; the W2^T
 // operand comes from the hidden-major stage through the transpose read.
@@ -78,20 +80,21 @@ constexpr int STAGE_BYTES = 3 * HB * 256;  // W1^T, W3^T, W2 rows of the stage
 // disjoint 4-chunk groups: conflict-free on the 64 four-byte banks.
 __device__ __forceinline__ int swza(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 
-// 32x16 MFMA operand fragment transposed out of a swizzled row-major
-// [rows][128] bf16 stage: operand row = source column col0 + lane%32,
-// operand k 0..3 = source rows rbase0..+3, k 4..7 = source rows rbase1..+3.
-__device__ __forceinline__ bf16x8 tr_frag_a(const unsigned char* buf, int rbase0, int rbase1, int col0, int lane) {
+// Per-lane byte offset, within a stage's W2 block, of one half of a 32x16
+// MFMA operand fragment transposed out of the swizzled row-major [rows][128]
+// bf16 rows: operand row = W2 column 32 dt + lane%32, operand k 0..3 = W2
+// rows 16 s + 4 lg + {0..3} (hi = 0) and k 4..7 the same + 8 (hi = 1).  The
+// k-step s adds 16 rows, 4096 bytes, and does not change the swizzle.
+__device__ __forceinline__ unsigned tr_offset(int dt, int hi, int lane) {
     const int p = lane & 15, G = lane >> 4;
-    const int col = col0 + 16 * (G & 1) + 4 * (p & 3);
-    const int chunk = col >> 3;
-    const int half = p & 1;
-    const int r0 = rbase0 + (p >> 2);
-    const int r1 = rbase1 + (p >> 2);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4_t*)(buf + r0 * 256 + 16 * (chunk ^ swza(r0)) + 8 * half));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4_t*)(buf + r1 * 256 + 16 * (chunk ^ swza(r1)) + 8 * half));
+    const int r = 4 * (G >> 1) + 8 * hi + (p >> 2);
+    const int chunk = 4 * dt + 2 * (G & 1) + ((p & 3) >> 1);
+    return (unsigned)(r * 256 + 16 * (chunk ^ swza(r)) + 8 * (p & 1));
+}
+
+__device__ __forceinline__ bf16x8 tr_frag_at(const unsigned char* base, unsigned off0, unsigned off1) {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + off0));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + off1));
     bf16x8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -101,27 +104,87 @@ __device__ __forceinline__ bf16x8 tr_frag_a(const unsigned char* buf, int rbase0
     return r;
 }
 
+// Wave-uniform values the compiler cannot prove uniform (loop-carried
+// cursors): read from the first lane so buffer descriptors stay in SGPRs.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (void*)(((uint64_t)hi << 32) | lo);
+}
+
 // direct HBM->LDS copy of 16 bytes per lane (buffer form; lane L writes
 // dst + 16 L); offsets at or past num_bytes read zeros
 __device__ __forceinline__ void lds_copy16(const void* base, int num_bytes, unsigned char* dst, unsigned voff) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, num_bytes, RSRC_W3);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), 0, uniform(num_bytes), RSRC_W3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, 0, 0, 0);
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(N) with every other counter left alone (N < 64)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses but not for its
+// HBM -> LDS copies in flight (__syncthreads would wait for every load).
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The stage ring: separate LDS objects, so that the compiler can tell the
+// copies in flight from the reads of the stage being consumed.
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb0[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb1[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb2[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb3[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb4[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) unsigned char apply_sb5[STAGE_BYTES];
+constexpr int NS_MAX = 6;
+
+template <int I>
+__device__ __forceinline__ unsigned char* stage_buf() {
+    static_assert(I >= 0 && I < NS_MAX, "stage ring index");
+    if constexpr (I == 0) return apply_sb0;
+    else if constexpr (I == 1) return apply_sb1;
+    else if constexpr (I == 2) return apply_sb2;
+    else if constexpr (I == 3) return apply_sb3;
+    else if constexpr (I == 4) return apply_sb4;
+    else return apply_sb5;
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// LDS of a compute unit, and workgroups of the output kernel per compute unit
+constexpr int LDS_PER_CU = 160 * 1024;
+template <int NS>
+constexpr int apply_wg_per_cu() { return LDS_PER_CU / (NS * STAGE_BYTES); }
+
 // Persistent: every workgroup walks a list of items (an item = 32 NWA tokens
-// of one chunk) so the stage copies never stop between items.  Each
-// wavefront copies its own 32 query rows of the next item into its own LDS
-// rows while the current item runs.
-template <int NWA>
+// of one chunk) so the stage copies never stop between items.  NS stage
+// buffers form a ring with NS - 1 stages in flight while one is consumed.
+// Each wavefront loads its own 32 query rows of the next item straight into
+// registers while the current item runs.
+template <int NWA, int NS>
 __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
-    // three stage buffers as separate arrays, so the compiler can tell copies
-    // in flight from the reads of the stage being consumed
-    __shared__ __attribute__((aligned(16))) unsigned char sb0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char sb1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char sb2[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char qs[NWA * 32 * 256];  // [wave][32 tokens][128] bf16
     constexpr int NI = 24 / NWA;  // stage copy instructions per wave per stage
-    constexpr int NQ = 8;         // query copy instructions per wave per item (32 rows, 4 per copy)
+    constexpr int NQ = 8;         // query loads per wave per item (16 bytes per lane each)
+    static_assert(NS >= 3 && NS <= NS_MAX, "stage ring size");
+    static_assert((NS - 2) * NI + 3 * NQ < 64, "wait counts must fit vmcnt");
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 31, lg = lane >> 5;
     const int Hd = a.Hd;
@@ -130,7 +193,6 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
     const int64_t nitems = (int64_t)a.nb * a.nc * a.rbc;
     // items of this workgroup: blockIdx.x + k gridDim.x
     const int nmine = (int)((nitems - blockIdx.x + gridDim.x - 1) / gridDim.x);
-    unsigned char* qw = qs + wave * 32 * 256;
 
     struct Item {
         const __bf16* sn;  // snapshot of the item's chunk
@@ -138,7 +200,7 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         int nrec;          // bytes the copies may read (0 past the last item: zeros)
         int nrows;         // rows of this wave inside the sequence (a short last chunk has fewer)
     };
-    auto item = [&](int k) {
+    auto item = [&](int k) __attribute__((always_inline)) {
         Item it;
         const int64_t x = blockIdx.x + (int64_t)k * gridDim.x;
         const bool ok = k < nmine;
@@ -165,55 +227,81 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         voff[n] = (unsigned)((m * Hd * D + row * D + 8 * ((lane & 15) ^ swza(row))) * 2);
         mrow[n] = m * HB * 256 + r0 * 256;
     }
-    // global stage index gs = k nhb + ih
-    auto issue_stage = [&](int gs, unsigned char* buf) {
-        const Item it = item(gs / nhb);
-        const unsigned ho = (unsigned)((gs % nhb) * HB * D * 2);
+    // The copy stream runs NS - 1 stages ahead of the computation.  Each
+    // stream keeps a cursor (item, stage within the item), so an item's
+    // position (64-bit divisions, done by the scalar unit) is worked out once
+    // per item rather than at every stage.
+    Item citem = item(0);
+    int ck = 0, cih = 0;
+    auto issue_next_copy = [&](unsigned char* buf) __attribute__((always_inline)) {
+        const unsigned ho = (unsigned)(cih * HB * D * 2);
 #pragma unroll
-        for (int n = 0; n < NI; ++n) lds_copy16(it.sn, it.nrec, buf + mrow[n], voff[n] + ho);
+        for (int n = 0; n < NI; ++n) lds_copy16(citem.sn, citem.nrec, buf + mrow[n], voff[n] + ho);
+        if (++cih == nhb) {
+            cih = 0;
+            citem = item(++ck);
+        }
     };
-    // the wave's 32 query rows of item k, row-major with the stage swizzle
-    auto issue_q = [&](int k) {
-        const Item it = item(k);
-        const int qrec = it.nrows * D * 2;  // rows past the sequence read zeros
+    // Q^T as the B operand of the first product (col = token li, k = d):
+    // lane (li, lg) holds q[li][16 ks + 8 lg .. + 7] for k-step ks.  Rows past
+    // the sequence read zeros.
+    auto load_q = [&](const Item& it, bf16x8(&dst)[8]) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.q + it.tok * D), 0, uniform(it.nrows * D * 2), RSRC_W3);
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int row = 4 * n + (lane >> 4);
-            const unsigned vo = (unsigned)((row * D + 8 * ((lane & 15) ^ swza(row))) * 2);
-            lds_copy16(a.q + it.tok * D, qrec, qw + 4 * n * 256, vo);
+        for (int ks = 0; ks < NQ; ++ks) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, (li * D + 16 * ks + 8 * lg) * 2, 0, 0);
+            dst[ks] = __builtin_bit_cast(bf16x8, w);
         }
     };
 
-    bf16x8 qf[8];  // Q^T as B operand: col = token, k = d
-    f32x16 oacc[4] = {};
-    issue_q(0);
-    issue_stage(0, sb0);
-    issue_stage(1, sb1);
+    // per-lane LDS offsets of the stage reads, the same for every buffer of the ring
+    unsigned rd_off[8], tr_off[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) rd_off[ks] = (unsigned)(li * 256 + 16 * ((2 * ks + lg) ^ swza(li)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tr_off[i] = tr_offset(i >> 1, i & 1, lane);
 
-    auto stage = [&](int gs, const unsigned char* st, unsigned char* refill) {
-        const int ih = gs % nhb;
-        // this stage's copies (and, at an item start, the item's queries)
-        // landed: the loads issued after them are the next stage's copies and,
-        // within two stages of an item start, the next item's queries.  (Loads
-        // complete in order; a count that ignores later stores only waits longer.)
-        if (ih == 1 || ih == 2)
-            __builtin_amdgcn_s_waitcnt(((NI + NQ) & 15) | (((NI + NQ) >> 4) << 14) | 0x0F70);
-        else
-            __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | 0x0F70);
-        __syncthreads();
-        issue_stage(gs + 2, refill);  // refill = buffer of stage gs - 1, free after the barrier
+    bf16x8 qf[8], qn[8];
+    f32x16 oacc[4] = {};
+    Item cur = item(0), nxt = cur;  // the item being computed, and the next one
+    load_q(cur, qn);                // the first item's queries precede every copy
+    static_for<0, NS - 1>([&](auto I) __attribute__((always_inline)) { issue_next_copy(stage_buf<decltype(I)::value>()); });
+
+    int ih = 0;          // stage within the current item
+    unsigned qmask = 0;  // bit j: a query batch was issued j + 1 stages ago (j < NS - 1)
+    int k = 0;           // current item
+    auto stage = [&](const unsigned char* st, unsigned char* refill) __attribute__((always_inline)) {
+        // This stage's copies landed once at most the loads issued after them
+        // are outstanding: the copies of the next NS - 2 stages and the query
+        // batches of the last NS - 1 stages.  (Loads complete in order; the
+        // output stores are not counted, which only waits longer.)
+        switch (__builtin_popcount(qmask)) {
+            case 0: wait_vm<(NS - 2) * NI>(); break;
+            case 1: wait_vm<(NS - 2) * NI + NQ>(); break;
+            case 2: wait_vm<(NS - 2) * NI + 2 * NQ>(); break;
+            default: wait_vm<(NS - 2) * NI + 3 * NQ>(); break;
+        }
+        stage_barrier();
+        issue_next_copy(refill);  // refill = buffer of the previous stage, free after the barrier
+        qmask = (qmask << 1) & ((1u << (NS - 1)) - 1);
         if (ih == 0) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qw + li * 256 + 16 * ((2 * ks + lg) ^ swza(li)));
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the query rows are in registers
-            issue_q(gs / nhb + 1);
+            for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
+            nxt = item(k + 1);
+            load_q(nxt, qn);
+            qmask |= 1;
         }
+        // The offsets are opaque to the optimiser here, so each read adds its
+        // offset to this stage's buffer instead of the kernel keeping the
+        // addresses of every buffer of the ring in registers.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(rd_off[i]), "+v"(tr_off[i]));
         f32x16 x1 = {}, x3 = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const int ch = (2 * ks + lg) ^ swza(li);
-            x1 = mfma32(*(const bf16x8*)(st + li * 256 + 16 * ch), qf[ks], x1);
-            x3 = mfma32(*(const bf16x8*)(st + HB * 256 + li * 256 + 16 * ch), qf[ks], x3);
+            x1 = mfma32(*(const bf16x8*)(st + rd_off[ks]), qf[ks], x1);
+            x3 = mfma32(*(const bf16x8*)(st + HB * 256 + rd_off[ks]), qf[ks], x3);
         }
         // U^T tile: rows j = 8(r/4) + 4 lg + r%4, col = token
         bf16x8 ub[2];
@@ -229,16 +317,13 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         // {4lg..4lg+3, 8+4lg..8+4lg+3}; the transpose read fetches W2 rows in that order.
         const unsigned char* w2 = st + 2 * HB * 256;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int jb = 16 * s + 4 * lg;
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-                oacc[dt] = mfma32(tr_frag_a(w2, jb, jb + 8, 32 * dt, lane), ub[s], oacc[dt]);
-        }
-        if (ih == nhb - 1) {
-            const Item it = item(gs / nhb);
-            __bf16* ob = a.out + it.tok * D;
-            const bool row_ok = li < it.nrows;  // no stores past the sequence
+                oacc[dt] = mfma32(tr_frag_at(w2 + 4096 * s, tr_off[2 * dt], tr_off[2 * dt + 1]), ub[s], oacc[dt]);
+        if (++ih == nhb) {
+            __bf16* ob = a.out + cur.tok * D;
+            const bool row_ok = li < cur.nrows;  // no stores past the sequence
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -250,13 +335,17 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
                 }
                 oacc[dt] = f32x16{};
             }
+            ih = 0;
+            ++k;
+            cur = nxt;
         }
     };
     const int nst = nmine * nhb;
-    for (int gs = 0; gs < nst; gs += 3) {
-        stage(gs, sb0, sb2);
-        if (gs + 1 < nst) stage(gs + 1, sb1, sb0);
-        if (gs + 2 < nst) stage(gs + 2, sb2, sb1);
+    for (int gs = 0; gs < nst; gs += NS) {
+        static_for<0, NS>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if (gs + i < nst) stage(stage_buf<i>(), stage_buf<(i + NS - 1) % NS>());
+        });
     }
     wait_vmem();  // copies past the last item (zeros) land before the LDS goes away
 }
@@ -287,21 +376,24 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.C = (int)d.chunk;
     aa.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     aa.nb = (int)BH;
-    // persistent grid: one workgroup per compute unit (the LDS of one fills it)
+    // persistent grid: as many workgroups as the compute units hold at once
     int dev = 0, ncu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     const int64_t nck = BH * aa.nc;
-    auto grid = [&](int64_t items) { return dim3((unsigned)(items < ncu ? items : ncu)); };
+    auto grid = [&](int64_t items, int per_cu) {
+        const int64_t cap = (int64_t)ncu * per_cu;
+        return dim3((unsigned)(items < cap ? items : cap));
+    };
     if (d.chunk % 256 == 0) {
         aa.rbc = (int)(d.chunk / 256);
-        hipLaunchKernelGGL(swiglu_apply_kernel<8>, grid(nck * aa.rbc), dim3(512), 0, s, aa);
+        hipLaunchKernelGGL((swiglu_apply_kernel<8, 6>), grid(nck * aa.rbc, apply_wg_per_cu<6>()), dim3(512), 0, s, aa);
     } else if (d.chunk % 128 == 0) {
         aa.rbc = (int)(d.chunk / 128);
-        hipLaunchKernelGGL(swiglu_apply_kernel<4>, grid(nck * aa.rbc), dim3(256), 0, s, aa);
+        hipLaunchKernelGGL((swiglu_apply_kernel<4, 3>), grid(nck * aa.rbc, apply_wg_per_cu<3>()), dim3(256), 0, s, aa);
     } else {
         aa.rbc = (int)(d.chunk / 64);
-        hipLaunchKernelGGL(swiglu_apply_kernel<2>, grid(nck * aa.rbc), dim3(128), 0, s, aa);
+        hipLaunchKernelGGL((swiglu_apply_kernel<2, 3>), grid(nck * aa.rbc, apply_wg_per_cu<3>()), dim3(128), 0, s, aa);
     }
     return hipGetLastError();
 }
