@@ -46,6 +46,8 @@
 // a 12 KB exchange area: two half-block factor sets, or at a chunk boundary
 // the 12 bf16 grad operands.  HBM -> LDS copies are waited for one slot
 // before their first reader, so a barrier never waits on them.
+#include <type_traits>
+
 #include "e2ttt_internal.h"
 
 namespace e2ttt {
@@ -58,9 +60,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 constexpr int D = 128;             // head dim
-constexpr int S = 64;              // hidden units per workgroup slice
 constexpr int CB = 64;             // tokens per LDS block
-constexpr int NT = 512;            // 4 state + 4 gradient wavefronts
 constexpr int KVB = CB * 256;      // one [64][128] bf16 token block
 constexpr int COB = 1024;          // cM [64] f32 | cW [64] f32 | spare
 constexpr int KVBUF = 2 * KVB + COB;
@@ -195,19 +195,25 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
     }
 }
 
-template <bool MOM, bool SAVEM>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+// UG: 16-unit groups per workgroup (4: a 64-unit slice, 8 wavefronts, two
+// per SIMD; 2 or 1 for small grids, where each wavefront gets a SIMD of its
+// own and a head's hidden units spread over more workgroups).
+template <bool MOM, bool SAVEM, int UG>
+__global__ void __attribute__((amdgpu_flat_work_group_size(128 * UG, 128 * UG), amdgpu_waves_per_eu(2, 2)))
 swiglu_loop_kernel(LoopArgs a) {
+    static_assert(UG == 1 || UG == 2 || UG == 4, "unit groups per workgroup");
+    constexpr int S = 16 * UG;     // hidden units per workgroup slice
+    constexpr int RPW = CB / UG;   // token rows each state wave copies per block
     // MOM = false: the recurrence without momentum; the scalar kernels then
     // have beta = 0 (cM unused, gamma = Bb = 0) and the M half of the state,
     // its aggregation MFMAs and its HBM traffic are compiled out.
     // SAVEM: also write a bf16 snapshot of every chunk's start momentum, in
     // the layout of the weight snapshot (for the backward pass).
     __shared__ __attribute__((aligned(16))) unsigned char kvs[NBUF * KVBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char xch[4 * XW];
+    __shared__ __attribute__((aligned(16))) unsigned char xch[UG * XW];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int u = wave & 3;
+    const int u = wave & (UG - 1);
     const int lane = tid & 63;
     const int jl = lane & 15, g = lane >> 4;
 
@@ -229,7 +235,7 @@ swiglu_loop_kernel(LoopArgs a) {
     unsigned char* const xw = xch + u * XW;  // this unit group's exchange area
     const int xl = 16 * lane;                // this lane's 16 bytes in an exchange fragment
 
-    if (wave < 4) {
+    if (wave < UG) {
         // ------------------------------------------------------------ state wave
         // K^T / V^T fragment offsets for state tile i (16x16x32 A operand, rows
         // d in state_d order, k = 32 tokens of a half-block): lane (p, g)
@@ -266,11 +272,11 @@ swiglu_loop_kernel(LoopArgs a) {
             const unsigned dst = kvs_lds + (unsigned)((X % NBUF) * KVBUF);
             const unsigned tb = (unsigned)X * CB * D * 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * u + 4 * i + (ln >> 4);
+            for (int i = 0; i < RPW / 4; ++i) {
+                const int row = RPW * u + 4 * i + (ln >> 4);
                 const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
-                copy16(krs, dst + (16 * u + 4 * i) * 256, ko);
-                copy16(vrs, dst + KVB + (16 * u + 4 * i) * 256, ko);
+                copy16(krs, dst + (RPW * u + 4 * i) * 256, ko);
+                copy16(vrs, dst + KVB + (RPW * u + 4 * i) * 256, ko);
             }
             if (u == 0) {
                 const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
@@ -552,6 +558,10 @@ swiglu_loop_kernel(LoopArgs a) {
 
 }  // namespace
 
+static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
+    return BH * (Hd / 64) >= ncu ? 4 : 2;
+}
+
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
                               void* snap, void* snapM, hipStream_t s) {
@@ -573,15 +583,33 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.C = (int)d.chunk;
     la.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     la.ldc = ldc;
-    la.nsl = (int)(d.Hd / S);
+    // 16-unit groups per workgroup: 64-unit slices while they fill the chip,
+    // else 32-unit slices, whose wavefronts each get a SIMD of their own
+    int dev = 0, ncu = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int ug = loop_unit_groups(BH, d.Hd, ncu);
+    la.nsl = (int)(d.Hd / (16 * ug));
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
-    if (d.flags & E2TTT_FLAG_NO_MOMENTUM)
-        hipLaunchKernelGGL((swiglu_loop_kernel<false, false>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
-    else if (snapM)
-        hipLaunchKernelGGL((swiglu_loop_kernel<true, true>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+    const dim3 grid((unsigned)la.nwg), block((unsigned)(128 * ug));
+    const bool nomom = (d.flags & E2TTT_FLAG_NO_MOMENTUM) != 0;
+    auto go = [&](auto UGc) {
+        constexpr int U = decltype(UGc)::value;
+        if (nomom)
+            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, U>), grid, block, 0, s, la);
+        else if (snapM)
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, true, U>), grid, block, 0, s, la);
+        else
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, U>), grid, block, 0, s, la);
+    };
+    if (ug == 4)
+        go(std::integral_constant<int, 4>{});
+    else if (ug == 2)
+        go(std::integral_constant<int, 2>{});
     else
-        hipLaunchKernelGGL((swiglu_loop_kernel<true, false>), dim3((unsigned)la.nwg), dim3(NT), 0, s, la);
+        go(std::integral_constant<int, 1>{});
     return hipGetLastError();
 }
 
