@@ -22,7 +22,7 @@
 // whole sequence.
 //
 // Workgroup = 8 wavefronts, two per SIMD, in two roles over the same 16-unit
-// groups u = 0..3:
+// groups u = 0..3 (on small grids 4 wavefronts over a 32-unit slice, u = 0..1):
 //   state wave u (wave u):      the group's fp32 W and M (6 x 128 x 16 values)
 //                               as MFMA accumulators; per 32 tokens it scales
 //                               the gradient wave's factors by the tokens'
@@ -41,7 +41,7 @@
 // gradient waves wait one extra half-block: the next chunk's grad operands
 // are the state after the previous chunk's last aggregation.
 //
-// LDS (150.5 KB): three 64-token K/V/coefficient blocks (the state waves'
+// LDS (150.5 KB; 123 KB for 32-unit slices): three 64-token K/V/coefficient blocks (the state waves'
 // block, the gradient waves' block, one in flight from HBM) and per unit group
 // a 12 KB exchange area: two half-block factor sets, or at a chunk boundary
 // the 12 bf16 grad operands.  HBM -> LDS copies are waited for one slot
@@ -253,7 +253,7 @@ swiglu_loop_kernel(LoopArgs a) {
             tdelta = 8 - 2 * h0;
         }
         // HBM -> LDS copies of block X into buffer X % 3, issued by the state
-        // waves (they have the slack): wave u moves K and V rows 16u..16u+15, 4
+        // waves (they have the slack): wave u moves K and V rows RPW u .. + RPW-1, 4
         // rows per instruction (lane L: row + L/16, chunk (L%16) ^ swz4(row),
         // landing at physical chunk L%16); wave 0 also moves the block's cM and
         // cW (one resource based at cM).
