@@ -198,7 +198,10 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 // UG: 16-unit groups per workgroup (4: a 64-unit slice, 8 wavefronts, two
 // per SIMD; 2 or 1 for small grids, where each wavefront gets a SIMD of its
 // own and a head's hidden units spread over more workgroups).
-template <bool MOM, bool SAVEM, int UG>
+// SPREAD: the gradient waves store the weight snapshots, a few fragments per
+// half-block (short chunks); else the state waves store them at the chunk
+// boundary.
+template <bool MOM, bool SAVEM, int UG, bool SPREAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(128 * UG, 128 * UG), amdgpu_waves_per_eu(2, 2)))
 swiglu_loop_kernel(LoopArgs a) {
     static_assert(UG == 1 || UG == 2 || UG == 4, "unit groups per workgroup");
@@ -302,6 +305,7 @@ swiglu_loop_kernel(LoopArgs a) {
         state_io<false, MOM>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd);
 
         // chunk-start weights -> grad operands (exchange area) + bf16 snapshot
+        // (with SPREAD the gradient waves store the snapshot instead)
         const bool godd = (g & 1) != 0;
         auto grad_operands = [&](int c) {
             unsigned char* snap = (unsigned char*)(a.snap + (bh * nc + c) * P);
@@ -320,7 +324,7 @@ swiglu_loop_kernel(LoopArgs a) {
                         w8[4 + e] = hi[e];
                     }
                     *(bf16x8*)(xw + (4 * m + kk) * 1024 + xl) = w8;
-                    *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
+                    if (!SPREAD) *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
                     if (SAVEM) {
                         unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
                         const bf16x4 s0 = pack4(acc[m][0][2 * kk]), s1 = pack4(acc[m][0][2 * kk + 1]);
@@ -513,6 +517,22 @@ swiglu_loop_kernel(LoopArgs a) {
 #pragma unroll
             for (int x = 0; x < 3; ++x) *(bf16x8*)(fb + x * 1024) = f[x];
         };
+        // With SPREAD (short chunks, whose chunk-boundary slots are a
+        // large share of all slots) the gradient waves store the chunk's bf16
+        // snapshot from wb, which holds it in the exchange area's lane layout
+        // (fragment f = 4m + kk), a few fragments per half-block: fragments
+        // f0 .. f1-1 here.  Otherwise the state waves store it at the chunk
+        // boundary, which costs less on long chunks.
+        auto store_snap = [&](int c, int f0, int f1) {
+            unsigned char* snap = (unsigned char*)(a.snap + (bh * nc + c) * P);
+            unsigned snap_lane = (unsigned)(j * D + 8 * g) * 2u;
+            asm volatile("" : "+v"(snap_lane));
+#pragma unroll
+            for (int f = 0; f < 12; ++f)
+                if (f >= f0 && f < f1)
+                    *(bf16x8*)(snap + (snap_lane + (unsigned)((f >> 2) * Hd * D + 32 * (f & 3)) * 2u)) = wb[f >> 2][f & 3];
+            __builtin_amdgcn_sched_barrier(0);
+        };
         // Slots as in the state waves' loop.  The grad MFMAs of the next
         // half-block are issued before the backward of the current one, so they
         // run in the MFMA pipe while the backward runs on the VALU; only a
@@ -529,6 +549,7 @@ swiglu_loop_kernel(LoopArgs a) {
             }
             const int nhc = halves(c);
             for (int k = 0; k + 1 < nhc; ++k) {
+                if (SPREAD) store_snap(c, 12 * k / nhc, 12 * (k + 1) / nhc);
                 const int hh = c * nh + k;
                 // next half-block's fragments, this one's backward with the next
                 // one's MFMAs slotted in between its VALU work, factor writes last
@@ -550,6 +571,7 @@ swiglu_loop_kernel(LoopArgs a) {
 #pragma unroll
                     for (int m = 0; m < 3; ++m) hg[ti][m] = hn[ti][m];
             }
+            if (SPREAD) store_snap(c, 12 * (nhc - 1) / nhc, 12);
             backward(c * nh + nhc - 1, hg);
             slot_barrier();
         }
@@ -559,7 +581,7 @@ swiglu_loop_kernel(LoopArgs a) {
 }  // namespace
 
 static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
-    return BH * (Hd / 64) >= ncu ? 4 : 2;
+    return BH * (Hd / 64) >= ncu ? 4 : 2;  // 16-unit slices measured slower than both
 }
 
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
@@ -595,21 +617,28 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
     const dim3 grid((unsigned)la.nwg), block((unsigned)(128 * ug));
     const bool nomom = (d.flags & E2TTT_FLAG_NO_MOMENTUM) != 0;
-    auto go = [&](auto UGc) {
+    // short chunks: the snapshot stores spread over the gradient waves' half-blocks
+    const bool spread = d.chunk <= 64;
+    auto go = [&](auto UGc, auto SPc) {
         constexpr int U = decltype(UGc)::value;
+        constexpr bool SP = decltype(SPc)::value;
         if (nomom)
-            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, U>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, U, SP>), grid, block, 0, s, la);
         else if (snapM)
-            hipLaunchKernelGGL((swiglu_loop_kernel<true, true, U>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, true, U, SP>), grid, block, 0, s, la);
         else
-            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, U>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, U, SP>), grid, block, 0, s, la);
     };
-    if (ug == 4)
-        go(std::integral_constant<int, 4>{});
-    else if (ug == 2)
-        go(std::integral_constant<int, 2>{});
+    auto go_ug = [&](auto SPc) {
+        if (ug == 4)
+            go(std::integral_constant<int, 4>{}, SPc);
+        else
+            go(std::integral_constant<int, 2>{}, SPc);
+    };
+    if (spread)
+        go_ug(std::true_type{});
     else
-        go(std::integral_constant<int, 1>{});
+        go_ug(std::false_type{});
     return hipGetLastError();
 }
 
