@@ -313,7 +313,7 @@ def main() -> int:
                          "profile of this command holds the HBM counters of a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the (batch, head) recurrences would shard across GPUs without communication).",
               file=sys.stderr)
         return 2
