@@ -126,6 +126,10 @@ MFMA_CASES = [
     dict(B=2, H=3, T=384, Hd=128, chunk=64),    # 12 workgroups (no XCD remap), 6 chunks
     dict(B=2, H=4, T=512, Hd=256, chunk=512),   # one long chunk of 8 blocks
     dict(B=1, H=2, T=1024, Hd=320, chunk=256),  # 5 slices
+    # output kernel: 320 items on 256 workgroups (two items on some), items of
+    # 2 and 4 hidden-unit stages, so up to 3 query batches in flight
+    dict(B=8, H=40, T=256, Hd=64, chunk=256),
+    dict(B=4, H=80, T=256, Hd=128, chunk=256),
 ]
 
 
