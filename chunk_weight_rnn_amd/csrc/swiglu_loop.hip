@@ -580,8 +580,12 @@ swiglu_loop_kernel(LoopArgs a) {
 
 }  // namespace
 
+// 32-unit slices only while their grid still fits on the chip at once: a
+// slot takes about as long either way, so a second round of workgroups would
+// cost more than the smaller slices gain.  (16-unit slices measured slower
+// than both.)
 static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
-    return BH * (Hd / 64) >= ncu ? 4 : 2;  // 16-unit slices measured slower than both
+    return BH * (Hd / 32) <= ncu ? 2 : 4;
 }
 
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
@@ -605,8 +609,8 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.C = (int)d.chunk;
     la.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     la.ldc = ldc;
-    // 16-unit groups per workgroup: 64-unit slices while they fill the chip,
-    // else 32-unit slices, whose wavefronts each get a SIMD of their own
+    // 16-unit groups per workgroup: 32-unit slices (each wavefront gets a SIMD
+    // of its own) on grids small enough for them, else 64-unit slices
     int dev = 0, ncu = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
