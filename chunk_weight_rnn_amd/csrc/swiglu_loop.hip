@@ -41,11 +41,12 @@
 // gradient waves wait one extra half-block: the next chunk's grad operands
 // are the state after the previous chunk's last aggregation.
 //
-// LDS (150.5 KB; 123 KB for 32-unit slices): three 64-token K/V/coefficient blocks (the state waves'
-// block, the gradient waves' block, one in flight from HBM) and per unit group
-// a 12 KB exchange area: two half-block factor sets, or at a chunk boundary
-// the 12 bf16 grad operands.  HBM -> LDS copies are waited for one slot
-// before their first reader, so a barrier never waits on them.
+// LDS (150.5 KB; 123 KB for 32-unit slices): three 64-token K/V/coefficient
+// blocks (the state waves' block, the gradient waves' block, one in flight
+// from HBM) and per unit group a 12 KB exchange area: two half-block factor
+// sets, or at a chunk boundary the 12 bf16 grad operands.  HBM -> LDS copies
+// are waited for one slot before their first reader, so a barrier never
+// waits on them.
 #include <type_traits>
 
 #include "e2ttt_internal.h"
@@ -196,15 +197,15 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 }
 
 // UG: 16-unit groups per workgroup (4: a 64-unit slice, 8 wavefronts, two
-// per SIMD; 2 or 1 for small grids, where each wavefront gets a SIMD of its
-// own and a head's hidden units spread over more workgroups).
+// per SIMD; 2 for small grids: a 32-unit slice whose 4 wavefronts each get a
+// SIMD of their own, and a head's hidden units over more workgroups).
 // SPREAD: the gradient waves store the weight snapshots, a few fragments per
 // half-block (short chunks); else the state waves store them at the chunk
 // boundary.
 template <bool MOM, bool SAVEM, int UG, bool SPREAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(128 * UG, 128 * UG), amdgpu_waves_per_eu(2, 2)))
 swiglu_loop_kernel(LoopArgs a) {
-    static_assert(UG == 1 || UG == 2 || UG == 4, "unit groups per workgroup");
+    static_assert(UG == 2 || UG == 4, "unit groups per workgroup");
     constexpr int S = 16 * UG;     // hidden units per workgroup slice
     constexpr int RPW = CB / UG;   // token rows each state wave copies per block
     // MOM = false: the recurrence without momentum; the scalar kernels then
