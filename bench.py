@@ -12,7 +12,8 @@ With --backward one step is one e2ttt_chunk_backward call instead (forward
 recompute, reverse chunk loop, scalar-kernel backward): the gradients of a
 training step for the same workload.  With --train one step is a training
 step: e2ttt_chunk_forward with E2TTT_FLAG_SAVE_STATES, then
-e2ttt_chunk_backward on the same workspace (no recompute).
+e2ttt_chunk_backward on the same workspace (no recompute).  With --peaks it
+measures the chip's own bf16 MFMA and HBM ceilings instead.
 """
 from __future__ import annotations
 
@@ -306,6 +307,59 @@ def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
                       f"the workload), fp64 numpy closed form, {wall:.1f} s"}
 
 
+def run_peaks(torch) -> dict:
+    """The chip's own ceilings, next to the vendor peaks the roofline uses: bf16
+    MFMA throughput of the two shapes the kernels issue (independent
+    accumulations, 8 wavefronts per SIMD), HBM read bandwidth (grid-stride
+    16-byte loads) and a plain torch copy (read + write)."""
+    probe = ctypes.CDLL(os.path.join(ROOT, "chunk_weight_rnn_amd", "libe2ttt_probe.so"))
+    probe.e2ttt_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    probe.e2ttt_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e-3)
+        return best
+
+    res = {"probe": "peaks", "vendor": {"bf16_mfma_TFLOPs": PEAK_BF16_TFLOPS, "hbm_GBs": PEAK_HBM_GBS}}
+    grid, iters = ncu * 8, 2000
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    for shape, name, flop_wave_iter in [(0, "mfma_16x16x32_bf16", 8 * 16 * 16 * 32 * 2),
+                                        (2, "mfma_16x16x32_bf16_16acc", 16 * 16 * 16 * 32 * 2),
+                                        (3, "mfma_16x16x16_bf16", 8 * 16 * 16 * 16 * 2),
+                                        (1, "mfma_32x32x16_bf16", 4 * 32 * 32 * 16 * 2)]:
+        def launch(shape=shape):
+            assert probe.e2ttt_probe_mfma(shape, iters, ctypes.c_void_p(out.data_ptr()), grid, sp) == 0
+        t = timed(launch)
+        res[name + "_TFLOPs"] = grid * 4 * iters * flop_wave_iter / t / 1e12
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    rgrid = ncu * 16
+    rout = torch.empty(rgrid * 256, dtype=torch.float32, device="cuda")
+
+    def read():
+        assert probe.e2ttt_probe_read(ctypes.c_void_p(src.data_ptr()), n // 4, ctypes.c_void_p(rout.data_ptr()),
+                                      rgrid, sp) == 0
+    res["hbm_read_GBs"] = n * 4 / timed(read) / 1e9
+    dst = torch.empty_like(src)
+    res["hbm_copy_GBs"] = 2 * n * 4 / timed(lambda: dst.copy_(src)) / 1e9
+    res["note"] = ("min over 5 timed launches after 2 warm-up launches; 1 GiB buffers; "
+                   "the roofline in the benchmark line is priced against the vendor peaks")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +371,8 @@ def main() -> int:
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward saving states, then backward from them")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the chip's bf16 MFMA and HBM ceilings instead (one JSON line)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MiB",
                     help="first run a plain fp32 copy kernel over MiB of data (3 launches), so that a counter "
                          "profile of this command holds the HBM counters of a copy of known size")
@@ -340,6 +396,9 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    if args.peaks:
+        print(json.dumps(run_peaks(torch)), flush=True)
+        return 0
     cfg = synth.CONFIGS[args.config]
     if args.backward:
         print(json.dumps(run_backward(args, cfg, lib, e2, torch)), flush=True)

@@ -15,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libe2ttt.so")
+PROBE_LIB = os.path.join(PKG, "libe2ttt_probe.so")  # microbenchmarks of the chip's ceilings (bench.py --peaks)
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["abi.hip", "logscan.hip", "generic.hip", "generic_bwd.hip", "swiglu_loop.hip", "swiglu_mfma.hip",
            "swiglu_bwd.hip"]
 ARCH = "gfx950"
@@ -50,15 +52,20 @@ def build(verbose: bool = False) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+
+    def link(objects: list[str], lib: str) -> None:
+        tmp = lib + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objects, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
+
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 
