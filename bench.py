@@ -13,7 +13,8 @@ recompute, reverse chunk loop, scalar-kernel backward): the gradients of a
 training step for the same workload.  With --train one step is a training
 step: e2ttt_chunk_forward with E2TTT_FLAG_SAVE_STATES, then
 e2ttt_chunk_backward on the same workspace (no recompute).  With --peaks it
-measures the chip's own bf16 MFMA and HBM ceilings instead.
+measures the chip's own bf16 MFMA and HBM ceilings instead; --graph times
+replays of the forward call captured in a HIP graph.
 """
 from __future__ import annotations
 
@@ -213,6 +214,8 @@ def run_backward(args, cfg, lib, e2, torch) -> dict:
         "whole_call": whole,
         "stages_ms": st_ms,
     }
+    if graph:
+        res["graph"] = "each step replays one HIP graph of the whole call (no per-stage events)"
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_budget)
     return res
@@ -371,6 +374,8 @@ def main() -> int:
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward saving states, then backward from them")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="forward: capture the call in a HIP graph once and time its replays")
     ap.add_argument("--peaks", action="store_true",
                     help="measure the chip's bf16 MFMA and HBM ceilings instead (one JSON line)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MiB",
@@ -419,40 +424,55 @@ def main() -> int:
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     hev = HipEvents(4 * max(args.steps, 1))
 
-    def step(i=None):
+    def step(i=None, stream_handle=None):
         evs = None
         if i is not None:
             evs = (ctypes.c_void_p * 4)(*hev.ev[4 * i:4 * i + 4])
         st = lib.e2ttt_chunk_forward_events(ctypes.byref(desc), p(x["q"]), p(x["k"]), p(x["v"]), p(x["eta"]),
                                             p(x["alpha"]), p(x["beta"]), p(x["W0"]), p(x["M0"]), p(out), p(W),
-                                            p(M), p(ws), ctypes.c_size_t(ws_bytes), hs, evs)
+                                            p(M), p(ws), ctypes.c_size_t(ws_bytes), stream_handle or hs, evs)
         if st != 0:
             raise e2.E2TTTError("e2ttt_chunk_forward_events", st)
 
+    graph = None
+    if args.graph:  # the whole call captured once, then replayed
+        def on_current():
+            step(stream_handle=ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            on_current()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            on_current()
     for _ in range(args.warmup):
-        step()
+        graph.replay() if graph else step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        graph.replay() if graph else step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_step = 1e3 * wall / args.steps
-    stages = {"logscan": [], "loop": [], "apply": []}
-    for i in range(args.steps):
-        e = hev.ev[4 * i:4 * i + 4]
-        stages["logscan"].append(hev.elapsed_ms(e[0], e[1]))
-        stages["loop"].append(hev.elapsed_ms(e[1], e[2]))
-        stages["apply"].append(hev.elapsed_ms(e[2], e[3]))
-    st_ms = {k: sum(v) / len(v) for k, v in stages.items()}
+    st_ms = None
+    if not graph:
+        stages = {"logscan": [], "loop": [], "apply": []}
+        for i in range(args.steps):
+            e = hev.ev[4 * i:4 * i + 4]
+            stages["logscan"].append(hev.elapsed_ms(e[0], e[1]))
+            stages["loop"].append(hev.elapsed_ms(e[1], e[2]))
+            stages["apply"].append(hev.elapsed_ms(e[2], e[3]))
+        st_ms = {k: sum(v) / len(v) for k, v in stages.items()}
 
     tokens = cfg.B * cfg.T
     fpt = flops_per_token_head(cfg)
     heads_tokens = cfg.B * cfg.H * cfg.T
     peak = PEAK_BF16_TFLOPS if cfg.io_dtype == "bf16" and cfg.kind == "swiglu" else PEAK_F32_TFLOPS
     loop_flops = (fpt["grad"] + fpt["aggregate"]) * heads_tokens
-    loop_tflops = loop_flops / (st_ms["loop"] * 1e-3) / 1e12
+    loop_tflops = loop_flops / (st_ms["loop"] * 1e-3) / 1e12 if st_ms else None
     call_flops = sum(fpt.values()) * heads_tokens
     call_tflops = call_flops / (ms_step * 1e-3) / 1e12
     traffic = measured_traffic(0.0) if args.config == "swiglu_1p3b" else None
@@ -473,15 +493,18 @@ def main() -> int:
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "kind": cfg.kind, "loss": cfg.loss, "B": cfg.B,
                    "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk, "io": cfg.io_dtype,
                    "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg},
-        "roofline": {"bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
-                     "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,
-                     "traffic": traffic,
-                     "per_launch": f"{(fpt['grad'] + fpt['aggregate'])} flop/token/head x {heads_tokens} "
-                                   f"token-heads = {loop_flops:.4g} flop"},
+        "roofline": None if graph else {
+            "bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
+            "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,
+            "traffic": traffic,
+            "per_launch": f"{(fpt['grad'] + fpt['aggregate'])} flop/token/head x {heads_tokens} "
+                          f"token-heads = {loop_flops:.4g} flop"},
         "whole_call": {"tflops": call_tflops, "frac_of_peak": call_tflops / peak,
                        "hbm_alg_GBs": alg_bytes(cfg) / (ms_step * 1e-3) / 1e9},
         "stages_ms": st_ms,
     }
+    if graph:
+        res["graph"] = "each step replays one HIP graph of the whole call (no per-stage events)"
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(res), flush=True)
