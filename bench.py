@@ -214,8 +214,6 @@ def run_backward(args, cfg, lib, e2, torch) -> dict:
         "whole_call": whole,
         "stages_ms": st_ms,
     }
-    if graph:
-        res["graph"] = "each step replays one HIP graph of the whole call (no per-stage events)"
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_budget)
     return res
