@@ -83,6 +83,19 @@ def test_backward_shapes(T, chunk):
     _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
 
 
+@pytest.mark.parametrize("Hd,T,chunk", [(64, 128, 128), (320, 256, 128)])
+def test_backward_hidden_widths(Hd, T, chunk):
+    """One 64-unit slice, and five slices (the weight kernel's slice grid and
+    the token kernel's unit loop at other widths).  The 64-unit head runs one
+    chunk: over several chunks its bf16 error grows past the tolerance, as
+    the forward's does."""
+    cfg = SMALL.with_(T=T, chunk=chunk, Hd=Hd, name=f"bwd_Hd{Hd}_T{T}_C{chunk}")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=7, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=8)
+    _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
 def test_backward_full_size_sampled_heads():
     """The 1.3B-shaped workload (B=8, H=16, T=2048, chunk 256) in one call;
     two (b, h) pairs checked against the oracle."""
