@@ -6,6 +6,14 @@ kernels, fast-weight forward/backward at the chunk-start weights, both
 gradient aggregations, state transition and chunk outputs for every chunk of
 every (batch, head)), inputs resident in HBM.  Prints one JSON line.
 
+Timing protocol: W warm-up calls, then K timed calls.  Before each timed call
+a 512 MiB buffer is overwritten on the same stream (outside the call's
+events), so that neither the L2 caches nor the 256 MB last-level cache still
+hold the previous call's inputs or state.  Each call is timed by HIP events
+recorded inside it, on its own stream; ``ms_per_step`` and ``value`` use the
+median call time, and p10 / p90 / mean / min are reported beside it.
+``--no-flush`` times back-to-back calls instead.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--backward]
 
 With --backward one step is one e2ttt_chunk_backward call instead (forward
@@ -80,6 +88,7 @@ class HipEvents:
         self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
@@ -91,6 +100,38 @@ class HipEvents:
         assert self.rt.hipEventSynchronize(b) == 0
         assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return float(ms.value)
+
+
+FLUSH_BYTES = 512 << 20
+
+
+class Flusher:
+    """Overwrites a 512 MiB device buffer on the current stream between timed
+    calls (a fill kernel: every cache line it writes evicts older data)."""
+
+    def __init__(self, torch, enabled: bool):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if enabled else None
+        self.n = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.n += 1
+            self.buf.fill_(self.n & 255)
+
+
+def stats(ms: list) -> dict:
+    """median, p10, p90, mean, min of per-call times (ms)."""
+    v = sorted(ms)
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "mean": sum(v) / len(v), "min": v[0], "n": len(v)}
+
+
+def timing_record(call: dict, wall_ms: float, args) -> dict:
+    """How the step time was taken, for the JSON line."""
+    return {"per_call_ms": call, "wall_ms_per_step": wall_ms,
+            "flush": None if args.no_flush else f"{FLUSH_BYTES >> 20} MiB overwritten before each timed call",
+            "ms_per_step_is": "median of the per-call HIP-event times (the wall time per step includes the "
+                              "flush and host launch gaps)"}
 
 
 def code_fingerprint(path: str) -> str:
@@ -171,21 +212,27 @@ def run_backward(args, cfg, lib, e2, torch) -> dict:
         if st != 0:
             raise e2.E2TTTError("e2ttt_chunk_backward_events", st)
 
+    flush = Flusher(torch, not args.no_flush)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(i)
     torch.cuda.synchronize()
-    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    wall_ms = 1e3 * (time.perf_counter() - t0) / args.steps
     st = {"recompute": [], "reverse_loop": [], "scalar": []}
+    calls = []
     for i in range(args.steps):
         e = hev.ev[4 * i:4 * i + 4]
         st["recompute"].append(hev.elapsed_ms(e[0], e[1]))
         st["reverse_loop"].append(hev.elapsed_ms(e[1], e[2]))
         st["scalar"].append(hev.elapsed_ms(e[2], e[3]))
+        calls.append(hev.elapsed_ms(e[0], e[3]))
     st_ms = {k: sum(v) / len(v) for k, v in st.items()}
+    call = stats(calls)
+    ms_step = call["median"]
     th = cfg.B * cfg.H * cfg.T
     mfma_path = bool(lib.e2ttt_path(ctypes.byref(desc)) == 1)
     if mfma_path:
@@ -213,6 +260,7 @@ def run_backward(args, cfg, lib, e2, torch) -> dict:
         "roofline": roof,
         "whole_call": whole,
         "stages_ms": st_ms,
+        "timing": timing_record(call, wall_ms, args),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_budget)
@@ -250,16 +298,20 @@ def run_train(args, cfg, lib, e2, torch) -> dict:
         if st != 0:
             raise e2.E2TTTError("e2ttt_chunk_backward_events", st)
 
+    flush = Flusher(torch, not args.no_flush)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(i)
     torch.cuda.synchronize()
-    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    wall_ms = 1e3 * (time.perf_counter() - t0) / args.steps
     fw = [hev.elapsed_ms(hev.ev[8 * i], hev.ev[8 * i + 3]) for i in range(args.steps)]
     bw = [hev.elapsed_ms(hev.ev[8 * i + 4], hev.ev[8 * i + 7]) for i in range(args.steps)]
+    call = stats([hev.elapsed_ms(hev.ev[8 * i], hev.ev[8 * i + 7]) for i in range(args.steps)])
+    ms_step = call["median"]
     th = cfg.B * cfg.H * cfg.T
     f_fwd = sum(flops_per_token_head(cfg).values())
     fb = bwd_flops_per_token_head(cfg)
@@ -277,6 +329,7 @@ def run_train(args, cfg, lib, e2, torch) -> dict:
                        "flop_model": f"forward {f_fwd} + backward (token and weight kernels) {f_bwd} flop per "
                                      f"token and head"},
         "stages_ms": {"forward": sum(fw) / len(fw), "backward": sum(bw) / len(bw)},
+        "timing": timing_record(call, wall_ms, args),
     }
 
 
@@ -364,10 +417,12 @@ def run_peaks(torch) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="swiglu_1p3b", choices=list(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time back-to-back calls (no 512 MiB cache flush before each timed call)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward saving states, then backward from them")
@@ -445,25 +500,38 @@ def main() -> int:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             on_current()
+    flush = Flusher(torch, not args.no_flush)
+    gev = HipEvents(2 * max(args.steps, 1)) if graph else None
     for _ in range(args.warmup):
         graph.replay() if graph else step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        graph.replay() if graph else step(i)
+        flush()
+        if graph:
+            assert gev.rt.hipEventRecord(gev.ev[2 * i], hs) == 0
+            graph.replay()
+            assert gev.rt.hipEventRecord(gev.ev[2 * i + 1], hs) == 0
+        else:
+            step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_ms = 1e3 * (time.perf_counter() - t0) / args.steps
 
-    ms_step = 1e3 * wall / args.steps
     st_ms = None
     if not graph:
         stages = {"logscan": [], "loop": [], "apply": []}
+        calls = []
         for i in range(args.steps):
             e = hev.ev[4 * i:4 * i + 4]
             stages["logscan"].append(hev.elapsed_ms(e[0], e[1]))
             stages["loop"].append(hev.elapsed_ms(e[1], e[2]))
             stages["apply"].append(hev.elapsed_ms(e[2], e[3]))
+            calls.append(hev.elapsed_ms(e[0], e[3]))
         st_ms = {k: sum(v) / len(v) for k, v in stages.items()}
+    else:
+        calls = [gev.elapsed_ms(gev.ev[2 * i], gev.ev[2 * i + 1]) for i in range(args.steps)]
+    call = stats(calls)
+    ms_step = call["median"]
 
     tokens = cfg.B * cfg.T
     fpt = flops_per_token_head(cfg)
@@ -500,6 +568,7 @@ def main() -> int:
         "whole_call": {"tflops": call_tflops, "frac_of_peak": call_tflops / peak,
                        "hbm_alg_GBs": alg_bytes(cfg) / (ms_step * 1e-3) / 1e9},
         "stages_ms": st_ms,
+        "timing": timing_record(call, wall_ms, args),
     }
     if graph:
         res["graph"] = "each step replays one HIP graph of the whole call (no per-stage events)"

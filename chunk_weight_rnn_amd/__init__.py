@@ -84,20 +84,10 @@ def training_workspace(q, *, chunk: int, kind: str = "swiglu", loss: str = "negd
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=q.device)
 
 
-def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
-                  out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False,
-                  momentum: bool = True, chunk_avg: bool = False, save_states: bool = False, stream=None):
-    """Run the chunk update; returns (out, W_end, M_end).
-
-    q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
-    eta, alpha, beta: [B, H, T] float32; W0, M0: [B, H, P] float32.
-    ``W_end=W0`` / ``M_end=M0`` update the state in place.  With
-    ``momentum=False`` beta and M0 are ignored (may be None) and M_end is None.
-    ``save_states`` keeps in ``workspace`` (from training_workspace, required)
-    what chunk_backward(saved=True) needs, so that it skips its recompute.
-    """
-    if save_states and workspace is None:
-        raise ValueError("save_states needs the shared workspace from training_workspace()")
+def _forward_args(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic,
+                  momentum, chunk_avg, save_states):
+    """Argument checks and descriptor of chunk_forward;
+    returns (lib, desc, beta, M0, out, W_end, M_end)."""
     lib = library()
     if not momentum:
         beta = M0 = None
@@ -133,6 +123,26 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
         W_end = torch.empty_like(W0)
     if M_end is None and momentum:
         M_end = torch.empty_like(M0)
+    return lib, desc, beta, M0, out, W_end, M_end
+
+
+def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
+                  out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False,
+                  momentum: bool = True, chunk_avg: bool = False, save_states: bool = False, stream=None):
+    """Run the chunk update; returns (out, W_end, M_end).
+
+    q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
+    eta, alpha, beta: [B, H, T] float32; W0, M0: [B, H, P] float32.
+    ``W_end=W0`` / ``M_end=M0`` update the state in place.  With
+    ``momentum=False`` beta and M0 are ignored (may be None) and M_end is None.
+    ``save_states`` keeps in ``workspace`` (from training_workspace, required)
+    what chunk_backward(saved=True) needs, so that it skips its recompute.
+    """
+    if save_states and workspace is None:
+        raise ValueError("save_states needs the shared workspace from training_workspace()")
+    lib, desc, beta, M0, out, W_end, M_end = _forward_args(
+        q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic, momentum,
+        chunk_avg, save_states)
     ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
     if ws_bytes == ctypes.c_size_t(-1).value:
         raise E2TTTError("e2ttt_workspace_size", 1)

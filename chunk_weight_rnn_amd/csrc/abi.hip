@@ -3,9 +3,32 @@
 // dispatch of the device kernels on the caller's stream.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "e2ttt_internal.h"
 
 namespace e2ttt {
+
+hipError_t device_cu_count(int* ncu) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];  // 0 = not queried yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *ncu = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if (n < 1) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    *ncu = n;
+    return hipSuccess;
+}
 
 static bool desc_ok(const e2ttt_desc* d) {
     if (!d) return false;
@@ -13,6 +36,7 @@ static bool desc_ok(const e2ttt_desc* d) {
     if (d->loss < E2TTT_LOSS_MSE || d->loss > E2TTT_LOSS_NEGDOT) return false;
     if (d->io_dtype < E2TTT_F32 || d->io_dtype > E2TTT_BF16) return false;
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->D < 1 || d->chunk < 1) return false;
+    if (d->chunk > INT32_MAX) return false;  // kernels take the chunk length as a 32-bit int
     if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
     if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG |
                      E2TTT_FLAG_SAVE_STATES))
@@ -21,6 +45,19 @@ static bool desc_ok(const e2ttt_desc* d) {
     const int64_t lim = (int64_t)1 << 40;
     if (d->B > lim || d->H > lim || d->T > lim || d->D > 65536 || d->Hd > 65536) return false;
     if (d->B * d->H > lim || d->B * d->H * d->T > lim) return false;
+    return true;
+}
+
+// The fields e2ttt_logscan reads: sizes, the chunk length and the flags
+// (kind, loss, dtype, D and Hd are ignored there).
+static bool logscan_desc_ok(const e2ttt_desc* d) {
+    if (!d) return false;
+    if (d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1 || d->chunk > INT32_MAX) return false;
+    if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG |
+                     E2TTT_FLAG_SAVE_STATES))
+        return false;
+    const int64_t lim = (int64_t)1 << 40;
+    if (d->B > lim || d->H > lim || d->T > lim || d->B * d->H > lim || d->B * d->H * d->T > lim) return false;
     return true;
 }
 
@@ -458,11 +495,14 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
 
 int e2ttt_logscan(const e2ttt_desc* d, const float* eta, const float* alpha, const float* beta, float* cM,
                   float* cW, float* scal, void* stream) {
-    if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1) return E2TTT_ERR_INVALID_ARG;
+    if (!logscan_desc_ok(d)) return E2TTT_ERR_INVALID_ARG;
     const int64_t BH = d->B * d->H;
     if (BH * d->T == 0) return E2TTT_OK;
     if (!eta || !alpha || !cM || !cW || !scal) return E2TTT_ERR_INVALID_ARG;
     if (!beta && !(d->flags & E2TTT_FLAG_NO_MOMENTUM)) return E2TTT_ERR_INVALID_ARG;
+    const float* const ptrs[6] = {eta, alpha, beta, cM, cW, scal};
+    for (const float* p : ptrs)
+        if ((uintptr_t)p % alignof(float)) return E2TTT_ERR_INVALID_ARG;
     return launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, d->T, scal, (hipStream_t)stream) ==
                    hipSuccess
                ? E2TTT_OK

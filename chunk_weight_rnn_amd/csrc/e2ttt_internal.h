@@ -24,6 +24,10 @@ struct Workspace {
 
 Workspace workspace_layout(const e2ttt_desc& d, int path);
 
+// Compute units of the current device, queried once per device and cached
+// (launch sizing reads it on every call).
+hipError_t device_cu_count(int* ncu);
+
 // Launchers (return hipError_t of the launch).
 // cM / cW rows have stride ldc >= T; entries T .. ldc-1 are written as zeros.
 hipError_t launch_logscan(int64_t BH, int64_t T, int64_t chunk, int flags, const float* eta, const float* alpha,

@@ -612,10 +612,9 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.ldc = ldc;
     // 16-unit groups per workgroup: 32-unit slices (each wavefront gets a SIMD
     // of its own) on grids small enough for them, else 64-unit slices
-    int dev = 0, ncu = 0;
+    int ncu = 0;
     hipError_t e;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
     const int ug = loop_unit_groups(BH, d.Hd, ncu);
     la.nsl = (int)(d.Hd / (16 * ug));
     la.nwg = (int)(BH * la.nsl);

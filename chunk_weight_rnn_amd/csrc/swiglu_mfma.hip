@@ -377,9 +377,8 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     aa.nb = (int)BH;
     // persistent grid: as many workgroups as the compute units hold at once
-    int dev = 0, ncu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    int ncu = 0;
+    if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
     const int64_t nck = BH * aa.nc;
     auto grid = [&](int64_t items, int per_cu) {
         const int64_t cap = (int64_t)ncu * per_cu;

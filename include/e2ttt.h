@@ -74,10 +74,10 @@ typedef enum {
  * W_end = prod(alpha) W0 - sum_t alpha(t:end] eta_t g_t. */
 #define E2TTT_FLAG_NO_MOMENTUM 2
 /* Chunk average: the chunk-averaged ablation of the same paper (atlas summary,
- * "Surprising findings": per-token factors collapsed to chunk scalars).  The
- * per-token momentum and weight kernels m_t, w_t are replaced by their mean
- * over the chunk; each token keeps its own eta_t, and the chunk scalars
- * prod alpha, prod beta, gamma are unchanged.  Combines with NO_MOMENTUM. */
+ * "Surprising findings"), read as: the per-token momentum and weight kernels
+ * m_t, w_t are replaced by their mean over the chunk; each token keeps its
+ * own eta_t, and the chunk scalars prod alpha, prod beta, gamma are
+ * unchanged.  Combines with NO_MOMENTUM. */
 #define E2TTT_FLAG_CHUNK_AVG 4
 /* Save states for the backward (training): with this flag the forward and
  * the backward share one workspace, sized by e2ttt_workspace_size() ==
@@ -116,7 +116,7 @@ E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
  * Host-only validation of a call, touching no device memory (usable without
  * a GPU).  ptrs[] holds, in order: q, k, v, eta, alpha, beta, W0, M0, out,
  * W_end, M_end.  Returns E2TTT_OK or the first problem found:
- *   - sizes: B, H, T >= 0; D >= 1; chunk >= 1; Hd >= 1 for MLP / SWIGLU;
+ *   - sizes: B, H, T >= 0; D >= 1; 1 <= chunk <= 2^31 - 1; Hd >= 1 for MLP / SWIGLU;
  *     enums and flags in range (E2TTT_ERR_INVALID_ARG);
  *   - pointers: non-null when the tensor is non-empty, 16-byte aligned
  *     (eta, alpha, beta: 4-byte aligned) (E2TTT_ERR_INVALID_ARG); with
@@ -130,7 +130,12 @@ E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
 E2TTT_API int e2ttt_validate(const e2ttt_desc* desc, const void* const ptrs[11]);
 
 /*
- * The chunk update over whole sequences (the hot path).
+ * The chunk update over whole sequences (the hot path).  "Rethinking
+ * Expressivity and Efficiency in Test-Time Training": abstract (gradients at
+ * the chunk-start weights, closed-form transition to the exact chunk-end
+ * fast weight and momentum), atlas summary "Approach" (momentum and weight
+ * kernels from log-space sums, two weighted gradient aggregations), arxivlens
+ * "Limitations" (the chunk output from the chunk-start weights).
  *   q, k, v   [B][H][T][D]  io_dtype, contiguous
  *   eta, alpha, beta [B][H][T] fp32 (domain: eta >= 0, alpha, beta in [0, 1])
  *   W0, M0    [B][H][P] fp32 chunk-0 fast weight and momentum
@@ -167,7 +172,10 @@ E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
                         void* const events[4]);
 
 /*
- * The scalar-kernel step alone (per-subsystem parity).  For every chunk of
+ * The scalar-kernel step alone (per-subsystem parity): the momentum and weight
+ * kernels of "Rethinking Expressivity and Efficiency in Test-Time Training"
+ * (atlas summary "Approach"; the log-space suffix sums the arxivlens
+ * "Results" section counts as the method's overhead).  For every chunk of
  * every (b, h), from log-space suffix sums of log alpha and log beta:
  *   cM[b][h][t] = eta_t * m_t,  m_t = prod_{s after t in its chunk} beta_s
  *   cW[b][h][t] = eta_t * w_t,  w_t = sum_{tau >= t} alpha(tau:end] * beta(t:tau]
@@ -176,7 +184,9 @@ E2TTT_API int e2ttt_chunk_forward_events(const e2ttt_desc* desc,
  * (a shorter last chunk takes the same sums over its tokens).
  * Only desc->B, H, T, chunk and flags are read: E2TTT_FLAG_NO_MOMENTUM takes
  * beta = 0 (beta may be NULL), E2TTT_FLAG_CHUNK_AVG replaces m_t and w_t by
- * their chunk means.
+ * their chunk means.  E2TTT_ERR_INVALID_ARG for negative sizes, chunk outside
+ * [1, 2^31 - 1], unknown flag bits, or a null or misaligned pointer (for a
+ * non-empty call).  The outputs must not overlap the inputs.
  */
 E2TTT_API int e2ttt_logscan(const e2ttt_desc* desc, const float* eta, const float* alpha, const float* beta,
                   float* cM, float* cW, float* scal, void* stream);

@@ -66,8 +66,7 @@ Variants (flags of ``chunk_forward``):
   name a tail-length helper among the official code's functions; the
   plainest reading is a shorter last chunk).
 * ``chunk_avg=True``: the chunk-averaged variant the pages report as an
-  ablation (atlas, "Surprising findings": per-token factors collapsed to chunk
-  scalars).  Reading: the per-token kernel values m_i and w_i are replaced by
+  ablation (atlas, "Surprising findings").  Reading: the per-token kernel values m_i and w_i are replaced by
   their mean over the chunk, the per-token learning rate eta_i is kept, and
   the chunk scalars A, Bb, gamma are unchanged.  It is defined by this closed
   form (there is no per-token recurrence behind it).

@@ -139,7 +139,7 @@ def test_validate_unsupported_shape(lib):
 
 
 def test_chunk_forward_rejects_before_launch(lib):
-    d = _desc(flags=16)  # unknown flag
+    d = _desc(flags=1 << 20)  # unknown flag
     v = ctypes.c_void_p
     args = [v(1 << 40)] * 11
     assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(0), ctypes.c_size_t(0), v(0)) == 1
@@ -151,6 +151,36 @@ def test_chunk_forward_rejects_before_launch(lib):
     assert lib.e2ttt_chunk_forward(ctypes.byref(d), *args, v(1 << 50), ctypes.c_size_t(16), v(0)) == 4
     assert lib.e2ttt_chunk_forward(None, *args, v(0), ctypes.c_size_t(0), v(0)) == 1
     assert lib.e2ttt_logscan(None, v(0), v(0), v(0), v(0), v(0), v(0), v(0)) == 1
+
+
+def test_chunk_beyond_int32_rejected(lib):
+    """Kernels take the chunk length as a 32-bit int: a longer chunk is
+    refused rather than truncated (2^32 + 16 would otherwise run as 16)."""
+    for c in ((1 << 31), (1 << 32) + 16):
+        d = _desc(T=256, chunk=c)
+        assert _validate(lib, d, _ptrs(d)) == 1
+        assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    d = _desc(T=256, chunk=(1 << 31) - 1)  # the largest chunk: one chunk of T tokens
+    assert _validate(lib, d, _ptrs(d)) == 0
+
+
+def test_logscan_validates_its_desc(lib):
+    """e2ttt_logscan returns E2TTT_ERR_INVALID_ARG before any launch for
+    unknown flags, a chunk outside [1, 2^31 - 1], negative sizes and
+    misaligned pointers."""
+    v = ctypes.c_void_p
+    good = [v((1 << 40) + i * (1 << 32)) for i in range(6)]
+    for d in (_desc(flags=1 << 20), _desc(chunk=(1 << 32) + 16), _desc(chunk=0), _desc(T=-1)):
+        assert lib.e2ttt_logscan(ctypes.byref(d), *good, v(0)) == 1
+    bad = list(good)
+    bad[3] = v(good[3].value + 2)  # cM not float-aligned
+    assert lib.e2ttt_logscan(ctypes.byref(_desc()), *bad, v(0)) == 1
+    # null beta is only allowed without momentum
+    nob = list(good)
+    nob[2] = v(0)
+    assert lib.e2ttt_logscan(ctypes.byref(_desc()), *nob, v(0)) == 1
+    # an empty call touches nothing and succeeds
+    assert lib.e2ttt_logscan(ctypes.byref(_desc(B=0)), *[v(0)] * 6, v(0)) == 0
 
 
 def test_status_strings(lib):
