@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, FLAG_SAVE_STATES, make_desc
 
-__all__ = ["chunk_forward", "chunk_backward", "chunk_update", "training_workspace", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
+__all__ = ["chunk_forward", "chunk_forward_noalloc", "chunk_backward", "chunk_update", "training_workspace", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
 
 
@@ -86,7 +86,7 @@ def training_workspace(q, *, chunk: int, kind: str = "swiglu", loss: str = "negd
 
 def _forward_args(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic,
                   momentum, chunk_avg, save_states):
-    """Argument checks and descriptor of chunk_forward;
+    """Checks and descriptor shared by chunk_forward and chunk_forward_noalloc;
     returns (lib, desc, beta, M0, out, W_end, M_end)."""
     lib = library()
     if not momentum:
@@ -153,6 +153,24 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
                                  _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(stream))
     if st != 0:
         raise E2TTTError("e2ttt_chunk_forward", st)
+    return out, W_end, M_end
+
+
+def chunk_forward_noalloc(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
+                          out=None, W_end=None, M_end=None, force_generic: bool = False, momentum: bool = True,
+                          chunk_avg: bool = False, stream=None):
+    """chunk_forward through e2ttt_chunk_forward_noalloc: the library's own
+    per-GPU scratch instead of a workspace (no device allocation by the
+    library; pass ``out``, ``W_end`` and ``M_end`` to allocate nothing here
+    either).  Calls that overlap in time on one GPU race on that scratch."""
+    lib, desc, beta, M0, out, W_end, M_end = _forward_args(
+        q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic, momentum,
+        chunk_avg, False)
+    st = lib.e2ttt_chunk_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha),
+                                         _ptr(beta), _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end),
+                                         _stream_handle(stream))
+    if st != 0:
+        raise E2TTTError("e2ttt_chunk_forward_noalloc", st)
     return out, W_end, M_end
 
 

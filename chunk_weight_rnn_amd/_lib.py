@@ -15,12 +15,13 @@ FLAG_CHUNK_AVG = 4
 FLAG_SAVE_STATES = 8
 
 STATUS = {0: "E2TTT_OK", 1: "E2TTT_ERR_INVALID_ARG", 2: "E2TTT_ERR_UNSUPPORTED", 3: "E2TTT_ERR_ALIAS",
-          4: "E2TTT_ERR_WORKSPACE", 5: "E2TTT_ERR_HIP"}
+          4: "E2TTT_ERR_WORKSPACE", 5: "E2TTT_ERR_HIP", 6: "E2TTT_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # E2TTT_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("e2ttt_param_count", "e2ttt_workspace_size", "e2ttt_path", "e2ttt_validate",
            "e2ttt_chunk_forward", "e2ttt_chunk_forward_events", "e2ttt_logscan", "e2ttt_status_string",
            "e2ttt_backward_workspace_size", "e2ttt_validate_backward", "e2ttt_chunk_backward",
-           "e2ttt_chunk_backward_events")
+           "e2ttt_chunk_backward_events", "e2ttt_chunk_forward_noalloc")
 
 
 class Desc(ctypes.Structure):
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.e2ttt_chunk_forward.restype = ctypes.c_int
     lib.e2ttt_chunk_forward_events.argtypes = [pd] + [vp] * 11 + [vp, sz, vp, ctypes.POINTER(vp)]
     lib.e2ttt_chunk_forward_events.restype = ctypes.c_int
+    lib.e2ttt_chunk_forward_noalloc.argtypes = [pd] + [vp] * 11 + [vp]
+    lib.e2ttt_chunk_forward_noalloc.restype = ctypes.c_int
     lib.e2ttt_logscan.argtypes = [pd] + [vp] * 6 + [vp]
     lib.e2ttt_logscan.restype = ctypes.c_int
     lib.e2ttt_backward_workspace_size.argtypes = [pd]

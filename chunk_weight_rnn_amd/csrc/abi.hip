@@ -4,10 +4,44 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "e2ttt_internal.h"
 
+// Scratch of e2ttt_chunk_forward_noalloc: a file-scope device array, one copy
+// per GPU, allocated when the code object loads and held until the process
+// ends.  Host code never uses its name as an address: the address of the
+// current device's copy comes from hipGetSymbolAddress (scratch_address).
+static __device__ __align__(256) unsigned char scratch[E2TTT_NOALLOC_SCRATCH_BYTES];
+
 namespace e2ttt {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];  // per device, filled on its first no-allocation call
+std::mutex scratch_mu;
+}  // namespace
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+static hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 hipError_t device_cu_count(int* ncu) {
     constexpr int kMaxDevices = 64;
@@ -325,6 +359,22 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     return e == hipSuccess ? E2TTT_OK : E2TTT_ERR_HIP;
 }
 
+int e2ttt_chunk_forward_noalloc(const e2ttt_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                                const float* alpha, const float* beta, const float* W0, const float* M0, void* out,
+                                float* W_end, float* M_end, void* stream) {
+    const void* ptrs[11] = {q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end};
+    const int st = e2ttt_validate(d, ptrs);
+    if (st != E2TTT_OK) return st;
+    // saved states would not survive the next call on this GPU
+    if (d->flags & E2TTT_FLAG_SAVE_STATES) return E2TTT_ERR_INVALID_ARG;
+    const size_t need = e2ttt_workspace_size(d);
+    if (need > (size_t)E2TTT_NOALLOC_SCRATCH_BYTES) return E2TTT_ERR_SCRATCH_LIMIT;  // before any device call
+    void* ws = nullptr;
+    if (need > 0 && scratch_address(&ws) != hipSuccess) return E2TTT_ERR_HIP;
+    return e2ttt_chunk_forward_events(d, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws,
+                                      need > 0 ? (size_t)E2TTT_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
+}
+
 size_t e2ttt_backward_workspace_size(const e2ttt_desc* d) {
     if (!desc_ok(d)) return (size_t)-1;
     return bwd_workspace_layout(*d).total;
@@ -517,6 +567,7 @@ const char* e2ttt_status_string(int s) {
         case E2TTT_ERR_ALIAS: return "output aliases another buffer";
         case E2TTT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case E2TTT_ERR_HIP: return "HIP launch failed";
+        case E2TTT_ERR_SCRATCH_LIMIT: return "call needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }

@@ -32,9 +32,10 @@
  *   - Return values report argument validation synchronously; a failed
  *     kernel launch returns E2TTT_ERR_HIP.  No exception crosses the ABI.
  *   - NaN/Inf in the inputs propagate; the hot path performs no checks.
- *   - The library keeps no mutable global state; calls on different streams
- *     may run concurrently as long as they do not share output or workspace
- *     buffers.
+ *   - The library keeps no mutable global state other than the scratch of
+ *     e2ttt_chunk_forward_noalloc; calls on different streams may run
+ *     concurrently as long as they do not share output or workspace buffers
+ *     (or, for e2ttt_chunk_forward_noalloc, the GPU).
  */
 #ifndef E2TTT_H
 #define E2TTT_H
@@ -62,7 +63,9 @@ typedef enum {
     E2TTT_ERR_UNSUPPORTED = 2, /* shape outside what any kernel handles (e.g. D > 256, Hd > 1024) */
     E2TTT_ERR_ALIAS = 3,       /* an output overlaps an input or another output */
     E2TTT_ERR_WORKSPACE = 4,   /* workspace null or smaller than e2ttt_workspace_size() */
-    E2TTT_ERR_HIP = 5          /* a kernel launch failed */
+    E2TTT_ERR_HIP = 5,         /* a kernel launch failed */
+    E2TTT_ERR_SCRATCH_LIMIT = 6 /* e2ttt_chunk_forward_noalloc: the call needs more than
+                                   E2TTT_NOALLOC_SCRATCH_BYTES of scratch */
 } e2ttt_status;
 
 /* flags */
@@ -154,6 +157,34 @@ E2TTT_API int e2ttt_chunk_forward(const e2ttt_desc* desc,
                         const float* W0, const float* M0,
                         void* out, float* W_end, float* M_end,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * e2ttt_chunk_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * (e.g. one chunk per call on a carried state), harnesses that forbid
+ * allocation.  It allocates nothing and calls no allocating routine.  Its
+ * scratch is a device array built into the library, E2TTT_NOALLOC_SCRATCH_BYTES
+ * per GPU, present on every GPU the library runs on until the process ends.
+ * Arguments, layouts, results and aliasing rules as e2ttt_chunk_forward
+ * (results are identical to it bit for bit).  Errors:
+ *   - E2TTT_ERR_SCRATCH_LIMIT when e2ttt_workspace_size(desc) exceeds
+ *     E2TTT_NOALLOC_SCRATCH_BYTES (checked before any device call; e.g. one
+ *     256-token chunk of a B = 8, H = 16, D = 128, Hd = 256 SwiGLU layer needs
+ *     25.4 MB and fits, its whole 2048-token sequence needs 203 MB and does not);
+ *   - E2TTT_ERR_INVALID_ARG with E2TTT_FLAG_SAVE_STATES (a saved state would
+ *     not survive the next call on the GPU);
+ *   - the others as e2ttt_chunk_forward.
+ * Every call on a GPU uses that GPU's one scratch array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race and give wrong
+ * results.  Calls on one stream are ordered and safe.  Nothing in the scratch
+ * needs to start at zero, and nothing is kept from one call to the next.
+ */
+#define E2TTT_NOALLOC_SCRATCH_BYTES (64u << 20)
+E2TTT_API int e2ttt_chunk_forward_noalloc(const e2ttt_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        const float* eta, const float* alpha, const float* beta,
+                        const float* W0, const float* M0,
+                        void* out, float* W_end, float* M_end, void* stream);
 
 /*
  * e2ttt_chunk_forward plus per-stage timing for profilers and benchmarks.

@@ -29,7 +29,7 @@ def _desc(kind="swiglu", loss="negdot", io="bf16", B=2, H=3, T=256, D=128, Hd=25
 
 def test_exports_every_declared_symbol(lib):
     names = set(re.findall(r"E2TTT_API[^;(]*?\b(e2ttt_\w+)\s*\(", open(HEADER).read()))
-    assert len(names) == 12
+    assert len(names) == 13
     from chunk_weight_rnn_amd import _lib
     assert names == set(_lib.EXPORTS)
     for n in names:
@@ -184,7 +184,7 @@ def test_logscan_validates_its_desc(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.e2ttt_status_string(s)
     assert lib.e2ttt_status_string(99) == b"unknown status"
 
