@@ -427,6 +427,8 @@ def main() -> int:
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward saving states, then backward from them")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--precise", action="store_true",
+                    help="forward: E2TTT_FLAG_PRECISE (hi/lo bf16 operands on the SwiGLU MFMA path)")
     ap.add_argument("--graph", action="store_true",
                     help="forward: capture the call in a HIP graph once and time its replays")
     ap.add_argument("--peaks", action="store_true",
@@ -469,7 +471,7 @@ def main() -> int:
     W = torch.empty_like(x["W0"])
     M = torch.empty_like(x["M0"])
     desc = e2._lib.make_desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk,
-                             cfg.flags)
+                             cfg.flags | (e2._lib.FLAG_PRECISE if args.precise else 0))
     ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -558,7 +560,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "kind": cfg.kind, "loss": cfg.loss, "B": cfg.B,
                    "H": cfg.H, "T": cfg.T, "D": cfg.D, "Hd": cfg.Hd, "chunk": cfg.chunk, "io": cfg.io_dtype,
-                   "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg},
+                   "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg,
+                   "precise": bool(args.precise)},
         "roofline": None if graph else {
             "bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
             "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,

@@ -22,7 +22,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, FLAG_SAVE_STATES, make_desc
+from ._lib import (E2TTTError, FLAG_CHUNK_AVG, FLAG_FORCE_GENERIC, FLAG_NO_MOMENTUM, FLAG_PRECISE, FLAG_SAVE_STATES,
+                   make_desc)
 
 __all__ = ["chunk_forward", "chunk_forward_noalloc", "chunk_backward", "chunk_update", "training_workspace", "logscan", "workspace_size", "param_count", "path", "validate", "E2TTTError",
            "library"]
@@ -85,7 +86,7 @@ def training_workspace(q, *, chunk: int, kind: str = "swiglu", loss: str = "negd
 
 
 def _forward_args(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic,
-                  momentum, chunk_avg, save_states):
+                  momentum, chunk_avg, save_states, precise=False):
     """Checks and descriptor shared by chunk_forward and chunk_forward_noalloc;
     returns (lib, desc, beta, M0, out, W_end, M_end)."""
     lib = library()
@@ -108,7 +109,8 @@ def _forward_args(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out,
             raise TypeError(f"{name} must be float32")
     B, H, T, D = q.shape
     flags = (FLAG_FORCE_GENERIC if force_generic else 0) | (0 if momentum else FLAG_NO_MOMENTUM) | \
-        (FLAG_CHUNK_AVG if chunk_avg else 0) | (FLAG_SAVE_STATES if save_states else 0)
+        (FLAG_CHUNK_AVG if chunk_avg else 0) | (FLAG_SAVE_STATES if save_states else 0) | \
+        (FLAG_PRECISE if precise else 0)
     desc = make_desc(kind, loss, io, B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
     if tuple(W0.shape) != (B, H, P) or (M0 is not None and tuple(M0.shape) != (B, H, P)):
@@ -128,7 +130,8 @@ def _forward_args(q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out,
 
 def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
                   out=None, W_end=None, M_end=None, workspace=None, force_generic: bool = False,
-                  momentum: bool = True, chunk_avg: bool = False, save_states: bool = False, stream=None):
+                  momentum: bool = True, chunk_avg: bool = False, save_states: bool = False, precise: bool = False,
+                  stream=None):
     """Run the chunk update; returns (out, W_end, M_end).
 
     q, k, v: [B, H, T, D] float32 or bfloat16 (same dtype), contiguous, on GPU;
@@ -137,12 +140,14 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
     ``momentum=False`` beta and M0 are ignored (may be None) and M_end is None.
     ``save_states`` keeps in ``workspace`` (from training_workspace, required)
     what chunk_backward(saved=True) needs, so that it skips its recompute.
+    ``precise`` (E2TTT_FLAG_PRECISE): hi/lo bf16 operands on the SwiGLU MFMA
+    path, for states the bf16 operands cannot follow closely enough.
     """
     if save_states and workspace is None:
         raise ValueError("save_states needs the shared workspace from training_workspace()")
     lib, desc, beta, M0, out, W_end, M_end = _forward_args(
         q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic, momentum,
-        chunk_avg, save_states)
+        chunk_avg, save_states, precise)
     ws_bytes = int(lib.e2ttt_workspace_size(ctypes.byref(desc)))
     if ws_bytes == ctypes.c_size_t(-1).value:
         raise E2TTTError("e2ttt_workspace_size", 1)
@@ -158,14 +163,14 @@ def chunk_forward(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, l
 
 def chunk_forward_noalloc(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind: str, loss: str, Hd: int = 0,
                           out=None, W_end=None, M_end=None, force_generic: bool = False, momentum: bool = True,
-                          chunk_avg: bool = False, stream=None):
+                          chunk_avg: bool = False, precise: bool = False, stream=None):
     """chunk_forward through e2ttt_chunk_forward_noalloc: the library's own
     per-GPU scratch instead of a workspace (no device allocation by the
     library; pass ``out``, ``W_end`` and ``M_end`` to allocate nothing here
     either).  Calls that overlap in time on one GPU race on that scratch."""
     lib, desc, beta, M0, out, W_end, M_end = _forward_args(
         q, k, v, eta, alpha, beta, W0, M0, chunk, kind, loss, Hd, out, W_end, M_end, force_generic, momentum,
-        chunk_avg, False)
+        chunk_avg, False, precise)
     st = lib.e2ttt_chunk_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha),
                                          _ptr(beta), _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end),
                                          _stream_handle(stream))
@@ -176,12 +181,14 @@ def chunk_forward_noalloc(q, k, v, eta, alpha, beta, W0, M0, *, chunk: int, kind
 
 def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, chunk: int, Hd: int,
                    kind: str = "swiglu", loss: str = "negdot", momentum: bool = True, chunk_avg: bool = False,
-                   force_generic: bool = False, workspace=None, saved: bool = False, stream=None):
+                   force_generic: bool = False, precise: bool = False, workspace=None, saved: bool = False,
+                   stream=None):
     """Gradients of <dout, out> + <dW_end, W_end> + <dM_end, M_end> through
     ``chunk_forward``; returns a dict with keys q, k, v (the I/O dtype), eta,
     alpha, beta, W0, M0 (float32).  Without momentum beta, M0 and dM_end are
     ignored and the beta / M0 gradients are None.  ``force_generic`` takes the
-    portable fp32 backward where the SwiGLU MFMA one applies.  ``saved``:
+    portable fp32 backward where the SwiGLU MFMA one applies; so does
+    ``precise`` (the backward of a precise forward).  ``saved``:
     ``workspace`` holds the states a chunk_forward(save_states=True) call on
     the same inputs left in it; the forward is then not recomputed."""
     if saved and workspace is None:
@@ -204,7 +211,8 @@ def chunk_backward(q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, *, c
             raise TypeError(f"{name} must be {want}")
     B, H, T, D = q.shape
     flags = (0 if momentum else FLAG_NO_MOMENTUM) | (FLAG_CHUNK_AVG if chunk_avg else 0) | \
-        (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_SAVE_STATES if saved else 0)
+        (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_SAVE_STATES if saved else 0) | \
+        (FLAG_PRECISE if precise else 0)
     desc = make_desc(kind, loss, _io_name(q), B, H, T, D, Hd, chunk, flags)
     P = int(lib.e2ttt_param_count(ctypes.byref(desc)))
     for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("dout", dout, q.shape),

@@ -13,6 +13,7 @@ FLAG_FORCE_GENERIC = 1
 FLAG_NO_MOMENTUM = 2
 FLAG_CHUNK_AVG = 4
 FLAG_SAVE_STATES = 8
+FLAG_PRECISE = 16
 
 STATUS = {0: "E2TTT_OK", 1: "E2TTT_ERR_INVALID_ARG", 2: "E2TTT_ERR_UNSUPPORTED", 3: "E2TTT_ERR_ALIAS",
           4: "E2TTT_ERR_WORKSPACE", 5: "E2TTT_ERR_HIP", 6: "E2TTT_ERR_SCRATCH_LIMIT"}

@@ -73,7 +73,7 @@ static bool desc_ok(const e2ttt_desc* d) {
     if (d->chunk > INT32_MAX) return false;  // kernels take the chunk length as a 32-bit int
     if (d->kind != E2TTT_LINEAR && d->Hd < 1) return false;
     if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG |
-                     E2TTT_FLAG_SAVE_STATES))
+                     E2TTT_FLAG_SAVE_STATES | E2TTT_FLAG_PRECISE))
         return false;
     // keep every product used for indexing far from int64 overflow
     const int64_t lim = (int64_t)1 << 40;
@@ -88,15 +88,18 @@ static bool logscan_desc_ok(const e2ttt_desc* d) {
     if (!d) return false;
     if (d->B < 0 || d->H < 0 || d->T < 0 || d->chunk < 1 || d->chunk > INT32_MAX) return false;
     if (d->flags & ~(E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_NO_MOMENTUM | E2TTT_FLAG_CHUNK_AVG |
-                     E2TTT_FLAG_SAVE_STATES))
+                     E2TTT_FLAG_SAVE_STATES | E2TTT_FLAG_PRECISE))
         return false;
     const int64_t lim = (int64_t)1 << 40;
     if (d->B > lim || d->H > lim || d->T > lim || d->B * d->H > lim || d->B * d->H * d->T > lim) return false;
     return true;
 }
 
+// 0: portable fp32 kernel, 1: SwiGLU bf16 MFMA path, 2: the same with hi/lo
+// bf16 operands (E2TTT_FLAG_PRECISE)
 static int path_of(const e2ttt_desc& d) {
-    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d)) return 1;
+    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d))
+        return (d.flags & E2TTT_FLAG_PRECISE) ? 2 : 1;
     return 0;
 }
 
@@ -110,7 +113,8 @@ static bool generic_supported(const e2ttt_desc& d) {
 // 1: SwiGLU MFMA backward, 0: portable fp32 backward, -1: unsupported
 static int backward_path(const e2ttt_desc& d) {
     if (d.chunk > 2048) return -1;  // the scalar backward stages one chunk in LDS
-    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d) &&
+    // a precise forward is differentiated by the portable fp32 backward
+    if (!(d.flags & (E2TTT_FLAG_FORCE_GENERIC | E2TTT_FLAG_PRECISE)) && swiglu_mfma_supported(d) &&
         d.T * d.D * 2 < ((int64_t)1 << 31) && 6 * d.Hd * d.D * 2 < ((int64_t)1 << 31))  // 32-bit copy offsets
         return 1;
     if (generic_supported(d) && generic_bwd_token_block(d) > 0) return 0;
@@ -347,7 +351,7 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
     const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
-    if (path == 1) {
+    if (path >= 1) {
         e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap,
                                save && mom ? wsb + bws.snapM : nullptr, s, ev[2]);
     } else {

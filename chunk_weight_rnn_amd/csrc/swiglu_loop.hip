@@ -41,6 +41,12 @@
 // gradient waves wait one extra half-block: the next chunk's grad operands
 // are the state after the previous chunk's last aggregation.
 //
+// Precise form (E2TTT_FLAG_PRECISE): the chunk-start weights in the grad
+// products, the factors handed to the state waves and the coefficient-scaled
+// aggregation operands are hi/lo bf16 pairs (16 significant bits), each
+// product two MFMAs into the same fp32 accumulator.  On 32-unit slices, one
+// wavefront per SIMD, with a 24 KB exchange area per unit group.
+//
 // LDS (150.5 KB; 123 KB for 32-unit slices): three 64-token K/V/coefficient
 // blocks (the state waves' block, the gradient waves' block, one in flight
 // from HBM) and per unit group a 12 KB exchange area: two half-block factor
@@ -66,8 +72,12 @@ constexpr int KVB = CB * 256;      // one [64][128] bf16 token block
 constexpr int COB = 1024;          // cM [64] f32 | cW [64] f32 | spare
 constexpr int KVBUF = 2 * KVB + COB;
 constexpr int NBUF = 3;            // token blocks resident in LDS
-constexpr int XW = 12 * 1024;      // exchange area per unit group
-constexpr int FACB = 3 * 1024;     // one half-block factor set (3 x 64 lanes x 16 B)
+// Exchange area per unit group: two half-block factor sets, or at a chunk
+// boundary the 12 bf16 grad operand fragments (64 lanes x 16 B each).  The
+// precise form (PRE) hands every operand over as a hi/lo bf16 pair: twice
+// the fragments, twice the area.
+template <bool PRE> constexpr int XW = (PRE ? 24 : 12) * 1024;
+template <bool PRE> constexpr int FACB = (PRE ? 6 : 3) * 1024;  // one half-block factor set
 constexpr int RSRC_W3 = 0x00020000;  // dword 3 of a raw buffer resource (32-bit format, no swizzle)
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -82,6 +92,17 @@ __device__ __forceinline__ bf16x4 pack4(f32x4 v) {
 }
 
 __device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): together 16
+// significant bits, against 8 for hi alone.  hi / lo are summed by two
+// MFMAs into one fp32 accumulator.
+__device__ __forceinline__ void split4(f32x4 v, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+}
 
 // 16-byte chunk swizzle of 256-byte token rows: chunk c of row t sits at
 // physical chunk c ^ swz4(t).  The LDS has 64 four-byte banks: ds_read_b128
@@ -202,10 +223,21 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][8], float* W, float*
 // SPREAD: the gradient waves store the weight snapshots, a few fragments per
 // half-block (short chunks); else the state waves store them at the chunk
 // boundary.
-template <bool MOM, bool SAVEM, int UG, bool SPREAD>
-__global__ void __attribute__((amdgpu_flat_work_group_size(128 * UG, 128 * UG), amdgpu_waves_per_eu(2, 2)))
+// PRE (precise form): every bf16 MFMA operand that is not an input -- the
+// chunk-start weights in the grad products and the coefficient-scaled
+// factors in the aggregation -- is a hi/lo bf16 pair summed by two MFMAs,
+// and the gradient waves hand the factors over as hi/lo pairs too.  Twice the
+// MFMAs and operand registers: 32-unit slices, one wavefront per SIMD (up to
+// 512 registers each).  The chunk-start weight snapshot for the output stays
+// the hi part.
+template <bool MOM, bool SAVEM, int UG, bool SPREAD, bool PRE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(128 * UG, 128 * UG),
+                               amdgpu_waves_per_eu(PRE ? 1 : 2, PRE ? 1 : 2)))
 swiglu_loop_kernel(LoopArgs a) {
     static_assert(UG == 2 || UG == 4, "unit groups per workgroup");
+    static_assert(!PRE || (UG == 2 && !SAVEM), "the precise form: 32-unit slices, weight snapshots only");
+    constexpr int XWB = XW<PRE>;
+    constexpr int FSET = FACB<PRE>;
     constexpr int S = 16 * UG;     // hidden units per workgroup slice
     constexpr int RPW = CB / UG;   // token rows each state wave copies per block
     // MOM = false: the recurrence without momentum; the scalar kernels then
@@ -214,7 +246,7 @@ swiglu_loop_kernel(LoopArgs a) {
     // SAVEM: also write a bf16 snapshot of every chunk's start momentum, in
     // the layout of the weight snapshot (for the backward pass).
     __shared__ __attribute__((aligned(16))) unsigned char kvs[NBUF * KVBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char xch[UG * XW];
+    __shared__ __attribute__((aligned(16))) unsigned char xch[UG * XWB];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int u = wave & (UG - 1);
@@ -236,7 +268,7 @@ swiglu_loop_kernel(LoopArgs a) {
     const int nh_last = (int)((T - (int64_t)(a.nc - 1) * a.C + 31) / 32);
     auto halves = [&](int c) { return c == a.nc - 1 ? nh_last : nh; };
     const int nc = a.nc;
-    unsigned char* const xw = xch + u * XW;  // this unit group's exchange area
+    unsigned char* const xw = xch + u * XWB;  // this unit group's exchange area
     const int xl = 16 * lane;                // this lane's 16 bytes in an exchange fragment
 
     if (wave < UG) {
@@ -316,7 +348,14 @@ swiglu_loop_kernel(LoopArgs a) {
             for (int m = 0; m < 3; ++m) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x4 t0 = pack4(acc[m][1][2 * kk]), t1 = pack4(acc[m][1][2 * kk + 1]);
+                    bf16x4 t0, t1, r0, r1;  // hi parts; lo parts (PRE)
+                    if (PRE) {
+                        split4(acc[m][1][2 * kk], t0, r0);
+                        split4(acc[m][1][2 * kk + 1], t1, r1);
+                    } else {
+                        t0 = pack4(acc[m][1][2 * kk]);
+                        t1 = pack4(acc[m][1][2 * kk + 1]);
+                    }
                     const bf16x4 lo = godd ? t1 : t0, hi = godd ? t0 : t1;
                     bf16x8 w8;
 #pragma unroll
@@ -325,6 +364,16 @@ swiglu_loop_kernel(LoopArgs a) {
                         w8[4 + e] = hi[e];
                     }
                     *(bf16x8*)(xw + (4 * m + kk) * 1024 + xl) = w8;
+                    if (PRE) {  // the lo parts, 12 fragments further on
+                        const bf16x4 rlo = godd ? r1 : r0, rhi = godd ? r0 : r1;
+                        bf16x8 l8;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            l8[e] = rlo[e];
+                            l8[4 + e] = rhi[e];
+                        }
+                        *(bf16x8*)(xw + (12 + 4 * m + kk) * 1024 + xl) = l8;
+                    }
                     if (!SPREAD) *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
                     if (SAVEM) {
                         unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
@@ -367,7 +416,7 @@ swiglu_loop_kernel(LoopArgs a) {
         // (M += G^M with G^M = sum cM g, W += -G^W; du = -hv).
         auto aggregate = [&](int h) {
             const unsigned char* kb = kvs + ((h >> 1) % NBUF) * KVBUF + (h & 1) * 32 * 256;
-            const unsigned char* fb = xw + (h & 1) * FACB + xl;
+            const unsigned char* fb = xw + (h & 1) * FSET + xl;
             const float* cob = (const float*)(kvs + ((h >> 1) % NBUF) * KVBUF + 2 * KVB) + (h & 1) * 32 + 4 * g;
             const f32x4 cm0 = *(const f32x4*)cob, cm1 = *(const f32x4*)(cob + 16);
             const f32x4 cw0 = *(const f32x4*)(cob + 64), cw1 = *(const f32x4*)(cob + 80);
@@ -378,6 +427,27 @@ swiglu_loop_kernel(LoopArgs a) {
                     fm[e] = (__bf16)(-(e < 4 ? cm0[e] : cm1[e - 4]) * x);
                     fw[e] = (__bf16)((e < 4 ? cw0[e] : cw1[e - 4]) * x);
                 }
+            };
+            // PRE: the factor is hi + lo of its fp32 value, and each scaled
+            // operand is split into hi / lo again
+            auto scale_pre = [&](bf16x8 raw, bf16x8 rawlo, bf16x8& fm, bf16x8& fw, bf16x8& fml, bf16x8& fwl) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (float)raw[e] + (float)rawlo[e];
+                    const float ym = -(e < 4 ? cm0[e] : cm1[e - 4]) * x;
+                    const float yw = (e < 4 ? cw0[e] : cw1[e - 4]) * x;
+                    fm[e] = (__bf16)ym;
+                    fw[e] = (__bf16)yw;
+                    fml[e] = (__bf16)(ym - (float)fm[e]);
+                    fwl[e] = (__bf16)(yw - (float)fw[e]);
+                }
+            };
+            auto scale_any = [&](int x, bf16x8& fm, bf16x8& fw, bf16x8& fml, bf16x8& fwl) {
+                if (PRE)
+                    scale_pre(*(const bf16x8*)(fb + x * 1024), *(const bf16x8*)(fb + (3 + x) * 1024), fm, fw, fml,
+                              fwl);
+                else
+                    scale(*(const bf16x8*)(fb + x * 1024), fm, fw);
             };
             auto frag = [&](int i, int mat) {  // mat 0: K^T, 1: V^T
                 const unsigned char* p = kb + mat * KVB + (i & 1 ? te[i >> 1] + tdelta : te[i >> 1]);
@@ -391,10 +461,11 @@ swiglu_loop_kernel(LoopArgs a) {
                 }
                 return r;
             };
-            // K^T part (W1, W3: 4 MFMAs per fragment), then V^T part (W2: 2)
-            bf16x8 f[4];
-            scale(*(const bf16x8*)fb, f[0], f[1]);
-            scale(*(const bf16x8*)(fb + 1024), f[2], f[3]);
+            // K^T part (W1, W3: 4 MFMAs per fragment, 8 with PRE), then V^T
+            // part (W2: 2, or 4)
+            bf16x8 f[4], fl[4];  // scaled operands; their lo parts (PRE)
+            scale_any(0, f[0], f[1], fl[0], fl[1]);
+            scale_any(1, f[2], f[3], fl[2], fl[3]);
             bf16x8 t = frag(0, 0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -404,7 +475,13 @@ swiglu_loop_kernel(LoopArgs a) {
                 acc[0][1][i] = mfma16(t, f[1], acc[0][1][i]);
                 if (MOM) acc[1][0][i] = mfma16(t, f[2], acc[1][0][i]);
                 acc[1][1][i] = mfma16(t, f[3], acc[1][1][i]);
-                if (i == 7) scale(*(const bf16x8*)(fb + 2 * 1024), f[0], f[1]);
+                if (PRE) {
+                    if (MOM) acc[0][0][i] = mfma16(t, fl[0], acc[0][0][i]);
+                    acc[0][1][i] = mfma16(t, fl[1], acc[0][1][i]);
+                    if (MOM) acc[1][0][i] = mfma16(t, fl[2], acc[1][0][i]);
+                    acc[1][1][i] = mfma16(t, fl[3], acc[1][1][i]);
+                }
+                if (i == 7) scale_any(2, f[0], f[1], fl[0], fl[1]);
                 t = tn;
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -414,6 +491,10 @@ swiglu_loop_kernel(LoopArgs a) {
                 if (i + 1 < 8) tn = frag(i + 1, 1);
                 if (MOM) acc[2][0][i] = mfma16(t, f[0], acc[2][0][i]);
                 acc[2][1][i] = mfma16(t, f[1], acc[2][1][i]);
+                if (PRE) {
+                    if (MOM) acc[2][0][i] = mfma16(t, fl[0], acc[2][0][i]);
+                    acc[2][1][i] = mfma16(t, fl[1], acc[2][1][i]);
+                }
                 t = tn;
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -458,11 +539,15 @@ swiglu_loop_kernel(LoopArgs a) {
         for (int kk = 0; kk < 4; ++kk) goff[kk] = jl * 256 + 16 * ((4 * kk + g) ^ swz4(jl));
 
         bf16x8 wb[3][4];  // chunk-start weights: k-slot e of lane group g is d = 32kk + 8g + e
+        bf16x8 wl[3][4];  // PRE: their lo parts
         auto load_operands = [&]() {
 #pragma unroll
             for (int m = 0; m < 3; ++m)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) wb[m][kk] = *(const bf16x8*)(xw + (4 * m + kk) * 1024 + xl);
+                for (int kk = 0; kk < 4; ++kk) {
+                    wb[m][kk] = *(const bf16x8*)(xw + (4 * m + kk) * 1024 + xl);
+                    if (PRE) wl[m][kk] = *(const bf16x8*)(xw + (12 + 4 * m + kk) * 1024 + xl);
+                }
         };
         // grad MFMAs of half-block h: H1, H3, HV tiles of its two 16-token rows.
         // The 16 K / V row fragments are read first (one LDS round trip), then
@@ -491,6 +576,14 @@ swiglu_loop_kernel(LoopArgs a) {
                     hg[ti][1] = mfma16(fr.k[kk][ti], wb[1][kk], kk ? hg[ti][1] : z);
                     hg[ti][2] = mfma16(fr.v[kk][ti], wb[2][kk], kk ? hg[ti][2] : z);
                 }
+                if (PRE) {
+#pragma unroll
+                    for (int ti = 0; ti < 2; ++ti) {
+                        hg[ti][0] = mfma16(fr.k[kk][ti], wl[0][kk], hg[ti][0]);
+                        hg[ti][1] = mfma16(fr.k[kk][ti], wl[1][kk], hg[ti][1]);
+                        hg[ti][2] = mfma16(fr.v[kk][ti], wl[2][kk], hg[ti][2]);
+                    }
+                }
             }
         };
         // backward of half-block h from its grad tiles: the three unscaled
@@ -499,7 +592,7 @@ swiglu_loop_kernel(LoopArgs a) {
         // factor fragment is token 32h + 16 (e/4) + 4g + e%4, the token order of
         // the transpose read.
         auto backward = [&](int h, const grad_acc& hg) {
-            bf16x8 f[3];
+            bf16x8 f[3], fl[3];  // factors; their lo parts (PRE)
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti) {
 #pragma unroll
@@ -509,14 +602,20 @@ swiglu_loop_kernel(LoopArgs a) {
                     const float s1 = x1 * sg;
                     const float ds = sg + s1 * (1.f - sg);
                     const int e = 4 * ti + r;
-                    f[0][e] = (__bf16)(y * x3 * ds);
-                    f[1][e] = (__bf16)(y * s1);
-                    f[2][e] = (__bf16)(s1 * x3);
+                    const float fv[3] = {y * x3 * ds, y * s1, s1 * x3};
+#pragma unroll
+                    for (int x = 0; x < 3; ++x) {
+                        f[x][e] = (__bf16)fv[x];
+                        if (PRE) fl[x][e] = (__bf16)(fv[x] - (float)f[x][e]);
+                    }
                 }
             }
-            unsigned char* fb = xw + (h & 1) * FACB + xl;
+            unsigned char* fb = xw + (h & 1) * FSET + xl;
 #pragma unroll
-            for (int x = 0; x < 3; ++x) *(bf16x8*)(fb + x * 1024) = f[x];
+            for (int x = 0; x < 3; ++x) {
+                *(bf16x8*)(fb + x * 1024) = f[x];
+                if (PRE) *(bf16x8*)(fb + (3 + x) * 1024) = fl[x];
+            }
         };
         // With SPREAD (short chunks, whose chunk-boundary slots are a
         // large share of all slots) the gradient waves store the chunk's bf16
@@ -559,13 +658,15 @@ swiglu_loop_kernel(LoopArgs a) {
                 grad_acc hn;
                 grad_mfma(fr, hn);
                 backward(hh, hg);
+                constexpr int NGM = PRE ? 48 : 24;  // grad MFMAs per half-block
+                constexpr int VPM = PRE ? 4 : 5;    // VALU instructions slotted between two of them
                 __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // LDS reads: fragments
 #pragma unroll
-                for (int q = 0; q < 24; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                for (int q = 0; q < NGM; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
                 }
-                __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);  // LDS writes: factors
+                __builtin_amdgcn_sched_group_barrier(0x200, PRE ? 6 : 3, 0);  // LDS writes: factors
                 slot_barrier();
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti)
@@ -615,7 +716,9 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     int ncu = 0;
     hipError_t e;
     if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
-    const int ug = loop_unit_groups(BH, d.Hd, ncu);
+    const bool pre = (d.flags & E2TTT_FLAG_PRECISE) != 0;
+    if (pre && snapM) return hipErrorInvalidValue;  // the precise form keeps no momentum snapshots
+    const int ug = pre ? 2 : loop_unit_groups(BH, d.Hd, ncu);
     la.nsl = (int)(d.Hd / (16 * ug));
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
@@ -627,14 +730,23 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
         constexpr int U = decltype(UGc)::value;
         constexpr bool SP = decltype(SPc)::value;
         if (nomom)
-            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, U, SP>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, U, SP, false>), grid, block, 0, s, la);
         else if (snapM)
-            hipLaunchKernelGGL((swiglu_loop_kernel<true, true, U, SP>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, true, U, SP, false>), grid, block, 0, s, la);
         else
-            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, U, SP>), grid, block, 0, s, la);
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, U, SP, false>), grid, block, 0, s, la);
+    };
+    auto go_pre = [&](auto SPc) {
+        constexpr bool SP = decltype(SPc)::value;
+        if (nomom)
+            hipLaunchKernelGGL((swiglu_loop_kernel<false, false, 2, SP, true>), grid, block, 0, s, la);
+        else
+            hipLaunchKernelGGL((swiglu_loop_kernel<true, false, 2, SP, true>), grid, block, 0, s, la);
     };
     auto go_ug = [&](auto SPc) {
-        if (ug == 4)
+        if (pre)
+            go_pre(SPc);
+        else if (ug == 4)
             go(std::integral_constant<int, 4>{}, SPc);
         else
             go(std::integral_constant<int, 2>{}, SPc);

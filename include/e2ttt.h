@@ -90,6 +90,20 @@ typedef enum {
  * included), the same inputs and the untouched workspace skips its forward
  * recompute.  Unsupported (E2TTT_ERR_UNSUPPORTED) where the backward is. */
 #define E2TTT_FLAG_SAVE_STATES 8
+/* Precise operands on the SwiGLU MFMA path (e2ttt_path 2).  The default MFMA
+ * path rounds the chunk-start weights (grad operands) and the
+ * coefficient-scaled per-token factors (aggregation operands) to bf16, 8
+ * significant bits.  While the state decays fast (the stated gates with a
+ * strongly driven momentum) the chunk-to-chunk transition amplifies those
+ * roundings: over 3-4 chunks the output error can pass 2e-2 at any hidden
+ * width.  With this flag each such operand is a hi/lo bf16 pair (16 bits)
+ * summed by two MFMAs into the fp32 accumulator; the state then stays within
+ * about 1e-4 of the exact recurrence.  About twice the MFMA work, on 32-unit
+ * hidden slices.  The chunk outputs still come from bf16 chunk-start
+ * weights.  The backward of a precise call runs the portable fp32 backward,
+ * so E2TTT_FLAG_SAVE_STATES is unsupported with it.  No effect on the
+ * portable path, which computes in fp32. */
+#define E2TTT_FLAG_PRECISE 16
 
 typedef struct {
     int32_t kind;     /* e2ttt_kind */
@@ -111,7 +125,8 @@ E2TTT_API size_t e2ttt_workspace_size(const e2ttt_desc* desc);
 
 /* Which device path e2ttt_chunk_forward takes: 0 = portable fp32 kernel,
  * 1 = SwiGLU bf16 MFMA path (SWIGLU, LOSS_NEGDOT, BF16, D == 128, Hd a
- * multiple of 64 up to 4096, chunk a multiple of 64, T * D * 2 < 2^31);
+ * multiple of 64 up to 4096, chunk a multiple of 64, T * D * 2 < 2^31),
+ * 2 = the same shapes with E2TTT_FLAG_PRECISE (hi/lo bf16 operands);
  * negative e2ttt_status for a bad desc. */
 E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
 

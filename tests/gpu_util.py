@@ -42,7 +42,8 @@ def to_dev(x: dict) -> dict:
     return {n: t.cuda() for n, t in x.items()}
 
 
-def run_gpu(cfg: synth.Config, x: dict, force_generic=False, in_place=False, momentum=None, chunk_avg=None):
+def run_gpu(cfg: synth.Config, x: dict, force_generic=False, in_place=False, momentum=None, chunk_avg=None,
+            precise=False):
     import chunk_weight_rnn_amd as e2
     momentum = cfg.momentum if momentum is None else momentum
     chunk_avg = cfg.chunk_avg if chunk_avg is None else chunk_avg
@@ -52,7 +53,8 @@ def run_gpu(cfg: synth.Config, x: dict, force_generic=False, in_place=False, mom
         kw = dict(W_end=d["W0"], M_end=d["M0"] if momentum else None)
     out, W, M = e2.chunk_forward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
                                  chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd,
-                                 force_generic=force_generic, momentum=momentum, chunk_avg=chunk_avg, **kw)
+                                 force_generic=force_generic, momentum=momentum, chunk_avg=chunk_avg,
+                                 precise=precise, **kw)
     torch.cuda.synchronize()
     return out.float().cpu(), W.cpu(), (M.cpu() if M is not None else None)
 

@@ -1,0 +1,84 @@
+"""A CPU model of where the SwiGLU MFMA path rounds to bf16 (analysis aid for
+the tests; it is neither the oracle nor the GPU path, and imports neither the
+GPU package nor anything the kernels use).
+
+The chunk loop's arithmetic, written out in float64 with explicit bf16
+roundings at the points where the kernels round (the kernels accumulate in
+fp32; at these sizes that is far below the bf16 roundings):
+
+* grad operands: the chunk-start weights W1, W3, W2 as bf16 (precise form:
+  a hi/lo pair, hi = bf16(w), lo = bf16(w - hi));
+* the three per-token factors handed to the aggregation, a = hv h3 silu'(h1),
+  b = hv silu(h1), u = silu(h1) h3 (hv = V W2^T), as bf16 (precise: hi/lo);
+* the coefficient-scaled aggregation operands -cM x, cW x as bf16
+  (precise: hi/lo of c (x_hi + x_lo));
+* the state in fp32 between chunks; the scalar kernels' outputs in fp32;
+* the output from bf16 chunk-start weights, the hidden activations
+  silu(h1) h3 as bf16, and the result rounded to bf16.
+
+The closed-form transition is the oracle's (M <- Bb M + G^M,
+W <- A W - gamma M_old - G^W), its scalar kernels taken from
+oracle.chunk_coefficients and rounded to fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def _rb(x):
+    return x.to(torch.bfloat16).to(torch.float64)
+
+
+def _hilo_sum(x):
+    hi = _rb(x)
+    return hi + _rb(x - hi)
+
+
+def swiglu_bf16_path(cfg, x, precise: bool = False):
+    """(out, W_end, M_end) of the bf16 MFMA path's rounding model for one
+    SwiGLU / negative-dot workload with whole chunks (T % chunk == 0)."""
+    D, Hd, C, T, B, H = cfg.D, cfg.Hd, cfg.chunk, cfg.T, cfg.B, cfg.H
+    assert T % C == 0
+    op = _hilo_sum if precise else _rb
+    q, k, v = (x[n].double() for n in ("q", "k", "v"))
+    W = x["W0"].double().clone()
+    M = x["M0"].double().clone()
+    nc, n = T // C, D * Hd
+    a = x["alpha"].double().numpy().reshape(B, H, nc, C)
+    bt = x["beta"].double().numpy().reshape(B, H, nc, C)
+    e = x["eta"].double().numpy().reshape(B, H, nc, C)
+    m, w, A, Bb, gamma = oracle.chunk_coefficients(a, bt)
+    f32 = lambda y: torch.from_numpy(np.asarray(y, dtype=np.float32)).double()
+    cM, cW, A, Bb, gamma = f32(m * e), f32(w * e), f32(A), f32(Bb), f32(gamma)
+    out = torch.zeros(B, H, T, D, dtype=torch.float64)
+    for c in range(nc):
+        sl = slice(c * C, (c + 1) * C)
+        W1 = W[..., :n].reshape(B, H, D, Hd)
+        W3 = W[..., n:2 * n].reshape(B, H, D, Hd)
+        W2 = W[..., 2 * n:].reshape(B, H, Hd, D)
+        K, V, Q = k[:, :, sl], v[:, :, sl], q[:, :, sl]
+        # grad products at the chunk-start weights and the factors
+        h1, h3 = K @ op(W1), K @ op(W3)
+        hv = V @ op(W2).transpose(-1, -2)
+        sg = torch.sigmoid(h1)
+        s1 = h1 * sg
+        ds = sg + s1 * (1 - sg)
+        fa, fb, fu = op(hv * h3 * ds), op(hv * s1), op(s1 * h3)
+        # output from the bf16 snapshot of the chunk-start weights
+        x1, x3 = Q @ _rb(W1), Q @ _rb(W3)
+        out[:, :, sl] = _rb(_rb(x1 * torch.sigmoid(x1) * x3) @ _rb(W2))
+        # transition with the old momentum, then the scaled aggregations
+        cm, cw = cM[:, :, c, :, None], cW[:, :, c, :, None]
+        Mold = M
+        W = A[:, :, c, None] * W - gamma[:, :, c, None] * Mold
+        M = Bb[:, :, c, None] * Mold
+        Kt, Vt = K.transpose(-1, -2), V.transpose(-1, -2)
+        gM = [Kt @ op(-cm * fa), Kt @ op(-cm * fb), (Vt @ op(-cm * fu)).transpose(-1, -2)]
+        gW = [Kt @ op(cw * fa), Kt @ op(cw * fb), (Vt @ op(cw * fu)).transpose(-1, -2)]
+        M = M + torch.cat([g.reshape(B, H, -1) for g in gM], -1)
+        W = W + torch.cat([g.reshape(B, H, -1) for g in gW], -1)
+        W, M = W.float().double(), M.float().double()
+    return _rb(out).numpy(), W.numpy(), M.numpy()

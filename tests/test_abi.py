@@ -153,6 +153,28 @@ def test_chunk_forward_rejects_before_launch(lib):
     assert lib.e2ttt_logscan(None, v(0), v(0), v(0), v(0), v(0), v(0), v(0)) == 1
 
 
+def test_paths_of_narrow_heads_and_precise_flag(lib):
+    """A 64-unit SwiGLU head takes the bf16 MFMA path (1); with
+    E2TTT_FLAG_PRECISE the hi/lo-operand form of it (2); forcing the portable
+    path wins over both (0).  A precise forward cannot save states for the
+    MFMA backward (its backward is the portable one)."""
+    from chunk_weight_rnn_amd._lib import FLAG_FORCE_GENERIC, FLAG_PRECISE, FLAG_SAVE_STATES
+    for Hd in (64, 128, 256):
+        assert lib.e2ttt_path(ctypes.byref(_desc(Hd=Hd, T=768, chunk=256))) == 1
+        assert lib.e2ttt_path(ctypes.byref(_desc(Hd=Hd, T=768, chunk=256, flags=FLAG_PRECISE))) == 2
+        assert lib.e2ttt_path(ctypes.byref(_desc(Hd=Hd, flags=FLAG_PRECISE | FLAG_FORCE_GENERIC))) == 0
+    d = _desc(Hd=64, flags=FLAG_PRECISE)
+    assert _validate(lib, d, _ptrs(d)) == 0
+    d = _desc(Hd=64, flags=FLAG_PRECISE | FLAG_SAVE_STATES)
+    assert _validate(lib, d, _ptrs(d)) == 2
+    # same workspace as the bf16 MFMA path (snapshot layout)
+    a = lib.e2ttt_workspace_size(ctypes.byref(_desc(Hd=64)))
+    assert lib.e2ttt_workspace_size(ctypes.byref(_desc(Hd=64, flags=FLAG_PRECISE))) == a
+    # the portable fp32 path is unaffected by the flag
+    d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=FLAG_PRECISE)
+    assert lib.e2ttt_path(ctypes.byref(d)) == 0
+
+
 def test_chunk_beyond_int32_rejected(lib):
     """Kernels take the chunk length as a 32-bit int: a longer chunk is
     refused rather than truncated (2^32 + 16 would otherwise run as 16)."""
@@ -225,7 +247,7 @@ def test_validate_variant_flags(lib):
         d = _desc(flags=f)
         assert _validate(lib, d, _ptrs(d)) == 0
     # unknown flag bits are rejected
-    d = _desc(flags=16)
+    d = _desc(flags=32)
     assert _validate(lib, d, _ptrs(d)) == 1
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == ctypes.c_size_t(-1).value
 

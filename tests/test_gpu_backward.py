@@ -21,7 +21,7 @@ SMALL = synth.Config("bwd_small", "swiglu", "negdot", 1, 2, 320, 128, 128, 128, 
                      "2.5 chunks of 128 (ragged tail of 64)")
 
 
-def _gpu(cfg, x, c, force_generic=False):
+def _gpu(cfg, x, c, force_generic=False, precise=False):
     import chunk_weight_rnn_amd as e2
     d = {n: t.cuda() for n, t in x.items()}
     dc = {n: t.cuda() for n, t in c.items()}
@@ -29,7 +29,7 @@ def _gpu(cfg, x, c, force_generic=False):
     g = e2.chunk_backward(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["beta"], d["W0"], d["M0"],
                           dc["dout"], dc["dW_end"], dc["dM_end"], chunk=cfg.chunk, Hd=cfg.Hd, kind=cfg.kind,
                           loss=cfg.loss, momentum=cfg.momentum, chunk_avg=cfg.chunk_avg,
-                          force_generic=force_generic)
+                          force_generic=force_generic, precise=precise)
     torch.cuda.synchronize()
     return {n: (None if t is None else t.float().cpu().numpy()) for n, t in g.items()}
 
@@ -83,17 +83,28 @@ def test_backward_shapes(T, chunk):
     _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
 
 
-@pytest.mark.parametrize("Hd,T,chunk", [(64, 128, 128), (320, 256, 128)])
+@pytest.mark.parametrize("Hd,T,chunk", [(64, 128, 128), (64, 768, 64), (320, 256, 128)])
 def test_backward_hidden_widths(Hd, T, chunk):
-    """One 64-unit slice, and five slices (the weight kernel's slice grid and
-    the token kernel's unit loop at other widths).  The 64-unit head runs one
-    chunk: over several chunks its bf16 error grows past the tolerance, as
-    the forward's does."""
+    """One 64-unit slice (one chunk; twelve 64-token chunks), and five slices
+    (the weight kernel's slice grid and the token kernel's unit loop at other
+    widths)."""
     cfg = SMALL.with_(T=T, chunk=chunk, Hd=Hd, name=f"bwd_Hd{Hd}_T{T}_C{chunk}")
     note(f"case {cfg.name}")
     x = synth.make_inputs(cfg, seed=7, m0_scale=0.5)
     c = synth.make_cotangents(cfg, seed=8)
     _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
+@pytest.mark.parametrize("Hd", [64, 128])
+def test_backward_precise_multichunk(Hd):
+    """The backward of a precise forward (E2TTT_FLAG_PRECISE) runs the portable
+    fp32 backward: three 256-token chunks with a strongly driven momentum, the
+    case where the bf16 operands drift (64- and 128-unit heads)."""
+    cfg = SMALL.with_(T=768, chunk=256, Hd=Hd, name=f"bwd_precise_Hd{Hd}")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=15, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=16)
+    _compare(cfg, _gpu(cfg, x, c, precise=True), _oracle(cfg, x, c))
 
 
 def test_backward_full_size_sampled_heads():

@@ -122,6 +122,7 @@ def test_config_persistent_state(name):
 # ---------------------------------------------------------------------------
 MFMA_CASES = [
     dict(B=1, H=1, T=64, Hd=64, chunk=64),      # one slice, one block, one chunk
+    dict(B=1, H=2, T=768, Hd=64, chunk=64),     # a 64-unit head over 12 chunks
     dict(B=1, H=3, T=256, Hd=192, chunk=128),   # 3 slices, 4-wave apply, 2 chunks
     dict(B=2, H=3, T=384, Hd=128, chunk=64),    # 12 workgroups (no XCD remap), 6 chunks
     dict(B=2, H=4, T=512, Hd=256, chunk=512),   # one long chunk of 8 blocks
@@ -152,6 +153,76 @@ def test_swiglu_mfma_cases(i, gates):
     got = gu.run_gpu(cfg, x)
     ref = gu.run_oracle(cfg, x)
     gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+def test_swiglu_mfma_multichunk_slow_decay():
+    """The bf16 MFMA path over several 256-token chunks with a strongly driven
+    momentum (M0 at half the W0 scale) where the state persists from chunk to
+    chunk (alpha = sigmoid(6 + z)): 64- and 128-unit heads, 4 chunks."""
+    _lib()
+    for Hd, seed in ((64, 15), (128, 14)):
+        cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"slow_decay_Hd{Hd}", B=1, H=2, T=1024, Hd=Hd, chunk=256)
+        gu.note(f"bf16 MFMA path, slow decay, Hd={Hd} T=1024 C=256 m0=0.5 seed={seed}")
+        x = synth.make_inputs(cfg, seed=seed, m0_scale=0.5)
+        g = torch.Generator().manual_seed(1234)
+        x["alpha"] = torch.sigmoid(6.0 + torch.randn(x["alpha"].shape, generator=g))
+        got = gu.run_gpu(cfg, x)
+        ref = gu.run_oracle(cfg, x)
+        gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+# ---------------------------------------------------------------------------
+# precise operands (E2TTT_FLAG_PRECISE): the stated gates with a strongly
+# driven momentum, several 256-token chunks.  While the state decays by
+# ~1e-3 per chunk, the bf16 path's operand roundings grow from chunk to chunk
+# (its output error reaches 2e-2 .. 3e-2 on these inputs at every width);
+# with hi/lo operands the state follows the exact recurrence to ~1e-4.
+# ---------------------------------------------------------------------------
+PRECISE_CASES = [
+    dict(B=1, H=2, T=768, Hd=64, chunk=256, seed=15),    # 3 chunks; bf16 path: out 2.75e-2
+    dict(B=1, H=2, T=1024, Hd=128, chunk=256, seed=14),  # bf16 path: out 2.9e-2
+    dict(B=1, H=2, T=1024, Hd=192, chunk=256, seed=14),  # bf16 path: out 3.0e-2
+    dict(B=1, H=2, T=1024, Hd=256, chunk=256, seed=15),
+    dict(B=2, H=3, T=512, Hd=64, chunk=64, seed=16),     # short chunks (snapshot stores spread)
+    dict(B=1, H=2, T=1000, Hd=128, chunk=256, seed=17),  # ragged tail
+    dict(B=4, H=20, T=512, Hd=128, chunk=256, seed=18),  # 320 workgroups: more than one round
+]
+PRECISE_STATE_TOL = 1e-3
+
+
+@pytest.mark.parametrize("i", range(len(PRECISE_CASES)))
+@pytest.mark.parametrize("momentum", [True, False], ids=["momentum", "no_momentum"])
+def test_swiglu_precise_cases(i, momentum):
+    e2 = _lib()
+    c = dict(PRECISE_CASES[i])
+    seed = c.pop("seed")
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"precise{i}", flags=0 if momentum else 2, **c)
+    gu.note(f"precise case {i} momentum={momentum}: {c} seed={seed} m0=0.5")
+    x = synth.make_inputs(cfg, seed=seed, m0_scale=0.5 if momentum else 0.0)
+    assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk,
+                   flags=e2.FLAG_PRECISE | cfg.flags) == 2
+    got = gu.run_gpu(cfg, x, precise=True)
+    ref = gu.run_oracle(cfg, x)
+    e = gu.assert_close(cfg, got, ref, x["W0"].numpy())
+    state = {n: v for n, v in e.items() if n.startswith(("W.", "M.")) and v is not None}
+    assert max(state.values()) < PRECISE_STATE_TOL, state
+
+
+def test_swiglu_precise_beats_bf16_operands():
+    """On the case where the bf16 operands drift furthest, the precise form's
+    state error is at least 20x smaller (same inputs, same kernels otherwise)."""
+    _lib()
+    c = dict(PRECISE_CASES[1])
+    seed = c.pop("seed")
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name="precise_vs_bf16", **c)
+    x = synth.make_inputs(cfg, seed=seed, m0_scale=0.5)
+    ref = gu.run_oracle(cfg, x)
+    ep = gu.errors(cfg, gu.run_gpu(cfg, x, precise=True), ref, x["W0"].numpy())
+    eb = gu.errors(cfg, gu.run_gpu(cfg, x), ref, x["W0"].numpy())
+    sp = max(v for n, v in ep.items() if n.startswith(("W.", "M.")))
+    sb = max(v for n, v in eb.items() if n.startswith(("W.", "M.")))
+    gu.note(f"  state error: precise {sp:.2e}, bf16 operands {sb:.2e}")
+    assert sp * 20 < sb
 
 
 # ---------------------------------------------------------------------------
