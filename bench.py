@@ -538,12 +538,16 @@ def main() -> int:
     tokens = cfg.B * cfg.T
     fpt = flops_per_token_head(cfg)
     heads_tokens = cfg.B * cfg.H * cfg.T
-    peak = PEAK_BF16_TFLOPS if cfg.io_dtype == "bf16" and cfg.kind == "swiglu" else PEAK_F32_TFLOPS
-    loop_flops = (fpt["grad"] + fpt["aggregate"]) * heads_tokens
+    path = int(lib.e2ttt_path(ctypes.byref(desc)))
+    peak = PEAK_BF16_TFLOPS if path in (1, 2) else PEAK_F32_TFLOPS
+    loop_kernel = {0: "generic_kernel", 1: "swiglu_loop_kernel", 2: "swiglu_loop_kernel", 3: "f32_chunk_kernel"}[path]
+    # the fp32 kernels compute the chunk outputs inside the chunk loop
+    loop_stages = ("grad", "aggregate") if path in (1, 2) else ("grad", "aggregate", "apply")
+    loop_flops = sum(fpt[k] for k in loop_stages) * heads_tokens
     loop_tflops = loop_flops / (st_ms["loop"] * 1e-3) / 1e12 if st_ms else None
     call_flops = sum(fpt.values()) * heads_tokens
     call_tflops = call_flops / (ms_step * 1e-3) / 1e12
-    traffic = measured_traffic(0.0) if args.config == "swiglu_1p3b" else None
+    traffic = measured_traffic(0.0) if args.config == "swiglu_1p3b" and not args.precise else None
 
     res = {
         "metric": METRIC,
@@ -563,11 +567,12 @@ def main() -> int:
                    "state": "f32", "momentum": cfg.momentum, "chunk_avg": cfg.chunk_avg,
                    "precise": bool(args.precise)},
         "roofline": None if graph else {
-            "bound": "mfma", "kernel": "swiglu_loop_kernel" if cfg.kind == "swiglu" else "generic_kernel",
+            "bound": "mfma", "kernel": loop_kernel,
             "achieved": loop_tflops, "peak": peak, "unit": "TFLOP/s", "frac": loop_tflops / peak,
             "traffic": traffic,
-            "per_launch": f"{(fpt['grad'] + fpt['aggregate'])} flop/token/head x {heads_tokens} "
+            "per_launch": f"{sum(fpt[k] for k in loop_stages)} flop/token/head x {heads_tokens} "
                           f"token-heads = {loop_flops:.4g} flop"},
+        "path": path,
         "whole_call": {"tflops": call_tflops, "frac_of_peak": call_tflops / peak,
                        "hbm_alg_GBs": alg_bytes(cfg) / (ms_step * 1e-3) / 1e9},
         "stages_ms": st_ms,

@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libe2ttt.so")
 PROBE_LIB = os.path.join(PKG, "libe2ttt_probe.so")  # microbenchmarks of the chip's ceilings (bench.py --peaks)
 PROBE_SOURCES = ["probe.hip"]
-SOURCES = ["abi.hip", "logscan.hip", "generic.hip", "generic_bwd.hip", "swiglu_loop.hip", "swiglu_mfma.hip",
-           "swiglu_bwd.hip"]
+SOURCES = ["abi.hip", "logscan.hip", "generic.hip", "generic_bwd.hip", "f32_mfma.hip", "swiglu_loop.hip",
+           "swiglu_mfma.hip", "swiglu_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -96,11 +96,19 @@ static bool logscan_desc_ok(const e2ttt_desc* d) {
 }
 
 // 0: portable fp32 kernel, 1: SwiGLU bf16 MFMA path, 2: the same with hi/lo
-// bf16 operands (E2TTT_FLAG_PRECISE)
+// bf16 operands (E2TTT_FLAG_PRECISE), 3: fp32 MFMA path (linear / MLP, fp32 I/O)
 static int path_of(const e2ttt_desc& d) {
-    if (!(d.flags & E2TTT_FLAG_FORCE_GENERIC) && swiglu_mfma_supported(d))
-        return (d.flags & E2TTT_FLAG_PRECISE) ? 2 : 1;
+    if (d.flags & E2TTT_FLAG_FORCE_GENERIC) return 0;
+    if (swiglu_mfma_supported(d)) return (d.flags & E2TTT_FLAG_PRECISE) ? 2 : 1;
+    if (f32_mfma_supported(d)) return 3;
     return 0;
+}
+
+// A forward with E2TTT_FLAG_SAVE_STATES leaves what its backward reads: the
+// bf16 snapshots for the MFMA backward, the fp32 chunk-start states for the
+// portable backward (written by both fp32 forward paths).
+static bool save_compatible(int fwd_path, int bwd_path) {
+    return (fwd_path == 1 && bwd_path == 1) || ((fwd_path == 0 || fwd_path == 3) && bwd_path == 0);
 }
 
 static bool generic_supported(const e2ttt_desc& d) {
@@ -212,9 +220,10 @@ Workspace workspace_layout(const e2ttt_desc& d, int path) {
     off += align_up(BH * nc * 4 * sizeof(float));
     w.gacc = w.snap = off;
     if (path == 0)
-        off += align_up(BH * 2 * P * sizeof(float));
-    else
-        off += align_up(BH * nc * P * 2);
+        off += align_up(BH * 2 * P * sizeof(float));  // portable path: G accumulators
+    else if (path == 1 || path == 2)
+        off += align_up(BH * nc * P * 2);  // bf16 chunk-start snapshots
+    // path 3 (fp32 MFMA) keeps its state and aggregations on chip
     w.total = (BH * T == 0) ? 0 : off;
     return w;
 }
@@ -255,7 +264,8 @@ int e2ttt_path(const e2ttt_desc* d) {
 int e2ttt_validate(const e2ttt_desc* d, const void* const ptrs[11]) {
     if (!desc_ok(d) || !ptrs) return E2TTT_ERR_INVALID_ARG;
     if (path_of(*d) == 0 && !generic_supported(*d)) return E2TTT_ERR_UNSUPPORTED;
-    if ((d->flags & E2TTT_FLAG_SAVE_STATES) && backward_path(*d) != path_of(*d)) return E2TTT_ERR_UNSUPPORTED;
+    if ((d->flags & E2TTT_FLAG_SAVE_STATES) && !save_compatible(path_of(*d), backward_path(*d)))
+        return E2TTT_ERR_UNSUPPORTED;
     const size_t BH = (size_t)(d->B * d->H);
     const size_t es = d->io_dtype == E2TTT_BF16 ? 2 : 4;
     const size_t P = (size_t)e2ttt_param_count(d);
@@ -351,9 +361,13 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
     const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
-    if (path >= 1) {
+    if (path == 1 || path == 2) {
         e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap,
                                save && mom ? wsb + bws.snapM : nullptr, s, ev[2]);
+    } else if (path == 3) {
+        e = launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, s,
+                            save ? (float*)(wsb + bws.save) : nullptr);
+        if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
     } else {
         e = launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc),
                            s, save ? (float*)(wsb + bws.save) : nullptr);
@@ -460,9 +474,14 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
         if (!(d->flags & E2TTT_FLAG_SAVE_STATES)) {  // else a forward call left them in the workspace
             if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
                 return E2TTT_ERR_HIP;
-            if (launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, (float*)(wsb + ws.gacc), s,
-                               save) != hipSuccess)
-                return E2TTT_ERR_HIP;
+            // the forward path e2ttt_chunk_forward takes, so that a saved forward
+            // and this recompute leave the same states
+            const hipError_t fe =
+                path_of(*d) == 3
+                    ? launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, s, save)
+                    : launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0,
+                                     (float*)(wsb + ws.gacc), s, save);
+            if (fe != hipSuccess) return E2TTT_ERR_HIP;
         }
         if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
         GenericBwdBuffers g;

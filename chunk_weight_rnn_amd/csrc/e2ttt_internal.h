@@ -39,6 +39,14 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
                           const float* M0, void* out, float* W_end, float* M_end, float* gacc,
                           hipStream_t s, float* save = nullptr);
 
+// fp32-MFMA chunk loop for the linear and MLP fast weights with fp32 I/O
+// (D and Hd multiples of 16, a head's state within 32 16x16 tiles per
+// matrix); save as launch_generic's.
+bool f32_mfma_supported(const e2ttt_desc& d);
+hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
+                           const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
+                           float* W_end, float* M_end, hipStream_t s, float* save);
+
 // SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
 bool swiglu_mfma_supported(const e2ttt_desc& d);
 // Chunk loop of the SwiGLU path: final state and the bf16 chunk-start weight

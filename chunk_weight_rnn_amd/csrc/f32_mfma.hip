@@ -1,0 +1,475 @@
+// fp32 MFMA chunk loop for the linear and MLP fast weights with fp32 q/k/v/out
+// on CDNA4 (gfx950): every contraction of the chunk update runs on
+// v_mfma_f32_16x16x4f32 (fp32 operands, fp32 accumulation).
+//
+// Method: "Rethinking Expressivity and Efficiency in Test-Time Training"
+// (abstract; atlas summary "Approach" and "Key results": an MLP fast weight).
+// Per (b, h) and chunk, with K, V, Q the chunk's [C x D] token rows and the
+// chunk-start weights (W for linear; W1 [Hd x D], W2 [D x Hd] for the MLP):
+//   output:     O = Q W^T                     | O = silu(Q W1^T) W2^T
+//   forward:    Y = K W^T                     | Z = K W1^T, A = silu(Z), Y = A W2^T
+//   loss:       dY = Y - V (MSE)  or  dY = -V (negative dot product)
+//   backward:                                 | dZ = (dY W2) * silu'(Z)
+//   aggregate:  G_W  = dY^T diag(c) K         | G_W2 = dY^T diag(c) A, G_W1 = dZ^T diag(c) K
+//               for c in {cM, cW} (per-token coefficients from e2ttt_logscan)
+//   transition: M <- Bb M + G^M,  W <- A W - gamma M_old - G^W
+//
+// One workgroup of 8 wavefronts per (b, h): the MLP's hidden units are coupled
+// through Y, so a head is not split.  The state (W and M) stays in MFMA
+// accumulator registers for the whole sequence as 16x16 tiles spread over the
+// wavefronts; its aggregation MFMAs accumulate into it directly.  Per chunk
+// the chunk-start weights are written to LDS once; per block of up to 64
+// tokens the token rows and the intermediates (silu(Z), dY, then dZ) go
+// through LDS between the stages.
+//
+// LDS matrices hold fp32 rows of RS floats (RS a multiple of 64) with element
+// (r, c) at r * RS + (c ^ swz(r)).  An MFMA operand read touches either 16
+// rows x 4 columns or 4 rows x 16 columns (the same matrix is contracted over
+// its rows in one product and over its columns in another); the swizzle puts
+// both patterns on 64 distinct banks.
+#include "e2ttt_internal.h"
+
+namespace e2ttt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NW = 8;          // wavefronts per workgroup
+constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int TBMAX = 64;      // tokens per block
+constexpr int MAXT = 4;        // 16x16 tiles per wavefront per matrix
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 4) | (((r >> 2) & 3) << 2); }
+
+// a matrix in LDS
+struct Lm {
+    float* p;
+    int rs;  // row stride in floats (a multiple of 64)
+    __device__ __forceinline__ float& at(int r, int c) const { return p[r * rs + (c ^ swz(r))]; }
+    __device__ __forceinline__ f32x4* row4(int r, int c4) const {  // 4 floats from column 4 c4, 16-byte aligned
+        return (f32x4*)&p[r * rs + ((4 * c4) ^ swz(r))];
+    }
+};
+
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); }
+
+struct F32Args {
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* cM;
+    const float* cW;
+    const float* scal;
+    const float* W0;
+    const float* M0;
+    float* out;
+    float* W;
+    float* M;
+    float* save;  // [BH][nc][2][P] chunk-start W, M (may be null)
+    int64_t T, ldc, P;
+    int D, Hd, C, nc, TB;
+    int rsd, rsh;  // LDS row strides for D- and Hd-wide rows
+};
+
+// tile s of a matrix with ncol 16-wide column tiles: (row tile, column tile)
+__device__ __forceinline__ int tr(int s, int ncol) { return s / ncol; }
+__device__ __forceinline__ int tc(int s, int ncol) { return s % ncol; }
+
+template <int KIND, int LOSS, bool MOM>
+__global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    int jl = lane & 15, g = lane >> 4;  // made opaque per chunk below (no per-lane address outlives a chunk)
+    const int64_t bh = blockIdx.x;
+    const int D = a.D, Hd = KIND == E2TTT_MLP ? a.Hd : 0, TB = a.TB;
+    const int64_t P = a.P, T = a.T;
+    const bool mlp = KIND == E2TTT_MLP;
+
+    // ---------------------------------------------------------------- LDS
+    // MLP:    W1s [Hd][rsd] | W2s [D][rsh] | Xs [TB][rsd] | As [TB][rsh] | dYs [TB][rsd] | c [2][TB]
+    // linear: Ws [D][rsd]                  | Xs [TB][rsd] |              | dYs [TB][rsd] | c [2][TB]
+    float* p = lds;
+    const Lm W1s{p, a.rsd};
+    p += (mlp ? Hd : D) * a.rsd;
+    const Lm W2s{p, a.rsh};
+    p += mlp ? D * a.rsh : 0;
+    const Lm Xs{p, a.rsd};
+    p += TB * a.rsd;
+    const Lm As{p, a.rsh};
+    p += mlp ? TB * a.rsh : 0;
+    const Lm dYs{p, a.rsd};
+    p += TB * a.rsd;
+    float* cms = p;
+    float* cws = p + TB;
+
+    // ---------------------------------------------------------------- state
+    // matrix 0: W1 [Hd x D] (linear: W [D x D]); matrix 1: W2 [D x Hd].
+    // Tile s of matrix m is held by wave s % NW in slot s / NW; lane (jl, g)
+    // register r holds element (16 tr + 4g + r, 16 tc + jl).
+    const int nr0 = mlp ? Hd / 16 : D / 16, nc0 = D / 16;  // tile rows / columns of matrix 0
+    const int nr1 = D / 16, nc1 = mlp ? Hd / 16 : 1;       // of matrix 1 (linear: none)
+    const int ns0 = nr0 * nc0, ns1 = mlp ? nr1 * nc1 : 0;
+    const int64_t off1 = (int64_t)(mlp ? Hd : D) * D;  // packed offset of matrix 1
+    const int cols0 = D, cols1 = Hd;                    // packed row lengths
+    f32x4 w0[MAXT], m0[MAXT], w1[MAXT], m1[MAXT];
+    auto gidx0 = [&](int s, int r) { return (int64_t)(16 * tr(s, nc0) + 4 * g + r) * cols0 + 16 * tc(s, nc0) + jl; };
+    auto gidx1 = [&](int s, int r) {
+        return off1 + (int64_t)(16 * tr(s, nc1) + 4 * g + r) * cols1 + 16 * tc(s, nc1) + jl;
+    };
+    {
+        const float* W0 = a.W0 + bh * P;
+        const float* M0 = MOM ? a.M0 + bh * P : nullptr;
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) {
+            const int s0 = wave + NW * q;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                w0[q][r] = s0 < ns0 ? W0[gidx0(s0, r)] : 0.f;
+                m0[q][r] = (MOM && s0 < ns0) ? M0[gidx0(s0, r)] : 0.f;
+                w1[q][r] = s0 < ns1 ? W0[gidx1(s0, r)] : 0.f;
+                m1[q][r] = (MOM && s0 < ns1) ? M0[gidx1(s0, r)] : 0.f;
+            }
+        }
+    }
+
+    const float* qh = a.q + bh * T * D;
+    const float* kh = a.k + bh * T * D;
+    const float* vh = a.v + bh * T * D;
+    float* oh = a.out + bh * T * D;
+    const float* cMh = a.cM + bh * a.ldc;
+    const float* cWh = a.cW + bh * a.ldc;
+
+    // rows [t, t + nb) of x [T][D] -> Xs, zero rows nb .. TB-1
+    auto load_rows = [&](const float* x, int64_t t, int nb) {
+        const int n4 = D / 4;
+        for (int i = tid; i < TB * n4; i += NT) {
+            const int r = i / n4, c4 = i % n4;
+            f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+            if (r < nb) v4 = *(const f32x4*)&x[(t + r) * D + 4 * c4];
+            *Xs.row4(r, c4) = v4;
+        }
+    };
+
+    // [TB x N] = X_lds [TB x K] * B^T where B_lds is [N][K] (contraction over
+    // columns of both): tiles s = wave + NW q of (TB/16) x (N/16); the result
+    // tiles go to fn(q, row tile, col tile, acc).
+    auto gemm_rows = [&](const Lm& X, const Lm& B, int N, int K, auto&& fn) {
+        const int ncn = N / 16, nst = (TB / 16) * ncn;
+        f32x4 acc[MAXT];
+        int ti[MAXT], tj[MAXT];
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) {
+            acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int s = wave + NW * q;
+            ti[q] = s < nst ? tr(s, ncn) : 0;
+            tj[q] = s < nst ? tc(s, ncn) : 0;
+        }
+        for (int kk = 0; kk < K / 4; ++kk) {
+#pragma unroll
+            for (int q = 0; q < MAXT; ++q) {
+                if (wave + NW * q < nst)
+                    acc[q] = mfma(X.at(16 * ti[q] + jl, 4 * kk + g), B.at(16 * tj[q] + jl, 4 * kk + g), acc[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q)
+            if (wave + NW * q < nst) fn(q, ti[q], tj[q], acc[q]);
+    };
+
+    const int nchunks = a.nc;
+    for (int c = 0; c < nchunks; ++c) {
+        // per-lane tile coordinates are re-derived in every chunk, so that the
+        // compiler does not keep dozens of per-tile addresses live across the loop
+        asm volatile("" : "+v"(jl), "+v"(g));
+        const int64_t t0 = (int64_t)c * a.C;
+        const int Cc = (int)min((int64_t)a.C, T - t0);  // the last chunk may be shorter
+        __syncthreads();  // the previous chunk's last reads of the weight snapshot are done
+        if (a.save) {     // chunk-start state for the backward pass
+            float* sv = a.save + (bh * nchunks + c) * 2 * P;
+#pragma unroll
+            for (int q = 0; q < MAXT; ++q) {
+                const int s0 = wave + NW * q;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (s0 < ns0) {
+                        sv[gidx0(s0, r)] = w0[q][r];
+                        sv[P + gidx0(s0, r)] = MOM ? m0[q][r] : 0.f;
+                    }
+                    if (s0 < ns1) {
+                        sv[gidx1(s0, r)] = w1[q][r];
+                        sv[P + gidx1(s0, r)] = MOM ? m1[q][r] : 0.f;
+                    }
+                }
+            }
+        }
+        // chunk-start weights -> LDS
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) {
+            const int s0 = wave + NW * q;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (s0 < ns0) W1s.at(16 * tr(s0, nc0) + 4 * g + r, 16 * tc(s0, nc0) + jl) = w0[q][r];
+                if (s0 < ns1) W2s.at(16 * tr(s0, nc1) + 4 * g + r, 16 * tc(s0, nc1) + jl) = w1[q][r];
+            }
+        }
+        // transition of the state with the chunk-start momentum; the
+        // aggregations below then add G^M to M and subtract G^W from W
+        {
+            const f32x4 sc = *(const f32x4*)(a.scal + (bh * nchunks + c) * 4);
+            const float A = sc[0], Bb = sc[1], gamma = sc[2];
+#pragma unroll
+            for (int q = 0; q < MAXT; ++q) {
+                if (MOM) {
+                    w0[q] = A * w0[q] - gamma * m0[q];
+                    m0[q] = Bb * m0[q];
+                    w1[q] = A * w1[q] - gamma * m1[q];
+                    m1[q] = Bb * m1[q];
+                } else {
+                    w0[q] = A * w0[q];
+                    w1[q] = A * w1[q];
+                }
+            }
+        }
+
+        for (int tb0 = 0; tb0 < Cc; tb0 += TB) {
+            const int nb = min(TB, Cc - tb0);
+            const int64_t tt = t0 + tb0;  // first token of the block
+            // ---------------------------------------------------- output
+            load_rows(qh, tt, nb);
+            for (int i = tid; i < TB; i += NT) {
+                cms[i] = (MOM && i < nb) ? cMh[tt + i] : 0.f;
+                cws[i] = i < nb ? cWh[tt + i] : 0.f;
+            }
+            __syncthreads();
+            auto store_out = [&](int, int ti, int tj, f32x4 o) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + 4 * g + r;
+                    if (row < nb) oh[(tt + row) * D + 16 * tj + jl] = o[r];
+                }
+            };
+            if (mlp) {
+                // Aq = silu(Q W1^T) -> As
+                gemm_rows(Xs, W1s, Hd, D, [&](int, int ti, int tj, f32x4 z) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) As.at(16 * ti + 4 * g + r, 16 * tj + jl) = z[r] * sigm(z[r]);
+                });
+                __syncthreads();
+                gemm_rows(As, W2s, D, Hd, store_out);  // O = Aq W2^T (W2s rows are W2[d][:])
+            } else {
+                gemm_rows(Xs, W1s, D, D, store_out);  // O = Q W^T
+            }
+            __syncthreads();
+            // ---------------------------------------------------- forward
+            load_rows(kh, tt, nb);
+            __syncthreads();
+            float sp[MAXT][4];  // silu'(Z) of this wave's Z tiles
+            auto to_dy = [&](int, int ti, int tj, f32x4 y) {  // dL/dy of this wave's Y tiles -> dYs
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + 4 * g + r, col = 16 * tj + jl;
+                    const float vv = row < nb ? vh[(tt + row) * D + col] : 0.f;
+                    dYs.at(row, col) = LOSS == E2TTT_LOSS_MSE ? y[r] - vv : -vv;
+                }
+            };
+            if (mlp) {
+                gemm_rows(Xs, W1s, Hd, D, [&](int q, int ti, int tj, f32x4 z) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float s = sigm(z[r]);
+                        As.at(16 * ti + 4 * g + r, 16 * tj + jl) = z[r] * s;
+                        sp[q][r] = s * (1.f + z[r] * (1.f - s));
+                    }
+                });
+                __syncthreads();
+                if (LOSS == E2TTT_LOSS_MSE) {
+                    gemm_rows(As, W2s, D, Hd, to_dy);  // Y = A W2^T
+                } else {
+                    const int ncn = D / 16, nst = (TB / 16) * ncn;
+                    for (int s = wave; s < nst; s += NW) to_dy(0, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+            } else {
+                if (LOSS == E2TTT_LOSS_MSE) {
+                    gemm_rows(Xs, W1s, D, D, to_dy);  // Y = K W^T
+                } else {
+                    const int ncn = D / 16, nst = (TB / 16) * ncn;
+                    for (int s = wave; s < nst; s += NW) to_dy(0, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+            }
+            __syncthreads();
+            // ---------------------------------------------------- aggregation, matrix 1
+            // MLP W2 [D x Hd]: M += (cM dY)^T A, W -= (cW dY)^T A
+            if (mlp) {
+                for (int kk = 0; kk < TB / 4; ++kk) {
+                    const int tok = 4 * kk + g;
+                    const float cm = cms[tok], cw = cws[tok];
+#pragma unroll
+                    for (int q = 0; q < MAXT; ++q) {
+                        const int s = wave + NW * q;
+                        if (s < ns1) {
+                            const float y = dYs.at(tok, 16 * tr(s, nc1) + jl);
+                            const float b = As.at(tok, 16 * tc(s, nc1) + jl);
+                            if (MOM) m1[q] = mfma(cm * y, b, m1[q]);
+                            w1[q] = mfma(-cw * y, b, w1[q]);
+                        }
+                    }
+                }
+                __syncthreads();  // every wave is done with A
+                // ------------------------------------------------ backward: dZ = (dY W2) * silu'(Z) -> As
+                const int ncn = Hd / 16, nst = (TB / 16) * ncn;
+                f32x4 dz[MAXT];
+#pragma unroll
+                for (int q = 0; q < MAXT; ++q) dz[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk < D / 4; ++kk) {
+#pragma unroll
+                    for (int q = 0; q < MAXT; ++q) {
+                        const int s = wave + NW * q;
+                        if (s < nst)
+                            dz[q] = mfma(dYs.at(16 * tr(s, ncn) + jl, 4 * kk + g),
+                                         W2s.at(4 * kk + g, 16 * tc(s, ncn) + jl), dz[q]);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < MAXT; ++q) {
+                    const int s = wave + NW * q;
+                    if (s < nst)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            As.at(16 * tr(s, ncn) + 4 * g + r, 16 * tc(s, ncn) + jl) = dz[q][r] * sp[q][r];
+                }
+                __syncthreads();
+            }
+            // matrix 0: MLP W1 [Hd x D]: M += (cM dZ)^T K, W -= (cW dZ)^T K;
+            //           linear W [D x D]: M += (cM dY)^T K, W -= (cW dY)^T K
+            {
+                const Lm& G = mlp ? As : dYs;
+                for (int kk = 0; kk < TB / 4; ++kk) {
+                    const int tok = 4 * kk + g;
+                    const float cm = cms[tok], cw = cws[tok];
+#pragma unroll
+                    for (int q = 0; q < MAXT; ++q) {
+                        const int s = wave + NW * q;
+                        if (s < ns0) {
+                            const float x = G.at(tok, 16 * tr(s, nc0) + jl);
+                            const float b = Xs.at(tok, 16 * tc(s, nc0) + jl);
+                            if (MOM) m0[q] = mfma(cm * x, b, m0[q]);
+                            w0[q] = mfma(-cw * x, b, w0[q]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();  // Xs, As, dYs are rewritten by the next block
+        }
+    }
+    // final state
+    asm volatile("" : "+v"(jl), "+v"(g));
+    {
+        float* W = a.W + bh * P;
+        float* M = MOM ? a.M + bh * P : nullptr;
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) {
+            const int s0 = wave + NW * q;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (s0 < ns0) {
+                    W[gidx0(s0, r)] = w0[q][r];
+                    if (MOM) M[gidx0(s0, r)] = m0[q][r];
+                }
+                if (s0 < ns1) {
+                    W[gidx1(s0, r)] = w1[q][r];
+                    if (MOM) M[gidx1(s0, r)] = m1[q][r];
+                }
+            }
+        }
+    }
+}
+
+constexpr size_t kLdsMax = 160 * 1024;
+
+int rs_of(int64_t cols) { return (int)((cols + 63) / 64 * 64); }
+
+int f32_block(const e2ttt_desc& d) { return (int)(d.chunk >= TBMAX ? TBMAX : (d.chunk + 15) / 16 * 16); }
+
+size_t f32_lds_bytes(const e2ttt_desc& d) {
+    const int64_t TB = f32_block(d), rsd = rs_of(d.D);
+    if (d.kind == E2TTT_MLP) {
+        const int64_t rsh = rs_of(d.Hd);
+        return (size_t)(d.Hd * rsd + d.D * rsh + TB * rsd + TB * rsh + TB * rsd + 2 * TB) * 4;
+    }
+    return (size_t)(d.D * rsd + 2 * TB * rsd + 2 * TB) * 4;
+}
+
+template <int KIND, int LOSS>
+hipError_t launch_kl(const e2ttt_desc& d, const F32Args& a, hipStream_t s) {
+    const size_t shmem = f32_lds_bytes(d);
+    const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
+    const void* f = mom ? (const void*)f32_chunk_kernel<KIND, LOSS, true> : (const void*)f32_chunk_kernel<KIND, LOSS, false>;
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(d.B * d.H)), block(NT);
+    if (mom)
+        hipLaunchKernelGGL((f32_chunk_kernel<KIND, LOSS, true>), grid, block, shmem, s, a);
+    else
+        hipLaunchKernelGGL((f32_chunk_kernel<KIND, LOSS, false>), grid, block, shmem, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool f32_mfma_supported(const e2ttt_desc& d) {
+    if (d.io_dtype != E2TTT_F32) return false;
+    if (d.kind != E2TTT_LINEAR && d.kind != E2TTT_MLP) return false;
+    if (d.D < 16 || d.D % 16) return false;
+    const int64_t TB = f32_block(d);
+    const int64_t nsd = d.D / 16;
+    if (d.kind == E2TTT_MLP) {
+        if (d.Hd < 16 || d.Hd % 16) return false;
+        const int64_t nsh = d.Hd / 16;
+        // state, Z / dZ and output tiles per wavefront
+        if (nsh * nsd > NW * MAXT || (TB / 16) * nsh > NW * MAXT || (TB / 16) * nsd > NW * MAXT) return false;
+    } else {
+        if (nsd * nsd > NW * MAXT || (TB / 16) * nsd > NW * MAXT) return false;
+    }
+    return f32_lds_bytes(d) <= kLdsMax;
+}
+
+hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
+                           const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
+                           float* W_end, float* M_end, hipStream_t s, float* save) {
+    F32Args a;
+    a.q = (const float*)q;
+    a.k = (const float*)k;
+    a.v = (const float*)v;
+    a.cM = cM;
+    a.cW = cW;
+    a.scal = scal;
+    a.W0 = W0;
+    a.M0 = M0;
+    a.out = (float*)out;
+    a.W = W_end;
+    a.M = M_end;
+    a.save = save;
+    a.T = d.T;
+    a.ldc = ldc;
+    a.P = e2ttt_param_count(&d);
+    a.D = (int)d.D;
+    a.Hd = d.kind == E2TTT_MLP ? (int)d.Hd : 0;
+    a.C = (int)d.chunk;
+    a.nc = (int)((d.T + d.chunk - 1) / d.chunk);
+    a.TB = f32_block(d);
+    a.rsd = rs_of(d.D);
+    a.rsh = d.kind == E2TTT_MLP ? rs_of(d.Hd) : 64;
+    if (d.kind == E2TTT_MLP)
+        return d.loss == E2TTT_LOSS_MSE ? launch_kl<E2TTT_MLP, E2TTT_LOSS_MSE>(d, a, s)
+                                        : launch_kl<E2TTT_MLP, E2TTT_LOSS_NEGDOT>(d, a, s);
+    return d.loss == E2TTT_LOSS_MSE ? launch_kl<E2TTT_LINEAR, E2TTT_LOSS_MSE>(d, a, s)
+                                    : launch_kl<E2TTT_LINEAR, E2TTT_LOSS_NEGDOT>(d, a, s);
+}
+
+}  // namespace e2ttt

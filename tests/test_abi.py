@@ -41,7 +41,7 @@ def test_param_count_and_paths(lib):
         d = _desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
         assert lib.e2ttt_param_count(ctypes.byref(d)) == cfg.P
         path = lib.e2ttt_path(ctypes.byref(d))
-        assert path == (1 if cfg.kind == "swiglu" else 0)
+        assert path == (1 if cfg.kind == "swiglu" else 3)  # linear / MLP: the fp32 MFMA path
         assert lib.e2ttt_workspace_size(ctypes.byref(d)) > 0
     d = _desc(flags=1)
     assert lib.e2ttt_path(ctypes.byref(d)) == 0
@@ -170,9 +170,34 @@ def test_paths_of_narrow_heads_and_precise_flag(lib):
     # same workspace as the bf16 MFMA path (snapshot layout)
     a = lib.e2ttt_workspace_size(ctypes.byref(_desc(Hd=64)))
     assert lib.e2ttt_workspace_size(ctypes.byref(_desc(Hd=64, flags=FLAG_PRECISE))) == a
-    # the portable fp32 path is unaffected by the flag
+    # the fp32 paths are unaffected by the flag
     d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=FLAG_PRECISE)
+    assert lib.e2ttt_path(ctypes.byref(d)) == 3
+    d = _desc(kind="mlp", loss="mse", io="f32", D=48, Hd=40, flags=FLAG_PRECISE)
     assert lib.e2ttt_path(ctypes.byref(d)) == 0
+
+
+def test_fp32_mfma_path_shapes(lib):
+    """Linear / MLP with fp32 I/O take the fp32 MFMA path (3) when D and Hd are
+    multiples of 16 and a head's state fits 32 tiles of 16x16 per matrix;
+    other shapes, bf16 I/O and E2TTT_FLAG_FORCE_GENERIC take the portable
+    path (0)."""
+    p = lambda **kw: lib.e2ttt_path(ctypes.byref(_desc(**kw)))
+    assert p(kind="linear", loss="mse", io="f32", D=32, Hd=0, chunk=16) == 3
+    assert p(kind="linear", loss="negdot", io="f32", D=64, Hd=0, chunk=100) == 3
+    assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=64) == 3
+    assert p(kind="mlp", loss="negdot", io="f32", D=16, Hd=48, chunk=1) == 3
+    assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=40) == 0          # Hd not a multiple of 16
+    assert p(kind="linear", loss="mse", io="f32", D=40, Hd=0) == 0        # D not a multiple of 16
+    assert p(kind="mlp", loss="mse", io="f32", D=128, Hd=256) == 0        # 128 tiles per matrix
+    assert p(kind="mlp", loss="mse", io="bf16", D=64, Hd=128) == 0        # bf16 I/O
+    assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=1) == 0
+    # no workspace beyond the scalar kernels' outputs
+    d = _desc(kind="mlp", loss="mse", io="f32", B=2, H=4, T=2048, D=64, Hd=128, chunk=64)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 2 * 8 * 2048 * 4 + 8 * 32 * 16
+    # saving states for the portable backward is allowed from this path
+    d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=64, flags=8)
+    assert _validate(lib, d, _ptrs(d)) == 0
 
 
 def test_chunk_beyond_int32_rejected(lib):
