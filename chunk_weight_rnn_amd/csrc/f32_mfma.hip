@@ -38,6 +38,7 @@ constexpr int NW = 8;          // wavefronts per workgroup
 constexpr int NT = 64 * NW;    // threads per workgroup
 constexpr int TBMAX = 64;      // tokens per block
 constexpr int MAXT = 4;        // 16x16 tiles per wavefront per matrix
+constexpr int MAXY = 2;        // 16x16 tiles per wavefront of a [TB x D] product (D <= 64)
 
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -55,7 +56,7 @@ struct Lm {
     }
 };
 
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 struct F32Args {
     const float* q;
@@ -92,8 +93,10 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
     const bool mlp = KIND == E2TTT_MLP;
 
     // ---------------------------------------------------------------- LDS
-    // MLP:    W1s [Hd][rsd] | W2s [D][rsh] | Xs [TB][rsd] | As [TB][rsh] | dYs [TB][rsd] | c [2][TB]
-    // linear: Ws [D][rsd]                  | Xs [TB][rsd] |              | dYs [TB][rsd] | c [2][TB]
+    // MLP:    W1s [Hd][rsd] | W2s [D][rsh] | Xs [TB][rsd] | As [TB][rsh] | Ks [TB][rsd] | c [2][TB]
+    // linear: Ws [D][rsd]                  | Xs [TB][rsd] |              | Ks [TB][rsd] | c [2][TB]
+    // Xs holds a block's Q rows, then (once the output stage has read them) dY;
+    // Ks its K rows.
     float* p = lds;
     const Lm W1s{p, a.rsd};
     p += (mlp ? Hd : D) * a.rsd;
@@ -103,8 +106,9 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
     p += TB * a.rsd;
     const Lm As{p, a.rsh};
     p += mlp ? TB * a.rsh : 0;
-    const Lm dYs{p, a.rsd};
+    const Lm Ks{p, a.rsd};
     p += TB * a.rsd;
+    const Lm& dYs = Xs;
     float* cms = p;
     float* cws = p + TB;
 
@@ -145,14 +149,18 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
     const float* cMh = a.cM + bh * a.ldc;
     const float* cWh = a.cW + bh * a.ldc;
 
-    // rows [t, t + nb) of x [T][D] -> Xs, zero rows nb .. TB-1
-    auto load_rows = [&](const float* x, int64_t t, int nb) {
+    // rows [t, t + nb) of q and k [T][D] -> Xs and Ks, zero rows nb .. TB-1
+    auto load_rows = [&](int64_t t, int nb) {
         const int n4 = D / 4;
         for (int i = tid; i < TB * n4; i += NT) {
             const int r = i / n4, c4 = i % n4;
-            f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
-            if (r < nb) v4 = *(const f32x4*)&x[(t + r) * D + 4 * c4];
-            *Xs.row4(r, c4) = v4;
+            f32x4 q4 = {0.f, 0.f, 0.f, 0.f}, k4 = q4;
+            if (r < nb) {
+                q4 = *(const f32x4*)&qh[(t + r) * D + 4 * c4];
+                k4 = *(const f32x4*)&kh[(t + r) * D + 4 * c4];
+            }
+            *Xs.row4(r, c4) = q4;
+            *Ks.row4(r, c4) = k4;
         }
     };
 
@@ -170,11 +178,34 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
             ti[q] = s < nst ? tr(s, ncn) : 0;
             tj[q] = s < nst ? tc(s, ncn) : 0;
         }
-        for (int kk = 0; kk < K / 4; ++kk) {
+        // k-slot (g, j) of MFMA j in group m is k = 16 m + 4 g + j: each lane
+        // reads its 4 k of a group with one 16-byte LDS read per operand.
+        // When the column tiles divide the wavefronts, all of a wave's tiles
+        // share one column tile and its B operand is read once.
+        if (NW % ncn == 0) {
+            for (int m = 0; m < K / 16; ++m) {
+                f32x4 av[MAXT];
+                const f32x4 bv = *B.row4(16 * tj[0] + jl, 4 * m + g);
 #pragma unroll
-            for (int q = 0; q < MAXT; ++q) {
-                if (wave + NW * q < nst)
-                    acc[q] = mfma(X.at(16 * ti[q] + jl, 4 * kk + g), B.at(16 * tj[q] + jl, 4 * kk + g), acc[q]);
+                for (int q = 0; q < MAXT; ++q)
+                    if (wave + NW * q < nst) av[q] = *X.row4(16 * ti[q] + jl, 4 * m + g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < MAXT; ++q)
+                        if (wave + NW * q < nst) acc[q] = mfma(av[q][j], bv[j], acc[q]);
+            }
+        } else {
+            for (int m = 0; m < K / 16; ++m) {
+#pragma unroll
+                for (int q = 0; q < MAXT; ++q) {
+                    if (wave + NW * q < nst) {
+                        const f32x4 av = *X.row4(16 * ti[q] + jl, 4 * m + g);
+                        const f32x4 bv = *B.row4(16 * tj[q] + jl, 4 * m + g);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[q] = mfma(av[j], bv[j], acc[q]);
+                    }
+                }
             }
         }
 #pragma unroll
@@ -241,7 +272,22 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
             const int nb = min(TB, Cc - tb0);
             const int64_t tt = t0 + tb0;  // first token of the block
             // ---------------------------------------------------- output
-            load_rows(qh, tt, nb);
+            // the block's Q and K rows, coefficients and this wave's V elements
+            // are loaded together: one load latency is exposed per block
+            float vr[MAXY][4];  // V at this wave's Y tiles (tiles s = wave + NW q of [TB x D])
+            {
+                const int ncn = D / 16, nst = (TB / 16) * ncn;
+#pragma unroll
+                for (int q = 0; q < MAXY; ++q) {
+                    const int s = wave + NW * q;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * tr(s, ncn) + 4 * g + r;
+                        vr[q][r] = (s < nst && row < nb) ? vh[(tt + row) * D + 16 * tc(s, ncn) + jl] : 0.f;
+                    }
+                }
+            }
+            load_rows(tt, nb);
             for (int i = tid; i < TB; i += NT) {
                 cms[i] = (MOM && i < nb) ? cMh[tt + i] : 0.f;
                 cws[i] = i < nb ? cWh[tt + i] : 0.f;
@@ -267,19 +313,16 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
             }
             __syncthreads();
             // ---------------------------------------------------- forward
-            load_rows(kh, tt, nb);
-            __syncthreads();
             float sp[MAXT][4];  // silu'(Z) of this wave's Z tiles
-            auto to_dy = [&](int, int ti, int tj, f32x4 y) {  // dL/dy of this wave's Y tiles -> dYs
+            auto to_dy = [&](int q, int ti, int tj, f32x4 y) {  // dL/dy of this wave's Y tiles -> dYs
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * ti + 4 * g + r, col = 16 * tj + jl;
-                    const float vv = row < nb ? vh[(tt + row) * D + col] : 0.f;
-                    dYs.at(row, col) = LOSS == E2TTT_LOSS_MSE ? y[r] - vv : -vv;
+                    dYs.at(row, col) = LOSS == E2TTT_LOSS_MSE ? y[r] - vr[q & (MAXY - 1)][r] : -vr[q & (MAXY - 1)][r];
                 }
             };
             if (mlp) {
-                gemm_rows(Xs, W1s, Hd, D, [&](int q, int ti, int tj, f32x4 z) {
+                gemm_rows(Ks, W1s, Hd, D, [&](int q, int ti, int tj, f32x4 z) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float s = sigm(z[r]);
@@ -292,20 +335,29 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
                     gemm_rows(As, W2s, D, Hd, to_dy);  // Y = A W2^T
                 } else {
                     const int ncn = D / 16, nst = (TB / 16) * ncn;
-                    for (int s = wave; s < nst; s += NW) to_dy(0, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int q = 0; q < MAXY; ++q) {
+                        const int s = wave + NW * q;
+                        if (s < nst) to_dy(q, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
                 }
             } else {
                 if (LOSS == E2TTT_LOSS_MSE) {
-                    gemm_rows(Xs, W1s, D, D, to_dy);  // Y = K W^T
+                    gemm_rows(Ks, W1s, D, D, to_dy);  // Y = K W^T
                 } else {
                     const int ncn = D / 16, nst = (TB / 16) * ncn;
-                    for (int s = wave; s < nst; s += NW) to_dy(0, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int q = 0; q < MAXY; ++q) {
+                        const int s = wave + NW * q;
+                        if (s < nst) to_dy(q, tr(s, ncn), tc(s, ncn), f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
                 }
             }
             __syncthreads();
             // ---------------------------------------------------- aggregation, matrix 1
             // MLP W2 [D x Hd]: M += (cM dY)^T A, W -= (cW dY)^T A
             if (mlp) {
+#pragma unroll 2
                 for (int kk = 0; kk < TB / 4; ++kk) {
                     const int tok = 4 * kk + g;
                     const float cm = cms[tok], cw = cws[tok];
@@ -326,6 +378,7 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
                 f32x4 dz[MAXT];
 #pragma unroll
                 for (int q = 0; q < MAXT; ++q) dz[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
                 for (int kk = 0; kk < D / 4; ++kk) {
 #pragma unroll
                     for (int q = 0; q < MAXT; ++q) {
@@ -349,6 +402,7 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
             //           linear W [D x D]: M += (cM dY)^T K, W -= (cW dY)^T K
             {
                 const Lm& G = mlp ? As : dYs;
+#pragma unroll 2
                 for (int kk = 0; kk < TB / 4; ++kk) {
                     const int tok = 4 * kk + g;
                     const float cm = cms[tok], cw = cws[tok];
@@ -357,7 +411,7 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
                         const int s = wave + NW * q;
                         if (s < ns0) {
                             const float x = G.at(tok, 16 * tr(s, nc0) + jl);
-                            const float b = Xs.at(tok, 16 * tc(s, nc0) + jl);
+                            const float b = Ks.at(tok, 16 * tc(s, nc0) + jl);
                             if (MOM) m0[q] = mfma(cm * x, b, m0[q]);
                             w0[q] = mfma(-cw * x, b, w0[q]);
                         }
@@ -425,7 +479,7 @@ hipError_t launch_kl(const e2ttt_desc& d, const F32Args& a, hipStream_t s) {
 bool f32_mfma_supported(const e2ttt_desc& d) {
     if (d.io_dtype != E2TTT_F32) return false;
     if (d.kind != E2TTT_LINEAR && d.kind != E2TTT_MLP) return false;
-    if (d.D < 16 || d.D % 16) return false;
+    if (d.D < 16 || d.D % 16 || d.D > 64) return false;
     const int64_t TB = f32_block(d);
     const int64_t nsd = d.D / 16;
     if (d.kind == E2TTT_MLP) {

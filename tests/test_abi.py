@@ -190,6 +190,8 @@ def test_fp32_mfma_path_shapes(lib):
     assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=40) == 0          # Hd not a multiple of 16
     assert p(kind="linear", loss="mse", io="f32", D=40, Hd=0) == 0        # D not a multiple of 16
     assert p(kind="mlp", loss="mse", io="f32", D=128, Hd=256) == 0        # 128 tiles per matrix
+    assert p(kind="mlp", loss="mse", io="f32", D=128, Hd=64) == 0         # D > 64
+    assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=80) == 3
     assert p(kind="mlp", loss="mse", io="bf16", D=64, Hd=128) == 0        # bf16 I/O
     assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=1) == 0
     # no workspace beyond the scalar kernels' outputs

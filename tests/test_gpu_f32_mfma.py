@@ -22,7 +22,7 @@ CASES = [
     ("mlp", "mse", 1, 2, 512, 64, 128, 64),      # the MLP workload's head shape
     ("mlp", "mse", 2, 1, 200, 32, 64, 48),       # 48-token blocks, an 8-token last chunk
     ("mlp", "negdot", 1, 2, 400, 16, 48, 130),   # three blocks per chunk (64 + 64 + 2)
-    ("mlp", "mse", 1, 2, 256, 128, 64, 64),      # 32 tiles per matrix (the largest head)
+    ("mlp", "mse", 1, 2, 256, 48, 80, 64),       # 5 column tiles: every tile reads its own B operand
     ("mlp", "negdot", 1, 1, 64, 64, 128, 16),
 ]
 
