@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libe2ttt.so")
+# E2TTT_LIB names another build of the same library (the host-sanitized copy
+# the CPU tests load); by default the in-tree libe2ttt.so.
+LIB_PATH = os.environ.get("E2TTT_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libe2ttt.so")
 
 KIND = {"linear": 0, "mlp": 1, "swiglu": 2}
 LOSS = {"mse": 0, "negdot": 1}
