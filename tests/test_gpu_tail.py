@@ -134,3 +134,29 @@ def test_streaming_chunk_by_chunk(name, momentum):
     assert torch.equal(W, full[1])
     if momentum:
         assert torch.equal(M, full[2])
+
+
+@pytest.mark.parametrize("name,momentum", [("swiglu_1p3b", True), ("swiglu_1p3b", False), ("mlp_fp32", True)])
+def test_streaming_matches_oracle(name, momentum):
+    """Streaming against the oracle directly: the sequence arrives one chunk
+    per call (eight whole chunks and a ragged remainder) with the state
+    carried between calls; every chunk's output and the final state are
+    compared with one oracle pass over the whole sequence.  Slow-decay gates
+    keep the carried state alive to the last chunk."""
+    e2 = _e2()
+    base = synth.CONFIGS[name]
+    cfg = base.with_(name=f"stream_{name}", B=1, H=4, T=8 * base.chunk + 37, flags=0 if momentum else 2)
+    gu.note(f"streaming vs oracle {name} momentum={momentum} T={cfg.T}")
+    x = gu.persistent_gates(cfg, synth.make_inputs(cfg, seed=19, m0_scale=0.5 if momentum else 0.0))
+    d = gu.to_dev(x)
+    kw = dict(chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd, momentum=momentum)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    W, M, outs = d["W0"], d["M0"], []
+    for t0 in range(0, cfg.T, cfg.chunk):
+        t1 = min(t0 + cfg.chunk, cfg.T)
+        o, W, M = e2.chunk_forward(*(sl(d[n], t0, t1) for n in ("q", "k", "v", "eta", "alpha", "beta")), W, M,
+                                   **kw)
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = (torch.cat(outs, dim=2).float().cpu(), W.cpu(), M.cpu() if momentum else None)
+    gu.assert_close(cfg, got, gu.run_oracle(cfg, x), x["W0"].numpy())

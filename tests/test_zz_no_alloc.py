@@ -77,6 +77,30 @@ def test_noalloc_portable_path_and_variants():
             assert (a is None and b is None) or torch.equal(a, b)
 
 
+@pytest.mark.gpu
+def test_noalloc_serving_loop():
+    """A serving loop: one 256-token chunk of a B = 2, H = 16 SwiGLU layer per
+    call on a carried state, through the no-allocation entry point with
+    preallocated outputs; every call's results equal e2ttt_chunk_forward's."""
+    e2 = _lib()
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name="noalloc_serving", B=2, T=4 * 256)
+    x = gu.to_dev(synth.make_inputs(cfg, seed=25, m0_scale=0.5))
+    kw = dict(chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    W, M = x["W0"].clone(), x["M0"].clone()
+    Wr, Mr = x["W0"].clone(), x["M0"].clone()
+    out = torch.empty(cfg.B, cfg.H, cfg.chunk, cfg.D, dtype=torch.bfloat16, device="cuda")
+    Wn, Mn = torch.empty_like(W), torch.empty_like(M)
+    for t0 in range(0, cfg.T, cfg.chunk):
+        args = [sl(x[n], t0, t0 + cfg.chunk) for n in ("q", "k", "v", "eta", "alpha", "beta")]
+        e2.chunk_forward_noalloc(*args, W, M, out=out, W_end=Wn, M_end=Mn, **kw)
+        ro, Wr, Mr = e2.chunk_forward(*args, Wr, Mr, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ro) and torch.equal(Wn, Wr) and torch.equal(Mn, Mr)
+        W, Wn = Wn, W
+        M, Mn = Mn, M
+
+
 def test_noalloc_refuses_oversized_call_before_device_work():
     """A call whose workspace exceeds the scratch returns
     E2TTT_ERR_SCRATCH_LIMIT (no device call happens first, so this runs
