@@ -540,7 +540,8 @@ def main() -> int:
     heads_tokens = cfg.B * cfg.H * cfg.T
     path = int(lib.e2ttt_path(ctypes.byref(desc)))
     peak = PEAK_BF16_TFLOPS if path in (1, 2) else PEAK_F32_TFLOPS
-    loop_kernel = {0: "generic_kernel", 1: "swiglu_loop_kernel", 2: "swiglu_loop_kernel", 3: "f32_chunk_kernel"}[path]
+    loop_kernel = {0: "generic_kernel", 1: "swiglu_loop_kernel", 2: "swiglu_loop_kernel", 3: "f32_chunk_kernel",
+                   4: "f32_split_kernel (one launch per chunk boundary)"}[path]
     # the fp32 kernels compute the chunk outputs inside the chunk loop
     loop_stages = ("grad", "aggregate") if path in (1, 2) else ("grad", "aggregate", "apply")
     loop_flops = sum(fpt[k] for k in loop_stages) * heads_tokens

@@ -96,11 +96,13 @@ static bool logscan_desc_ok(const e2ttt_desc* d) {
 }
 
 // 0: portable fp32 kernel, 1: SwiGLU bf16 MFMA path, 2: the same with hi/lo
-// bf16 operands (E2TTT_FLAG_PRECISE), 3: fp32 MFMA path (linear / MLP, fp32 I/O)
+// bf16 operands (E2TTT_FLAG_PRECISE), 3: fp32 MFMA path (linear / MLP, fp32
+// I/O, one workgroup per head), 4: the same for the MLP split over hidden
+// slices (few heads)
 static int path_of(const e2ttt_desc& d) {
     if (d.flags & E2TTT_FLAG_FORCE_GENERIC) return 0;
     if (swiglu_mfma_supported(d)) return (d.flags & E2TTT_FLAG_PRECISE) ? 2 : 1;
-    if (f32_mfma_supported(d)) return 3;
+    if (f32_mfma_supported(d)) return f32_split(d) ? 4 : 3;
     return 0;
 }
 
@@ -108,7 +110,7 @@ static int path_of(const e2ttt_desc& d) {
 // bf16 snapshots for the MFMA backward, the fp32 chunk-start states for the
 // portable backward (written by both fp32 forward paths).
 static bool save_compatible(int fwd_path, int bwd_path) {
-    return (fwd_path == 1 && bwd_path == 1) || ((fwd_path == 0 || fwd_path == 3) && bwd_path == 0);
+    return (fwd_path == 1 && bwd_path == 1) || ((fwd_path == 0 || fwd_path >= 3) && bwd_path == 0);
 }
 
 static bool generic_supported(const e2ttt_desc& d) {
@@ -130,7 +132,7 @@ static int backward_path(const e2ttt_desc& d) {
 }
 
 struct BwdWorkspace {
-    size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, total;
+    size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, split, total;
     size_t save, gacc;  // portable path: chunk-start states, forward G accumulators / dJ/dW
     int64_t ldc;
 };
@@ -157,6 +159,7 @@ static BwdWorkspace bwd_workspace_layout(const e2ttt_desc& d) {
         w.dcM = take(BH * ldc * 4);
         w.dcW = take(BH * ldc * 4);
         w.dpart = take(BH * nc * 4 * 4);
+        w.split = take(f32_split_bytes(d));  // the fp32 MFMA forward's partial sums (recompute / saved forward)
         w.total = (BH * (size_t)d.T == 0) ? 0 : off;
         return w;
     }
@@ -223,7 +226,10 @@ Workspace workspace_layout(const e2ttt_desc& d, int path) {
         off += align_up(BH * 2 * P * sizeof(float));  // portable path: G accumulators
     else if (path == 1 || path == 2)
         off += align_up(BH * nc * P * 2);  // bf16 chunk-start snapshots
-    // path 3 (fp32 MFMA) keeps its state and aggregations on chip
+    // path 3 (fp32 MFMA) keeps its state and aggregations on chip, except
+    // for the hidden-slice split, whose partial sums pass through here
+    w.split = off;
+    if (path == 4) off += align_up(f32_split_bytes(d));
     w.total = (BH * T == 0) ? 0 : off;
     return w;
 }
@@ -319,6 +325,7 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
         ws.scal = bws.scal;
         ws.snap = bws.snapW;
         ws.gacc = bws.gacc;
+        ws.split = bws.split;
         ws.total = bws.total;
     }
     if (ws.total > 0) {
@@ -364,9 +371,9 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (path == 1 || path == 2) {
         e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap,
                                save && mom ? wsb + bws.snapM : nullptr, s, ev[2]);
-    } else if (path == 3) {
+    } else if (path == 3 || path == 4) {
         e = launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, s,
-                            save ? (float*)(wsb + bws.save) : nullptr);
+                            save ? (float*)(wsb + bws.save) : nullptr, wsb + ws.split);
         if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
     } else {
         e = launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, (float*)(wsb + ws.gacc),
@@ -477,8 +484,9 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
             // the forward path e2ttt_chunk_forward takes, so that a saved forward
             // and this recompute leave the same states
             const hipError_t fe =
-                path_of(*d) == 3
-                    ? launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, s, save)
+                path_of(*d) >= 3
+                    ? launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0, s, save,
+                                      wsb + ws.split)
                     : launch_generic(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, dq, dW0, dM0,
                                      (float*)(wsb + ws.gacc), s, save);
             if (fe != hipSuccess) return E2TTT_ERR_HIP;

@@ -19,6 +19,7 @@ struct Workspace {
     int64_t ldc;          // T rounded up to a whole 64-token block
     size_t gacc;          // portable path: per-head gradient accumulators (fp32, 2*P)
     size_t snap;          // MFMA path: bf16 chunk-start weight snapshots (B*H*nc*P)
+    size_t split;         // fp32 MFMA path, MLP split over hidden slices: partial sums
     size_t total;
 };
 
@@ -43,9 +44,13 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
 // (D and Hd multiples of 16, a head's state within 32 16x16 tiles per
 // matrix); save as launch_generic's.
 bool f32_mfma_supported(const e2ttt_desc& d);
+// Whether the MLP is split over hidden slices (one launch per chunk
+// boundary), and the workspace bytes the split needs (0 otherwise).
+bool f32_split(const e2ttt_desc& d);
+size_t f32_split_bytes(const e2ttt_desc& d);
 hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
                            const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
-                           float* W_end, float* M_end, hipStream_t s, float* save);
+                           float* W_end, float* M_end, hipStream_t s, float* save, void* split_ws);
 
 // SwiGLU / negative-dot / bf16 / D == 128 / Hd % 64 == 0 / chunk % 64 == 0.
 bool swiglu_mfma_supported(const e2ttt_desc& d);

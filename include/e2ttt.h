@@ -126,7 +126,11 @@ E2TTT_API size_t e2ttt_workspace_size(const e2ttt_desc* desc);
 /* Which device path e2ttt_chunk_forward takes: 0 = portable fp32 kernel,
  * 1 = SwiGLU bf16 MFMA path (SWIGLU, LOSS_NEGDOT, BF16, D == 128, Hd a
  * multiple of 64 up to 4096, chunk a multiple of 64, T * D * 2 < 2^31),
- * 2 = the same shapes with E2TTT_FLAG_PRECISE (hi/lo bf16 operands);
+ * 2 = the same shapes with E2TTT_FLAG_PRECISE (hi/lo bf16 operands),
+ * 3 = fp32 MFMA path for LINEAR / MLP with F32 I/O (D a multiple of 16 up to
+ * 64, Hd a multiple of 16, a head's state within 32 16x16 tiles per matrix),
+ * 4 = the same for an MLP split over 16-unit hidden slices (B*H*Hd/16 <= 256,
+ * chunk <= 64; one kernel launch per chunk boundary);
  * negative e2ttt_status for a bad desc. */
 E2TTT_API int e2ttt_path(const e2ttt_desc* desc);
 

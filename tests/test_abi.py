@@ -41,7 +41,8 @@ def test_param_count_and_paths(lib):
         d = _desc(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk)
         assert lib.e2ttt_param_count(ctypes.byref(d)) == cfg.P
         path = lib.e2ttt_path(ctypes.byref(d))
-        assert path == (1 if cfg.kind == "swiglu" else 3)  # linear / MLP: the fp32 MFMA path
+        # linear / MLP: the fp32 MFMA path; the 8-head MLP workload split over hidden slices
+        assert path == {"swiglu": 1, "linear": 3, "mlp": 4}[cfg.kind]
         assert lib.e2ttt_workspace_size(ctypes.byref(d)) > 0
     d = _desc(flags=1)
     assert lib.e2ttt_path(ctypes.byref(d)) == 0
@@ -172,7 +173,7 @@ def test_paths_of_narrow_heads_and_precise_flag(lib):
     assert lib.e2ttt_workspace_size(ctypes.byref(_desc(Hd=64, flags=FLAG_PRECISE))) == a
     # the fp32 paths are unaffected by the flag
     d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=FLAG_PRECISE)
-    assert lib.e2ttt_path(ctypes.byref(d)) == 3
+    assert lib.e2ttt_path(ctypes.byref(d)) == 4
     d = _desc(kind="mlp", loss="mse", io="f32", D=48, Hd=40, flags=FLAG_PRECISE)
     assert lib.e2ttt_path(ctypes.byref(d)) == 0
 
@@ -185,18 +186,26 @@ def test_fp32_mfma_path_shapes(lib):
     p = lambda **kw: lib.e2ttt_path(ctypes.byref(_desc(**kw)))
     assert p(kind="linear", loss="mse", io="f32", D=32, Hd=0, chunk=16) == 3
     assert p(kind="linear", loss="negdot", io="f32", D=64, Hd=0, chunk=100) == 3
-    assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=64) == 3
-    assert p(kind="mlp", loss="negdot", io="f32", D=16, Hd=48, chunk=1) == 3
+    assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=64) == 4      # 2 x 3 heads x 8 slices
+    assert p(kind="mlp", loss="mse", io="f32", B=8, H=16, D=64, Hd=128, chunk=64) == 3  # 1024 slices: per head
+    assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=128) == 3     # chunks over 64 tokens
+    assert p(kind="mlp", loss="negdot", io="f32", D=16, Hd=48, chunk=1) == 4
     assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=40) == 0          # Hd not a multiple of 16
     assert p(kind="linear", loss="mse", io="f32", D=40, Hd=0) == 0        # D not a multiple of 16
     assert p(kind="mlp", loss="mse", io="f32", D=128, Hd=256) == 0        # 128 tiles per matrix
     assert p(kind="mlp", loss="mse", io="f32", D=128, Hd=64) == 0         # D > 64
-    assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=80) == 3
+    assert p(kind="mlp", loss="mse", io="f32", D=48, Hd=80) == 4
     assert p(kind="mlp", loss="mse", io="bf16", D=64, Hd=128) == 0        # bf16 I/O
     assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=1) == 0
-    # no workspace beyond the scalar kernels' outputs
+    # the scalar kernels' outputs, and for few heads the hidden-slice split's
+    # partial sums: partial Y and partial outputs [2][BH][S][64][D] and the
+    # slices' silu(Z), silu'(Z) [BH][S][2][64][16] (S = Hd / 16)
     d = _desc(kind="mlp", loss="mse", io="f32", B=2, H=4, T=2048, D=64, Hd=128, chunk=64)
-    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 2 * 8 * 2048 * 4 + 8 * 32 * 16
+    split = 4 * (2 * 8 * 8 * 64 * 64 * 2 + 8 * 8 * 2 * 64 * 16)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 2 * 8 * 2048 * 4 + 8 * 32 * 16 + split
+    # many heads fill the chip with one workgroup each: no split
+    d = _desc(kind="mlp", loss="mse", io="f32", B=8, H=16, T=2048, D=64, Hd=128, chunk=64)
+    assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 2 * 128 * 2048 * 4 + 128 * 32 * 16
     # saving states for the portable backward is allowed from this path
     d = _desc(kind="mlp", loss="mse", io="f32", D=64, Hd=128, chunk=64, flags=8)
     assert _validate(lib, d, _ptrs(d)) == 0
