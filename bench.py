@@ -363,9 +363,10 @@ def cpu_baseline(cfg: synth.Config, budget_s: float) -> dict:
 
 def run_peaks(torch) -> dict:
     """The chip's own ceilings, next to the vendor peaks the roofline uses: bf16
-    MFMA throughput of the two shapes the kernels issue (independent
-    accumulations, 8 wavefronts per SIMD), HBM read bandwidth (grid-stride
-    16-byte loads) and a plain torch copy (read + write)."""
+    MFMA throughput of the shapes the kernels issue (independent
+    accumulations, 8 wavefronts per SIMD), the overlap of MFMA and VALU work
+    on one SIMD, LDS bandwidth per compute unit, HBM read bandwidth
+    (grid-stride 16-byte loads) and a plain torch copy (read + write)."""
     probe = ctypes.CDLL(os.path.join(ROOT, "chunk_weight_rnn_amd", "libe2ttt_probe.so"))
     probe.e2ttt_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     probe.e2ttt_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
@@ -398,6 +399,32 @@ def run_peaks(torch) -> dict:
             assert probe.e2ttt_probe_mfma(shape, iters, ctypes.c_void_p(out.data_ptr()), grid, sp) == 0
         t = timed(launch)
         res[name + "_TFLOPs"] = grid * 4 * iters * flop_wave_iter / t / 1e12
+    # MFMA and VALU of two wavefronts on one SIMD: 16 MFMAs per round against
+    # 16 V FMAs per round, alone and together
+    probe.e2ttt_probe_overlap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    ogrid = ncu
+    oout = torch.empty(ogrid * 512, dtype=torch.float32, device="cuda")
+    ov = {}
+    for mode, v, name in [(1, 2, "mfma_alone"), (2, 2, "valu2_alone"), (3, 2, "mfma_with_valu2"),
+                          (2, 4, "valu4_alone"), (3, 4, "mfma_with_valu4")]:
+        def launch(mode=mode, v=v):
+            assert probe.e2ttt_probe_overlap(mode, v, iters, ctypes.c_void_p(oout.data_ptr()), ogrid, sp) == 0
+        ov[name + "_us"] = timed(launch) * 1e6
+    ov["note"] = ("per SIMD: one wavefront with 16 x iters independent 16x16x32 bf16 MFMAs, another with 16 V x iters "
+                  "fp32 FMAs; together vs alone shows the overlap")
+    res["mfma_valu_overlap"] = ov
+    # LDS bytes per ns per compute unit, 12 wavefronts
+    probe.e2ttt_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lout = torch.empty(ncu * 768, dtype=torch.int32, device="cuda")
+    lds = {}
+    for mode, name, lane_bytes in [(0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8), (2, "ds_write_b128", 16)]:
+        def launch(mode=mode):
+            assert probe.e2ttt_probe_lds(mode, 12, 1000, ctypes.c_void_p(lout.data_ptr()), ncu, sp) == 0
+        t = timed(launch)
+        lds[name + "_B_per_ns_per_CU"] = 12 * 1000 * 16 * 64 * lane_bytes / (t * 1e9)
+    res["lds"] = lds
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     rgrid = ncu * 16
@@ -541,7 +568,7 @@ def main() -> int:
     path = int(lib.e2ttt_path(ctypes.byref(desc)))
     peak = PEAK_BF16_TFLOPS if path in (1, 2) else PEAK_F32_TFLOPS
     loop_kernel = {0: "generic_kernel", 1: "swiglu_loop_kernel", 2: "swiglu_loop_kernel", 3: "f32_chunk_kernel",
-                   4: "f32_split_kernel (one launch per chunk boundary)"}[path]
+                   4: "f32_split_kernel"}[path]
     # the fp32 kernels compute the chunk outputs inside the chunk loop
     loop_stages = ("grad", "aggregate") if path in (1, 2) else ("grad", "aggregate", "apply")
     loop_flops = sum(fpt[k] for k in loop_stages) * heads_tokens

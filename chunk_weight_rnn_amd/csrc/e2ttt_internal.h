@@ -44,8 +44,9 @@ hipError_t launch_generic(const e2ttt_desc& d, const void* q, const void* k, con
 // (D and Hd multiples of 16, a head's state within 32 16x16 tiles per
 // matrix); save as launch_generic's.
 bool f32_mfma_supported(const e2ttt_desc& d);
-// Whether the MLP is split over hidden slices (one launch per chunk
-// boundary), and the workspace bytes the split needs (0 otherwise).
+// Whether the MLP is split over hidden slices (one workgroup per slice for
+// the whole sequence, the slices of a head meeting once per chunk), and the
+// workspace bytes the split needs (0 otherwise).
 bool f32_split(const e2ttt_desc& d);
 size_t f32_split_bytes(const e2ttt_desc& d);
 hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,

@@ -448,8 +448,8 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
 // ---------------------------------------------------------------------------
 // The MLP split over its hidden units: for heads too few to fill the chip,
 // the hidden units of a head go to S = Hd / 16 workgroups (16 units each),
-// and the chunk loop becomes one launch per chunk boundary.  Launch L
-// finishes chunk L - 1 and starts chunk L:
+// which run the whole sequence in one launch.  Step L (L = 0 .. nc) finishes
+// chunk L - 1 and starts chunk L:
 //   finish: Y = sum of the S slices' partial Y (fixed order), dY = Y - V;
 //           dZ_s = (dY W2_s) silu'(Z_s); the slice's aggregations
 //           G_W2_s = dY^T diag(c) A_s, G_W1_s = dZ_s^T diag(c) K and its
@@ -458,15 +458,29 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
 //   start:  Z_s = K W1_s^T, A_s = silu(Z_s) (kept for the finish), the
 //           partial Y_s = A_s W2_s^T and the partial output
 //           silu(Q W1_s^T) W2_s^T.
-// The kernel boundary makes every slice's partial sums visible to the next
-// launch; no workgroup waits for another.  Each workgroup keeps its slice's
-// state in registers within a launch and in W_end / M_end between launches.
+// The slices of a head meet once per step: a slice publishes its partial sums
+// (stores, a device-scope release, then an increment of the head's arrival
+// counter) and the next step's finish waits until all S slices have arrived.
+// Partial sums are double-buffered by chunk parity: a slice overwrites a
+// buffer only after every slice has arrived once more, i.e. has finished
+// reading it.  A slice's state stays in registers for the whole sequence,
+// and its K rows, A_s and chunk-start W2_s stay in LDS from the start of a
+// chunk to its finish.
+//
+// All S workgroups of a head must run at the same time: the launch holds at
+// most one workgroup per compute unit.  A wait gives up after 10 s of wall
+// time (which only a device that cannot run the whole grid at once could
+// reach); it then raises the flag word after the counters, stops waiting for
+// the rest of the call and the workgroup writes NaN into its final state.
+// The counters and the flag are zeroed by a one-workgroup kernel before the
+// loop on the same stream.
 // ---------------------------------------------------------------------------
 constexpr int SNW = 4;         // wavefronts per split workgroup
 constexpr int SNT = 64 * SNW;
 constexpr int HS = 16;         // hidden units per split workgroup
 constexpr int SMAX = 16;       // slices per head (Hd <= 256)
 constexpr int RPT = 4;         // 16-byte pieces of a [TB][D] block per thread (TB * D <= 4096)
+constexpr uint64_t kSpinTicks = 1000000000ull;  // 10 s of the 100 MHz wall clock
 
 struct SplitArgs {
     const float* q;
@@ -483,16 +497,21 @@ struct SplitArgs {
     float* save;   // [BH][nc][2][P] chunk-start W, M (may be null)
     float* ypart;  // [2][BH][S][TB][D] partial Y of each slice (parity of the chunk)
     float* opart;  // [2][BH][S][TB][D] partial outputs
-    float* act;    // [BH][S][2][TB][HS] silu(Z_s), silu'(Z_s) of the chunk last started
+    unsigned* sync;  // [BH] arrival counters, then the time-out flag
     int64_t T, ldc, P;
-    int D, Hd, C, nc, TB, S, L;
+    int D, Hd, C, nc, TB, S;
     int xcd_map, nwg;
 };
+
+__global__ void split_sync_init(unsigned* sync, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0u;
+}
 
 template <int LOSS, bool MOM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(SNT, SNT), amdgpu_waves_per_eu(1, 1)))
 f32_split_kernel(SplitArgs a) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
+    __shared__ unsigned gave_up;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, jl = lane & 15, g = lane >> 4;
@@ -506,6 +525,8 @@ f32_split_kernel(SplitArgs a) {
     const int64_t P = a.P, T = a.T;
     const int nd = D / 16;  // tiles along D
     const int64_t off1 = (int64_t)Hd * D;
+    unsigned* const cnt = a.sync + bh;      // this head's arrival counter
+    unsigned* const flag = a.sync + a.nwg / S;  // after the BH counters
 
     // LDS: W1s [16][64] | W2s [D][64] | Ks [TB][64] | Qs [TB][64] (Q, or dY) | Ab [TB][64] (A, or dZ) | Aq [TB][64] | c [2][TB]
     float* p = lds;
@@ -529,20 +550,293 @@ f32_split_kernel(SplitArgs a) {
     f32x4 w1 = {0.f, 0.f, 0.f, 0.f}, m1 = w1, w2 = w1, m2 = w1;
     auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
     auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
-    auto load_state = [&](const float* W, const float* M) {
-        if (!st) return;
+    if (st) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            w1[r] = W[bh * P + i1(r)];
-            w2[r] = W[bh * P + i2(r)];
+            w1[r] = a.W0[bh * P + i1(r)];
+            w2[r] = a.W0[bh * P + i2(r)];
             if (MOM) {
-                m1[r] = M[bh * P + i1(r)];
-                m2[r] = M[bh * P + i2(r)];
+                m1[r] = a.M0[bh * P + i1(r)];
+                m2[r] = a.M0[bh * P + i2(r)];
             }
         }
+    }
+    if (tid == 0) gave_up = 0u;
+    const int64_t slot = bh * S + sl;
+    const size_t part = (size_t)TB * D;                // floats of one slice's partial
+    const size_t parity = (size_t)(gridDim.x) * part;  // all slices' partials of one chunk parity
+    const int n4 = D / 4;
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};  // silu'(Z) of the chunk last started at this wave's dZ tile (rows 16 wave + 4g + r, unit jl)
+
+    // until all S slices of the head have arrived `target` times in total.
+    // The cache maintenance of a device-scope acquire (invalidation) and
+    // release (L2 write-back) acts on whole caches, so one wavefront of the
+    // workgroup issues it, ordered with the others' accesses by the
+    // workgroup barrier (and, for the release, their own wait for their stores).
+    auto wait_head = [&](unsigned target) {
+        if (tid == 0 && !gave_up) {
+            const uint64_t t0 = wall_clock64();
+            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+                    wall_clock64() - t0 > kSpinTicks) {
+                    __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    gave_up = 1u;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
     };
-    auto store_state = [&](float* W, float* M) {
-        if (!st) return;
+    // this slice's partial sums of the step are visible device-wide, then it arrives
+    auto publish = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's stores are done
+        __syncthreads();
+        if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (tid == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    for (int L = 0; L <= a.nc; ++L) {
+        // lane coordinates re-derived in every step: otherwise the compiler
+        // keeps dozens of per-lane 64-bit addresses live across the loop
+        int tid_s = threadIdx.x;
+        asm volatile("" : "+v"(tid_s));
+        const int tid = tid_s, lane = tid & 63, jl = lane & 15, g = lane >> 4;
+        auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
+        auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
+        auto rows = [&](const float* x, int64_t t, int nb, f32x4 (&v4)[RPT]) {
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) {
+                const int i = tid + SNT * u, r = i / n4;
+                v4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i < TB * n4 && r < nb) v4[u] = *(const f32x4*)&x[(bh * T + t + r) * D + 4 * (i % n4)];
+            }
+        };
+        const bool fin = L >= 1, sta = L < a.nc;
+        const int cf = L - 1, cs = L;  // the chunk finished, the chunk started
+        const int64_t tf = (int64_t)cf * a.C, ts = (int64_t)cs * a.C;
+        const int nbf = fin ? (int)min((int64_t)a.C, T - tf) : 0, nbs = sta ? (int)min((int64_t)a.C, T - ts) : 0;
+        const int nr = fin ? (nbf - sl + S - 1) / S : 0;  // output rows r = sl, sl + S, ... of the finished chunk
+        const int orow = sl + S * (tid / n4), oc4 = tid % n4;
+
+        // ------------------------------------------------------------ the step's loads: own rows first
+        f32x4 vf[RPT], ks[RPT], qs[RPT];
+        f32x4 ysum[RPT];                    // the finished chunk's Y summed over the slices (fixed order)
+        f32x4 osum = {0.f, 0.f, 0.f, 0.f};  // one piece of its output rows
+        float cmv = 0.f, cwv = 0.f;
+        if (fin) {
+            rows(a.v, tf, nbf, vf);
+            if (tid < TB && tid < nbf) {
+                if (MOM) cmv = a.cM[bh * a.ldc + tf + tid];
+                cwv = a.cW[bh * a.ldc + tf + tid];
+            }
+        }
+        if (sta) {
+            rows(a.k, ts, nbs, ks);
+            rows(a.q, ts, nbs, qs);
+        }
+        if (fin) {
+            wait_head((unsigned)(S * L));  // every slice has published chunk L - 1
+            const float* yp = a.ypart + (size_t)(cf & 1) * parity + (size_t)bh * S * part;
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) {
+                const int i = tid + SNT * u;
+                f32x4 ys[SMAX];
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2)
+                    if (s2 < S && i < TB * n4) ys[s2] = *(const f32x4*)&yp[s2 * part + 4 * i];
+                ysum[u] = ys[0];
+#pragma unroll
+                for (int s2 = 1; s2 < SMAX; ++s2)
+                    if (s2 < S) ysum[u] += ys[s2];
+            }
+            if (tid < nr * n4) {
+                const float* op = a.opart + (size_t)(cf & 1) * parity + (size_t)bh * S * part;
+                f32x4 os[SMAX];
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2)
+                    if (s2 < S) os[s2] = *(const f32x4*)&op[s2 * part + orow * D + 4 * oc4];
+                osum = os[0];
+#pragma unroll
+                for (int s2 = 1; s2 < SMAX; ++s2)
+                    if (s2 < S) osum += os[s2];
+            }
+        }
+
+        // ------------------------------------------------------------ finish chunk L - 1
+        // (Ks, Ab and W2s still hold its K rows, A_s and chunk-start W2_s)
+        if (fin) {
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) {
+                const int i = tid + SNT * u;
+                if (i < TB * n4) *Qs.row4(i / n4, i % n4) = LOSS == E2TTT_LOSS_MSE ? ysum[u] - vf[u] : -vf[u];  // dY
+            }
+            if (tid < TB) {
+                cms[tid] = cmv;
+                cws[tid] = cwv;
+            }
+            if (tid < nr * n4) *(f32x4*)&a.out[(bh * T + tf + orow) * D + 4 * oc4] = osum;
+            __syncthreads();
+            // transition with the chunk-start momentum; the aggregations add G
+            {
+                const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + cf) * 4);
+                if (MOM) {
+                    w1 = sc[0] * w1 - sc[2] * m1;
+                    m1 = sc[1] * m1;
+                    w2 = sc[0] * w2 - sc[2] * m2;
+                    m2 = sc[1] * m2;
+                } else {
+                    w1 = sc[0] * w1;
+                    w2 = sc[0] * w2;
+                }
+            }
+            // dA = dY W2_s on this wave's [16 tokens x 16 units] tile, dZ = dA silu'(Z)
+            // (the short contractions below run on 4 independent accumulators,
+            // k-step kk on accumulator kk % 4, summed in a fixed order)
+            f32x4 dz = {0.f, 0.f, 0.f, 0.f};
+            if (wave < TB / 16) {
+                f32x4 acc[4] = {dz, dz, dz, dz};
+                for (int k4 = 0; k4 < D / 16; ++k4)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kk = 4 * k4 + j;
+                        acc[j] = mfma(Qs.at(16 * wave + jl, 4 * kk + g), W2s.at(4 * kk + g, jl), acc[j]);
+                    }
+                dz = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dz[r] *= sp[r];
+            }
+            // G_W2_s: this wave's W2 tile (d 16 wave .., units): M += (cM dY)^T A, W -= (cW dY)^T A
+            if (st) {
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
+                for (int k4 = 0; k4 < TB / 16; ++k4)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tok = 16 * k4 + 4 * j + g;
+                        const float y = Qs.at(tok, 16 * wave + jl), b = Ab.at(tok, jl);
+                        if (MOM) am[j] = mfma(cms[tok] * y, b, am[j]);
+                        aw[j] = mfma(-cws[tok] * y, b, aw[j]);
+                    }
+                if (MOM) m2 += (am[0] + am[1]) + (am[2] + am[3]);
+                w2 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
+            }
+            __syncthreads();  // A is read
+            if (wave < TB / 16) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ab.at(16 * wave + 4 * g + r, jl) = dz[r];
+            }
+            __syncthreads();
+            // G_W1_s: this wave's W1 tile (units, d 16 wave ..): M += (cM dZ)^T K, W -= (cW dZ)^T K
+            if (st) {
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
+                for (int k4 = 0; k4 < TB / 16; ++k4)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tok = 16 * k4 + 4 * j + g;
+                        const float x = Ab.at(tok, jl), b = Ks.at(tok, 16 * wave + jl);
+                        if (MOM) am[j] = mfma(cms[tok] * x, b, am[j]);
+                        aw[j] = mfma(-cws[tok] * x, b, aw[j]);
+                    }
+                if (MOM) m1 += (am[0] + am[1]) + (am[2] + am[3]);
+                w1 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
+            }
+            __syncthreads();  // LDS is reused below
+        }
+        if (!sta) break;
+
+        // ------------------------------------------------------------ start chunk L
+        if (a.save && st) {  // chunk-start state for the backward pass
+            float* sv = a.save + (bh * a.nc + cs) * 2 * P;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sv[i1(r)] = w1[r];
+                sv[i2(r)] = w2[r];
+                sv[P + i1(r)] = MOM ? m1[r] : 0.f;
+                sv[P + i2(r)] = MOM ? m2[r] : 0.f;
+            }
+        }
+        if (st) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                W1s.at(4 * g + r, 16 * wave + jl) = w1[r];
+                W2s.at(16 * wave + 4 * g + r, jl) = w2[r];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int i = tid + SNT * u;
+            if (i < TB * n4) {
+                *Ks.row4(i / n4, i % n4) = ks[u];
+                *Qs.row4(i / n4, i % n4) = qs[u];
+            }
+        }
+        __syncthreads();
+        // Z_s = K W1_s^T and Zq_s = Q W1_s^T on this wave's [16 tokens x 16 units] tile
+        if (wave < TB / 16) {
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 za[4] = {z4, z4, z4, z4}, qa[4] = {z4, z4, z4, z4};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m < D / 16) {
+                    const f32x4 kv = *Ks.row4(16 * wave + jl, 4 * m + g), qv = *Qs.row4(16 * wave + jl, 4 * m + g);
+                    const f32x4 wv = *W1s.row4(jl, 4 * m + g);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        za[j] = mfma(kv[j], wv[j], za[j]);
+                        qa[j] = mfma(qv[j], wv[j], qa[j]);
+                    }
+                }
+            }
+            const f32x4 z = (za[0] + za[1]) + (za[2] + za[3]), zq = (qa[0] + qa[1]) + (qa[2] + qa[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * wave + 4 * g + r;
+                const float s1 = sigm(z[r]), s2 = sigm(zq[r]);
+                Ab.at(row, jl) = z[r] * s1;
+                Aq.at(row, jl) = zq[r] * s2;
+                sp[r] = s1 * (1.f + z[r] * (1.f - s1));
+            }
+        }
+        __syncthreads();
+        // partial Y_s = A_s W2_s^T and partial output = Aq_s W2_s^T, [TB x D] tiles over the waves
+        {
+            float* yp = a.ypart + (size_t)(cs & 1) * parity + (size_t)slot * part;
+            float* op = a.opart + (size_t)(cs & 1) * parity + (size_t)slot * part;
+            const int nt = (TB / 16) * nd;
+            for (int t = wave; t < nt; t += SNW) {
+                const int ti = t / nd, tj = t % nd;
+                f32x4 y = {0.f, 0.f, 0.f, 0.f}, o = y;
+                const f32x4 av = *Ab.row4(16 * ti + jl, g), qv = *Aq.row4(16 * ti + jl, g);
+                const f32x4 wv = *W2s.row4(16 * tj + jl, g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    y = mfma(av[j], wv[j], y);
+                    o = mfma(qv[j], wv[j], o);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + 4 * g + r, col = 16 * tj + jl;
+                    yp[row * D + col] = y[r];
+                    op[row * D + col] = o[r];
+                }
+            }
+        }
+        publish();
+    }
+    if (gave_up) {  // the synchronisation was abandoned: mark the result invalid
+        w1 = w2 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    if (st) {
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int jl = lane_e & 15, g = lane_e >> 4;
+        auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
+        auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
+        float* W = a.W + bh * P;
+        float* M = a.M + bh * P;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             W[i1(r)] = w1[r];
@@ -550,251 +844,6 @@ f32_split_kernel(SplitArgs a) {
             if (MOM) {
                 M[i1(r)] = m1[r];
                 M[i2(r)] = m2[r];
-            }
-        }
-    };
-    const int64_t slot = bh * S + sl;
-    const size_t part = (size_t)TB * D;                // floats of one slice's partial
-    const size_t parity = (size_t)(gridDim.x) * part;  // all slices' partials of one chunk parity
-    const bool fin = a.L >= 1, sta = a.L < a.nc;
-    const int cf = a.L - 1, cs = a.L;  // the chunk finished, the chunk started
-    const int64_t tf = (int64_t)cf * a.C, ts = (int64_t)cs * a.C;
-    const int nbf = fin ? (int)min((int64_t)a.C, T - tf) : 0, nbs = sta ? (int)min((int64_t)a.C, T - ts) : 0;
-    const int n4 = D / 4;
-
-    // ------------------------------------------------------------ every global load of the launch, issued up front
-    if (a.L >= 1) load_state(a.W, a.M);
-    else load_state(a.W0, a.M0);
-    auto rows = [&](const float* x, int64_t t, int nb, f32x4 (&v4)[RPT]) {
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int i = tid + SNT * u, r = i / n4;
-            v4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (i < TB * n4 && r < nb) v4[u] = *(const f32x4*)&x[(bh * T + t + r) * D + 4 * (i % n4)];
-        }
-    };
-    f32x4 kf[RPT], vf[RPT], ks[RPT], qs[RPT];
-    f32x4 ysum[RPT];       // the finished chunk's Y summed over the slices (fixed order)
-    f32x4 osum = {0.f, 0.f, 0.f, 0.f};  // one piece of its output rows
-    f32x4 actA = {0.f, 0.f, 0.f, 0.f};
-    float sp[4] = {0.f, 0.f, 0.f, 0.f};  // silu'(Z) at this wave's dZ tile (rows 16 wave + 4g + r, unit jl)
-    float cmv = 0.f, cwv = 0.f;
-    const int nr = fin ? (nbf - sl + S - 1) / S : 0;  // output rows r = sl, sl + S, ... of the finished chunk
-    const int orow = sl + S * (tid / n4), oc4 = tid % n4;
-    if (fin) {
-        rows(a.k, tf, nbf, kf);
-        rows(a.v, tf, nbf, vf);
-        if (tid < TB && tid < nbf) {
-            if (MOM) cmv = a.cM[bh * a.ldc + tf + tid];
-            cwv = a.cW[bh * a.ldc + tf + tid];
-        }
-        const float* act = a.act + slot * 2 * TB * HS;
-        if (tid < TB * HS / 4) actA = *(const f32x4*)&act[4 * tid];
-        if (wave < TB / 16) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sp[r] = act[TB * HS + (16 * wave + 4 * g + r) * HS + jl];
-        }
-        const float* yp = a.ypart + (size_t)(cf & 1) * parity + (size_t)bh * S * part;
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int i = tid + SNT * u;
-            f32x4 ys[SMAX];
-#pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2)
-                if (s2 < S && i < TB * n4) ys[s2] = *(const f32x4*)&yp[s2 * part + 4 * i];
-            ysum[u] = ys[0];
-#pragma unroll
-            for (int s2 = 1; s2 < SMAX; ++s2)
-                if (s2 < S) ysum[u] += ys[s2];
-        }
-        if (tid < nr * n4) {
-            const float* op = a.opart + (size_t)(cf & 1) * parity + (size_t)bh * S * part;
-            f32x4 os[SMAX];
-#pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2)
-                if (s2 < S) os[s2] = *(const f32x4*)&op[s2 * part + orow * D + 4 * oc4];
-            osum = os[0];
-#pragma unroll
-            for (int s2 = 1; s2 < SMAX; ++s2)
-                if (s2 < S) osum += os[s2];
-        }
-    }
-    if (sta) {
-        rows(a.k, ts, nbs, ks);
-        rows(a.q, ts, nbs, qs);
-    }
-
-    // ------------------------------------------------------------ finish chunk L - 1
-    if (fin) {
-        // chunk-start W2_s (the operand of dY W2) before the transition
-        if (st) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) W2s.at(16 * wave + 4 * g + r, jl) = w2[r];
-        }
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int i = tid + SNT * u;
-            if (i < TB * n4) {
-                *Ks.row4(i / n4, i % n4) = kf[u];
-                *Qs.row4(i / n4, i % n4) = LOSS == E2TTT_LOSS_MSE ? ysum[u] - vf[u] : -vf[u];  // dY
-            }
-        }
-        if (tid < TB) {
-            cms[tid] = cmv;
-            cws[tid] = cwv;
-        }
-        if (tid < TB * HS / 4) *Ab.row4(tid / (HS / 4), tid % (HS / 4)) = actA;
-        if (tid < nr * n4) *(f32x4*)&a.out[(bh * T + tf + orow) * D + 4 * oc4] = osum;
-        __syncthreads();
-        // transition with the chunk-start momentum; the aggregations add G
-        {
-            const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + cf) * 4);
-            if (MOM) {
-                w1 = sc[0] * w1 - sc[2] * m1;
-                m1 = sc[1] * m1;
-                w2 = sc[0] * w2 - sc[2] * m2;
-                m2 = sc[1] * m2;
-            } else {
-                w1 = sc[0] * w1;
-                w2 = sc[0] * w2;
-            }
-        }
-        // dA = dY W2_s on this wave's [16 tokens x 16 units] tile, dZ = dA silu'(Z)
-        // (the short contractions below run on 4 independent accumulators,
-        // k-step kk on accumulator kk % 4, summed in a fixed order)
-        f32x4 dz = {0.f, 0.f, 0.f, 0.f};
-        if (wave < TB / 16) {
-            f32x4 acc[4] = {dz, dz, dz, dz};
-            for (int k4 = 0; k4 < D / 16; ++k4)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kk = 4 * k4 + j;
-                    acc[j] = mfma(Qs.at(16 * wave + jl, 4 * kk + g), W2s.at(4 * kk + g, jl), acc[j]);
-                }
-            dz = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dz[r] *= sp[r];
-        }
-        // G_W2_s: this wave's W2 tile (d 16 wave .., units): M += (cM dY)^T A, W -= (cW dY)^T A
-        if (st) {
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
-            for (int k4 = 0; k4 < TB / 16; ++k4)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tok = 16 * k4 + 4 * j + g;
-                    const float y = Qs.at(tok, 16 * wave + jl), b = Ab.at(tok, jl);
-                    if (MOM) am[j] = mfma(cms[tok] * y, b, am[j]);
-                    aw[j] = mfma(-cws[tok] * y, b, aw[j]);
-                }
-            if (MOM) m2 += (am[0] + am[1]) + (am[2] + am[3]);
-            w2 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
-        }
-        __syncthreads();  // A is read
-        if (wave < TB / 16) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ab.at(16 * wave + 4 * g + r, jl) = dz[r];
-        }
-        __syncthreads();
-        // G_W1_s: this wave's W1 tile (units, d 16 wave ..): M += (cM dZ)^T K, W -= (cW dZ)^T K
-        if (st) {
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
-            for (int k4 = 0; k4 < TB / 16; ++k4)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tok = 16 * k4 + 4 * j + g;
-                    const float x = Ab.at(tok, jl), b = Ks.at(tok, 16 * wave + jl);
-                    if (MOM) am[j] = mfma(cms[tok] * x, b, am[j]);
-                    aw[j] = mfma(-cws[tok] * x, b, aw[j]);
-                }
-            if (MOM) m1 += (am[0] + am[1]) + (am[2] + am[3]);
-            w1 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
-        }
-        store_state(a.W + bh * P, MOM ? a.M + bh * P : nullptr);
-        __syncthreads();  // LDS is reused below
-    } else {
-        store_state(a.W + bh * P, MOM ? a.M + bh * P : nullptr);  // the working state starts as W0, M0
-    }
-    if (!sta) return;
-
-    // ------------------------------------------------------------ start chunk L
-    if (a.save && st) {  // chunk-start state for the backward pass
-        float* sv = a.save + (bh * a.nc + cs) * 2 * P;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            sv[i1(r)] = w1[r];
-            sv[i2(r)] = w2[r];
-            sv[P + i1(r)] = MOM ? m1[r] : 0.f;
-            sv[P + i2(r)] = MOM ? m2[r] : 0.f;
-        }
-    }
-    if (st) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            W1s.at(4 * g + r, 16 * wave + jl) = w1[r];
-            W2s.at(16 * wave + 4 * g + r, jl) = w2[r];
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        const int i = tid + SNT * u;
-        if (i < TB * n4) {
-            *Ks.row4(i / n4, i % n4) = ks[u];
-            *Qs.row4(i / n4, i % n4) = qs[u];
-        }
-    }
-    __syncthreads();
-    // Z_s = K W1_s^T and Zq_s = Q W1_s^T on this wave's [16 tokens x 16 units] tile
-    if (wave < TB / 16) {
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 za[4] = {z4, z4, z4, z4}, qa[4] = {z4, z4, z4, z4};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m < D / 16) {
-                const f32x4 kv = *Ks.row4(16 * wave + jl, 4 * m + g), qv = *Qs.row4(16 * wave + jl, 4 * m + g);
-                const f32x4 wv = *W1s.row4(jl, 4 * m + g);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    za[j] = mfma(kv[j], wv[j], za[j]);
-                    qa[j] = mfma(qv[j], wv[j], qa[j]);
-                }
-            }
-        }
-        const f32x4 z = (za[0] + za[1]) + (za[2] + za[3]), zq = (qa[0] + qa[1]) + (qa[2] + qa[3]);
-        float* act = a.act + slot * 2 * TB * HS;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * wave + 4 * g + r;
-            const float s1 = sigm(z[r]), s2 = sigm(zq[r]);
-            const float av = z[r] * s1;
-            Ab.at(row, jl) = av;
-            Aq.at(row, jl) = zq[r] * s2;
-            act[row * HS + jl] = av;
-            act[TB * HS + row * HS + jl] = s1 * (1.f + z[r] * (1.f - s1));
-        }
-    }
-    __syncthreads();
-    // partial Y_s = A_s W2_s^T and partial output = Aq_s W2_s^T, [TB x D] tiles over the waves
-    {
-        float* yp = a.ypart + (size_t)(cs & 1) * parity + (size_t)slot * part;
-        float* op = a.opart + (size_t)(cs & 1) * parity + (size_t)slot * part;
-        const int nt = (TB / 16) * nd;
-        for (int t = wave; t < nt; t += SNW) {
-            const int ti = t / nd, tj = t % nd;
-            f32x4 y = {0.f, 0.f, 0.f, 0.f}, o = y;
-            const f32x4 av = *Ab.row4(16 * ti + jl, g), qv = *Aq.row4(16 * ti + jl, g);
-            const f32x4 wv = *W2s.row4(16 * tj + jl, g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                y = mfma(av[j], wv[j], y);
-                o = mfma(qv[j], wv[j], o);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ti + 4 * g + r, col = 16 * tj + jl;
-                yp[row * D + col] = y[r];
-                op[row * D + col] = o[r];
             }
         }
     }
@@ -860,7 +909,8 @@ bool f32_split(const e2ttt_desc& d) {
 size_t f32_split_bytes(const e2ttt_desc& d) {
     if (!f32_split(d)) return 0;
     const size_t BH = (size_t)(d.B * d.H), S = (size_t)(d.Hd / HS), TB = (size_t)f32_block(d);
-    return 4 * (2 * BH * S * TB * d.D * 2 + BH * S * 2 * TB * HS);
+    // partial Y and outputs (two parities), the heads' arrival counters and the flag
+    return (4 * (2 * BH * S * TB * d.D * 2 + BH + 1) + 255) / 256 * 256;
 }
 
 namespace {
@@ -875,20 +925,26 @@ hipError_t launch_split(const e2ttt_desc& d, SplitArgs a, hipStream_t s) {
     const void* f = (const void*)f32_split_kernel<LOSS, MOM>;
     if (shmem > 64 * 1024 && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
         return hipErrorInvalidValue;
-    for (int L = 0; L <= a.nc; ++L) {  // launch L finishes chunk L - 1 and starts chunk L
-        a.L = L;
-        hipLaunchKernelGGL((f32_split_kernel<LOSS, MOM>), dim3((unsigned)a.nwg), dim3(SNT), shmem, s, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const int nsync = a.nwg / a.S + 1;
+    hipLaunchKernelGGL(split_sync_init, dim3(1), dim3(256), 0, s, a.sync, nsync);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((f32_split_kernel<LOSS, MOM>), dim3((unsigned)a.nwg), dim3(SNT), shmem, s, a);
+    return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v, const float* cM,
                            const float* cW, int64_t ldc, const float* scal, const float* W0, const float* M0, void* out,
                            float* W_end, float* M_end, hipStream_t s, float* save, void* split_ws) {
+    // the hidden-slice split needs all its workgroups resident at once (one per
+    // compute unit); on a device with fewer compute units the heads run whole
+    int ncu = 0;
     if (f32_split(d)) {
+        const hipError_t e = device_cu_count(&ncu);
+        if (e != hipSuccess) return e;
+    }
+    if (f32_split(d) && d.B * d.H * (d.Hd / HS) <= ncu) {
         SplitArgs a;
         a.q = (const float*)q;
         a.k = (const float*)k;
@@ -916,7 +972,7 @@ hipError_t launch_f32_mfma(const e2ttt_desc& d, const void* q, const void* k, co
         const size_t part = (size_t)a.nwg * a.TB * a.D;
         a.ypart = (float*)split_ws;
         a.opart = a.ypart + 2 * part;
-        a.act = a.opart + 2 * part;
+        a.sync = (unsigned*)(a.opart + 2 * part);
         const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
         if (d.loss == E2TTT_LOSS_MSE)
             return mom ? launch_split<E2TTT_LOSS_MSE, true>(d, a, s) : launch_split<E2TTT_LOSS_MSE, false>(d, a, s);

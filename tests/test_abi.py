@@ -198,10 +198,10 @@ def test_fp32_mfma_path_shapes(lib):
     assert p(kind="mlp", loss="mse", io="bf16", D=64, Hd=128) == 0        # bf16 I/O
     assert p(kind="mlp", loss="mse", io="f32", D=64, Hd=128, flags=1) == 0
     # the scalar kernels' outputs, and for few heads the hidden-slice split's
-    # partial sums: partial Y and partial outputs [2][BH][S][64][D] and the
-    # slices' silu(Z), silu'(Z) [BH][S][2][64][16] (S = Hd / 16)
+    # partial sums: partial Y and partial outputs [2][BH][S][64][D] (S = Hd / 16),
+    # then one arrival counter per head and a time-out flag
     d = _desc(kind="mlp", loss="mse", io="f32", B=2, H=4, T=2048, D=64, Hd=128, chunk=64)
-    split = 4 * (2 * 8 * 8 * 64 * 64 * 2 + 8 * 8 * 2 * 64 * 16)
+    split = (4 * (2 * 8 * 8 * 64 * 64 * 2 + 8 + 1) + 255) // 256 * 256  # partial sums, 8 head counters, a flag
     assert lib.e2ttt_workspace_size(ctypes.byref(d)) == 2 * 8 * 2048 * 4 + 8 * 32 * 16 + split
     # many heads fill the chip with one workgroup each: no split
     d = _desc(kind="mlp", loss="mse", io="f32", B=8, H=16, T=2048, D=64, Hd=128, chunk=64)
