@@ -107,20 +107,21 @@ def test_backward_precise_multichunk(Hd):
     _compare(cfg, _gpu(cfg, x, c, precise=True), _oracle(cfg, x, c))
 
 
-def test_backward_full_size_sampled_heads():
-    """The 1.3B-shaped workload (B=8, H=16, T=2048, chunk 256) in one call;
-    two (b, h) pairs checked against the oracle."""
+def test_backward_full_size_every_head():
+    """The 1.3B-shaped workload (B=8, H=16, T=2048, chunk 256) in one call,
+    every (b, h) pair checked against the oracle, 16 heads at a time."""
     cfg = synth.CONFIGS["swiglu_1p3b"]
     note(f"case {cfg.name} backward")
     x = synth.make_inputs(cfg, seed=0, m0_scale=0.5)
     c = synth.make_cotangents(cfg, seed=1)
     got = _gpu(cfg, x, c)
-    heads = [(0, 0), (5, 11)]
-    xs = synth.head_slice(x, heads)
-    cs = synth.head_slice(c, heads)
-    ref = _oracle(cfg.with_(B=1, H=len(heads)), xs, cs)
-    sub = {n: (None if t is None else np.stack([t[b, h] for b, h in heads])[None]) for n, t in got.items()}
-    _compare(cfg.with_(B=1, H=len(heads)), sub, ref)
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    for i in range(0, len(pairs), 16):
+        heads = pairs[i:i + 16]
+        sub_cfg = cfg.with_(B=1, H=len(heads))
+        ref = _oracle(sub_cfg, synth.head_slice(x, heads), synth.head_slice(c, heads))
+        sub = {n: (None if t is None else np.stack([t[b, h] for b, h in heads])[None]) for n, t in got.items()}
+        _compare(sub_cfg, sub, ref)
 
 
 def test_backward_deterministic():
