@@ -35,7 +35,11 @@
  *   - The library keeps no mutable global state other than the scratch of
  *     e2ttt_chunk_forward_noalloc; calls on different streams may run
  *     concurrently as long as they do not share output or workspace buffers
- *     (or, for e2ttt_chunk_forward_noalloc, the GPU).
+ *     (or, for e2ttt_chunk_forward_noalloc, the GPU).  Path 4 (see
+ *     e2ttt_path) needs all its workgroups resident at once: concurrent
+ *     path-4 calls whose grids together exceed the device's compute units
+ *     can hold part of each other's grid; their waits then end after 10 s
+ *     and the affected final states are NaN.
  */
 #ifndef E2TTT_H
 #define E2TTT_H
