@@ -475,11 +475,14 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
 // The counters and the flag are zeroed by a one-workgroup kernel before the
 // loop on the same stream.
 // ---------------------------------------------------------------------------
-constexpr int SNW = 4;         // wavefronts per split workgroup
+constexpr int SNW = 8;         // wavefronts per split workgroup: two groups of 4
 constexpr int SNT = 64 * SNW;
 constexpr int HS = 16;         // hidden units per split workgroup
 constexpr int SMAX = 16;       // slices per head (Hd <= 256)
-constexpr int RPT = 4;         // 16-byte pieces of a [TB][D] block per thread (TB * D <= 4096)
+constexpr int RPT = 2;         // 16-byte pieces of a [TB][D] block per thread (TB * D <= 4096)
+// A slice writes output rows sl, sl + S, ...: with S >= 2 at most TB / 2 rows
+// of D / 4 pieces, one piece per thread.
+static_assert(SNT >= (64 / 2) * (64 / 4), "output rows of a slice: one 16-byte piece per thread");
 constexpr uint64_t kSpinTicks = 1000000000ull;  // 10 s of the 100 MHz wall clock
 
 struct SplitArgs {
@@ -508,7 +511,7 @@ __global__ void split_sync_init(unsigned* sync, int n) {
 }
 
 template <int LOSS, bool MOM>
-__global__ void __attribute__((amdgpu_flat_work_group_size(SNT, SNT), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(SNT, SNT), amdgpu_waves_per_eu(2, 2)))
 f32_split_kernel(SplitArgs a) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     __shared__ unsigned gave_up;
@@ -545,20 +548,26 @@ f32_split_kernel(SplitArgs a) {
     float* cms = p;
     float* cws = p + TB;
 
-    // state tiles of this wave (w < nd): W1_s tile (units, d 16w..) and W2_s tile (d 16w.., units)
-    const bool st = wave < nd;
-    f32x4 w1 = {0.f, 0.f, 0.f, 0.f}, m1 = w1, w2 = w1, m2 = w1;
-    auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
-    auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
+    // Two groups of four wavefronts, wl = wave % 4 within the group:
+    //   group 0 holds the W1_s tile (units, d 16 wl ..) and its momentum, and
+    //     computes token tile wl's dA / dZ, its G_W1 tile, Z and partial Y;
+    //   group 1 holds the W2_s tile (d 16 wl .., units) and its momentum, and
+    //     computes its G_W2 tile, token tile wl's Zq and partial output.
+    // So the W2 aggregation overlaps dA, and Z overlaps Zq.
+    const int grp = wave >> 2, wl = wave & 3;
+    const bool st = wl < nd;
+    const bool tt = wl < TB / 16;  // owns token tile wl
+    f32x4 w = {0.f, 0.f, 0.f, 0.f}, m = w;
+    // packed index of element r of this wave's state tile
+    auto ix = [&](int r, int jl_, int g_) {
+        return grp == 0 ? (int64_t)(HS * sl + 4 * g_ + r) * D + 16 * wl + jl_
+                        : off1 + (int64_t)(16 * wl + 4 * g_ + r) * Hd + HS * sl + jl_;
+    };
     if (st) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            w1[r] = a.W0[bh * P + i1(r)];
-            w2[r] = a.W0[bh * P + i2(r)];
-            if (MOM) {
-                m1[r] = a.M0[bh * P + i1(r)];
-                m2[r] = a.M0[bh * P + i2(r)];
-            }
+            w[r] = a.W0[bh * P + ix(r, jl, g)];
+            if (MOM) m[r] = a.M0[bh * P + ix(r, jl, g)];
         }
     }
     if (tid == 0) gave_up = 0u;
@@ -566,7 +575,7 @@ f32_split_kernel(SplitArgs a) {
     const size_t part = (size_t)TB * D;                // floats of one slice's partial
     const size_t parity = (size_t)(gridDim.x) * part;  // all slices' partials of one chunk parity
     const int n4 = D / 4;
-    float sp[4] = {0.f, 0.f, 0.f, 0.f};  // silu'(Z) of the chunk last started at this wave's dZ tile (rows 16 wave + 4g + r, unit jl)
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};  // group 0: silu'(Z) of the chunk last started at token tile wl (rows 16 wl + 4g + r, unit jl)
 
     // until all S slices of the head have arrived `target` times in total.
     // The cache maintenance of a device-scope acquire (invalidation) and
@@ -603,8 +612,6 @@ f32_split_kernel(SplitArgs a) {
         int tid_s = threadIdx.x;
         asm volatile("" : "+v"(tid_s));
         const int tid = tid_s, lane = tid & 63, jl = lane & 15, g = lane >> 4;
-        auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
-        auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
         auto rows = [&](const float* x, int64_t t, int nb, f32x4 (&v4)[RPT]) {
 #pragma unroll
             for (int u = 0; u < RPT; ++u) {
@@ -682,66 +689,57 @@ f32_split_kernel(SplitArgs a) {
             {
                 const f32x4 sc = *(const f32x4*)(a.scal + (bh * a.nc + cf) * 4);
                 if (MOM) {
-                    w1 = sc[0] * w1 - sc[2] * m1;
-                    m1 = sc[1] * m1;
-                    w2 = sc[0] * w2 - sc[2] * m2;
-                    m2 = sc[1] * m2;
+                    w = sc[0] * w - sc[2] * m;
+                    m = sc[1] * m;
                 } else {
-                    w1 = sc[0] * w1;
-                    w2 = sc[0] * w2;
+                    w = sc[0] * w;
                 }
             }
-            // dA = dY W2_s on this wave's [16 tokens x 16 units] tile, dZ = dA silu'(Z)
             // (the short contractions below run on 4 independent accumulators,
             // k-step kk on accumulator kk % 4, summed in a fixed order)
-            f32x4 dz = {0.f, 0.f, 0.f, 0.f};
-            if (wave < TB / 16) {
-                f32x4 acc[4] = {dz, dz, dz, dz};
-                for (int k4 = 0; k4 < D / 16; ++k4)
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            if (grp == 0) {
+                // dA = dY W2_s on token tile wl, dZ = dA silu'(Z), parked in Aq
+                if (tt) {
+                    f32x4 acc[4] = {z4, z4, z4, z4};
+                    for (int k4 = 0; k4 < D / 16; ++k4)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int kk = 4 * k4 + j;
-                        acc[j] = mfma(Qs.at(16 * wave + jl, 4 * kk + g), W2s.at(4 * kk + g, jl), acc[j]);
-                    }
-                dz = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                        for (int j = 0; j < 4; ++j) {
+                            const int kk = 4 * k4 + j;
+                            acc[j] = mfma(Qs.at(16 * wl + jl, 4 * kk + g), W2s.at(4 * kk + g, jl), acc[j]);
+                        }
+                    const f32x4 dz = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dz[r] *= sp[r];
-            }
-            // G_W2_s: this wave's W2 tile (d 16 wave .., units): M += (cM dY)^T A, W -= (cW dY)^T A
-            if (st) {
-                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < 4; ++r) Aq.at(16 * wl + 4 * g + r, jl) = dz[r] * sp[r];
+                }
+            } else if (st) {
+                // G_W2_s tile (d 16 wl .., units): M += (cM dY)^T A, W -= (cW dY)^T A
                 f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
                 for (int k4 = 0; k4 < TB / 16; ++k4)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tok = 16 * k4 + 4 * j + g;
-                        const float y = Qs.at(tok, 16 * wave + jl), b = Ab.at(tok, jl);
+                        const float y = Qs.at(tok, 16 * wl + jl), b = Ab.at(tok, jl);
                         if (MOM) am[j] = mfma(cms[tok] * y, b, am[j]);
                         aw[j] = mfma(-cws[tok] * y, b, aw[j]);
                     }
-                if (MOM) m2 += (am[0] + am[1]) + (am[2] + am[3]);
-                w2 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
+                if (MOM) m += (am[0] + am[1]) + (am[2] + am[3]);
+                w += (aw[0] + aw[1]) + (aw[2] + aw[3]);
             }
-            __syncthreads();  // A is read
-            if (wave < TB / 16) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Ab.at(16 * wave + 4 * g + r, jl) = dz[r];
-            }
-            __syncthreads();
-            // G_W1_s: this wave's W1 tile (units, d 16 wave ..): M += (cM dZ)^T K, W -= (cW dZ)^T K
-            if (st) {
-                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            __syncthreads();  // dZ is in Aq
+            if (grp == 0 && st) {
+                // G_W1_s tile (units, d 16 wl ..): M += (cM dZ)^T K, W -= (cW dZ)^T K
                 f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
                 for (int k4 = 0; k4 < TB / 16; ++k4)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tok = 16 * k4 + 4 * j + g;
-                        const float x = Ab.at(tok, jl), b = Ks.at(tok, 16 * wave + jl);
+                        const float x = Aq.at(tok, jl), b = Ks.at(tok, 16 * wl + jl);
                         if (MOM) am[j] = mfma(cms[tok] * x, b, am[j]);
                         aw[j] = mfma(-cws[tok] * x, b, aw[j]);
                     }
-                if (MOM) m1 += (am[0] + am[1]) + (am[2] + am[3]);
-                w1 += (aw[0] + aw[1]) + (aw[2] + aw[3]);
+                if (MOM) m += (am[0] + am[1]) + (am[2] + am[3]);
+                w += (aw[0] + aw[1]) + (aw[2] + aw[3]);
             }
             __syncthreads();  // LDS is reused below
         }
@@ -752,17 +750,17 @@ f32_split_kernel(SplitArgs a) {
             float* sv = a.save + (bh * a.nc + cs) * 2 * P;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sv[i1(r)] = w1[r];
-                sv[i2(r)] = w2[r];
-                sv[P + i1(r)] = MOM ? m1[r] : 0.f;
-                sv[P + i2(r)] = MOM ? m2[r] : 0.f;
+                sv[ix(r, jl, g)] = w[r];
+                sv[P + ix(r, jl, g)] = MOM ? m[r] : 0.f;
             }
         }
         if (st) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                W1s.at(4 * g + r, 16 * wave + jl) = w1[r];
-                W2s.at(16 * wave + 4 * g + r, jl) = w2[r];
+                if (grp == 0)
+                    W1s.at(4 * g + r, 16 * wl + jl) = w[r];
+                else
+                    W2s.at(16 * wl + 4 * g + r, jl) = w[r];
             }
         }
 #pragma unroll
@@ -774,77 +772,57 @@ f32_split_kernel(SplitArgs a) {
             }
         }
         __syncthreads();
-        // Z_s = K W1_s^T and Zq_s = Q W1_s^T on this wave's [16 tokens x 16 units] tile
-        if (wave < TB / 16) {
+        // group 0: Z_s = K W1_s^T on token tile wl, A_s = silu(Z_s) into Ab,
+        // then the partial Y_s = A_s W2_s^T of those rows; group 1 the same
+        // with Q: Zq, silu(Zq) into Aq, the partial output.  Each wavefront
+        // reads back only the rows it wrote.
+        if (tt) {
+            const Lm& X = grp == 0 ? Ks : Qs;
+            const Lm& Act = grp == 0 ? Ab : Aq;
             const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 za[4] = {z4, z4, z4, z4}, qa[4] = {z4, z4, z4, z4};
+            f32x4 za[4] = {z4, z4, z4, z4};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (m < D / 16) {
-                    const f32x4 kv = *Ks.row4(16 * wave + jl, 4 * m + g), qv = *Qs.row4(16 * wave + jl, 4 * m + g);
-                    const f32x4 wv = *W1s.row4(jl, 4 * m + g);
+            for (int mm = 0; mm < 4; ++mm) {
+                if (mm < D / 16) {
+                    const f32x4 xv = *X.row4(16 * wl + jl, 4 * mm + g);
+                    const f32x4 wv = *W1s.row4(jl, 4 * mm + g);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        za[j] = mfma(kv[j], wv[j], za[j]);
-                        qa[j] = mfma(qv[j], wv[j], qa[j]);
-                    }
+                    for (int j = 0; j < 4; ++j) za[j] = mfma(xv[j], wv[j], za[j]);
                 }
             }
-            const f32x4 z = (za[0] + za[1]) + (za[2] + za[3]), zq = (qa[0] + qa[1]) + (qa[2] + qa[3]);
+            const f32x4 z = (za[0] + za[1]) + (za[2] + za[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * wave + 4 * g + r;
-                const float s1 = sigm(z[r]), s2 = sigm(zq[r]);
-                Ab.at(row, jl) = z[r] * s1;
-                Aq.at(row, jl) = zq[r] * s2;
-                sp[r] = s1 * (1.f + z[r] * (1.f - s1));
+                const int row = 16 * wl + 4 * g + r;
+                const float s1 = sigm(z[r]);
+                Act.at(row, jl) = z[r] * s1;
+                if (grp == 0) sp[r] = s1 * (1.f + z[r] * (1.f - s1));
             }
-        }
-        __syncthreads();
-        // partial Y_s = A_s W2_s^T and partial output = Aq_s W2_s^T, [TB x D] tiles over the waves
-        {
-            float* yp = a.ypart + (size_t)(cs & 1) * parity + (size_t)slot * part;
-            float* op = a.opart + (size_t)(cs & 1) * parity + (size_t)slot * part;
-            const int nt = (TB / 16) * nd;
-            for (int t = wave; t < nt; t += SNW) {
-                const int ti = t / nd, tj = t % nd;
-                f32x4 y = {0.f, 0.f, 0.f, 0.f}, o = y;
-                const f32x4 av = *Ab.row4(16 * ti + jl, g), qv = *Aq.row4(16 * ti + jl, g);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's rows are written
+            asm volatile("" ::: "memory");
+            float* dst = (grp == 0 ? a.ypart : a.opart) + (size_t)(cs & 1) * parity + (size_t)slot * part;
+            const f32x4 av = *Act.row4(16 * wl + jl, g);
+            for (int tj = 0; tj < nd; ++tj) {
                 const f32x4 wv = *W2s.row4(16 * tj + jl, g);
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    y = mfma(av[j], wv[j], y);
-                    o = mfma(qv[j], wv[j], o);
-                }
+                for (int j = 0; j < 4; ++j) y = mfma(av[j], wv[j], y);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * ti + 4 * g + r, col = 16 * tj + jl;
-                    yp[row * D + col] = y[r];
-                    op[row * D + col] = o[r];
-                }
+                for (int r = 0; r < 4; ++r) dst[(16 * wl + 4 * g + r) * D + 16 * tj + jl] = y[r];
             }
         }
         publish();
     }
-    if (gave_up) {  // the synchronisation was abandoned: mark the result invalid
-        w1 = w2 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    }
+    if (gave_up)  // the synchronisation was abandoned: mark the result invalid
+        w = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     if (st) {
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
-        const int jl = lane_e & 15, g = lane_e >> 4;
-        auto i1 = [&](int r) { return (int64_t)(HS * sl + 4 * g + r) * D + 16 * wave + jl; };
-        auto i2 = [&](int r) { return off1 + (int64_t)(16 * wave + 4 * g + r) * Hd + HS * sl + jl; };
-        float* W = a.W + bh * P;
-        float* M = a.M + bh * P;
+        const int jl_e = lane_e & 15, g_e = lane_e >> 4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            W[i1(r)] = w1[r];
-            W[i2(r)] = w2[r];
-            if (MOM) {
-                M[i1(r)] = m1[r];
-                M[i2(r)] = m2[r];
-            }
+            a.W[bh * P + ix(r, jl_e, g_e)] = w[r];
+            if (MOM) a.M[bh * P + ix(r, jl_e, g_e)] = m[r];
         }
     }
 }

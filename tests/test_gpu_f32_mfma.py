@@ -24,6 +24,8 @@ CASES = [
     ("mlp", "negdot", 1, 2, 400, 16, 48, 130),   # three blocks per chunk (64 + 64 + 2)
     ("mlp", "mse", 1, 2, 256, 48, 80, 64),       # 5 column tiles: every tile reads its own B operand
     ("mlp", "negdot", 1, 1, 64, 64, 128, 16),
+    ("mlp", "mse", 1, 2, 192, 64, 48, 64),       # 3 hidden slices: each writes 22 of the 64 output rows
+    ("mlp", "negdot", 2, 1, 130, 64, 32, 64),    # 2 hidden slices (32 output rows each), a 2-token last chunk
 ]
 
 
