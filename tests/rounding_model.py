@@ -9,9 +9,11 @@ fp32; at these sizes that is far below the bf16 roundings):
 * grad operands: the chunk-start weights W1, W3, W2 as bf16 (precise form:
   a hi/lo pair, hi = bf16(w), lo = bf16(w - hi));
 * the three per-token factors handed to the aggregation, a = hv h3 silu'(h1),
-  b = hv silu(h1), u = silu(h1) h3 (hv = V W2^T), as bf16 (precise: hi/lo);
+  b = hv silu(h1), u = silu(h1) h3 (hv = V W2^T): in fp32, as the kernels
+  hand them over (factors_rounded: as bf16, or with precise as the hi/lo
+  pairs the precise kernel hands over);
 * the coefficient-scaled aggregation operands -cM x, cW x as bf16
-  (precise: hi/lo of c (x_hi + x_lo));
+  (precise: hi/lo of c x);
 * the state in fp32 between chunks; the scalar kernels' outputs in fp32;
 * the output from bf16 chunk-start weights, the hidden activations
   silu(h1) h3 as bf16, and the result rounded to bf16.
@@ -37,9 +39,13 @@ def _hilo_sum(x):
     return hi + _rb(x - hi)
 
 
-def swiglu_bf16_path(cfg, x, precise: bool = False):
+def swiglu_bf16_path(cfg, x, precise: bool = False, factors_rounded: bool = False):
     """(out, W_end, M_end) of the bf16 MFMA path's rounding model for one
-    SwiGLU / negative-dot workload with whole chunks (T % chunk == 0)."""
+    SwiGLU / negative-dot workload with whole chunks (T % chunk == 0).
+    factors_rounded: the factors a, b, u are rounded to bf16 before the
+    coefficient scaling as well as after it (a form of the chunk loop that
+    handed them over in bf16); otherwise they are scaled in fp32 and rounded
+    once."""
     D, Hd, C, T, B, H = cfg.D, cfg.Hd, cfg.chunk, cfg.T, cfg.B, cfg.H
     assert T % C == 0
     op = _hilo_sum if precise else _rb
@@ -66,7 +72,9 @@ def swiglu_bf16_path(cfg, x, precise: bool = False):
         sg = torch.sigmoid(h1)
         s1 = h1 * sg
         ds = sg + s1 * (1 - sg)
-        fa, fb, fu = op(hv * h3 * ds), op(hv * s1), op(s1 * h3)
+        fa, fb, fu = hv * h3 * ds, hv * s1, s1 * h3
+        if factors_rounded:
+            fa, fb, fu = op(fa), op(fb), op(fu)
         # output from the bf16 snapshot of the chunk-start weights
         x1, x3 = Q @ _rb(W1), Q @ _rb(W3)
         out[:, :, sl] = _rb(_rb(x1 * torch.sigmoid(x1) * x3) @ _rb(W2))

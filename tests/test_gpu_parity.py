@@ -172,22 +172,49 @@ def test_swiglu_mfma_multichunk_slow_decay():
 
 
 # ---------------------------------------------------------------------------
-# precise operands (E2TTT_FLAG_PRECISE): the stated gates with a strongly
-# driven momentum, several 256-token chunks.  While the state decays by
-# ~1e-3 per chunk, the bf16 path's operand roundings grow from chunk to chunk
-# (its output error reaches 2e-2 .. 3e-2 on these inputs at every width);
-# with hi/lo operands the state follows the exact recurrence to ~1e-4.
+# Several 256-token chunks of the stated gates with a strongly driven momentum
+# (M0 at half the W0 scale).  While the state decays by ~1e-3 per chunk,
+# roundings of the aggregation operands accumulate from chunk to chunk.  With
+# the per-token factors rounded to bf16 both before and after their
+# coefficient scaling (an earlier form of the bf16 path) the output error
+# reached 2e-2 .. 3e-2 on these inputs; rounded once, after the scaling in
+# fp32, it stays within ~1e-2; with hi/lo operands (E2TTT_FLAG_PRECISE) the
+# state follows the exact recurrence to ~1e-4.
 # ---------------------------------------------------------------------------
 PRECISE_CASES = [
-    dict(B=1, H=2, T=768, Hd=64, chunk=256, seed=15),    # 3 chunks; bf16 path: out 2.75e-2
-    dict(B=1, H=2, T=1024, Hd=128, chunk=256, seed=14),  # bf16 path: out 2.9e-2
-    dict(B=1, H=2, T=1024, Hd=192, chunk=256, seed=14),  # bf16 path: out 3.0e-2
+    dict(B=1, H=2, T=768, Hd=64, chunk=256, seed=15),    # 3 chunks; factors rounded twice: out 2.75e-2
+    dict(B=1, H=2, T=1024, Hd=128, chunk=256, seed=14),  # factors rounded twice: out 2.9e-2
+    dict(B=1, H=2, T=1024, Hd=192, chunk=256, seed=14),  # factors rounded twice: out 3.0e-2
     dict(B=1, H=2, T=1024, Hd=256, chunk=256, seed=15),
     dict(B=2, H=3, T=512, Hd=64, chunk=64, seed=16),     # short chunks (snapshot stores spread)
     dict(B=1, H=2, T=1000, Hd=128, chunk=256, seed=17),  # ragged tail
     dict(B=4, H=20, T=512, Hd=128, chunk=256, seed=18),  # 320 workgroups: more than one round
 ]
 PRECISE_STATE_TOL = 1e-3
+
+
+# The default path meets the bf16 bound on these inputs except case 5 (the
+# ragged 1000-token sequence), where one momentum matrix ends at 2.31e-2
+# (out 1.47e-2): one rounding of the operands reduces the drift but does not
+# remove it on every input; the precise form covers that case.
+BF16_MULTICHUNK = [0, 1, 2, 3, 4, 6]
+
+
+@pytest.mark.parametrize("i", BF16_MULTICHUNK)
+def test_swiglu_bf16_multichunk_cases(i):
+    """The default bf16 path (no flag) on the same inputs, at the bf16 bound:
+    small grids take the split-role kernel, the 320-workgroup case the
+    64-unit one; both round each aggregation operand once."""
+    e2 = _lib()
+    c = dict(PRECISE_CASES[i])
+    seed = c.pop("seed")
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"bf16multi{i}", **c)
+    gu.note(f"bf16 multichunk case {i}: {c} seed={seed} m0=0.5")
+    x = synth.make_inputs(cfg, seed=seed, m0_scale=0.5)
+    assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
+    got = gu.run_gpu(cfg, x)
+    ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy())
 
 
 @pytest.mark.parametrize("i", range(len(PRECISE_CASES)))
