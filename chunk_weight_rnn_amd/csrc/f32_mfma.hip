@@ -478,7 +478,7 @@ __global__ __launch_bounds__(NT) void f32_chunk_kernel(F32Args a) {
 constexpr int SNW = 8;         // wavefronts per split workgroup: two groups of 4
 constexpr int SNT = 64 * SNW;
 constexpr int HS = 16;         // hidden units per split workgroup
-constexpr int SMAX = 16;       // slices per head (Hd <= 256)
+constexpr int SMAX = 8;        // slices per head (Hd <= 128)
 constexpr int RPT = 2;         // 16-byte pieces of a [TB][D] block per thread (TB * D <= 4096)
 // A slice writes output rows sl, sl + S, ...: with S >= 2 at most TB / 2 rows
 // of D / 4 pieces, one piece per thread.
@@ -620,6 +620,17 @@ f32_split_kernel(SplitArgs a) {
                 if (i < TB * n4 && r < nb) v4[u] = *(const f32x4*)&x[(bh * T + t + r) * D + 4 * (i % n4)];
             }
         };
+        // the columns 16 wl .. 16 wl + 15 of a chunk's rows (wave wl < nd of a
+        // group; 4 pieces of 4 floats per lane): piece p = lane + 64 u is row
+        // p / 4, column chunk 4 wl + p % 4
+        auto rows_tile = [&](const float* x, int64_t t, int nb, f32x4 (&v4)[4]) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int pc = lane + 64 * u, r = pc >> 2, c4 = 4 * wl + (pc & 3);
+                v4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (st && r < TB && r < nb) v4[u] = *(const f32x4*)&x[(bh * T + t + r) * D + 4 * c4];
+            }
+        };
         const bool fin = L >= 1, sta = L < a.nc;
         const int cf = L - 1, cs = L;  // the chunk finished, the chunk started
         const int64_t tf = (int64_t)cf * a.C, ts = (int64_t)cs * a.C;
@@ -628,7 +639,8 @@ f32_split_kernel(SplitArgs a) {
         const int orow = sl + S * (tid / n4), oc4 = tid % n4;
 
         // ------------------------------------------------------------ the step's loads: own rows first
-        f32x4 vf[RPT], ks[RPT], qs[RPT];
+        f32x4 vf[RPT];
+        f32x4 xs[4];  // the started chunk's K rows (group 0) or Q rows (group 1), columns of d-tile wl
         f32x4 ysum[RPT];                    // the finished chunk's Y summed over the slices (fixed order)
         f32x4 osum = {0.f, 0.f, 0.f, 0.f};  // one piece of its output rows
         float cmv = 0.f, cwv = 0.f;
@@ -639,10 +651,7 @@ f32_split_kernel(SplitArgs a) {
                 cwv = a.cW[bh * a.ldc + tf + tid];
             }
         }
-        if (sta) {
-            rows(a.k, ts, nbs, ks);
-            rows(a.q, ts, nbs, qs);
-        }
+        if (sta) rows_tile(grp == 0 ? a.k : a.q, ts, nbs, xs);
         if (fin) {
             wait_head((unsigned)(S * L));  // every slice has published chunk L - 1
             const float* yp = a.ypart + (size_t)(cf & 1) * parity + (size_t)bh * S * part;
@@ -726,7 +735,7 @@ f32_split_kernel(SplitArgs a) {
                 if (MOM) m += (am[0] + am[1]) + (am[2] + am[3]);
                 w += (aw[0] + aw[1]) + (aw[2] + aw[3]);
             }
-            __syncthreads();  // dZ is in Aq
+            __syncthreads();  // dZ is in Aq; dY, A and W2s are no longer read
             if (grp == 0 && st) {
                 // G_W1_s tile (units, d 16 wl ..): M += (cM dZ)^T K, W -= (cW dZ)^T K
                 f32x4 am[4] = {z4, z4, z4, z4}, aw[4] = {z4, z4, z4, z4};
@@ -741,7 +750,6 @@ f32_split_kernel(SplitArgs a) {
                 if (MOM) m += (am[0] + am[1]) + (am[2] + am[3]);
                 w += (aw[0] + aw[1]) + (aw[2] + aw[3]);
             }
-            __syncthreads();  // LDS is reused below
         }
         if (!sta) break;
 
@@ -763,12 +771,16 @@ f32_split_kernel(SplitArgs a) {
                     W2s.at(16 * wl + 4 * g + r, jl) = w[r];
             }
         }
+        // group 1 writes Q rows and W2s while group 0 still reads K rows and
+        // dZ for its W1 aggregation.  Group 0's wavefront wl writes the K-row
+        // columns of its own d-tile, the only ones its W1 aggregation reads,
+        // after that aggregation.
+        if (st) {
+            const Lm& Xs = grp == 0 ? Ks : Qs;
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int i = tid + SNT * u;
-            if (i < TB * n4) {
-                *Ks.row4(i / n4, i % n4) = ks[u];
-                *Qs.row4(i / n4, i % n4) = qs[u];
+            for (int u = 0; u < 4; ++u) {
+                const int pc = lane + 64 * u, r = pc >> 2;
+                if (r < TB) *Xs.row4(r, 4 * wl + (pc & 3)) = xs[u];
             }
         }
         __syncthreads();

@@ -134,7 +134,7 @@ E2TTT_API size_t e2ttt_workspace_size(const e2ttt_desc* desc);
  * 3 = fp32 MFMA path for LINEAR / MLP with F32 I/O (D a multiple of 16 up to
  * 64, Hd a multiple of 16, a head's state within 32 16x16 tiles per matrix),
  * 4 = the same for an MLP split over 16-unit hidden slices (B*H*Hd/16 <= 256,
- * chunk <= 64; the slices of a head synchronise through device memory once
+ * 32 <= Hd <= 128, chunk <= 64; the slices of a head synchronise through device memory once
  * per chunk, so all B*H*Hd/16 workgroups run at once, one per compute unit:
  * on a device with fewer compute units the call runs path 3's kernel);
  * negative e2ttt_status for a bad desc. */
