@@ -131,6 +131,12 @@ MFMA_CASES = [
     # 2 and 4 hidden-unit stages, so up to 3 query batches in flight
     dict(B=8, H=40, T=256, Hd=64, chunk=256),
     dict(B=4, H=80, T=256, Hd=128, chunk=256),
+    # grids the 64-unit kernel takes (more 32-unit slices than compute
+    # units), with ragged last chunks: 64-token chunks (snapshot stores spread
+    # over the gradient waves) ending in 8 tokens, and 128-token chunks
+    # ending in 60
+    dict(B=4, H=40, T=200, Hd=64, chunk=64),
+    dict(B=2, H=80, T=700, Hd=64, chunk=128),
 ]
 
 
