@@ -352,47 +352,54 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// The output kernel with a four-stage ring, for chunks of a multiple of 256
-// tokens and Hd a multiple of 128 (items of a multiple of four stages).
+// The output kernel for Hd = 256 (items of eight stages) and chunks of a
+// multiple of 256 tokens: a four-stage ring, so that every item starts at
+// ring buffer 0 and a loop iteration is straight-line code over two items
+// (the query registers alternate between them, so no register copy has to
+// wait for query loads).
 //
-// Every item starts at ring buffer 0, so an item is straight-line code: a
-// group of four stages that also starts the item (the next item's query
-// loads), further groups of four stages, then the item's end (output
-// stores).  Each wait on the in-order memory counter then allows exactly the
-// operations issued after the stage's copies: the copies of the next two
-// stages, the query loads when the item started one to three stages ago, the
-// output stores when the previous item ended one to three stages ago.  Loop
-// iterations take two items, with the query registers swapped, so that no
-// register copy has to wait for the query loads; the prologue issues eight
-// empty copies where an item's end issues its eight stores, so the first
-// item sees the same counts.  (With six stages and items of eight, the start
-// of an item moved through the unrolled loop, the compiler had to assume the
-// query loads were just issued, and its wait for them drained every copy in
-// flight.)
+// Each item's memory traffic besides the stage copies is spread over its
+// first four stages: two of the next item's eight query loads and two of
+// the previous item's eight output stores per stage.  Every wait on the
+// in-order memory counter therefore allows exactly the operations issued
+// after the stage's copies (vm_allowed below).  (The six-stage ring moved an
+// item's start through its unrolled loop; the compiler then had to assume
+// the query loads had just been issued, and its wait for them drained every
+// copy in flight, while the item's 16 stores went out at once from every
+// workgroup and the next stage's wait, which did not count them, waited for
+// them as well.)
 //
 // The outputs leave through LDS: each wavefront writes its 32 x 128 tile
 // there in halves of 64 columns and reads it back as rows, so that a store
 // instruction writes eight 128-byte row segments instead of 16-byte pieces
-// of 32 rows.  The stores are buffer stores whose range ends at the last
-// row inside the sequence: every lane issues them, and the hardware drops
-// the rows past it.
+// of 32 rows.  They are buffer stores whose range ends at the last row inside
+// the sequence: every lane issues them (so the counts hold), and the
+// hardware drops rows past it; the first item's stand-in stores have an
+// empty range.
 // ---------------------------------------------------------------------------
 __shared__ __attribute__((aligned(16))) unsigned char apply_ost[8 * 32 * 128];
 
+// Memory operations a stage at item position p (0..7) lets stay in flight
+// at its wait: issued after its copies (three stages earlier) are the copies
+// of the two stages between, and the query loads and output stores (two
+// each) of the item's first four positions among those three.
+__host__ __device__ constexpr int vm_allowed(int p, int ni) {
+    int n = 2 * ni;
+    for (int x = p - 3; x < p; ++x) n += ((x + 8) % 8) < 4 ? 4 : 0;
+    return n;
+}
+
 template <int NWA>
-__global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs a) {
-    constexpr int NS = 4;
+__global__ __launch_bounds__(64 * NWA) void swiglu_apply_h256_kernel(ApplyArgs a) {
+    constexpr int NS = 4;         // ring buffers
+    constexpr int NHB = 8;        // stages per item (Hd = 256)
     constexpr int NI = 24 / NWA;  // stage copy instructions per wave per stage
-    constexpr int NQ = 8;         // query loads per wave per item
-    constexpr int NO = 8;         // output stores per wave per item
-    static_assert(2 * NI + NQ + NO < 64, "wait counts must fit vmcnt");
+    static_assert(vm_allowed(3, NI) < 64, "wait counts must fit vmcnt");
     static_assert(NWA * 32 * 128 <= (int)sizeof(apply_ost), "output staging");
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int li = lane & 31, lg = lane >> 5;
-    const int Hd = a.Hd;
-    const int64_t P = 3 * (int64_t)D * Hd;
-    const int nhb = Hd / HB;  // stages per item, a multiple of 4
-    const int ngrp = nhb / 4;
+    constexpr int Hd = NHB * HB;
+    constexpr int64_t P = 3 * (int64_t)D * Hd;
     const int64_t nitems = (int64_t)a.nb * a.nc * a.rbc;
     const int nmine = (int)((nitems - blockIdx.x + gridDim.x - 1) / gridDim.x);
 
@@ -436,17 +443,19 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs 
         const unsigned ho = (unsigned)(cih * HB * D * 2);
 #pragma unroll
         for (int n = 0; n < NI; ++n) lds_copy16(citem.sn, citem.nrec, buf + mrow[n], voff[n] + ho);
-        if (++cih == nhb) {
+        if (++cih == NHB) {
             cih = 0;
             citem = item(++ck);
         }
     };
-    // Q^T as the B operand of the first product (as in swiglu_apply_kernel)
-    auto load_q = [&](const Item& it, bf16x8(&dst)[8]) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.q + it.tok * D), 0, uniform(it.nrows * D * 2), RSRC_W3);
+    // Q^T as the B operand of the first product (as in swiglu_apply_kernel):
+    // k-steps ks0, ks0 + 1 of an item's queries
+    auto q_rsrc = [&](const Item& it) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.q + it.tok * D), 0, uniform(it.nrows * D * 2), RSRC_W3);
+    };
+    auto load_q2 = [&](__amdgpu_buffer_rsrc_t r, int ks0, bf16x8(&dst)[8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) {
+        for (int ks = ks0; ks < ks0 + 2; ++ks) {
             const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, (li * D + 16 * ks + 8 * lg) * 2, 0, 0);
             dst[ks] = __builtin_bit_cast(bf16x8, w);
         }
@@ -458,31 +467,47 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs 
 #pragma unroll
     for (int i = 0; i < 8; ++i) tr_off[i] = tr_offset(i >> 1, i & 1, lane);
 
+    // output pieces: piece 4 h + i is row 8 i + 2 ((L >> 3) & 3) + (L >> 5),
+    // columns 64 h + 8 (L & 7) .. + 7 of lane L
+    const int orow = 2 * ((lane >> 3) & 3) + (lane >> 5), ocol = 8 * (lane & 7);
     unsigned char* const ost = apply_ost + wave * (32 * 128);  // this wave's output staging
     bf16x8 qa[8], qb[8];
+    u32x4 vout[8];                                               // the previous item's output pieces
+    __amdgpu_buffer_rsrc_t orsrc = q_rsrc(Item{a.q, 0, 0, 0});  // their range: empty before the first item
     f32x16 oacc[4] = {};
     Item cur = item(0);
     int k = 0;
-    load_q(cur, qa);  // the first item's queries precede every copy
-    static_for<0, NS - 1>([&](auto I) __attribute__((always_inline)) { issue_next_copy(stage_buf<decltype(I)::value>()); });
+    {
+        const __amdgpu_buffer_rsrc_t r = q_rsrc(cur);  // the first item's queries precede every copy
 #pragma unroll
-    for (int n = 0; n < NO; ++n) lds_copy16(a.q, 0, ost, 0);  // empty: stand-ins for an item's stores
+        for (int ks = 0; ks < 8; ks += 2) load_q2(r, ks, qa);
+    }
+    static_for<0, NS - 1>([&](auto I) __attribute__((always_inline)) { issue_next_copy(stage_buf<decltype(I)::value>()); });
 
-    // one stage on ring buffer I; VM: operations allowed in flight at its wait
-    auto stage = [&](auto Ic, auto VMc, const bf16x8(&qf)[8]) __attribute__((always_inline)) {
-        constexpr int I = decltype(Ic)::value;
-        constexpr int VM = decltype(VMc)::value;
+    // the stage at item position p (ring buffer p % 4) on queries qu; at
+    // positions 0..3 also two of the next item's query loads into qn and two
+    // of the previous item's output stores
+    auto stage = [&](auto Pc, const bf16x8(&qu)[8], bf16x8(&qn)[8], __amdgpu_buffer_rsrc_t qr)
+        __attribute__((always_inline)) {
+        constexpr int p = decltype(Pc)::value;
+        constexpr int I = p % NS;
         const unsigned char* st = stage_buf<I>();
-        wait_vm<VM>();
+        wait_vm<vm_allowed(p, NI)>();
         stage_barrier();
         issue_next_copy(stage_buf<(I + NS - 1) % NS>());  // the buffer the previous stage read
+        if constexpr (p < 4) {
+            load_q2(qr, 2 * p, qn);
+#pragma unroll
+            for (int j = 2 * p; j < 2 * p + 2; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(vout[j], orsrc, ((8 * (j & 3) + orow) * D + 64 * (j >> 2) + ocol) * 2, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(rd_off[i]), "+v"(tr_off[i]));
         f32x16 x1 = {}, x3 = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            x1 = mfma32(*(const bf16x8*)(st + rd_off[ks]), qf[ks], x1);
-            x3 = mfma32(*(const bf16x8*)(st + HB * 256 + rd_off[ks]), qf[ks], x3);
+            x1 = mfma32(*(const bf16x8*)(st + rd_off[ks]), qu[ks], x1);
+            x3 = mfma32(*(const bf16x8*)(st + HB * 256 + rd_off[ks]), qu[ks], x3);
         }
         bf16x8 ub[2];
 #pragma unroll
@@ -500,18 +525,13 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs 
             for (int dt = 0; dt < 4; ++dt)
                 oacc[dt] = mfma32(tr_frag_at(w2 + 4096 * s2, tr_off[2 * dt], tr_off[2 * dt + 1]), ub[s2], oacc[dt]);
     };
-    // The item's outputs through the staging, in two halves of 64 columns.
-    // Staging row t holds token t's 128 bytes of the half, 16-byte chunk c at
-    // physical chunk c ^ ((t >> 1) & 7); written by lane (li, lg) in 8-byte
-    // pieces (columns 32 dt + 8 qd + 4 lg ..), read back by lane L as row
-    // 8 i + 2 ((L >> 3) & 3) + (L >> 5), chunk L & 7, so that the two 8-lane
-    // groups a 128-bit read serves together see rows of opposite parity.
+    // The item's outputs into vout through the staging, in two halves of 64
+    // columns.  Staging row t holds token t's 128 bytes of the half, 16-byte
+    // chunk c at physical chunk c ^ ((t >> 1) & 7); written by lane (li, lg)
+    // in 8-byte pieces (columns 32 dt + 8 qd + 4 lg ..), read back as the
+    // output pieces, so that the two 8-lane groups a 128-bit read serves
+    // together see rows of opposite parity.
     auto item_end = [&]() __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.out + cur.tok * D), 0, uniform(cur.nrows * D * 2), RSRC_W3);
-        // both halves are read back before the first store, so that no store's
-        // data registers are reused while it may still read them
-        u32x4 v[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -525,42 +545,18 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs 
                 }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 8 * i + 2 * ((lane >> 3) & 3) + (lane >> 5), c = lane & 7;
-                v[h][i] = *(const u32x4*)(ost + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
+                const int row = 8 * i + orow;
+                vout[4 * h + i] = *(const u32x4*)(ost + row * 128 + 16 * ((ocol >> 3) ^ ((row >> 1) & 7)));
             }
         }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 8 * i + 2 * ((lane >> 3) & 3) + (lane >> 5), c = lane & 7;
-                __builtin_amdgcn_raw_buffer_store_b128(v[h][i], r, (row * D + 64 * h + 8 * c) * 2, 0, 0);
-            }
+        orsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.out + cur.tok * D), 0, uniform(cur.nrows * D * 2), RSRC_W3);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    constexpr int V0 = 2 * NI;  // the copies of the next two stages
-    using W0 = std::integral_constant<int, V0 + NO>;
-    using W12 = std::integral_constant<int, V0 + NQ + NO>;
-    using W3 = std::integral_constant<int, V0 + NQ>;
-    using WG = std::integral_constant<int, V0>;
     // one item on the queries in qu, loading the next item's into qn
     auto one_item = [&](const bf16x8(&qu)[8], bf16x8(&qn)[8]) __attribute__((always_inline)) {
-        stage(I0{}, W0{}, qu);
-        load_q(item(k + 1), qn);
-        stage(I1{}, W12{}, qu);
-        stage(I2{}, W12{}, qu);
-        stage(I3{}, W3{}, qu);
-        for (int g = 1; g < ngrp; ++g) {
-            stage(I0{}, WG{}, qu);
-            stage(I1{}, WG{}, qu);
-            stage(I2{}, WG{}, qu);
-            stage(I3{}, WG{}, qu);
-        }
+        const __amdgpu_buffer_rsrc_t qr = q_rsrc(item(k + 1));
+        static_for<0, NHB>([&](auto Pc) __attribute__((always_inline)) { stage(Pc, qu, qn, qr); });
         item_end();
         cur = item(++k);
     };
@@ -570,7 +566,10 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_ring4_kernel(ApplyArgs 
         one_item(qb, qa);
         if (k >= nmine) break;
     }
-    wait_vmem();  // copies past the last item (zeros) land before the LDS goes away
+#pragma unroll
+    for (int j = 0; j < 8; ++j)  // the last item's outputs
+        __builtin_amdgcn_raw_buffer_store_b128(vout[j], orsrc, ((8 * (j & 3) + orow) * D + 64 * (j >> 2) + ocol) * 2, 0, 0);
+    wait_vmem();  // and the copies past the last item (zeros) land before the LDS goes away
 }
 
 }  // namespace
@@ -607,9 +606,9 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
         const int64_t cap = (int64_t)ncu * per_cu;
         return dim3((unsigned)(items < cap ? items : cap));
     };
-    if (d.chunk % 256 == 0 && d.Hd % (4 * HB) == 0) {
+    if (d.chunk % 256 == 0 && d.Hd == 8 * HB) {
         aa.rbc = (int)(d.chunk / 256);
-        hipLaunchKernelGGL((swiglu_apply_ring4_kernel<8>), grid(nck * aa.rbc, 1), dim3(512), 0, s, aa);
+        hipLaunchKernelGGL((swiglu_apply_h256_kernel<8>), grid(nck * aa.rbc, 1), dim3(512), 0, s, aa);
     } else if (d.chunk % 256 == 0) {
         aa.rbc = (int)(d.chunk / 256);
         hipLaunchKernelGGL((swiglu_apply_kernel<8, 6>), grid(nck * aa.rbc, apply_wg_per_cu<6>()), dim3(512), 0, s, aa);
