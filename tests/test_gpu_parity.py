@@ -28,7 +28,9 @@ def _lib():
 # ---------------------------------------------------------------------------
 LOGSCAN_CASES = [(1, 2, 256, 16, "random"), (2, 3, 2048, 64, "random"), (1, 4, 2048, 256, "random"),
                  (2, 2, 2048, 1024, "random"), (1, 1, 9, 3, "random"), (1, 2, 7, 1, "random"),
-                 (1, 2, 512, 128, "edges"), (1, 1, 1024, 1024, "ones"), (1, 1, 256, 64, "zero_beta")]
+                 (1, 2, 512, 128, "edges"), (1, 1, 1024, 1024, "ones"), (1, 1, 256, 64, "zero_beta"),
+                 # four wavefronts per chunk (chunks of 257..1024 tokens), the last one partly or wholly empty
+                 (1, 2, 1536, 512, "edges"), (1, 1, 1280, 320, "random"), (2, 1, 2048, 1024, "edges")]
 
 
 @pytest.mark.parametrize("B,H,T,C,gates", LOGSCAN_CASES)

@@ -19,7 +19,8 @@ def _e2():
     return e2
 
 
-@pytest.mark.parametrize("T,C", [(100, 64), (1, 64), (1000, 256), (1030, 1024), (2047, 1024), (29, 8), (5000, 2048)])
+@pytest.mark.parametrize("T,C", [(100, 64), (1, 64), (1000, 256), (1030, 1024), (2047, 1024), (29, 8), (5000, 2048),
+                                 (700, 320), (900, 512)])
 @pytest.mark.parametrize("momentum,chunk_avg", [(True, False), (False, True)])
 def test_logscan_tail(T, C, momentum, chunk_avg):
     e2 = _e2()
