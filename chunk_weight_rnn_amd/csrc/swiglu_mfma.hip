@@ -359,8 +359,10 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
 // wait for query loads).
 //
 // Each item's memory traffic besides the stage copies is spread over its
-// first four stages: two of the next item's eight query loads and two of
-// the previous item's eight output stores per stage.  Every wait on the
+// first stages: the next item's eight query loads in its first two stages
+// (four a stage: each a whole 128-byte line of every query row; two a stage
+// over four stages fetched 15% more than the queries from HBM), and two of
+// the previous item's eight output stores in each of its first four.  Every wait on the
 // in-order memory counter therefore allows exactly the operations issued
 // after the stage's copies (vm_allowed below).  (The six-stage ring moved an
 // item's start through its unrolled loop; the compiler then had to assume
@@ -381,11 +383,14 @@ __shared__ __attribute__((aligned(16))) unsigned char apply_ost[8 * 32 * 128];
 
 // Memory operations a stage at item position p (0..7) lets stay in flight
 // at its wait: issued after its copies (three stages earlier) are the copies
-// of the two stages between, and the query loads and output stores (two
-// each) of the item's first four positions among those three.
+// of the two stages between, and the query loads (four at positions 0 and
+// 1) and output stores (two at positions 0..3) among those three positions.
 __host__ __device__ constexpr int vm_allowed(int p, int ni) {
     int n = 2 * ni;
-    for (int x = p - 3; x < p; ++x) n += ((x + 8) % 8) < 4 ? 4 : 0;
+    for (int x = p - 3; x < p; ++x) {
+        const int y = (x + 8) % 8;
+        n += (y < 2 ? 4 : 0) + (y < 4 ? 2 : 0);
+    }
     return n;
 }
 
@@ -485,8 +490,8 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_h256_kernel(ApplyArgs a
     static_for<0, NS - 1>([&](auto I) __attribute__((always_inline)) { issue_next_copy(stage_buf<decltype(I)::value>()); });
 
     // the stage at item position p (ring buffer p % 4) on queries qu; at
-    // positions 0..3 also two of the next item's query loads into qn and two
-    // of the previous item's output stores
+    // positions 0 and 1 also four of the next item's query loads into qn, at
+    // positions 0..3 two of the previous item's output stores
     auto stage = [&](auto Pc, const bf16x8(&qu)[8], bf16x8(&qn)[8], __amdgpu_buffer_rsrc_t qr)
         __attribute__((always_inline)) {
         constexpr int p = decltype(Pc)::value;
@@ -495,8 +500,11 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_h256_kernel(ApplyArgs a
         wait_vm<vm_allowed(p, NI)>();
         stage_barrier();
         issue_next_copy(stage_buf<(I + NS - 1) % NS>());  // the buffer the previous stage read
+        if constexpr (p < 2) {
+            load_q2(qr, 4 * p, qn);
+            load_q2(qr, 4 * p + 2, qn);
+        }
         if constexpr (p < 4) {
-            load_q2(qr, 2 * p, qn);
 #pragma unroll
             for (int j = 2 * p; j < 2 * p + 2; ++j)
                 __builtin_amdgcn_raw_buffer_store_b128(vout[j], orsrc, ((8 * (j & 3) + orow) * D + 64 * (j >> 2) + ocol) * 2, 0, 0);
