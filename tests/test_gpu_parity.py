@@ -208,6 +208,27 @@ PRECISE_STATE_TOL = 1e-3
 BF16_MULTICHUNK = [0, 1, 2, 3, 4, 6]
 
 
+# The output kernel for Hd = 256 takes two items (chunks of 256 tokens) per
+# loop iteration, with alternating query registers; on 256 compute units
+# these grids give workgroups 3 or 4 items (784), 1 or 2 (480), and 1 (6).
+APPLY_ITEM_CASES = [dict(B=7, H=16, T=1792), dict(B=6, H=16, T=1280), dict(B=1, H=3, T=512)]
+
+
+@pytest.mark.parametrize("i", range(len(APPLY_ITEM_CASES)))
+def test_apply_item_counts(i):
+    e2 = _lib()
+    c = APPLY_ITEM_CASES[i]
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"apply_items{i}", **c)
+    gu.note(f"output kernel item counts, case {i}: {c}")
+    assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
+    # slow-decay gates and M0 = 0, so that every chunk's output stays well
+    # above the bf16 path's drift (with M0 at half the W0 scale the seven-chunk
+    # grid reaches 3.1e-2 at chunk 5, identically with the six-stage kernel)
+    x = gu.persistent_gates(cfg, synth.make_inputs(cfg, seed=40 + i))
+    got = gu.run_gpu(cfg, x)
+    gu.assert_close(cfg, got, gu.run_oracle(cfg, x), x["W0"].numpy())
+
+
 @pytest.mark.parametrize("i", BF16_MULTICHUNK)
 def test_swiglu_bf16_multichunk_cases(i):
     """The default bf16 path (no flag) on the same inputs, at the bf16 bound:
