@@ -65,6 +65,10 @@ MFMA_TAILS = [
     dict(B=1, H=3, Hd=256, chunk=256, T=3 * 256 + 64),
     dict(B=2, H=2, Hd=128, chunk=256, T=256 + 200),
     dict(B=1, H=2, Hd=128, chunk=512, T=100),
+    # the Hd = 256 output kernel with one partial item: a single token, and
+    # one row short of a whole 256-token item
+    dict(B=2, H=2, Hd=256, chunk=256, T=1),
+    dict(B=1, H=3, Hd=256, chunk=512, T=255),
 ]
 
 
