@@ -703,7 +703,9 @@ swiglu_loop_kernel(LoopArgs a) {
 // ---------------------------------------------------------------------------
 // Small grids: UG 16-unit groups per workgroup (1 or 2), each group's work
 // split over four wavefronts; one state and one gradient wavefront per SIMD
-// for UG = 2, one wavefront per SIMD for UG = 1.
+// for UG = 2, one wavefront per SIMD for UG = 1.  (Grids of 16-unit slices
+// take the block-slot kernel below instead; the launcher instantiates this
+// one with UG = 2.)
 //
 // When the grid leaves compute units idle, a slot's length is the latency
 // of one wavefront's chain, not the chip's throughput.  So each of the two
@@ -1065,12 +1067,364 @@ swiglu_loop_sg_kernel(LoopArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small grids with one 16-unit group per workgroup: block slots.  Every
+// gradient of a chunk is taken at the chunk-start weights, so the tokens of a
+// chunk need no order among themselves; only the aggregation into the state
+// has to finish before the chunk boundary.  This kernel gives each slot a
+// whole 64-token block and twice the wavefronts of the split-role kernel, two
+// per SIMD, so a chunk of C tokens takes C/64 + 1 slots instead of C/32 + 1:
+//   state wave hf (wave hf, hf = 0..3): rows d = 32 hf .. 32 hf + 31 of the
+//       group's six state matrices (tiles 2 hf, 2 hf + 1: 48 accumulator
+//       registers); per block 24 MFMAs (12 without momentum) of K^T F and V^T F
+//       over the block's two half-blocks; it also issues the HBM -> LDS copies;
+//   gradient wave ti (wave 4 + ti): tokens 16 ti .. 16 ti + 15 of every
+//       block: H1, H3, HV (12 MFMAs), the backward and the scaling by the
+//       tokens' coefficients in fp32, written into its quarter of the block's
+//       factor set.
+// The state wave of SIMD s and the gradient wave of SIMD s overlap each
+// other's MFMAs, VALU work and LDS waits.
+//
+// Slots (one barrier each): the slot of block X holds the gradient waves'
+// work on X and the state waves' aggregation of block X - 1; a chunk's first
+// slot holds the state waves' rescale instead, and a boundary slot after the
+// chunk's last block holds the aggregation of that block and the hand-over.
+// Four LDS blocks: block X + 2 is copied during the slot of block X, into the
+// buffer block X - 2 left (its last reader, the state waves, finished in the
+// slot before), and waited for at the end of the slot of block X + 1, so
+// each copy has two slots to land.
+//
+// Hand-over: at a chunk boundary each state wave writes the operand
+// fragments of its rows of d (k-step hf of every matrix) and stores the
+// snapshot.  With momentum the operands go into the factor set that the
+// chunk's first block will use (12 KB, not read in the boundary slot), so the
+// chunk's first slot starts with a barrier after the gradient waves have
+// loaded them; without momentum they have an area of their own, and the
+// same barrier is kept so that both forms share one schedule.
+//
+// LDS: four 64-token blocks with their coefficients (132 KB), two factor sets
+// (24 KB, or 12 KB and the 12 KB operand area without momentum).
+template <bool MOM, bool SAVEM>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+swiglu_loop_bs_kernel(LoopArgs a) {
+    constexpr int NF = MOM ? 6 : 3;        // factor fragments per half-block
+    constexpr int FSET = 2 * NF * 1024;    // one block's factor set (two half-blocks)
+    constexpr int NB = 4;                  // LDS token blocks
+    constexpr int RPW = CB / 4;            // token rows each state wave copies per block
+    __shared__ __attribute__((aligned(16))) unsigned char kvs[NB * KVBUF];
+    __shared__ __attribute__((aligned(16))) unsigned char fxs[2 * FSET + (MOM ? 0 : 12 * 1024)];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int jl = lane & 15, g = lane >> 4;
+    const int xl = 16 * lane;
+
+    int L_id = blockIdx.x;
+    if (a.xcd_map) L_id = (blockIdx.x % 8) * (a.nwg / 8) + blockIdx.x / 8;
+    const int64_t bh = L_id / a.nsl;
+    const int Hd = a.Hd;
+    const int64_t j = (int64_t)(L_id % a.nsl) * 16 + jl;  // this lane's hidden unit
+    const int64_t T = a.T;
+    const int64_t P = 3 * (int64_t)D * Hd;
+    const int nblk = (int)((T + CB - 1) / CB);
+    const int nbc = a.C / CB;  // blocks per chunk
+    const int nc = a.nc;
+    const int nb_last = (int)((T - (int64_t)(nc - 1) * a.C + CB - 1) / CB);
+    auto blocks = [&](int c) { return c == nc - 1 ? nb_last : nbc; };
+    // chunk c's grad operands: with momentum the factor set of its first block
+    auto opnd = [&](int c) { return MOM ? fxs + ((c * nbc) & 1) * FSET : fxs + 2 * FSET; };
+
+    if (wave < 4) {
+        // ------------------------------------------------------------ state wave
+        const int hf = wave;
+        int te, tdelta;  // transpose-read offset of this wave's rows of d (tile 2 hf; + tdelta: 2 hf + 1)
+        {
+            const int p = lane & 15, q = p & 3;
+            const int r0 = 4 * g + (p >> 2);
+            const int h0 = 8 * (q & 1);
+            te = r0 * 256 + 16 * ((4 * hf + q) ^ swz4(r0)) + h0;
+            tdelta = 8 - 2 * h0;
+        }
+        const __bf16* kbase = a.k + bh * T * D;
+        const __bf16* vbase = a.v + bh * T * D;
+        const float* cMb = a.cM + bh * a.ldc;
+        const unsigned cw_rel = (unsigned)((const char*)(a.cW + bh * a.ldc) - (const char*)cMb);
+        const u32x4 krs = buffer_rsrc(kbase, (unsigned)(T * D * 2));
+        const u32x4 vrs = buffer_rsrc(vbase, (unsigned)(T * D * 2));
+        const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(a.ldc * 4));
+        const unsigned kvs_lds = lds_addr(kvs);
+        // rows RPW hf .. + RPW - 1 of block X's K and V (rows past T read as
+        // zeros), and wave 0 the block's coefficients: 8 copies, 9 for wave 0
+        auto issue_block = [&](int X) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const unsigned dst = kvs_lds + (unsigned)((X % NB) * KVBUF);
+            const unsigned tb = (unsigned)X * CB * D * 2;
+#pragma unroll
+            for (int i = 0; i < RPW / 4; ++i) {
+                const int row = RPW * hf + 4 * i + (ln >> 4);
+                const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
+                copy16(krs, dst + (RPW * hf + 4 * i) * 256, ko);
+                copy16(vrs, dst + KVB + (RPW * hf + 4 * i) * 256, ko);
+            }
+            if (hf == 0) {
+                const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
+                copy16(crs, dst + 2 * KVB, coff + (unsigned)X * CB * 4);
+            }
+        };
+        // every copy older than this wave's copies of one block has landed
+        auto wait_all_but_block = [&]() {
+            if (hf == 0)
+                wait_vm<2 * (RPW / 4) + 1>();
+            else
+                wait_vm<2 * (RPW / 4)>();
+        };
+        // the slot of block X copies block X + 2 at its start and waits for
+        // block X + 1 at its end
+        auto issue_next = [&](int X) {
+            if (X + 2 < nblk) issue_block(X + 2);
+        };
+        auto slot_end = [&](int X) {
+            if (X + 2 < nblk)
+                wait_all_but_block();
+            else
+                wait_vm<0>();
+        };
+
+        issue_block(0);
+        if (nblk > 1) issue_block(1);
+        f32x4 acc[3][2][2];
+        state_io<false, MOM, 2>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd, 2 * hf);
+
+        const bool godd = (g & 1) != 0;
+        // chunk c's grad operands (k-step hf of each matrix) and snapshot rows
+        auto operands = [&](int c) {
+            unsigned char* const od = opnd(c);
+            unsigned char* snap = (unsigned char*)(a.snap + (bh * nc + c) * P);
+            unsigned snap_lane = (unsigned)(j * D + 8 * g) * 2u;
+            asm volatile("" : "+v"(snap_lane));
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const bf16x4 t0 = pack4(acc[m][1][0]), t1 = pack4(acc[m][1][1]);
+                const bf16x4 lo = godd ? t1 : t0, hi = godd ? t0 : t1;
+                bf16x8 w8;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w8[e] = lo[e];
+                    w8[4 + e] = hi[e];
+                }
+                *(bf16x8*)(od + (4 * m + hf) * 1024 + xl) = w8;
+                *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * hf) * 2u)) = w8;
+                if (SAVEM) {
+                    unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
+                    const bf16x4 s0 = pack4(acc[m][0][0]), s1 = pack4(acc[m][0][1]);
+                    const bf16x4 mlo = godd ? s1 : s0, mhi = godd ? s0 : s1;
+                    bf16x8 m8;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        m8[e] = mlo[e];
+                        m8[4 + e] = mhi[e];
+                    }
+                    *(bf16x8*)(snapm + (snap_lane + (unsigned)(m * Hd * D + 32 * hf) * 2u)) = m8;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // (the chunk scalars through the scalar cache: a vector load here would
+        // make the compiler wait for the block copies in flight before it)
+        auto rescale = [&](int c) {
+            typedef const __attribute__((address_space(4))) f32x4 const_f32x4;
+            const f32x4 sc = *(const_f32x4*)(a.scal + (bh * nc + c) * 4);
+            const float A = sc[0], Bb = sc[1], gamma = sc[2];
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    if (MOM) {
+                        const f32x4 mm = acc[m][0][i];
+                        acc[m][1][i] = A * acc[m][1][i] - gamma * mm;
+                        acc[m][0][i] = Bb * mm;
+                    } else {
+                        acc[m][1][i] = A * acc[m][1][i];
+                    }
+                }
+            }
+        };
+        // state rows += K^T F, V^T F over both half-blocks of block X with the
+        // operands of factor set X % 2: (-cM a, cW a, -cM b, cW b, -cM u, cW u),
+        // without momentum (cW a, cW b, cW u)
+        auto aggregate = [&](int X) {
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const unsigned char* kb = kvs + (X % NB) * KVBUF + hl * 32 * 256;
+                const unsigned char* fb = fxs + (X & 1) * FSET + hl * NF * 1024 + xl;
+                bf16x8 f[NF];
+#pragma unroll
+                for (int x = 0; x < NF; ++x) f[x] = *(const bf16x8*)(fb + x * 1024);
+                auto frag = [&](int i, int mat) {
+                    const unsigned char* p = kb + mat * KVB + (i ? te + tdelta : te);
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4096));
+                    bf16x8 r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        r[e] = lo[e];
+                        r[4 + e] = hi[e];
+                    }
+                    return r;
+                };
+                const bf16x8 k0 = frag(0, 0), k1 = frag(1, 0), v0 = frag(0, 1), v1 = frag(1, 1);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const bf16x8 t = i ? k1 : k0;
+                    if (MOM) {
+                        acc[0][0][i] = mfma16(t, f[0], acc[0][0][i]);
+                        acc[0][1][i] = mfma16(t, f[1], acc[0][1][i]);
+                        acc[1][0][i] = mfma16(t, f[2], acc[1][0][i]);
+                        acc[1][1][i] = mfma16(t, f[3], acc[1][1][i]);
+                    } else {
+                        acc[0][1][i] = mfma16(t, f[0], acc[0][1][i]);
+                        acc[1][1][i] = mfma16(t, f[1], acc[1][1][i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const bf16x8 t = i ? v1 : v0;
+                    if (MOM) {
+                        acc[2][0][i] = mfma16(t, f[4], acc[2][0][i]);
+                        acc[2][1][i] = mfma16(t, f[5], acc[2][1][i]);
+                    } else {
+                        acc[2][1][i] = mfma16(t, f[2], acc[2][1][i]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        operands(0);
+        if (nblk > 1)
+            wait_all_but_block();  // block 0 has landed
+        else
+            wait_vm<0>();
+        slot_barrier();
+        // (nested loops with unconditional state updates keep every state
+        // tile in one register tuple for the whole sequence)
+        for (int c = 0;; ++c) {
+            const int X0 = c * nbc;
+            const int n = blocks(c);
+            rescale(c);
+            slot_barrier();  // the gradient waves have loaded the chunk's operands
+            issue_next(X0);  // the slot of block X0
+            slot_end(X0);
+            slot_barrier();
+            for (int k = 1; k < n; ++k) {  // the slot of block X0 + k
+                issue_next(X0 + k);
+                aggregate(X0 + k - 1);
+                slot_end(X0 + k);
+                slot_barrier();
+            }
+            aggregate(X0 + n - 1);  // the boundary slot
+            if (c + 1 == nc) break;
+            operands(c + 1);
+            slot_barrier();
+        }
+        wait_vm<0>();
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        state_io<true, MOM, 2>(acc, a.W_end + bh * P, MOM ? a.M_end + bh * P : nullptr,
+                               (int64_t)(L_id % a.nsl) * 16 + (lane_e & 15), lane_e >> 4, Hd, 2 * hf);
+    } else {
+        // ------------------------------------------------------------ gradient wave
+        const int ti = wave - 4;  // token rows 16 ti .. 16 ti + 15 of every block
+        int goff[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) goff[kk] = jl * 256 + 16 * ((4 * kk + g) ^ swz4(jl)) + 16 * ti * 256;
+        bf16x8 wb[3][4];  // chunk-start weights: k-slot e of lane group g is d = 32kk + 8g + e
+        typedef f32x4 grad_acc[3];
+        typedef bf16x8 rows[4];  // K or V row fragments of this wave's 16 tokens
+        auto read_rows = [&](int X, int mat, rows& fr) {
+            const unsigned char* kb = kvs + (X % NB) * KVBUF + mat * KVB;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) fr[kk] = *(const bf16x8*)(kb + goff[kk]);
+        };
+        // backward of this wave's tokens of block X and the scaling:
+        // a = hv h3 silu'(h1), b = hv silu(h1), u = silu(h1) h3 (hv = V W2^T =
+        // -du) times the tokens' cM and cW, into k-slots 4 (ti % 2) .. + 3 of
+        // the fragments of half-block ti / 2 in factor set X % 2 (k-slot e of a
+        // fragment is token 16 (e/4) + 4g + e%4 of the half-block, the token
+        // order of the transpose read)
+        auto backward = [&](int X, const grad_acc& hg) {
+            const float* cob = (const float*)(kvs + (X % NB) * KVBUF + 2 * KVB) + 16 * ti + 4 * g;
+            const f32x4 cm = *(const f32x4*)cob, cw = *(const f32x4*)(cob + 64);
+            float fa[4], fb[4], fu[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x1 = hg[0][r], x3 = hg[1][r], y = hg[2][r];
+                const float sg = fast_sigmoid(x1);
+                const float s1 = x1 * sg;
+                const float ds = sg + s1 * (1.f - sg);
+                fa[r] = y * x3 * ds;
+                fb[r] = y * s1;
+                fu[r] = s1 * x3;
+            }
+            unsigned char* const fo = fxs + (X & 1) * FSET + (ti >> 1) * NF * 1024 + xl + 8 * (ti & 1);
+            auto put = [&](int x, const float (&v)[4], bool mom) {
+                bf16x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = (__bf16)(mom ? -cm[e] * v[e] : cw[e] * v[e]);
+                *(bf16x4*)(fo + x * 1024) = r;
+            };
+            if (MOM) {
+                put(0, fa, true);
+                put(1, fa, false);
+                put(2, fb, true);
+                put(3, fb, false);
+                put(4, fu, true);
+                put(5, fu, false);
+            } else {
+                put(0, fa, false);
+                put(1, fb, false);
+                put(2, fu, false);
+            }
+        };
+        slot_barrier();
+        for (int c = 0; c < nc; ++c) {
+            const unsigned char* const od = opnd(c);
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) wb[m][kk] = *(const bf16x8*)(od + (4 * m + kk) * 1024 + xl);
+            slot_barrier();  // every gradient wave has its operands (the factors may overwrite them)
+            const int X0 = c * nbc;
+            const int n = blocks(c);
+            for (int k = 0; k < n; ++k) {  // the slot of block X0 + k
+                const int X = X0 + k;
+                grad_acc hg;
+                rows fk, fv;
+                read_rows(X, 0, fk);
+                read_rows(X, 1, fv);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+                    hg[0] = mfma16(fk[kk], wb[0][kk], kk ? hg[0] : z);
+                    hg[1] = mfma16(fk[kk], wb[1][kk], kk ? hg[1] : z);
+                    hg[2] = mfma16(fv[kk], wb[2][kk], kk ? hg[2] : z);
+                }
+                backward(X, hg);
+                slot_barrier();
+            }
+            if (c + 1 < nc) slot_barrier();  // the boundary slot: the state waves hand over the next operands
+        }
+    }
+}
+
 }  // namespace
 
 // Smaller slices only while their grid still fits on the chip at once: a
 // slot takes about as long either way, so a second round of workgroups would
 // cost more than the smaller slices gain.  16-unit slices take the
-// split-role kernel (four wavefronts sharing one unit group's work).
+// block-slot kernel (eight wavefronts on one unit group, a 64-token block per
+// slot), 32-unit slices the split-role kernel.
 static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
     if (BH * (Hd / 16) <= ncu) return 1;
     return BH * (Hd / 32) <= ncu ? 2 : 4;
@@ -1120,10 +1474,17 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
             else
                 hipLaunchKernelGGL((swiglu_loop_sg_kernel<true, false, U>), g1, b1, 0, s, la);
         };
-        if (ug == 1)
-            go_sg(std::integral_constant<int, 1>{});
-        else
+        if (ug == 1) {  // one 16-unit group per workgroup: block slots, eight wavefronts
+            const dim3 g1((unsigned)la.nwg), b1(512);
+            if (nm)
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<false, false>), g1, b1, 0, s, la);
+            else if (snapM)
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, true>), g1, b1, 0, s, la);
+            else
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, false>), g1, b1, 0, s, la);
+        } else {
             go_sg(std::integral_constant<int, 2>{});
+        }
         return hipGetLastError();
     }
     const dim3 grid((unsigned)la.nwg), block((unsigned)(128 * ug));
