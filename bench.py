@@ -569,6 +569,13 @@ def main() -> int:
     peak = PEAK_BF16_TFLOPS if path in (1, 2) else PEAK_F32_TFLOPS
     loop_kernel = {0: "generic_kernel", 1: "swiglu_loop_kernel", 2: "swiglu_loop_kernel", 3: "f32_chunk_kernel",
                    4: "f32_split_kernel"}[path]
+    if path == 1:  # the chunk loop's form follows the grid (16- or 32-unit slices when they fit at once)
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        bh = cfg.B * cfg.H
+        if bh * (cfg.Hd // 16) <= ncu:
+            loop_kernel = "swiglu_loop_bs_kernel"
+        elif bh * (cfg.Hd // 32) <= ncu:
+            loop_kernel = "swiglu_loop_sg_kernel"
     # the fp32 kernels compute the chunk outputs inside the chunk loop
     loop_stages = ("grad", "aggregate") if path in (1, 2) else ("grad", "aggregate", "apply")
     loop_flops = sum(fpt[k] for k in loop_stages) * heads_tokens
