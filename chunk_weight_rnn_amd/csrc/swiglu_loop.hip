@@ -1104,17 +1104,23 @@ swiglu_loop_sg_kernel(LoopArgs a) {
 //
 // LDS: four 64-token blocks with their coefficients (132 KB), two factor sets
 // (24 KB, or 12 KB and the 12 KB operand area without momentum).
-template <bool MOM, bool SAVEM>
-__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <bool MOM, bool SAVEM, int UG>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512 * UG, 512 * UG), amdgpu_waves_per_eu(2 * UG, 2 * UG)))
 swiglu_loop_bs_kernel(LoopArgs a) {
+    static_assert(UG == 1 || UG == 2, "unit groups per workgroup");
     constexpr int NF = MOM ? 6 : 3;        // factor fragments per half-block
     constexpr int FSET = 2 * NF * 1024;    // one block's factor set (two half-blocks)
-    constexpr int NB = 4;                  // LDS token blocks
-    constexpr int RPW = CB / 4;            // token rows each state wave copies per block
+    constexpr int GSZ = 2 * FSET + (MOM ? 0 : 12 * 1024);  // a unit group's factor sets (and operand area)
+    constexpr int NB = UG == 1 ? 4 : 3;    // LDS token blocks
+    constexpr int LEAD = NB - 2;           // blocks a copy runs ahead of the slot that issues it
+    constexpr int RPW = CB / (4 * UG);     // token rows each state wave copies per block
     __shared__ __attribute__((aligned(16))) unsigned char kvs[NB * KVBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char fxs[2 * FSET + (MOM ? 0 : 12 * 1024)];
+    __shared__ __attribute__((aligned(16))) unsigned char fxs_all[UG * GSZ];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int u = wave >> 3;   // unit group
+    const int lw = wave & 7;   // wave within the group: 0..3 state, 4..7 gradient
+    unsigned char* const fxs = fxs_all + u * GSZ;
     const int lane = tid & 63;
     const int jl = lane & 15, g = lane >> 4;
     const int xl = 16 * lane;
@@ -1123,7 +1129,7 @@ swiglu_loop_bs_kernel(LoopArgs a) {
     if (a.xcd_map) L_id = (blockIdx.x % 8) * (a.nwg / 8) + blockIdx.x / 8;
     const int64_t bh = L_id / a.nsl;
     const int Hd = a.Hd;
-    const int64_t j = (int64_t)(L_id % a.nsl) * 16 + jl;  // this lane's hidden unit
+    const int64_t j = (int64_t)(L_id % a.nsl) * 16 * UG + 16 * u + jl;  // this lane's hidden unit
     const int64_t T = a.T;
     const int64_t P = 3 * (int64_t)D * Hd;
     const int nblk = (int)((T + CB - 1) / CB);
@@ -1134,9 +1140,10 @@ swiglu_loop_bs_kernel(LoopArgs a) {
     // chunk c's grad operands: with momentum the factor set of its first block
     auto opnd = [&](int c) { return MOM ? fxs + ((c * nbc) & 1) * FSET : fxs + 2 * FSET; };
 
-    if (wave < 4) {
+    if (lw < 4) {
         // ------------------------------------------------------------ state wave
-        const int hf = wave;
+        const int hf = lw;
+        const int cw = 4 * u + hf;  // this wave's share of the block copies
         int te, tdelta;  // transpose-read offset of this wave's rows of d (tile 2 hf; + tdelta: 2 hf + 1)
         {
             const int p = lane & 15, q = p & 3;
@@ -1153,8 +1160,9 @@ swiglu_loop_bs_kernel(LoopArgs a) {
         const u32x4 vrs = buffer_rsrc(vbase, (unsigned)(T * D * 2));
         const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(a.ldc * 4));
         const unsigned kvs_lds = lds_addr(kvs);
-        // rows RPW hf .. + RPW - 1 of block X's K and V (rows past T read as
-        // zeros), and wave 0 the block's coefficients: 8 copies, 9 for wave 0
+        // rows RPW cw .. + RPW - 1 of block X's K and V (rows past T read as
+        // zeros), and copy wave 0 the block's coefficients: 2 RPW / 4 copies,
+        // one more for copy wave 0
         auto issue_block = [&](int X) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
@@ -1162,37 +1170,38 @@ swiglu_loop_bs_kernel(LoopArgs a) {
             const unsigned tb = (unsigned)X * CB * D * 2;
 #pragma unroll
             for (int i = 0; i < RPW / 4; ++i) {
-                const int row = RPW * hf + 4 * i + (ln >> 4);
+                const int row = RPW * cw + 4 * i + (ln >> 4);
                 const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
-                copy16(krs, dst + (RPW * hf + 4 * i) * 256, ko);
-                copy16(vrs, dst + KVB + (RPW * hf + 4 * i) * 256, ko);
+                copy16(krs, dst + (RPW * cw + 4 * i) * 256, ko);
+                copy16(vrs, dst + KVB + (RPW * cw + 4 * i) * 256, ko);
             }
-            if (hf == 0) {
+            if (cw == 0) {
                 const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
                 copy16(crs, dst + 2 * KVB, coff + (unsigned)X * CB * 4);
             }
         };
         // every copy older than this wave's copies of one block has landed
         auto wait_all_but_block = [&]() {
-            if (hf == 0)
+            if (cw == 0)
                 wait_vm<2 * (RPW / 4) + 1>();
             else
                 wait_vm<2 * (RPW / 4)>();
         };
-        // the slot of block X copies block X + 2 at its start and waits for
-        // block X + 1 at its end
+        // the slot of block X copies block X + LEAD at its start; at its end
+        // block X + 1 has landed (with LEAD = 2 the copy of block X + 2 may
+        // still be in flight)
         auto issue_next = [&](int X) {
-            if (X + 2 < nblk) issue_block(X + 2);
+            if (X + LEAD < nblk) issue_block(X + LEAD);
         };
         auto slot_end = [&](int X) {
-            if (X + 2 < nblk)
+            if (LEAD == 2 && X + 2 < nblk)
                 wait_all_but_block();
             else
                 wait_vm<0>();
         };
 
         issue_block(0);
-        if (nblk > 1) issue_block(1);
+        if (LEAD == 2 && nblk > 1) issue_block(1);
         f32x4 acc[3][2][2];
         state_io<false, MOM, 2>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd, 2 * hf);
 
@@ -1302,7 +1311,7 @@ swiglu_loop_bs_kernel(LoopArgs a) {
         };
 
         operands(0);
-        if (nblk > 1)
+        if (LEAD == 2 && nblk > 1)
             wait_all_but_block();  // block 0 has landed
         else
             wait_vm<0>();
@@ -1332,10 +1341,10 @@ swiglu_loop_bs_kernel(LoopArgs a) {
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
         state_io<true, MOM, 2>(acc, a.W_end + bh * P, MOM ? a.M_end + bh * P : nullptr,
-                               (int64_t)(L_id % a.nsl) * 16 + (lane_e & 15), lane_e >> 4, Hd, 2 * hf);
+                               (int64_t)(L_id % a.nsl) * 16 * UG + 16 * u + (lane_e & 15), lane_e >> 4, Hd, 2 * hf);
     } else {
         // ------------------------------------------------------------ gradient wave
-        const int ti = wave - 4;  // token rows 16 ti .. 16 ti + 15 of every block
+        const int ti = lw - 4;  // token rows 16 ti .. 16 ti + 15 of every block
         int goff[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) goff[kk] = jl * 256 + 16 * ((4 * kk + g) ^ swz4(jl)) + 16 * ti * 256;
@@ -1474,17 +1483,21 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
             else
                 hipLaunchKernelGGL((swiglu_loop_sg_kernel<true, false, U>), g1, b1, 0, s, la);
         };
-        if (ug == 1) {  // one 16-unit group per workgroup: block slots, eight wavefronts
-            const dim3 g1((unsigned)la.nwg), b1(512);
+        // block slots: eight wavefronts per 16-unit group, a 64-token block per slot
+        auto go_bs = [&](auto UGc) {
+            constexpr int U = decltype(UGc)::value;
+            const dim3 g1((unsigned)la.nwg), b1(512 * U);
             if (nm)
-                hipLaunchKernelGGL((swiglu_loop_bs_kernel<false, false>), g1, b1, 0, s, la);
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<false, false, U>), g1, b1, 0, s, la);
             else if (snapM)
-                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, true>), g1, b1, 0, s, la);
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, true, U>), g1, b1, 0, s, la);
             else
-                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, false>), g1, b1, 0, s, la);
-        } else {
-            go_sg(std::integral_constant<int, 2>{});
-        }
+                hipLaunchKernelGGL((swiglu_loop_bs_kernel<true, false, U>), g1, b1, 0, s, la);
+        };
+        if (ug == 1)
+            go_bs(std::integral_constant<int, 1>{});
+        else
+            go_bs(std::integral_constant<int, 2>{});
         return hipGetLastError();
     }
     const dim3 grid((unsigned)la.nwg), block((unsigned)(128 * ug));

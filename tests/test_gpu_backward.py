@@ -95,6 +95,17 @@ def test_backward_hidden_widths(Hd, T, chunk):
     _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
 
 
+def test_backward_two_group_grid():
+    """A grid of 32-unit slices (24 heads of 256 units on 256 compute units):
+    the forward recompute runs the block-slot loop with two unit groups per
+    workgroup and writes the momentum snapshots from it."""
+    cfg = SMALL.with_(H=24, T=512, chunk=256, Hd=256, name="bwd_two_group")
+    note(f"case {cfg.name}")
+    x = synth.make_inputs(cfg, seed=11, m0_scale=0.5)
+    c = synth.make_cotangents(cfg, seed=12)
+    _compare(cfg, _gpu(cfg, x, c), _oracle(cfg, x, c))
+
+
 @pytest.mark.parametrize("Hd", [64, 128])
 def test_backward_precise_multichunk(Hd):
     """The backward of a precise forward (E2TTT_FLAG_PRECISE) runs the portable

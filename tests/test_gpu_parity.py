@@ -232,7 +232,7 @@ def test_apply_item_counts(i):
 @pytest.mark.parametrize("i", BF16_MULTICHUNK)
 def test_swiglu_bf16_multichunk_cases(i):
     """The default bf16 path (no flag) on the same inputs, at the bf16 bound:
-    small grids take the split-role kernel, the 320-workgroup case the
+    small grids take the block-slot kernel, the 320-workgroup case the
     64-unit one; both round each aggregation operand once."""
     e2 = _lib()
     c = dict(PRECISE_CASES[i])
@@ -243,6 +243,32 @@ def test_swiglu_bf16_multichunk_cases(i):
     assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
     got = gu.run_gpu(cfg, x)
     ref = gu.run_oracle(cfg, x)
+    gu.assert_close(cfg, got, ref, x["W0"].numpy())
+
+
+# The chunk loop's form follows the grid on 256 compute units: one 16-unit
+# group per workgroup when B·H·Hd/16 workgroups fit (block slots, four LDS
+# blocks), two groups when B·H·Hd/32 fit (block slots, three blocks), else
+# 64-unit slices.  Each with several chunks and a ragged tail.
+LOOP_FORM_CASES = [
+    dict(B=1, H=2, T=700, Hd=256, chunk=256),   # 32 workgroups of one group
+    dict(B=1, H=24, T=700, Hd=256, chunk=256),  # 192 workgroups of two groups
+    dict(B=1, H=24, T=448, Hd=256, chunk=64),   # the same with one-block chunks
+    dict(B=1, H=40, T=300, Hd=256, chunk=256),  # 160 workgroups of 64-unit slices
+]
+
+
+@pytest.mark.parametrize("i", range(len(LOOP_FORM_CASES)))
+@pytest.mark.parametrize("momentum", [True, False], ids=["momentum", "no_momentum"])
+def test_loop_forms(i, momentum):
+    e2 = _lib()
+    c = LOOP_FORM_CASES[i]
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name=f"loopform{i}", flags=0 if momentum else 2, **c)
+    gu.note(f"loop form case {i}: {c} momentum={momentum}")
+    assert e2.path("swiglu", "negdot", "bf16", cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
+    x = synth.make_inputs(cfg, seed=90 + i, m0_scale=0.5 if momentum else 0.0)
+    got = gu.run_gpu(cfg, x, momentum=momentum)
+    ref = gu.run_oracle(cfg, x, momentum=momentum)
     gu.assert_close(cfg, got, ref, x["W0"].numpy())
 
 

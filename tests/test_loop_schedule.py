@@ -64,7 +64,7 @@ def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB):
             if k > 0:
                 read(slot, X - 1, "state")
                 fsets.append((slot, (X - 1) & 1, "r", X - 1))
-            wait(copies_per_block if X + lead < nblk else 0)
+            wait(copies_per_block * max(0, min(X + lead, nblk - 1) - (X + 1)))  # blocks after X + 1 in flight
             bar_state += 1
         slot += 1
         read(slot, X0 + n - 1, "state")
@@ -78,24 +78,27 @@ def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB):
 
 
 @pytest.mark.parametrize("C", [64, 128, 192, 256, 512, 1024, 2048])
-def test_block_slot_schedule(C):
+@pytest.mark.parametrize("lead,nb,copies", [(2, 4, 8), (2, 4, 9), (1, 3, 4), (1, 3, 5)])
+def test_block_slot_schedule(C, lead, nb, copies):
+    """One unit group per workgroup: four blocks, copies two blocks ahead, 8
+    copies per state wave (9 for the one that also copies the coefficients);
+    two unit groups: three blocks, one ahead, 4 (5) copies."""
     for T in list(range(1, 400)) + [2000, 2048, 4096, 5000, 16384]:
-        for copies in (8, 9):  # wave 0 also copies the block's coefficients
-            for stores in (3, 6):  # with the momentum snapshot
-                nblk, bs, bg, reads, fsets = schedule(T, C, copies, stores)
-                assert bs == bg, (T, C)
-                # every block read once by each role, the state after the gradient waves
-                grad = {X: s for s, X, r in reads if r == "grad"}
-                state = {X: s for s, X, r in reads if r == "state"}
-                assert sorted(grad) == sorted(state) == list(range(nblk)), (T, C)
-                assert all(state[X] > grad[X] for X in grad), (T, C)
-                # a factor set is not rewritten between its write and its read
-                for s_r, fs, kind, X in fsets:
-                    if kind != "r":
-                        continue
-                    s_w = grad[X]
-                    assert not any(k == "w" and st == fs and s_w < s <= s_r and Y != X
-                                   for s, st, k, Y in fsets), (T, C, X)
+        for stores in (3, 6):  # with the momentum snapshot
+            nblk, bs, bg, reads, fsets = schedule(T, C, copies, stores, lead=lead, nb=nb)
+            assert bs == bg, (T, C)
+            # every block read once by each role, the state after the gradient waves
+            grad = {X: s for s, X, r in reads if r == "grad"}
+            state = {X: s for s, X, r in reads if r == "state"}
+            assert sorted(grad) == sorted(state) == list(range(nblk)), (T, C)
+            assert all(state[X] > grad[X] for X in grad), (T, C)
+            # a factor set is not rewritten between its write and its read
+            for s_r, fs, kind, X in fsets:
+                if kind != "r":
+                    continue
+                s_w = grad[X]
+                assert not any(k == "w" and st == fs and s_w < s <= s_r and Y != X
+                               for s, st, k, Y in fsets), (T, C, X)
 
 
 def test_schedule_model_catches_an_overwrite():
