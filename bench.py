@@ -571,11 +571,8 @@ def main() -> int:
                    4: "f32_split_kernel"}[path]
     if path == 1:  # the chunk loop's form follows the grid (16- or 32-unit slices when they fit at once)
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        bh = cfg.B * cfg.H
-        if bh * (cfg.Hd // 16) <= ncu:
+        if cfg.B * cfg.H * (cfg.Hd // 32) <= ncu:
             loop_kernel = "swiglu_loop_bs_kernel"
-        elif bh * (cfg.Hd // 32) <= ncu:
-            loop_kernel = "swiglu_loop_sg_kernel"
     # the fp32 kernels compute the chunk outputs inside the chunk loop
     loop_stages = ("grad", "aggregate") if path in (1, 2) else ("grad", "aggregate", "apply")
     loop_flops = sum(fpt[k] for k in loop_stages) * heads_tokens

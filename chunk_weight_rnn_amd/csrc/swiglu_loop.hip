@@ -23,7 +23,7 @@
 //
 // Workgroup = 8 wavefronts, two per SIMD, in two roles over the same 16-unit
 // groups u = 0..3 (the precise form: 4 wavefronts over a 32-unit slice,
-// u = 0..1; grids that leave compute units idle take the split-role kernel
+// u = 0..1; grids that leave compute units idle take the block-slot kernel
 // further below):
 //   state wave u (wave u):      the group's fp32 W and M (6 x 128 x 16 values)
 //                               as MFMA accumulators; per 32 tokens it scales
@@ -701,384 +701,20 @@ swiglu_loop_kernel(LoopArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Small grids: UG 16-unit groups per workgroup (1 or 2), each group's work
-// split over four wavefronts; one state and one gradient wavefront per SIMD
-// for UG = 2, one wavefront per SIMD for UG = 1.  (Grids of 16-unit slices
-// take the block-slot kernel below instead; the launcher instantiates this
-// one with UG = 2.)
-//
-// When the grid leaves compute units idle, a slot's length is the latency
-// of one wavefront's chain, not the chip's throughput.  So each of the two
-// roles is split in two:
-//   state wave (hf, u) (wave UG hf + u): rows d of tiles 4 hf .. 4 hf + 3 of the
-//       group's six state matrices (96 accumulator registers); per 32 tokens
-//       24 MFMAs (12 without momentum) of K^T F and V^T F on its rows, with
-//       the scaled aggregation operands read from LDS;
-//   gradient wave (ti, u) (wave 2 UG + UG ti + u): the 16 tokens 32h + 16 ti .. + 15 of
-//       every half-block h: their H1, H3, HV (12 MFMAs), the backward and the
-//       scaling by the tokens' coefficients in fp32 (one rounding to bf16),
-//       written into its half of each operand fragment.
-// The chunk-start hand-over of the grad operands takes two barriers, as
-// both state waves read the same factor set: the first half writes its six
-// operand fragments into the set not read in the boundary slot; after the
-// barrier the second half writes its six into the set that was, while the
-// gradient waves already run the chunk's first grad MFMAs over the first
-// half's rows of d.  The snapshot is stored by the state waves at the
-// hand-over.
-template <bool MOM, bool SAVEM, int UG>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256 * UG, 256 * UG), amdgpu_waves_per_eu(UG, UG)))
-swiglu_loop_sg_kernel(LoopArgs a) {
-    static_assert(UG == 1 || UG == 2, "unit groups per workgroup");
-    constexpr int S = 16 * UG;     // hidden units per workgroup
-    constexpr int NSW = 2 * UG;    // state waves
-    constexpr int RPW = CB / NSW;  // token rows each state wave copies per block
-    constexpr int FS = 6 * 1024;   // one factor set (six fragments) or half the grad operands
-    constexpr int NF = MOM ? 6 : 3;  // factor fragments per half-block
-    __shared__ __attribute__((aligned(16))) unsigned char kvs[NBUF * KVBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char xch[UG * 2 * FS];
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int u = wave & (UG - 1);
-    unsigned char* const xw = xch + u * 2 * FS;  // this unit group's exchange area
-    const int lane = tid & 63;
-    const int jl = lane & 15, g = lane >> 4;
-
-    int L_id = blockIdx.x;
-    if (a.xcd_map) L_id = (blockIdx.x % 8) * (a.nwg / 8) + blockIdx.x / 8;
-    const int64_t bh = L_id / a.nsl;
-    const int Hd = a.Hd;
-    const int64_t j = (int64_t)(L_id % a.nsl) * S + 16 * u + jl;
-    const int64_t T = a.T;
-    const int64_t P = 3 * (int64_t)D * Hd;
-    const int nblk = (int)((T + CB - 1) / CB);
-    const int nh = a.C / 32;
-    const int nh_last = (int)((T - (int64_t)(a.nc - 1) * a.C + 31) / 32);
-    auto halves = [&](int c) { return c == a.nc - 1 ? nh_last : nh; };
-    const int nc = a.nc;
-    const int xl = 16 * lane;
-    // Chunk c's grad operands: the second state half's go to set pset(c), the
-    // set of the previous chunk's last half-block, the first half's to the
-    // other set.
-    auto pset = [&](int c) { return c == 0 ? 1 : (c * nh - 1) & 1; };
-
-    if (wave < NSW) {
-        // ------------------------------------------------------------ state wave
-        const int hf = wave / UG;
-        int te[2], tdelta;
-        {
-            const int p = lane & 15, q = p & 3;
-            const int r0 = 4 * g + (p >> 2);
-            const int h0 = 8 * (q & 1);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) te[t] = r0 * 256 + 16 * ((4 * (2 * hf + t) + q) ^ swz4(r0)) + h0;
-            tdelta = 8 - 2 * h0;
-        }
-        const __bf16* kbase = a.k + bh * T * D;
-        const __bf16* vbase = a.v + bh * T * D;
-        const float* cMb = a.cM + bh * a.ldc;
-        const unsigned cw_rel = (unsigned)((const char*)(a.cW + bh * a.ldc) - (const char*)cMb);
-        const u32x4 krs = buffer_rsrc(kbase, (unsigned)(T * D * 2));
-        const u32x4 vrs = buffer_rsrc(vbase, (unsigned)(T * D * 2));
-        const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(a.ldc * 4));
-        const unsigned kvs_lds = lds_addr(kvs);
-        auto issue_block = [&](int X) {
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const unsigned dst = kvs_lds + (unsigned)((X % NBUF) * KVBUF);
-            const unsigned tb = (unsigned)X * CB * D * 2;
-#pragma unroll
-            for (int i = 0; i < RPW / 4; ++i) {
-                const int row = RPW * wave + 4 * i + (ln >> 4);
-                const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
-                copy16(krs, dst + (RPW * wave + 4 * i) * 256, ko);
-                copy16(vrs, dst + KVB + (RPW * wave + 4 * i) * 256, ko);
-            }
-            if (wave == 0) {
-                const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
-                copy16(crs, dst + 2 * KVB, coff + (unsigned)X * CB * 4);
-            }
-        };
-        auto copy_step = [&](int h) {
-            if (h & 1) {
-                const int X = (h + 3) >> 1;
-                if (X < nblk) issue_block(X);
-            } else {
-                wait_vm<0>();
-            }
-        };
-
-        issue_block(0);
-        if (nblk > 1) issue_block(1);
-        f32x4 acc[3][2][4];
-        state_io<false, MOM, 4>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd, 4 * hf);
-
-        const bool godd = (g & 1) != 0;
-        auto operands = [&](int c, int set) {
-            unsigned char* snap = (unsigned char*)(a.snap + (bh * nc + c) * P);
-            unsigned snap_lane = (unsigned)(j * D + 8 * g) * 2u;
-            asm volatile("" : "+v"(snap_lane));
-            unsigned char* const xs = xw + set * FS + xl;
-#pragma unroll
-            for (int m = 0; m < 3; ++m) {
-#pragma unroll
-                for (int kl = 0; kl < 2; ++kl) {
-                    const int kk = 2 * hf + kl;
-                    const bf16x4 t0 = pack4(acc[m][1][2 * kl]), t1 = pack4(acc[m][1][2 * kl + 1]);
-                    const bf16x4 lo = godd ? t1 : t0, hi = godd ? t0 : t1;
-                    bf16x8 w8;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        w8[e] = lo[e];
-                        w8[4 + e] = hi[e];
-                    }
-                    *(bf16x8*)(xs + (2 * m + kl) * 1024) = w8;
-                    *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
-                    if (SAVEM) {
-                        unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
-                        const bf16x4 s0 = pack4(acc[m][0][2 * kl]), s1 = pack4(acc[m][0][2 * kl + 1]);
-                        const bf16x4 mlo = godd ? s1 : s0, mhi = godd ? s0 : s1;
-                        bf16x8 m8;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            m8[e] = mlo[e];
-                            m8[4 + e] = mhi[e];
-                        }
-                        *(bf16x8*)(snapm + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = m8;
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        };
-        auto rescale = [&](int c) {
-            const f32x4 sc = *(const f32x4*)(a.scal + (bh * nc + c) * 4);
-            const float A = sc[0], Bb = sc[1], gamma = sc[2];
-#pragma unroll
-            for (int m = 0; m < 3; ++m) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (MOM) {
-                        const f32x4 mm = acc[m][0][i];
-                        acc[m][1][i] = A * acc[m][1][i] - gamma * mm;
-                        acc[m][0][i] = Bb * mm;
-                    } else {
-                        acc[m][1][i] = A * acc[m][1][i];
-                    }
-                }
-            }
-        };
-        // state rows += K^T F, V^T F over half-block h with the operands of
-        // factor set h % 2: (-cM a, cW a, -cM b, cW b, -cM u, cW u), without
-        // momentum (cW a, cW b, cW u)
-        auto aggregate = [&](int h) {
-            const unsigned char* kb = kvs + ((h >> 1) % NBUF) * KVBUF + (h & 1) * 32 * 256;
-            const unsigned char* fb = xw + (h & 1) * FS + xl;
-            bf16x8 f[NF];
-#pragma unroll
-            for (int x = 0; x < NF; ++x) f[x] = *(const bf16x8*)(fb + x * 1024);
-            auto frag = [&](int i, int mat) {
-                const unsigned char* p = kb + mat * KVB + (i & 1 ? te[i >> 1] + tdelta : te[i >> 1]);
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4096));
-                bf16x8 r;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    r[e] = lo[e];
-                    r[4 + e] = hi[e];
-                }
-                return r;
-            };
-            bf16x8 t = frag(0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x8 tn = i + 1 < 4 ? frag(i + 1, 0) : frag(0, 1);
-                if (MOM) {
-                    acc[0][0][i] = mfma16(t, f[0], acc[0][0][i]);
-                    acc[0][1][i] = mfma16(t, f[1], acc[0][1][i]);
-                    acc[1][0][i] = mfma16(t, f[2], acc[1][0][i]);
-                    acc[1][1][i] = mfma16(t, f[3], acc[1][1][i]);
-                } else {
-                    acc[0][1][i] = mfma16(t, f[0], acc[0][1][i]);
-                    acc[1][1][i] = mfma16(t, f[1], acc[1][1][i]);
-                }
-                t = tn;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bf16x8 tn = t;
-                if (i + 1 < 4) tn = frag(i + 1, 1);
-                if (MOM) {
-                    acc[2][0][i] = mfma16(t, f[4], acc[2][0][i]);
-                    acc[2][1][i] = mfma16(t, f[5], acc[2][1][i]);
-                } else {
-                    acc[2][1][i] = mfma16(t, f[2], acc[2][1][i]);
-                }
-                t = tn;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
-        // Slots as in the 64-unit kernel, with the chunk start in two parts.
-        // (Nested loops with unconditional state updates keep every state tile
-        // in one register tuple for the whole sequence.)
-        for (int c = 0;; ++c) {
-            const int ps = pset(c);
-            if (hf == 0) operands(c, ps ^ 1);
-            if (c == 0) wait_vm<0>();  // blocks 0 and 1 have landed
-            slot_barrier();            // chunk start, part one
-            if (hf == 1) operands(c, ps);
-            rescale(c);
-            slot_barrier();            // part two
-            copy_step(c * nh);
-            slot_barrier();            // the slot of the chunk's first half-block
-            const int nhc = halves(c);
-            for (int k = 1; k < nhc; ++k) {
-                aggregate(c * nh + k - 1);
-                copy_step(c * nh + k);
-                slot_barrier();
-            }
-            aggregate(c * nh + nhc - 1);
-            if (c + 1 == nc) break;
-        }
-        wait_vm<0>();
-        int lane_e = lane;
-        asm volatile("" : "+v"(lane_e));
-        state_io<true, MOM, 4>(acc, a.W_end + bh * P, MOM ? a.M_end + bh * P : nullptr,
-                               (int64_t)(L_id % a.nsl) * S + 16 * u + (lane_e & 15), lane_e >> 4, Hd, 4 * hf);
-    } else {
-        // ------------------------------------------------------------ gradient wave
-        const int ti = (wave - NSW) / UG;  // token rows 16 ti .. 16 ti + 15 of every half-block
-        int goff[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) goff[kk] = jl * 256 + 16 * ((4 * kk + g) ^ swz4(jl)) + 16 * ti * 256;
-
-        bf16x8 wb[3][4];  // chunk-start weights: k-slot e of lane group g is d = 32kk + 8g + e
-        auto load_half = [&](int set, int hf) {
-#pragma unroll
-            for (int m = 0; m < 3; ++m)
-#pragma unroll
-                for (int kl = 0; kl < 2; ++kl) wb[m][2 * hf + kl] = *(const bf16x8*)(xw + set * FS + (2 * m + kl) * 1024 + xl);
-        };
-        typedef f32x4 grad_acc[3];
-        typedef bf16x8 rows[4];  // K or V row fragments of this wave's 16 tokens
-        auto read_rows = [&](int h, int mat, rows& fr) {
-            const unsigned char* kb = kvs + ((h >> 1) % NBUF) * KVBUF + (h & 1) * 32 * 256 + mat * KVB;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) fr[kk] = *(const bf16x8*)(kb + goff[kk]);
-        };
-        auto mfma_k = [&](const rows& fr, grad_acc& hg, int kk0, int kk1) {
-#pragma unroll
-            for (int kk = kk0; kk < kk1; ++kk) {
-                const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-                hg[0] = mfma16(fr[kk], wb[0][kk], kk ? hg[0] : z);
-                hg[1] = mfma16(fr[kk], wb[1][kk], kk ? hg[1] : z);
-            }
-        };
-        auto mfma_v = [&](const rows& fr, grad_acc& hg, int kk0, int kk1) {
-#pragma unroll
-            for (int kk = kk0; kk < kk1; ++kk) {
-                const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-                hg[2] = mfma16(fr[kk], wb[2][kk], kk ? hg[2] : z);
-            }
-        };
-        // backward of this wave's tokens of half-block h and the scaling:
-        // a = hv h3 silu'(h1), b = hv silu(h1), u = silu(h1) h3 (hv = V W2^T =
-        // -du) times the tokens' cM and cW, into k-slots 4 ti .. 4 ti + 3 of
-        // the fragments of factor set h % 2 (k-slot e of a fragment is token
-        // 32h + 16 (e/4) + 4g + e%4, the token order of the transpose read)
-        auto backward = [&](int h, const grad_acc& hg) {
-            const float* cob = (const float*)(kvs + ((h >> 1) % NBUF) * KVBUF + 2 * KVB) + (h & 1) * 32 + 16 * ti + 4 * g;
-            const f32x4 cm = *(const f32x4*)cob, cw = *(const f32x4*)(cob + 64);
-            float fa[4], fb[4], fu[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x1 = hg[0][r], x3 = hg[1][r], y = hg[2][r];
-                const float sg = fast_sigmoid(x1);
-                const float s1 = x1 * sg;
-                const float ds = sg + s1 * (1.f - sg);
-                fa[r] = y * x3 * ds;
-                fb[r] = y * s1;
-                fu[r] = s1 * x3;
-            }
-            unsigned char* const fo = xw + (h & 1) * FS + xl + 8 * ti;
-            auto put = [&](int x, const float (&v)[4], bool mom) {
-                bf16x4 r;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = (__bf16)(mom ? -cm[e] * v[e] : cw[e] * v[e]);
-                *(bf16x4*)(fo + x * 1024) = r;
-            };
-            if (MOM) {
-                put(0, fa, true);
-                put(1, fa, false);
-                put(2, fb, true);
-                put(3, fb, false);
-                put(4, fu, true);
-                put(5, fu, false);
-            } else {
-                put(0, fa, false);
-                put(1, fb, false);
-                put(2, fu, false);
-            }
-        };
-        for (int c = 0; c < nc; ++c) {
-            const int ps = pset(c);
-            grad_acc hg;
-            slot_barrier();  // chunk start, part one: the first state half's operands
-            load_half(ps ^ 1, 0);
-            {
-                rows fk, fv;
-                read_rows(c * nh, 0, fk);
-                read_rows(c * nh, 1, fv);
-                mfma_k(fk, hg, 0, 2);
-                mfma_v(fv, hg, 0, 2);
-                slot_barrier();  // part two: the second half's
-                load_half(ps, 1);
-                mfma_k(fk, hg, 2, 4);
-                mfma_v(fv, hg, 2, 4);
-            }
-            const int nhc = halves(c);
-            for (int k = 0; k + 1 < nhc; ++k) {
-                const int hh = c * nh + k;
-                // the next half-block's grad MFMAs with this one's backward
-                // slotted in between
-                grad_acc hn;
-                {
-                    rows fk, fv;
-                    read_rows(hh + 1, 0, fk);
-                    read_rows(hh + 1, 1, fv);
-                    mfma_k(fk, hn, 0, 4);
-                    mfma_v(fv, hn, 0, 4);
-                }
-                backward(hh, hg);
-                constexpr int VPM = 7;  // VALU instructions slotted between two MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads: K and V rows
-#pragma unroll
-                for (int q = 0; q < 12; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-                slot_barrier();
-#pragma unroll
-                for (int m = 0; m < 3; ++m) hg[m] = hn[m];
-            }
-            backward(c * nh + nhc - 1, hg);
-            slot_barrier();
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Small grids with one 16-unit group per workgroup: block slots.  Every
+// Small grids (16- or 32-unit slices that all fit on the chip at once): block
+// slots.  When the grid leaves compute units idle, a slot's length is the
+// latency of one wavefront's chain, not the chip's throughput.  Every
 // gradient of a chunk is taken at the chunk-start weights, so the tokens of a
 // chunk need no order among themselves; only the aggregation into the state
 // has to finish before the chunk boundary.  This kernel gives each slot a
-// whole 64-token block and twice the wavefronts of the split-role kernel, two
-// per SIMD, so a chunk of C tokens takes C/64 + 1 slots instead of C/32 + 1:
-//   state wave hf (wave hf, hf = 0..3): rows d = 32 hf .. 32 hf + 31 of the
+// whole 64-token block and each 16-unit group eight wavefronts, so a chunk of
+// C tokens takes C/64 + 1 slots (the 64-unit kernel: C/32 + 1).  Per unit
+// group u (UG groups per workgroup, two or four wavefronts per SIMD):
+//   state wave hf (wave 8u + hf, hf = 0..3): rows d = 32 hf .. 32 hf + 31 of the
 //       group's six state matrices (tiles 2 hf, 2 hf + 1: 48 accumulator
 //       registers); per block 24 MFMAs (12 without momentum) of K^T F and V^T F
 //       over the block's two half-blocks; it also issues the HBM -> LDS copies;
-//   gradient wave ti (wave 4 + ti): tokens 16 ti .. 16 ti + 15 of every
+//   gradient wave ti (wave 8u + 4 + ti): tokens 16 ti .. 16 ti + 15 of every
 //       block: H1, H3, HV (12 MFMAs), the backward and the scaling by the
 //       tokens' coefficients in fp32, written into its quarter of the block's
 //       factor set.
@@ -1089,10 +725,12 @@ swiglu_loop_sg_kernel(LoopArgs a) {
 // work on X and the state waves' aggregation of block X - 1; a chunk's first
 // slot holds the state waves' rescale instead, and a boundary slot after the
 // chunk's last block holds the aggregation of that block and the hand-over.
-// Four LDS blocks: block X + 2 is copied during the slot of block X, into the
-// buffer block X - 2 left (its last reader, the state waves, finished in the
-// slot before), and waited for at the end of the slot of block X + 1, so
-// each copy has two slots to land.
+// One unit group: four LDS blocks; block X + 2 is copied during the slot of
+// block X, into the buffer block X - 2 left (its last reader, the state
+// waves, finished in the slot before), and waited for at the end of the slot
+// of block X + 1, so each copy has two slots to land.  Two unit groups (their
+// own factor sets, the token blocks shared): three LDS blocks, block X + 1
+// copied during the slot of block X and waited for at its end.
 //
 // Hand-over: at a chunk boundary each state wave writes the operand
 // fragments of its rows of d (k-step hf of every matrix) and stores the
@@ -1102,8 +740,9 @@ swiglu_loop_sg_kernel(LoopArgs a) {
 // loaded them; without momentum they have an area of their own, and the
 // same barrier is kept so that both forms share one schedule.
 //
-// LDS: four 64-token blocks with their coefficients (132 KB), two factor sets
-// (24 KB, or 12 KB and the 12 KB operand area without momentum).
+// LDS: four (one group) or three (two groups) 64-token blocks with their
+// coefficients, 33 KB each; per unit group two factor sets (24 KB, or 12 KB
+// and the 12 KB operand area without momentum): 156 KB or 147 KB.
 template <bool MOM, bool SAVEM, int UG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512 * UG, 512 * UG), amdgpu_waves_per_eu(2 * UG, 2 * UG)))
 swiglu_loop_bs_kernel(LoopArgs a) {
@@ -1431,9 +1070,9 @@ swiglu_loop_bs_kernel(LoopArgs a) {
 
 // Smaller slices only while their grid still fits on the chip at once: a
 // slot takes about as long either way, so a second round of workgroups would
-// cost more than the smaller slices gain.  16-unit slices take the
-// block-slot kernel (eight wavefronts on one unit group, a 64-token block per
-// slot), 32-unit slices the split-role kernel.
+// cost more than the smaller slices gain.  16- and 32-unit slices take the
+// block-slot kernel (eight wavefronts per unit group, a 64-token block per
+// slot).
 static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
     if (BH * (Hd / 16) <= ncu) return 1;
     return BH * (Hd / 32) <= ncu ? 2 : 4;
@@ -1471,18 +1110,8 @@ hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v,
     la.nsl = (int)(d.Hd / (16 * ug));
     la.nwg = (int)(BH * la.nsl);
     la.xcd_map = (la.nwg % 8 == 0) ? 1 : 0;
-    if (!pre && ug <= 2) {  // small grids: split roles over four wavefronts per 16-unit group
+    if (!pre && ug <= 2) {  // small grids: block slots, 16- or 32-unit slices
         const bool nm = (d.flags & E2TTT_FLAG_NO_MOMENTUM) != 0;
-        auto go_sg = [&](auto UGc) {
-            constexpr int U = decltype(UGc)::value;
-            const dim3 g1((unsigned)la.nwg), b1(256 * U);
-            if (nm)
-                hipLaunchKernelGGL((swiglu_loop_sg_kernel<false, false, U>), g1, b1, 0, s, la);
-            else if (snapM)
-                hipLaunchKernelGGL((swiglu_loop_sg_kernel<true, true, U>), g1, b1, 0, s, la);
-            else
-                hipLaunchKernelGGL((swiglu_loop_sg_kernel<true, false, U>), g1, b1, 0, s, la);
-        };
         // block slots: eight wavefronts per 16-unit group, a 64-token block per slot
         auto go_bs = [&](auto UGc) {
             constexpr int U = decltype(UGc)::value;
