@@ -132,7 +132,7 @@ static int backward_path(const e2ttt_desc& d) {
 }
 
 struct BwdWorkspace {
-    size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, split, total;
+    size_t cM, cW, scal, snapW, snapM, lamW, lamM, lam, inter, dcM, dcW, dpart, part, split, total;
     size_t save, gacc;  // portable path: chunk-start states, forward G accumulators / dJ/dW
     int64_t ldc;
 };
@@ -187,6 +187,7 @@ static BwdWorkspace bwd_workspace_layout(const e2ttt_desc& d) {
     w.dcM = take(BH * ldc * 4);
     w.dcW = take(BH * ldc * 4);
     w.dpart = take(BH * nc * (size_t)(d.Hd / 64) * 4 * 4);
+    w.part = take((size_t)swiglu_bwd_part_elems(d, w.ldc) * 4);
     w.total = (BH * (size_t)d.T == 0) ? 0 : off;
     return w;
 }
@@ -560,6 +561,7 @@ int e2ttt_chunk_backward_events(const e2ttt_desc* d, const void* q, const void* 
     b.dcM = (float*)(wsb + ws.dcM);
     b.dcW = (float*)(wsb + ws.dcW);
     b.dpart = (float*)(wsb + ws.dpart);
+    b.part = swiglu_bwd_part_elems(*d, ws.ldc) > 0 ? (float*)(wsb + ws.part) : nullptr;
     b.dq = dq;
     b.dk = dk;
     b.dv = dv;

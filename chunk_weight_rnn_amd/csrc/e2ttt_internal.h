@@ -80,6 +80,7 @@ struct BwdBuffers {
     void* inter;                       // [BH][6][Hd][chunk] bf16 per-chunk terms
     float *dcM, *dcW;                  // [BH][ldc]
     float* dpart;                      // [BH][nc][Hd/64][4]
+    float* part;                       // swiglu_bwd_part_elems floats (null when that is 0)
     void *dq, *dk, *dv;                // [BH][T][D] bf16
     float *deta, *dalpha, *dbeta;      // [BH][T]
     float *dW0, *dM0;                  // [BH][P]
@@ -89,6 +90,9 @@ struct BwdBuffers {
 // scalar kernels' backward.
 hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipStream_t s, hipEvent_t ev_loop);
 int64_t swiglu_bwd_inter_elems(const e2ttt_desc& d);  // per (b, h)
+// token-kernel hidden-unit parts (1, 2 or 4) and the fp32 partial sums they need
+int swiglu_bwd_unit_parts(const e2ttt_desc& d);
+int64_t swiglu_bwd_part_elems(const e2ttt_desc& d, int64_t ldc);
 
 // Scalar kernels' backward: d eta, d alpha, d beta from dcM, dcW (per token)
 // and the partial dA, dBb, dgamma in dpart [BH][nc][nsl][4].

@@ -208,8 +208,10 @@ struct TokArgs {
     __bf16* inter;                   // [BH][6][Hd][C]: F1, F3, -E, dhq1, dhq3, uq
     __bf16 *dq, *dk, *dv;            // [BH][T][D]
     float *dcM, *dcW;                // [BH][ldc]
-    int64_t T, ldc;
+    float* part;                     // U > 1: [U][3][BH][T][D] dk, dv, dq and [U][2][BH][ldc] dcM, dcW partial sums
+    int64_t T, ldc, BH;
     int Hd, C, nc, c, nb;            // nb: 64-token blocks of chunk c
+    int U;                           // parts of the hidden units, one workgroup each
     int nwg, xcd_map;
 };
 
@@ -221,8 +223,9 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tl = lane & 15, g = lane >> 4;
     const int lid = xcd_remap(a.nwg, a.xcd_map);
-    const int64_t bh = lid / a.nb;
-    const int blk = lid % a.nb;
+    const int64_t bh = lid / (a.nb * a.U);
+    const int blk = (lid / a.U) % a.nb;
+    const int part = lid % a.U;  // hidden units part * Hd / U .. of the head
     const int64_t T = a.T;
     const int Hd = a.Hd;
     const int64_t P = 3 * (int64_t)D * Hd;
@@ -275,7 +278,24 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
             }
         }
     };
-    const int nsteps = Hd / US;
+    const int nsteps = Hd / a.U / US;
+    const int jp = part * (Hd / a.U);  // the workgroup's first hidden unit
+    // with U > 1 the sums over hidden units (dk, dv, dq, dcM, dcW) leave as
+    // fp32 partial sums of this part, added up in a fixed order afterwards
+    const int64_t BHTD = a.BH * T * D;
+    float* const ptok = a.part + (int64_t)part * 3 * BHTD;
+    float* const pdc = a.part + (int64_t)a.U * 3 * BHTD + (int64_t)part * 2 * a.BH * a.ldc;
+    auto part_tok = [&](int which, const f32x4 (&acc)[8]) {
+        float* const X = ptok + which * BHTD;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t tt = tc0 + 4 * g + r;
+            if (tt < T) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) X[(bh * T + tt) * D + 16 * n + tl] = acc[n][r];
+            }
+        }
+    };
 
     // ---------------- pass A: k / v side (needs W_c and the cotangents)
     {
@@ -288,13 +308,13 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) dk[n] = dv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         float sM = 0.f, sW = 0.f;
-        issue(0, 0, nmat);
+        issue(jp, 0, nmat);
         for (int js = 0; js < nsteps; ++js) {
             wait_stage(js);
             barrier_lds();
-            if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, nmat);
+            if (js + 1 < nsteps) issue(jp + US * (js + 1), (js + 1) & 1, nmat);
             const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
-            const int j0 = US * js;
+            const int j0 = jp + US * js;
             f32x4 pr[NMAT];
 #pragma unroll
             for (int mi = 0; mi < nmat; ++mi) pr[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -367,8 +387,13 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        store_tok(a.dk, dk);
-        store_tok(a.dv, dv);
+        if (a.U == 1) {
+            store_tok(a.dk, dk);
+            store_tok(a.dv, dv);
+        } else {
+            part_tok(0, dk);
+            part_tok(1, dv);
+        }
         sW += __shfl_xor(sW, 16);
         sW += __shfl_xor(sW, 32);
         if (MOM) {
@@ -377,8 +402,10 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
         }
         if (g == 0) {
             const int64_t o = bh * a.ldc + (int64_t)a.c * a.C + tcl;
-            a.dcW[o] = sW;
-            if (MOM) a.dcM[o] = sM;
+            float* const dcw = a.U == 1 ? a.dcW : pdc + a.BH * a.ldc;
+            float* const dcm = a.U == 1 ? a.dcM : pdc;
+            dcw[o] = sW;
+            if (MOM) dcm[o] = sM;
         }
     }
     barrier_lds();  // every wave is done with the stage buffers
@@ -391,13 +418,13 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
         f32x4 dq[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        issue(0, 0, 3);
+        issue(jp, 0, 3);
         for (int js = 0; js < nsteps; ++js) {
             wait_stage(js);
             barrier_lds();
-            if (js + 1 < nsteps) issue(US * (js + 1), (js + 1) & 1, 3);
+            if (js + 1 < nsteps) issue(jp + US * (js + 1), (js + 1) & 1, 3);
             const unsigned char* sb = stage + (js & 1) * NMAT * STEPB;
-            const int j0 = US * js;
+            const int j0 = jp + US * js;
             f32x4 pr[3];
 #pragma unroll
             for (int mi = 0; mi < 3; ++mi) pr[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -431,7 +458,45 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
                 if (n & 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        store_tok(a.dq, dq);
+        if (a.U == 1)
+            store_tok(a.dq, dq);
+        else
+            part_tok(2, dq);
+    }
+}
+
+// The U parts' partial sums of one chunk loop, added in part order: dk, dv,
+// dq to bf16, dcM and dcW (the padded rows too) in fp32.
+struct ReduceArgs {
+    const float* part;
+    __bf16 *dk, *dv, *dq;
+    float *dcM, *dcW;
+    int64_t BHTD, BHL;  // B*H*T*D, B*H*ldc
+    int U, mom;
+};
+
+__global__ void __launch_bounds__(256) bwd_part_reduce_kernel(ReduceArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = 3 * a.BHTD / 4;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const int which = (int)(i / (a.BHTD / 4));
+        const int64_t e = 4 * (i - which * (a.BHTD / 4));
+        f32x4 sum = *(const f32x4*)(a.part + which * a.BHTD + e);
+        for (int u = 1; u < a.U; ++u) sum += *(const f32x4*)(a.part + ((int64_t)u * 3 + which) * a.BHTD + e);
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (__bf16)sum[r];
+        __bf16* const dst = which == 0 ? a.dk : which == 1 ? a.dv : a.dq;
+        *(bf16x4*)(dst + e) = o;
+    }
+    const float* const pdc = a.part + (int64_t)a.U * 3 * a.BHTD;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < 2 * a.BHL; i += stride) {
+        const int which = (int)(i / a.BHL);  // 0: dcM, 1: dcW
+        if (which == 0 && !a.mom) continue;
+        const int64_t e = i - which * a.BHL;
+        float sum = pdc[which * a.BHL + e];
+        for (int u = 1; u < a.U; ++u) sum += pdc[((int64_t)u * 2 + which) * a.BHL + e];
+        (which == 0 ? a.dcM : a.dcW)[e] = sum;
     }
 }
 
@@ -895,6 +960,24 @@ __global__ void __launch_bounds__(64) bwd_scalar_kernel(ScalArgs a) {
 
 int64_t swiglu_bwd_inter_elems(const e2ttt_desc& d) { return (int64_t)NQ * d.Hd * d.chunk; }
 
+// Parts of the hidden units in the token kernel: a head's chunk gives
+// B·H·(chunk/64) workgroups; small grids split each one's hidden units over
+// 2 or 4 workgroups (shorter chains, more of the 256 compute units busy).
+int swiglu_bwd_unit_parts(const e2ttt_desc& d) {
+    const int64_t span = d.chunk < d.T ? d.chunk : d.T;
+    const int64_t wg = d.B * d.H * ((span + TB - 1) / TB);
+    if (wg * 4 <= 256 && d.Hd % (4 * US) == 0) return 4;
+    if (wg * 2 <= 256 && d.Hd % (2 * US) == 0) return 2;
+    return 1;
+}
+
+int64_t swiglu_bwd_part_elems(const e2ttt_desc& d, int64_t ldc) {
+    const int U = swiglu_bwd_unit_parts(d);
+    if (U == 1) return 0;
+    const int64_t BH = d.B * d.H;
+    return (int64_t)U * (3 * BH * d.T * D + 2 * BH * ldc);
+}
+
 hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipStream_t s, hipEvent_t ev_loop) {
     const int64_t BH = d.B * d.H;
     const bool mom = !(d.flags & E2TTT_FLAG_NO_MOMENTUM);
@@ -902,6 +985,8 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
     const int nc = (int)((d.T + d.chunk - 1) / d.chunk);
     const int nsl = Hd / WS;
     const int nx = mom ? 2 : 1;
+    const int U = swiglu_bwd_unit_parts(d);
+    if (U > 1 && !b.part) return hipErrorInvalidValue;
     {  // working copy and bf16 copies of dW_end, dM_end
         LayoutArgs la{b.dW_end, b.dM_end, b.lamW, b.lamM, (__bf16*)b.lam, Hd, nsl, nx};
         hipLaunchKernelGGL(bwd_layout_kernel<true>, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, la);
@@ -925,14 +1010,17 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
         ta.dv = (__bf16*)b.dv;
         ta.dcM = b.dcM;
         ta.dcW = b.dcW;
+        ta.part = b.part;
         ta.T = d.T;
         ta.ldc = b.ldc;
+        ta.BH = BH;
         ta.Hd = Hd;
         ta.C = C;
         ta.nc = nc;
         ta.c = c;
         ta.nb = nb;
-        ta.nwg = (int)(BH * nb);
+        ta.U = U;
+        ta.nwg = (int)(BH * nb * U);
         ta.xcd_map = ta.nwg % 8 == 0 ? 1 : 0;
         if (mom)
             hipLaunchKernelGGL(bwd_tok_kernel<true>, dim3((unsigned)ta.nwg), dim3(NT), 0, s, ta);
@@ -970,6 +1058,12 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
     {  // chunk 0's state cotangents -> packed dW0, dM0
         LayoutArgs la{b.lamW, b.lamM, b.dW0, b.dM0, nullptr, Hd, nsl, nx};
         hipLaunchKernelGGL(bwd_layout_kernel<false>, dim3((unsigned)(BH * nx * nsl)), dim3(NT), 0, s, la);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    if (U > 1) {  // the parts' dk, dv, dq, dcM, dcW
+        ReduceArgs ra{b.part, (__bf16*)b.dk, (__bf16*)b.dv, (__bf16*)b.dq, b.dcM, b.dcW, BH * d.T * D, BH * b.ldc, U,
+                      mom ? 1 : 0};
+        hipLaunchKernelGGL(bwd_part_reduce_kernel, dim3(1024), dim3(256), 0, s, ra);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
