@@ -208,7 +208,7 @@ struct TokArgs {
     __bf16* inter;                   // [BH][6][Hd][C]: F1, F3, -E, dhq1, dhq3, uq
     __bf16 *dq, *dk, *dv;            // [BH][T][D]
     float *dcM, *dcW;                // [BH][ldc]
-    float* part;                     // U > 1: [U][3][BH][T][D] dk, dv, dq and [U][2][BH][ldc] dcM, dcW partial sums
+    float* part;                     // U > 1: [3][BH][T][U][D] dk, dv, dq and [2][BH][ldc][U] dcM, dcW partial sums
     int64_t T, ldc, BH;
     int Hd, C, nc, c, nb;            // nb: 64-token blocks of chunk c
     int U;                           // parts of the hidden units, one workgroup each
@@ -282,17 +282,17 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
     const int jp = part * (Hd / a.U);  // the workgroup's first hidden unit
     // with U > 1 the sums over hidden units (dk, dv, dq, dcM, dcW) leave as
     // fp32 partial sums of this part, added up in a fixed order afterwards
-    const int64_t BHTD = a.BH * T * D;
-    float* const ptok = a.part + (int64_t)part * 3 * BHTD;
-    float* const pdc = a.part + (int64_t)a.U * 3 * BHTD + (int64_t)part * 2 * a.BH * a.ldc;
+    // (the U parts of one row side by side, so that the sum reads one stream)
+    const int64_t BHTDU = a.BH * T * D * a.U;
+    float* const pdc = a.part + 3 * BHTDU + part;  // [2][BH][ldc][U]
     auto part_tok = [&](int which, const f32x4 (&acc)[8]) {
-        float* const X = ptok + which * BHTD;
+        float* const X = a.part + which * BHTDU + (int64_t)part * D;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t tt = tc0 + 4 * g + r;
             if (tt < T) {
 #pragma unroll
-                for (int n = 0; n < 8; ++n) X[(bh * T + tt) * D + 16 * n + tl] = acc[n][r];
+                for (int n = 0; n < 8; ++n) X[(bh * T + tt) * a.U * D + 16 * n + tl] = acc[n][r];
             }
         }
     };
@@ -402,10 +402,13 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
         }
         if (g == 0) {
             const int64_t o = bh * a.ldc + (int64_t)a.c * a.C + tcl;
-            float* const dcw = a.U == 1 ? a.dcW : pdc + a.BH * a.ldc;
-            float* const dcm = a.U == 1 ? a.dcM : pdc;
-            dcw[o] = sW;
-            if (MOM) dcm[o] = sM;
+            if (a.U == 1) {
+                a.dcW[o] = sW;
+                if (MOM) a.dcM[o] = sM;
+            } else {
+                pdc[(a.BH * a.ldc + o) * a.U] = sW;
+                if (MOM) pdc[o * a.U] = sM;
+            }
         }
     }
     barrier_lds();  // every wave is done with the stage buffers
@@ -465,10 +468,10 @@ __global__ void __launch_bounds__(NT) bwd_tok_kernel(TokArgs a) {
     }
 }
 
-// The U parts' partial sums of one chunk loop, added in part order: dk, dv,
+// The U parts' partial sums of the reverse loop, added in part order: dk, dv,
 // dq to bf16, dcM and dcW (the padded rows too) in fp32.
 struct ReduceArgs {
-    const float* part;
+    const float* part;  // [3][BH][T][U][D], then [2][BH][ldc][U]
     __bf16 *dk, *dv, *dq;
     float *dcM, *dcW;
     int64_t BHTD, BHL;  // B*H*T*D, B*H*ldc
@@ -477,26 +480,30 @@ struct ReduceArgs {
 
 __global__ void __launch_bounds__(256) bwd_part_reduce_kernel(ReduceArgs a) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t n4 = 3 * a.BHTD / 4;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const int which = (int)(i / (a.BHTD / 4));
-        const int64_t e = 4 * (i - which * (a.BHTD / 4));
-        f32x4 sum = *(const f32x4*)(a.part + which * a.BHTD + e);
-        for (int u = 1; u < a.U; ++u) sum += *(const f32x4*)(a.part + ((int64_t)u * 3 + which) * a.BHTD + e);
-        bf16x4 o;
+    const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (__bf16)sum[r];
+    for (int which = 0; which < 3; ++which) {
+        const float* const src = a.part + which * a.BHTD * a.U;
         __bf16* const dst = which == 0 ? a.dk : which == 1 ? a.dv : a.dq;
-        *(bf16x4*)(dst + e) = o;
+        for (int64_t e = 4 * i0; e < a.BHTD; e += 4 * stride) {
+            const float* const p = src + (e / D) * a.U * D + e % D;  // row e / D, columns e % D .. + 3
+            f32x4 sum = *(const f32x4*)p;
+            for (int u = 1; u < a.U; ++u) sum += *(const f32x4*)(p + u * D);
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)sum[r];
+            *(bf16x4*)(dst + e) = o;
+        }
     }
-    const float* const pdc = a.part + (int64_t)a.U * 3 * a.BHTD;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < 2 * a.BHL; i += stride) {
-        const int which = (int)(i / a.BHL);  // 0: dcM, 1: dcW
-        if (which == 0 && !a.mom) continue;
-        const int64_t e = i - which * a.BHL;
-        float sum = pdc[which * a.BHL + e];
-        for (int u = 1; u < a.U; ++u) sum += pdc[((int64_t)u * 2 + which) * a.BHL + e];
-        (which == 0 ? a.dcM : a.dcW)[e] = sum;
+    const float* const pdc = a.part + 3 * a.BHTD * a.U;
+    for (int which = a.mom ? 0 : 1; which < 2; ++which) {  // 0: dcM, 1: dcW
+        float* const dst = which == 0 ? a.dcM : a.dcW;
+        for (int64_t e = i0; e < a.BHL; e += stride) {
+            const float* const p = pdc + (which * a.BHL + e) * a.U;
+            float sum = p[0];
+            for (int u = 1; u < a.U; ++u) sum += p[u];
+            dst[e] = sum;
+        }
     }
 }
 
@@ -1063,7 +1070,7 @@ hipError_t launch_swiglu_backward(const e2ttt_desc& d, const BwdBuffers& b, hipS
     if (U > 1) {  // the parts' dk, dv, dq, dcM, dcW
         ReduceArgs ra{b.part, (__bf16*)b.dk, (__bf16*)b.dv, (__bf16*)b.dq, b.dcM, b.dcW, BH * d.T * D, BH * b.ldc, U,
                       mom ? 1 : 0};
-        hipLaunchKernelGGL(bwd_part_reduce_kernel, dim3(1024), dim3(256), 0, s, ra);
+        hipLaunchKernelGGL(bwd_part_reduce_kernel, dim3(4096), dim3(256), 0, s, ra);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (ev_loop && hipEventRecord(ev_loop, s) != hipSuccess) return hipErrorLaunchFailure;
