@@ -68,7 +68,20 @@ struct ApplyArgs {
     int64_t T;
     int Hd, C, nc, rbc;  // rbc: items per chunk
     int nb;              // B H
+    int hord;            // 1: the chunk loop placed heads by XCD (B H a multiple of 8), see apply_head
 };
+
+// The head of the output kernels' r-th group of items.  Heads are visited in
+// the reverse of the order in which the chunk loop's workgroups were
+// dispatched, so that the snapshots written last are read first, while the
+// 256 MB last-level cache may still hold them.  With B H a multiple of 8 the
+// loop places the slices of head x (B H / 8) + i on XCD x and dispatches the
+// heads in the order (i, x); otherwise in head order (a permutation either
+// way: only the cache hits depend on it).
+__device__ __forceinline__ int64_t apply_head(int64_t r, int64_t BH, int hord) {
+    const int64_t n = BH - 1 - r;  // the head's dispatch rank in the chunk loop
+    return hord ? (n % 8) * (BH / 8) + n / 8 : n;
+}
 
 constexpr int HB = 32;                     // hidden units per stage
 constexpr int STAGE_BYTES = 3 * HB * 256;  // W1^T, W3^T, W2 rows of the stage
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_kernel(ApplyArgs a) {
         const int64_t x = blockIdx.x + (int64_t)k * gridDim.x;
         const bool ok = k < nmine;
         const int64_t xx = ok ? x : 0;
-        const int64_t bh = xx / ((int64_t)a.nc * a.rbc);
+        const int64_t bh = apply_head(xx / ((int64_t)a.nc * a.rbc), a.nb, a.hord);
         const int rem = (int)(xx % ((int64_t)a.nc * a.rbc));
         const int c = rem / a.rbc, rb = rem % a.rbc;
         it.sn = a.snap + (bh * a.nc + c) * P;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(64 * NWA) void swiglu_apply_h256_kernel(ApplyArgs a
         const int64_t x = blockIdx.x + (int64_t)k * gridDim.x;
         const bool ok = k < nmine;
         const int64_t xx = ok ? x : 0;
-        const int64_t bh = xx / ((int64_t)a.nc * a.rbc);
+        const int64_t bh = apply_head(xx / ((int64_t)a.nc * a.rbc), a.nb, a.hord);
         const int rem = (int)(xx % ((int64_t)a.nc * a.rbc));
         const int c = rem / a.rbc, rb = rem % a.rbc;
         it.sn = a.snap + (bh * a.nc + c) * P;
@@ -606,6 +619,7 @@ hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k,
     aa.C = (int)d.chunk;
     aa.nc = (int)((d.T + d.chunk - 1) / d.chunk);  // the last chunk may be shorter
     aa.nb = (int)BH;
+    aa.hord = (BH % 8 == 0) ? 1 : 0;  // the loop's XCD placement (its grid is then a multiple of 8)
     // persistent grid: as many workgroups as the compute units hold at once
     int ncu = 0;
     if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
