@@ -39,36 +39,40 @@ def _hilo_sum(x):
     return hi + _rb(x - hi)
 
 
-def swiglu_bf16_path(cfg, x, precise: bool = False, factors_rounded: bool = False):
+def swiglu_bf16_path(cfg, x, precise: bool = False, factors_rounded: bool = False, hilo_grad=()):
     """(out, W_end, M_end) of the bf16 MFMA path's rounding model for one
-    SwiGLU / negative-dot workload with whole chunks (T % chunk == 0).
+    SwiGLU / negative-dot workload (a shorter last chunk when T % chunk != 0).
     factors_rounded: the factors a, b, u are rounded to bf16 before the
     coefficient scaling as well as after it (a form of the chunk loop that
     handed them over in bf16); otherwise they are scaled in fp32 and rounded
-    once."""
+    once.  hilo_grad: names among "W1", "W3", "W2" whose grad operand is a
+    hi/lo pair while the rest of the path stays bf16 (precise: all of them,
+    and the aggregation operands too)."""
     D, Hd, C, T, B, H = cfg.D, cfg.Hd, cfg.chunk, cfg.T, cfg.B, cfg.H
-    assert T % C == 0
     op = _hilo_sum if precise else _rb
+    gop = {name: (_hilo_sum if (precise or name in hilo_grad) else _rb) for name in ("W1", "W3", "W2")}
     q, k, v = (x[n].double() for n in ("q", "k", "v"))
     W = x["W0"].double().clone()
     M = x["M0"].double().clone()
-    nc, n = T // C, D * Hd
-    a = x["alpha"].double().numpy().reshape(B, H, nc, C)
-    bt = x["beta"].double().numpy().reshape(B, H, nc, C)
-    e = x["eta"].double().numpy().reshape(B, H, nc, C)
-    m, w, A, Bb, gamma = oracle.chunk_coefficients(a, bt)
+    n = D * Hd
     f32 = lambda y: torch.from_numpy(np.asarray(y, dtype=np.float32)).double()
-    cM, cW, A, Bb, gamma = f32(m * e), f32(w * e), f32(A), f32(Bb), f32(gamma)
     out = torch.zeros(B, H, T, D, dtype=torch.float64)
-    for c in range(nc):
-        sl = slice(c * C, (c + 1) * C)
+    for c0 in range(0, T, C):
+        L = min(C, T - c0)
+        sl = slice(c0, c0 + L)
+        # the chunk's scalar kernels (oracle), rounded to fp32 as the scan kernel writes them
+        g = lambda name: x[name][:, :, sl].double().numpy().reshape(B, H, 1, L)
+        m, w, A, Bb, gamma = oracle.chunk_coefficients(g("alpha"), g("beta"))
+        e = g("eta")
+        cM, cW = f32(m * e)[:, :, 0], f32(w * e)[:, :, 0]
+        A, Bb, gamma = f32(A)[:, :, 0], f32(Bb)[:, :, 0], f32(gamma)[:, :, 0]
         W1 = W[..., :n].reshape(B, H, D, Hd)
         W3 = W[..., n:2 * n].reshape(B, H, D, Hd)
         W2 = W[..., 2 * n:].reshape(B, H, Hd, D)
         K, V, Q = k[:, :, sl], v[:, :, sl], q[:, :, sl]
         # grad products at the chunk-start weights and the factors
-        h1, h3 = K @ op(W1), K @ op(W3)
-        hv = V @ op(W2).transpose(-1, -2)
+        h1, h3 = K @ gop["W1"](W1), K @ gop["W3"](W3)
+        hv = V @ gop["W2"](W2).transpose(-1, -2)
         sg = torch.sigmoid(h1)
         s1 = h1 * sg
         ds = sg + s1 * (1 - sg)
@@ -79,10 +83,10 @@ def swiglu_bf16_path(cfg, x, precise: bool = False, factors_rounded: bool = Fals
         x1, x3 = Q @ _rb(W1), Q @ _rb(W3)
         out[:, :, sl] = _rb(_rb(x1 * torch.sigmoid(x1) * x3) @ _rb(W2))
         # transition with the old momentum, then the scaled aggregations
-        cm, cw = cM[:, :, c, :, None], cW[:, :, c, :, None]
+        cm, cw = cM[..., None], cW[..., None]
         Mold = M
-        W = A[:, :, c, None] * W - gamma[:, :, c, None] * Mold
-        M = Bb[:, :, c, None] * Mold
+        W = A[..., None] * W - gamma[..., None] * Mold
+        M = Bb[..., None] * Mold
         Kt, Vt = K.transpose(-1, -2), V.transpose(-1, -2)
         gM = [Kt @ op(-cm * fa), Kt @ op(-cm * fb), (Vt @ op(-cm * fu)).transpose(-1, -2)]
         gW = [Kt @ op(cw * fa), Kt @ op(cw * fb), (Vt @ op(cw * fu)).transpose(-1, -2)]
