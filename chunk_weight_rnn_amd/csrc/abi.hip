@@ -364,14 +364,17 @@ int e2ttt_chunk_forward_events(const e2ttt_desc* d, const void* q, const void* k
     if (events)
         for (int i = 0; i < 4; ++i) ev[i] = (hipEvent_t)events[i];
     if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return E2TTT_ERR_HIP;
-    if (launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
+    // the SwiGLU chunk loop computes the scalar kernels itself where it can
+    const bool fold = (path == 1 || path == 2) && swiglu_loop_scans(*d);
+    if (!fold &&
+        launch_logscan(BH, d->T, d->chunk, d->flags, eta, alpha, beta, cM, cW, ws.ldc, scal, s) != hipSuccess)
         return E2TTT_ERR_HIP;
     if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return E2TTT_ERR_HIP;
     hipError_t e;
     const bool mom = !(d->flags & E2TTT_FLAG_NO_MOMENTUM);
     if (path == 1 || path == 2) {
         e = launch_swiglu_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, wsb + ws.snap,
-                               save && mom ? wsb + bws.snapM : nullptr, s, ev[2]);
+                               save && mom ? wsb + bws.snapM : nullptr, s, ev[2], eta, alpha, beta, fold);
     } else if (path == 3 || path == 4) {
         e = launch_f32_mfma(*d, q, k, v, cM, cW, ws.ldc, scal, W0, M0, out, W_end, M_end, s,
                             save ? (float*)(wsb + bws.save) : nullptr, wsb + ws.split);

@@ -58,15 +58,21 @@ bool swiglu_mfma_supported(const e2ttt_desc& d);
 // Chunk loop of the SwiGLU path: final state and the bf16 chunk-start weight
 // snapshots [BH][nc][W1^T | W3^T | W2] (each [Hd][D]); with snapM non-null
 // (momentum only) also the chunk-start momentum snapshots in the same layout.
+// With fold the loop writes cM, cW and scal itself from eta, alpha, beta
+// (no separate launch_logscan before it); only where swiglu_loop_scans(d).
+bool swiglu_loop_scans(const e2ttt_desc& d);
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
-                              void* snap, void* snapM, hipStream_t s);
+                              void* snap, void* snapM, hipStream_t s, const float* eta = nullptr,
+                              const float* alpha = nullptr, const float* beta = nullptr, bool fold = false);
 // ev_mid (may be null) is recorded between the chunk-loop and output launches;
-// snapM (may be null) receives the momentum snapshots.
+// snapM (may be null) receives the momentum snapshots; fold as for
+// launch_swiglu_loop.
 hipError_t launch_swiglu_mfma(const e2ttt_desc& d, const void* q, const void* k, const void* v,
                               const float* cM, const float* cW, int64_t ldc, const float* scal, const float* W0,
                               const float* M0, void* out, float* W_end, float* M_end, void* snap, void* snapM,
-                              hipStream_t s, hipEvent_t ev_mid);
+                              hipStream_t s, hipEvent_t ev_mid, const float* eta = nullptr,
+                              const float* alpha = nullptr, const float* beta = nullptr, bool fold = false);
 
 // Backward pass of the SwiGLU path (same shape support, chunk <= 2048).
 struct BwdBuffers {

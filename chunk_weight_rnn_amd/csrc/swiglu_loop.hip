@@ -60,6 +60,7 @@
 #include <type_traits>
 
 #include "e2ttt_internal.h"
+#include "scan_wave.h"
 
 namespace e2ttt {
 namespace {
@@ -184,6 +185,12 @@ struct LoopArgs {
     int64_t T;
     int64_t ldc;  // row stride of cM / cW (T rounded up to a whole block, zero padded)
     int Hd, C, nc, nsl, nwg, xcd_map;
+    // fold: the 64-unit kernel computes the scalar kernels itself (cM, cW,
+    // scal from eta, alpha, beta) before its first slot, instead of a separate
+    // scan launch before it (two more workgroup barriers); avg:
+    // chunk-averaged kernels
+    const float *eta, *alpha, *beta;
+    int fold, avg;
 };
 
 // State tiles <-> packed fp32 parameters (W1 [D][Hd] | W3 [D][Hd] | W2 [Hd][D]).
@@ -309,20 +316,24 @@ swiglu_loop_kernel(LoopArgs a) {
         const u32x4 vrs = buffer_rsrc(vbase, (unsigned)(T * D * 2));
         const u32x4 crs = buffer_rsrc(cMb, cw_rel + (unsigned)(a.ldc * 4));
         const unsigned kvs_lds = lds_addr(kvs);
-        auto issue_block = [&](int X) {
+        // (kv / coef: which parts; the folded scan copies a block's
+        // coefficients only once it has written them)
+        auto issue_block = [&](int X, bool kv = true, bool coef = true) {
             // per-lane offsets recomputed here rather than kept in registers
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const unsigned dst = kvs_lds + (unsigned)((X % NBUF) * KVBUF);
             const unsigned tb = (unsigned)X * CB * D * 2;
+            if (kv) {
 #pragma unroll
-            for (int i = 0; i < RPW / 4; ++i) {
-                const int row = RPW * u + 4 * i + (ln >> 4);
-                const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
-                copy16(krs, dst + (RPW * u + 4 * i) * 256, ko);
-                copy16(vrs, dst + KVB + (RPW * u + 4 * i) * 256, ko);
+                for (int i = 0; i < RPW / 4; ++i) {
+                    const int row = RPW * u + 4 * i + (ln >> 4);
+                    const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
+                    copy16(krs, dst + (RPW * u + 4 * i) * 256, ko);
+                    copy16(vrs, dst + KVB + (RPW * u + 4 * i) * 256, ko);
+                }
             }
-            if (u == 0) {
+            if (coef && u == 0) {
                 const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
                 copy16(crs, dst + 2 * KVB, coff + (unsigned)X * CB * 4);
             }
@@ -340,8 +351,10 @@ swiglu_loop_kernel(LoopArgs a) {
             }
         };
 
-        issue_block(0);
-        if (nblk > 1) issue_block(1);
+        const bool fold = a.fold != 0;
+        issue_block(0, true, !fold);
+        if (nblk > 1) issue_block(1, true, !fold);
+        if (fold) slot_barrier();  // the gradient waves' gate loads are out
         f32x4 acc[3][2][8];
         state_io<false, MOM, 8>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd);
 
@@ -517,6 +530,11 @@ swiglu_loop_kernel(LoopArgs a) {
         // (Nested loops with unconditional state updates keep every state tile
         // in one register tuple for the whole sequence.)
         grad_operands(0);
+        if (fold) {
+            slot_barrier();  // the gradient waves have written every chunk's coefficients
+            issue_block(0, false, true);  // blocks 0 and 1's, landing beside the momentum loads
+            if (nblk > 1) issue_block(1, false, true);
+        }
         wait_vm<0>();  // blocks 0 and 1 have landed
         slot_barrier();
         for (int c = 0;; ++c) {
@@ -652,6 +670,31 @@ swiglu_loop_kernel(LoopArgs a) {
                     *(bf16x8*)(snap + (snap_lane + (unsigned)((f >> 2) * Hd * D + 32 * (f & 3)) * 2u)) = wb[f >> 2][f & 3];
             __builtin_amdgcn_sched_barrier(0);
         };
+        // The folded scan: while the state waves load the state, gradient wave
+        // u computes the scalar kernels of chunks u, u + UG, ... of its head
+        // (every slice of the head writes the same values), then waits for its
+        // stores, so that the state waves' coefficient copies after the next
+        // barrier and the rescales read them.
+        // Its gate loads (at most two chunks a wave; the launcher takes one)
+        // go out before the state
+        // waves start the state load (the first barrier), so that they do not
+        // queue behind it.
+        if (a.fold) {
+            const int npl = (a.C + 63) / 64, nm = MOM ? 0 : 1;
+            scan::Gates<4> g0, g1;
+            const int c0 = u, c1 = u + UG;
+            if (c0 < nc) scan::load_gates<1, 4>(lane, 0, bh, c0, T, a.C, npl, nm, a.eta, a.alpha, a.beta, g0);
+            if (c1 < nc) scan::load_gates<1, 4>(lane, 0, bh, c1, T, a.C, npl, nm, a.eta, a.alpha, a.beta, g1);
+            slot_barrier();
+            if (c0 < nc)
+                scan::scan_chunk_from<1, 4>(lane, 0, bh, c0, nc, T, a.C, npl, nm, a.avg, g0, a.beta, (float*)a.cM,
+                                            (float*)a.cW, a.ldc, (float*)a.scal, nullptr);
+            if (c1 < nc)
+                scan::scan_chunk_from<1, 4>(lane, 0, bh, c1, nc, T, a.C, npl, nm, a.avg, g1, a.beta, (float*)a.cM,
+                                            (float*)a.cW, a.ldc, (float*)a.scal, nullptr);
+            wait_vm<0>();
+            slot_barrier();
+        }
         // Slots as in the state waves' loop.  The grad MFMAs of the next
         // half-block are issued before the backward of the current one, so they
         // run in the MFMA pipe while the backward runs on the VALU; only a
@@ -1078,11 +1121,37 @@ static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
     return BH * (Hd / 32) <= ncu ? 2 : 4;
 }
 
+// Whether the chunk loop computes the scalar kernels itself (see the
+// gradient waves' prologue): the 64-unit kernel, chunks of at most 256 tokens
+// (one wavefront per chunk) and at most one chunk per gradient wavefront.
+// That is a streaming call of one or a few chunks, where the separate scan
+// launch is a large share of the call.  With more chunks per wavefront the
+// folded scan costs the loop about what the launch costs (1.3B-shaped
+// workload, 8 chunks of 256 tokens, two per wavefront: call time equal within
+// noise, loop 4 us longer).
+bool swiglu_loop_scans(const e2ttt_desc& d) {
+    int ncu = 0;
+    if (device_cu_count(&ncu) != hipSuccess) return false;
+    const bool pre = (d.flags & E2TTT_FLAG_PRECISE) != 0;
+    const int ug = pre ? 2 : loop_unit_groups(d.B * d.H, d.Hd, ncu);
+    if (!pre && ug <= 2) return false;  // the block-slot kernel
+    const int64_t nc = (d.T + d.chunk - 1) / d.chunk;
+    return d.chunk <= 256 && nc >= 1 && nc <= ug;
+}
+
 hipError_t launch_swiglu_loop(const e2ttt_desc& d, const void* k, const void* v, const float* cM, const float* cW,
                               int64_t ldc, const float* scal, const float* W0, const float* M0, float* W_end, float* M_end,
-                              void* snap, void* snapM, hipStream_t s) {
+                              void* snap, void* snapM, hipStream_t s, const float* eta, const float* alpha,
+                              const float* beta, bool fold) {
     const int64_t BH = d.B * d.H;
     LoopArgs la;
+    la.eta = eta;
+    la.alpha = alpha;
+    la.beta = beta;
+    la.fold = fold ? 1 : 0;
+    la.avg = (d.flags & E2TTT_FLAG_CHUNK_AVG) ? 1 : 0;
+    if (fold && (!eta || !alpha || (!(d.flags & E2TTT_FLAG_NO_MOMENTUM) && !beta) || !swiglu_loop_scans(d)))
+        return hipErrorInvalidValue;
     la.k = (const __bf16*)k;
     la.v = (const __bf16*)v;
     la.cM = cM;

@@ -141,6 +141,48 @@ def test_streaming_chunk_by_chunk(name, momentum):
         assert torch.equal(M, full[2])
 
 
+@pytest.mark.parametrize("flags", [0, 2, 4])
+def test_streaming_folded_scan(flags):
+    """Streaming on a grid of 64-unit slices (B=8, H=16): a call of one
+    256-token chunk takes the chunk loop that computes the scalar kernels in
+    its own prologue, a call of five chunks takes the separate scan launch.
+    One chunk per call (the last a ragged remainder), state carried, equals
+    the single call bit for bit: with momentum, without (flags 2) and with
+    chunk-averaged kernels (flags 4)."""
+    e2 = _e2()
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(T=4 * 256 + 128 + 5, flags=flags)
+    momentum, avg = not (flags & 2), bool(flags & 4)
+    gu.note(f"streaming, folded scan, B=8 H=16 T={cfg.T} flags={flags}")
+    x = gu.to_dev(synth.make_inputs(cfg, seed=21, m0_scale=0.5 if momentum else 0.0))
+    kw = dict(chunk=cfg.chunk, kind=cfg.kind, loss=cfg.loss, Hd=cfg.Hd, momentum=momentum, chunk_avg=avg)
+    full = e2.chunk_forward(x["q"], x["k"], x["v"], x["eta"], x["alpha"], x["beta"], x["W0"], x["M0"], **kw)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    W, M, outs = x["W0"], x["M0"], []
+    for t0 in range(0, cfg.T, cfg.chunk):
+        t1 = min(t0 + cfg.chunk, cfg.T)
+        o, W, M = e2.chunk_forward(*(sl(x[n], t0, t1) for n in ("q", "k", "v", "eta", "alpha", "beta")), W, M,
+                                   **kw)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), full[0])
+    assert torch.equal(W, full[1])
+    if momentum:
+        assert torch.equal(M, full[2])
+
+
+def test_folded_scan_single_chunk_oracle():
+    """One 256-token chunk of the 1.3B-shaped layer (B=8, H=16, the streaming
+    workload's call, scalar kernels computed inside the chunk loop) against
+    the oracle on every head."""
+    e2 = _e2()
+    cfg = synth.CONFIGS["swiglu_1p3b"].with_(name="folded1", T=256)
+    gu.note("folded scan, one chunk, B=8 H=16 T=256")
+    x = synth.make_inputs(cfg, seed=22, m0_scale=0.5)
+    assert e2.path(cfg.kind, cfg.loss, cfg.io_dtype, cfg.B, cfg.H, cfg.T, cfg.D, cfg.Hd, cfg.chunk) == 1
+    got = gu.run_gpu(cfg, x)
+    gu.assert_close(cfg, got, gu.run_oracle(cfg, x), x["W0"].numpy())
+
+
 @pytest.mark.parametrize("name,momentum", [("swiglu_1p3b", True), ("swiglu_1p3b", False), ("mlp_fp32", True)])
 def test_streaming_matches_oracle(name, momentum):
     """Streaming against the oracle directly: the sequence arrives one chunk
