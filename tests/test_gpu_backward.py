@@ -202,13 +202,17 @@ def test_backward_rejects_aliased_output():
     assert st == 3
 
 
-@pytest.mark.parametrize("case", ["swiglu_mfma", "swiglu_mfma_c64", "swiglu_nomom", "mlp_portable", "linear_portable"])
+@pytest.mark.parametrize("case", ["swiglu_mfma", "swiglu_mfma_c64", "swiglu_nomom", "swiglu_folded", "mlp_portable",
+                                  "linear_portable"])
 def test_backward_from_saved_forward_states(case):
     """chunk_forward(save_states=True) then chunk_backward(saved=True) on one
     shared workspace gives the recomputing backward's result bit for bit."""
     import chunk_weight_rnn_amd as e2
     cfg = {"swiglu_mfma": SMALL, "swiglu_nomom": SMALL.with_(flags=2),
            "swiglu_mfma_c64": SMALL.with_(chunk=64),  # short chunks: the gradient waves store the snapshots
+           # 64-unit slices, one chunk per gradient wave: the saving forward's chunk
+           # loop computes the scalar kernels itself, the recompute launches the scan
+           "swiglu_folded": SMALL.with_(B=8, H=16, T=448, Hd=256, chunk=256),
            "mlp_portable": synth.Config("saved_mlp", "mlp", "mse", 1, 2, 80, 16, 24, 32, "f32", ""),
            "linear_portable": synth.Config("saved_lin", "linear", "negdot", 1, 2, 80, 16, 0, 32, "f32", "")}[case]
     note(f"case saved {case}")
