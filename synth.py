@@ -107,6 +107,9 @@ CONFIGS = {
     # streaming: one 256-token chunk per call, state carried in from the previous call
     "swiglu_1p3b_stream": Config("swiglu_1p3b_stream", "swiglu", "negdot", 8, 16, 256, 128, 256, 256, "bf16",
                                  "1.3B-shaped TTT branch, streaming: one chunk per call"),
+    # the 16K extrapolation sequence streamed one chunk per call (one row)
+    "swiglu_16k_stream": Config("swiglu_16k_stream", "swiglu", "negdot", 1, 16, 256, 128, 256, 256, "bf16",
+                                "1.3B-shaped TTT branch, 16K sequence streamed: one chunk of one row per call"),
     # a ragged sequence: 7 whole chunks and a 208-token tail
     "swiglu_1p3b_tail": Config("swiglu_1p3b_tail", "swiglu", "negdot", 8, 16, 2000, 128, 256, 256, "bf16",
                                "1.3B-shaped TTT branch, T = 7 x 256 + 208"),
