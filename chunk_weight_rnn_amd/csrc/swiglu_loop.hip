@@ -845,19 +845,22 @@ swiglu_loop_bs_kernel(LoopArgs a) {
         // rows RPW cw .. + RPW - 1 of block X's K and V (rows past T read as
         // zeros), and copy wave 0 the block's coefficients: 2 RPW / 4 copies,
         // one more for copy wave 0
-        auto issue_block = [&](int X) {
+        // (kv / coef: which parts, as in the 64-unit kernel)
+        auto issue_block = [&](int X, bool kv = true, bool coef = true) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const unsigned dst = kvs_lds + (unsigned)((X % NB) * KVBUF);
             const unsigned tb = (unsigned)X * CB * D * 2;
+            if (kv) {
 #pragma unroll
-            for (int i = 0; i < RPW / 4; ++i) {
-                const int row = RPW * cw + 4 * i + (ln >> 4);
-                const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
-                copy16(krs, dst + (RPW * cw + 4 * i) * 256, ko);
-                copy16(vrs, dst + KVB + (RPW * cw + 4 * i) * 256, ko);
+                for (int i = 0; i < RPW / 4; ++i) {
+                    const int row = RPW * cw + 4 * i + (ln >> 4);
+                    const unsigned ko = (unsigned)(row * D + 8 * ((ln & 15) ^ swz4(row))) * 2u + tb;
+                    copy16(krs, dst + (RPW * cw + 4 * i) * 256, ko);
+                    copy16(vrs, dst + KVB + (RPW * cw + 4 * i) * 256, ko);
+                }
             }
-            if (cw == 0) {
+            if (coef && cw == 0) {
                 const unsigned coff = ln < 16 ? 16u * ln : ln < 32 ? cw_rel + 16u * (ln - 16) : 16u * (ln - 32);
                 copy16(crs, dst + 2 * KVB, coff + (unsigned)X * CB * 4);
             }
@@ -882,8 +885,12 @@ swiglu_loop_bs_kernel(LoopArgs a) {
                 wait_vm<0>();
         };
 
-        issue_block(0);
-        if (LEAD == 2 && nblk > 1) issue_block(1);
+        // With the folded scan (see the gradient waves): the coefficients of
+        // blocks 0 and 1 are copied once the scan has written them.
+        const bool fold = a.fold != 0;
+        issue_block(0, true, !fold);
+        if (LEAD == 2 && nblk > 1) issue_block(1, true, !fold);
+        if (fold) slot_barrier();  // the gradient waves' gate loads are out
         f32x4 acc[3][2][2];
         state_io<false, MOM, 2>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd, 2 * hf);
 
@@ -993,10 +1000,16 @@ swiglu_loop_bs_kernel(LoopArgs a) {
         };
 
         operands(0);
-        if (LEAD == 2 && nblk > 1)
+        if (fold) {
+            slot_barrier();  // the scan's coefficients are written
+            issue_block(0, false, true);
+            if (LEAD == 2 && nblk > 1) issue_block(1, false, true);
+            wait_vm<0>();  // blocks 0 and 1 with their coefficients have landed
+        } else if (LEAD == 2 && nblk > 1) {
             wait_all_but_block();  // block 0 has landed
-        else
+        } else {
             wait_vm<0>();
+        }
         slot_barrier();
         // (nested loops with unconditional state updates keep every state
         // tile in one register tuple for the whole sequence)
@@ -1078,6 +1091,22 @@ swiglu_loop_bs_kernel(LoopArgs a) {
                 put(2, fu, false);
             }
         };
+        // The folded scan (calls of at most four chunks): gradient wave ti of
+        // unit group 0 computes chunk ti's scalar kernels while the state
+        // waves load the state, its gate loads issued before that load, as in
+        // the 64-unit kernel (every slice of the head writes the same values).
+        if (a.fold) {
+            const int npl = (a.C + 63) / 64, nm = MOM ? 0 : 1;
+            const bool mine = u == 0 && ti < nc;
+            scan::Gates<4> gt;
+            if (mine) scan::load_gates<1, 4>(lane, 0, bh, ti, T, a.C, npl, nm, a.eta, a.alpha, a.beta, gt);
+            slot_barrier();
+            if (mine)
+                scan::scan_chunk_from<1, 4>(lane, 0, bh, ti, nc, T, a.C, npl, nm, a.avg, gt, a.beta, (float*)a.cM,
+                                            (float*)a.cW, a.ldc, (float*)a.scal, nullptr);
+            wait_vm<0>();
+            slot_barrier();
+        }
         slot_barrier();
         for (int c = 0; c < nc; ++c) {
             const unsigned char* const od = opnd(c);
@@ -1122,8 +1151,9 @@ static int loop_unit_groups(int64_t BH, int64_t Hd, int ncu) {
 }
 
 // Whether the chunk loop computes the scalar kernels itself (see the
-// gradient waves' prologue): the 64-unit kernel, chunks of at most 256 tokens
-// (one wavefront per chunk) and at most one chunk per gradient wavefront.
+// gradient waves' prologue): chunks of at most 256 tokens (one wavefront per
+// chunk) and at most one chunk per gradient wavefront (of unit group 0 in the
+// block-slot kernel).
 // That is a streaming call of one or a few chunks, where the separate scan
 // launch is a large share of the call.  With more chunks per wavefront the
 // folded scan costs the loop about what the launch costs (1.3B-shaped
@@ -1134,8 +1164,8 @@ bool swiglu_loop_scans(const e2ttt_desc& d) {
     if (device_cu_count(&ncu) != hipSuccess) return false;
     const bool pre = (d.flags & E2TTT_FLAG_PRECISE) != 0;
     const int ug = pre ? 2 : loop_unit_groups(d.B * d.H, d.Hd, ncu);
-    if (!pre && ug <= 2) return false;  // the block-slot kernel
     const int64_t nc = (d.T + d.chunk - 1) / d.chunk;
+    if (!pre && ug <= 2) return d.chunk <= 256 && nc >= 1 && nc <= 4;  // the block-slot kernel: group 0's 4 waves
     return d.chunk <= 256 && nc >= 1 && nc <= ug;
 }
 
