@@ -200,7 +200,7 @@ struct LoopArgs {
 // NT tiles from tile t0 on (a state wave that holds only some rows of d).
 template <bool STORE, bool MOM, int NT>
 __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][NT], float* W, float* M, int64_t j, int g, int Hd,
-                                         int t0 = 0) {
+                                         int t0 = 0, int part = 3) {
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
 #pragma unroll
@@ -214,8 +214,8 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][NT], float* W, float
                         if (MOM) M[o + r * Hd] = acc[m][0][i][r];
                         W[o + r * Hd] = acc[m][1][i][r];
                     } else {
-                        acc[m][0][i][r] = MOM ? M[o + r * Hd] : 0.f;
-                        acc[m][1][i][r] = W[o + r * Hd];
+                        if (part & 2) acc[m][0][i][r] = MOM ? M[o + r * Hd] : 0.f;
+                        if (part & 1) acc[m][1][i][r] = W[o + r * Hd];
                     }
                 }
             } else {
@@ -224,8 +224,8 @@ __device__ __forceinline__ void state_io(f32x4 (&acc)[3][2][NT], float* W, float
                     if (MOM) *(f32x4*)&M[o] = acc[m][0][i];
                     *(f32x4*)&W[o] = acc[m][1][i];
                 } else {
-                    acc[m][0][i] = MOM ? *(const f32x4*)&M[o] : f32x4{0.f, 0.f, 0.f, 0.f};
-                    acc[m][1][i] = *(const f32x4*)&W[o];
+                    if (part & 2) acc[m][0][i] = MOM ? *(const f32x4*)&M[o] : f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (part & 1) acc[m][1][i] = *(const f32x4*)&W[o];
                 }
             }
         }
@@ -355,8 +355,12 @@ swiglu_loop_kernel(LoopArgs a) {
         issue_block(0, true, !fold);
         if (nblk > 1) issue_block(1, true, !fold);
         if (fold) slot_barrier();  // the gradient waves' gate loads are out
+        // The chunk-start W first, then M: the hand-over below waits only for
+        // W (loads complete in order), and M lands during the first slot,
+        // where these waves only rescale while the gradient waves start.
         f32x4 acc[3][2][8];
-        state_io<false, MOM, 8>(acc, (float*)a.W0 + bh * P, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd);
+        state_io<false, MOM, 8>(acc, (float*)a.W0 + bh * P, nullptr, j, g, Hd, 0, 1);
+        state_io<false, MOM, 8>(acc, nullptr, MOM ? (float*)a.M0 + bh * P : nullptr, j, g, Hd, 0, 2);
 
         // chunk-start weights -> grad operands (exchange area) + bf16 snapshot
         // (with SPREAD the gradient waves store the snapshot instead)
@@ -529,13 +533,13 @@ swiglu_loop_kernel(LoopArgs a) {
         // extra slot, which also hands over the next chunk's grad operands.
         // (Nested loops with unconditional state updates keep every state tile
         // in one register tuple for the whole sequence.)
-        grad_operands(0);
+        grad_operands(0);  // (its reads of W have waited for blocks 0 and 1's copies, issued before)
         if (fold) {
             slot_barrier();  // the gradient waves have written every chunk's coefficients
             issue_block(0, false, true);  // blocks 0 and 1's, landing beside the momentum loads
             if (nblk > 1) issue_block(1, false, true);
+            wait_vm<0>();  // and have landed
         }
-        wait_vm<0>();  // blocks 0 and 1 have landed
         slot_barrier();
         for (int c = 0;; ++c) {
             rescale(c);
