@@ -185,10 +185,10 @@ struct LoopArgs {
     int64_t T;
     int64_t ldc;  // row stride of cM / cW (T rounded up to a whole block, zero padded)
     int Hd, C, nc, nsl, nwg, xcd_map;
-    // fold: the 64-unit kernel computes the scalar kernels itself (cM, cW,
-    // scal from eta, alpha, beta) before its first slot, instead of a separate
-    // scan launch before it (two more workgroup barriers); avg:
-    // chunk-averaged kernels
+    // fold: the chunk loop computes the scalar kernels itself (cM, cW, scal
+    // from eta, alpha, beta) before its first slot, instead of a separate scan
+    // launch before it (two more workgroup barriers); avg: chunk-averaged
+    // kernels
     const float *eta, *alpha, *beta;
     int fold, avg;
 };
@@ -675,14 +675,13 @@ swiglu_loop_kernel(LoopArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         };
         // The folded scan: while the state waves load the state, gradient wave
-        // u computes the scalar kernels of chunks u, u + UG, ... of its head
-        // (every slice of the head writes the same values), then waits for its
-        // stores, so that the state waves' coefficient copies after the next
-        // barrier and the rescales read them.
-        // Its gate loads (at most two chunks a wave; the launcher takes one)
-        // go out before the state
-        // waves start the state load (the first barrier), so that they do not
-        // queue behind it.
+        // u computes the scalar kernels of chunks u and u + UG of its head (the
+        // launcher folds only calls of at most UG chunks; every slice of the
+        // head writes the same values), then waits for its stores, so that the
+        // state waves' coefficient copies after the next barrier and the
+        // rescales read them.  Its gate loads go out before the state waves
+        // start the state load (the first barrier), so that they do not queue
+        // behind it.
         if (a.fold) {
             const int npl = (a.C + 63) / 64, nm = MOM ? 0 : 1;
             scan::Gates<4> g0, g1;
