@@ -20,7 +20,7 @@ NB = 4  # LDS token blocks
 CB = 64  # tokens per block
 
 
-def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB):
+def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB, fold=False, grad_fold_barriers=2):
     nblk = (T + CB - 1) // CB
     nbc = C // CB
     nc = (T + C - 1) // C
@@ -46,11 +46,27 @@ def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB):
         reads.append((slot, X, role))
 
     # state waves
-    for X in range(min(lead, nblk)):
-        issue(X)
-    ops.extend([("store",)] * stores_per_handover)
-    wait(copies_per_block * (min(lead, nblk) - 1))
-    bar_state, slot = 1, 0
+    bar_state = 0
+    if fold:
+        # the scalar kernels computed in the prologue: the token rows of the
+        # first blocks go out first, their coefficients (one copy of the copy
+        # wave) only after the gradient waves have written them (barrier after
+        # the gate loads, barrier after the scan), then every copy is waited for
+        for X in range(min(lead, nblk)):
+            owner[X % nb] = X
+            ops.extend([("copy", X)] * (copies_per_block - 1))
+        bar_state += 1
+        ops.extend([("store",)] * stores_per_handover)
+        bar_state += 1
+        for X in range(min(lead, nblk)):
+            ops.append(("copy", X))
+        wait(0)
+    else:
+        for X in range(min(lead, nblk)):
+            issue(X)
+        ops.extend([("store",)] * stores_per_handover)
+        wait(copies_per_block * (min(lead, nblk) - 1))
+    bar_state, slot = bar_state + 1, 0
     for c in itertools.count():
         X0, n = c * nbc, blocks[c]
         bar_state += 1  # the chunk's start barrier
@@ -73,7 +89,7 @@ def schedule(T, C, copies_per_block, stores_per_handover, lead=2, nb=NB):
             break
         ops.extend([("store",)] * stores_per_handover)
         bar_state += 1
-    bar_grad = 1 + sum(1 + n for n in blocks) + (nc - 1)
+    bar_grad = 1 + sum(1 + n for n in blocks) + (nc - 1) + (grad_fold_barriers if fold else 0)
     return nblk, bar_state, bar_grad, reads, fsets
 
 
@@ -99,6 +115,23 @@ def test_block_slot_schedule(C, lead, nb, copies):
                 s_w = grad[X]
                 assert not any(k == "w" and st == fs and s_w < s <= s_r and Y != X
                                for s, st, k, Y in fsets), (T, C, X)
+
+
+@pytest.mark.parametrize("C", [64, 128, 192, 256])
+@pytest.mark.parametrize("lead,nb,copies", [(2, 4, 9), (1, 3, 5)])
+def test_block_slot_schedule_folded_scan(C, lead, nb, copies):
+    """Calls of at most four chunks, whose prologue computes the scalar
+    kernels: the same barrier counts on both roles (two more each), every
+    block landed before its first read, with the coefficients of the first
+    blocks copied after the scan."""
+    for T in range(1, 4 * C + 1):
+        nblk, bs, bg, reads, _ = schedule(T, C, copies, 3, lead=lead, nb=nb, fold=True)
+        assert bs == bg, (T, C)
+        grad = {X: s for s, X, r in reads if r == "grad"}
+        assert sorted(grad) == list(range(nblk)), (T, C)
+    # a gradient-wave prologue with one barrier fewer than the state waves' is caught
+    _, bs, bg, _, _ = schedule(C, C, copies, 3, lead=lead, nb=nb, fold=True, grad_fold_barriers=1)
+    assert bs != bg
 
 
 def test_schedule_model_catches_an_overwrite():
