@@ -400,18 +400,30 @@ swiglu_loop_kernel(LoopArgs a) {
                         *(bf16x8*)(xw + (12 + 4 * m + kk) * 1024 + xl) = l8;
                     }
                     if (!SPREAD) *(bf16x8*)(snap + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = w8;
-                    if (SAVEM) {
-                        unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
-                        const bf16x4 s0 = pack4(acc[m][0][2 * kk]), s1 = pack4(acc[m][0][2 * kk + 1]);
-                        const bf16x4 mlo = godd ? s1 : s0, mhi = godd ? s0 : s1;
-                        bf16x8 m8;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        // SAVEM: the bf16 snapshot of chunk c's start momentum, stored in the
+        // chunk's first slot before its rescale (not with the grad operands,
+        // so that the first hand-over waits for W only)
+        auto momentum_snapshot = [&](int c) {
+            unsigned char* snapm = (unsigned char*)(a.snapM + (bh * nc + c) * P);
+            unsigned snap_lane = (unsigned)(j * D + 8 * g) * 2u;
+            asm volatile("" : "+v"(snap_lane));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            m8[e] = mlo[e];
-                            m8[4 + e] = mhi[e];
-                        }
-                        *(bf16x8*)(snapm + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = m8;
+            for (int m = 0; m < 3; ++m) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x4 s0 = pack4(acc[m][0][2 * kk]), s1 = pack4(acc[m][0][2 * kk + 1]);
+                    const bf16x4 mlo = godd ? s1 : s0, mhi = godd ? s0 : s1;
+                    bf16x8 m8;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        m8[e] = mlo[e];
+                        m8[4 + e] = mhi[e];
                     }
+                    *(bf16x8*)(snapm + (snap_lane + (unsigned)(m * Hd * D + 32 * kk) * 2u)) = m8;
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -542,6 +554,7 @@ swiglu_loop_kernel(LoopArgs a) {
         }
         slot_barrier();
         for (int c = 0;; ++c) {
+            if (SAVEM) momentum_snapshot(c);
             rescale(c);
             copy_step(c * nh);
             slot_barrier();
